@@ -1,0 +1,479 @@
+"""Pins of the fp64 oracle against facts that do not come from the oracle.
+
+Each test names the pin it implements: hand-derived values (tests/golden),
+brute force on tiny inputs written here with plain loops, textbook library
+routines, exact algebraic identities, closed forms and invariants. A dropped
+term, a wrong sign or index, or a transposed operand anywhere in the oracle
+fails at least one of them.
+"""
+import json
+import math
+import os
+
+import numpy as np
+import pytest
+import scipy.special
+
+from oracle import sparsepr_oracle as orc
+from free_block_sparse_rcp_amd import configs, inputs
+
+GOLD = json.load(open(os.path.join(os.path.dirname(__file__), "golden", "hand_cases.json")))
+
+
+# ---------------------------------------------------------------- helpers
+
+def tiny_case(n=48, d=6, seed=0, n_clusters=4):
+    """Generic (tie-free) tiny inputs with some cluster structure."""
+    rng = np.random.default_rng(seed)
+    mu = rng.standard_normal((n_clusters, d)) * 1.5
+    lab = rng.integers(0, n_clusters, n)
+    Q = mu[lab] + 0.6 * rng.standard_normal((n, d))
+    K = mu[lab] + 0.6 * rng.standard_normal((n, d))
+    V = rng.standard_normal((n, d))
+    return Q, K, V
+
+
+def run_head(Q, K, V, scale=0.7, n_samples=12, **kw):
+    n = Q.shape[0]
+    rng = np.random.default_rng(123)
+    args = dict(q_block=8, n_groups=6, kmeans_iters=4, density=0.5, n_probes=5, rank=3,
+                ridge_lambda=1e-3)
+    args.update(kw)
+    sample_idx = rng.choice(n, n_samples, replace=False)
+    init_idx = rng.choice(n, args["n_groups"], replace=False)
+    res = orc.sparsepr_head(Q, K, V, scale, sample_idx=sample_idx, init_idx=init_idx, **args)
+    return res, sample_idx, init_idx
+
+
+# ------------------------------------------------------ golden hand cases
+
+def test_golden_probe_positions():
+    for c in GOLD["probe_positions"]:
+        got = orc.probe_positions(c["N"], c["m"])
+        if "expected" in c:
+            assert got.tolist() == c["expected"]
+        else:
+            assert got[:3].tolist() == c["expected_first"] and got[-1] == c["expected_last"]
+
+
+def test_golden_key_budget():
+    for c in GOLD["key_budget"]:
+        assert orc.key_budget(c["N"], c["rho"], c["m"]) == c["expected"]
+
+
+def test_golden_probe_weights():
+    for c in GOLD["probe_weights"]:
+        np.testing.assert_allclose(orc.probe_weights(np.array(c["O_probe"])), c["expected"],
+                                   rtol=0, atol=1e-15)
+
+
+def test_golden_select_groups():
+    for c in GOLD["select_groups"]:
+        got = orc.select_groups(np.array(c["sigma"]), np.array(c["sizes"]), c["kappa"])
+        assert got.tolist() == c["expected"]
+
+
+def test_golden_attention():
+    for c in GOLD["attention"]:
+        out, lse = orc.softmax_attention(np.array(c["q"]), np.array(c["K"]), np.array(c["V"]),
+                                         c["scale"])
+        np.testing.assert_allclose(out, c["expected_out"], atol=1e-15)
+        np.testing.assert_allclose(lse, c["expected_lse"], atol=1e-15)
+
+
+def test_golden_kmeans():
+    for c in GOLD["kmeans"]:
+        r = orc.kmeans(np.array(c["X"]), c["init_idx"], c["iters"])
+        assert r.labels.tolist() == c["expected_labels"]
+        np.testing.assert_allclose(r.centroids, c["expected_centroids"], atol=1e-15)
+
+
+def test_golden_relative_l2():
+    for c in GOLD["relative_l2"]:
+        np.testing.assert_allclose(orc.relative_l2_rows(np.array(c["O"]), np.array(c["ref"])),
+                                   c["expected"], atol=1e-15)
+
+
+# ------------------------------------------------ P5 brute force, tiny inputs
+
+def brute_attention(q, Ks, Vs, scale):
+    out = []
+    lses = []
+    for qi in q:
+        logits = [scale * sum(qi[t] * kj[t] for t in range(len(qi))) for kj in Ks]
+        mx = max(logits)
+        ws = [math.exp(x - mx) for x in logits]
+        z = sum(ws)
+        out.append([sum(ws[j] * Vs[j][t] for j in range(len(Ks))) / z for t in range(len(Vs[0]))])
+        lses.append(mx + math.log(z))
+    return np.array(out), np.array(lses)
+
+
+def brute_kmeans(Q, K, scale, sample_idx, init_idx, iters):
+    n = len(K)
+    prof = [[scale * sum(Q[s][t] * K[j][t] for t in range(len(K[j]))) for s in sample_idx]
+            for j in range(n)]
+    cents = [list(prof[i]) for i in init_idx]
+    labels = [0] * n
+    for _ in range(iters):
+        for j in range(n):
+            best, bestg = None, -1
+            for g, c in enumerate(cents):
+                dist = sum((prof[j][s] - c[s]) ** 2 for s in range(len(c)))
+                if best is None or dist < best:
+                    best, bestg = dist, g
+            labels[j] = bestg
+        for g in range(len(cents)):
+            mem = [j for j in range(n) if labels[j] == g]
+            if mem:
+                cents[g] = [sum(prof[j][s] for j in mem) / len(mem) for s in range(len(cents[g]))]
+    return np.array(labels), np.array(cents)
+
+
+def test_p5_brute_attention():
+    Q, K, V = tiny_case(n=20, d=5, seed=3)
+    out, lse = orc.softmax_attention(Q[:7], K, V, 0.9)
+    bo, bl = brute_attention(Q[:7].tolist(), K.tolist(), V.tolist(), 0.9)
+    np.testing.assert_allclose(out, bo, rtol=0, atol=1e-13)
+    np.testing.assert_allclose(lse, bl, rtol=0, atol=1e-13)
+
+
+def test_p5_brute_kmeans_on_responses():
+    Q, K, V = tiny_case(n=30, d=4, seed=5)
+    rng = np.random.default_rng(1)
+    sidx = rng.choice(30, 7, replace=False)
+    iidx = rng.choice(30, 5, replace=False)
+    R = orc.key_responses(Q, K, 0.8, sidx)
+    km = orc.kmeans(R, iidx, 4)
+    bl, bc = brute_kmeans(Q.tolist(), K.tolist(), 0.8, sidx, iidx, 4)
+    assert km.labels.tolist() == bl.tolist()
+    np.testing.assert_allclose(km.centroids, bc, rtol=0, atol=1e-12)
+
+
+def test_p5_brute_full_head():
+    """The whole routing path by enumeration: groups, query order, blocks,
+    selection, density by counting mask entries, sparse output by loops."""
+    Q, K, V = tiny_case(n=40, d=5, seed=7)
+    scale = 0.6
+    res, sidx, iidx = run_head(Q, K, V, scale, q_block=8, n_groups=5, kmeans_iters=3,
+                               density=0.45, n_probes=4, rank=2)
+    n, G = 40, 5
+    labels, _ = brute_kmeans(Q.tolist(), K.tolist(), scale, sidx, iidx, 3)
+    assert res.labels.tolist() == labels.tolist()
+    members = [[j for j in range(n) if labels[j] == g] for g in range(G)]
+    kbar = [np.mean(K[m], axis=0) if m else None for m in members]
+    coords = [[scale * float(np.dot(Q[q], kbar[g])) if members[g] else -np.inf for g in range(G)]
+              for q in range(n)]
+    g1 = []
+    for q in range(n):
+        best = max(range(G), key=lambda g: (coords[q][g], -g))
+        g1.append(best)
+    v = [coords[q][g1[q]] for q in range(n)]
+    order = sorted(range(n), key=lambda q: (g1[q], -v[q], q))
+    assert res.query_perm.tolist() == order
+    kappa = math.floor(0.45 * n - 4)
+    mask = np.zeros((n, n), bool)
+    S = np.zeros((n, 5))
+    for b0 in range(0, n, 8):
+        blk = order[b0:b0 + 8]
+        sig = [np.mean([coords[q][g] for q in blk]) if members[g] else None for g in range(G)]
+        ranked = sorted([g for g in range(G) if members[g]], key=lambda g: (-sig[g], g))
+        chosen, tot = [], 0
+        for g in ranked:
+            if tot + len(members[g]) > kappa:
+                break
+            chosen.append(g)
+            tot += len(members[g])
+        if not chosen:
+            chosen = ranked[:1]
+        keys = [j for g in sorted(chosen) for j in members[g]]
+        for q in blk:
+            mask[q, keys] = True
+        bo, _ = brute_attention(Q[blk].tolist(), K[keys].tolist(), V[keys].tolist(), scale)
+        S[blk] = bo
+    E = int(mask.sum()) + 4 * n
+    assert res.executed_pairs == E
+    np.testing.assert_allclose(res.S, S, rtol=0, atol=1e-13)
+
+
+# ---------------------------------------------- P6 library reductions
+
+def test_p6_sparse_equals_masked_dense_softmax():
+    Q, K, V = tiny_case(n=48, d=6, seed=11)
+    res, _, _ = run_head(Q, K, V, 0.7)
+    n = 48
+    logits = 0.7 * Q @ K.T
+    mask = np.full((n, n), -np.inf)
+    for blk, ks in zip(res.blocks, res.key_sets):
+        for q in blk:
+            mask[q, ks] = 0.0
+    P = scipy.special.softmax(logits + mask, axis=1)
+    np.testing.assert_allclose(res.S, P @ V, rtol=0, atol=1e-12)
+    np.testing.assert_allclose(res.lse, scipy.special.logsumexp(logits + mask, axis=1),
+                               rtol=0, atol=1e-12)
+
+
+def test_p6_subspace_equals_svd():
+    rng = np.random.default_rng(2)
+    R = rng.standard_normal((20, 8)) @ np.diag([5, 4, 3, 2, 1, .5, .2, .1])
+    w = rng.random(20)
+    w /= w.sum()
+    U, ev = orc.residual_subspace(R, w, 3)
+    _, s, vt = np.linalg.svd(np.sqrt(w)[:, None] * R)
+    P1 = U @ U.T
+    P2 = vt[:3].T @ vt[:3]
+    np.testing.assert_allclose(P1, P2, rtol=0, atol=1e-10)
+    np.testing.assert_allclose(ev[:8], s ** 2, rtol=0, atol=1e-10)
+
+
+def test_p6_ridge_limit_equals_lstsq():
+    rng = np.random.default_rng(4)
+    m, d, k = 30, 6, 6
+    S = rng.standard_normal((m, d))
+    Y = rng.standard_normal((m, k))
+    w = rng.random(m)
+    w /= w.sum()
+    Th = orc.ridge_fit(S, Y, w, 0.0)
+    X = np.hstack([S, np.ones((m, 1))]) * np.sqrt(w)[:, None]
+    ref, *_ = np.linalg.lstsq(X, Y * np.sqrt(w)[:, None], rcond=None)
+    np.testing.assert_allclose(Th, ref, rtol=0, atol=1e-10)
+
+
+def test_p6_dense_equals_torch_sdpa():
+    import torch
+    Q, K, V = tiny_case(n=33, d=8, seed=9)
+    out, _ = orc.dense_attention(Q, K, V, 0.5)
+    ref = torch.nn.functional.scaled_dot_product_attention(
+        torch.from_numpy(Q)[None], torch.from_numpy(K)[None], torch.from_numpy(V)[None],
+        scale=0.5)[0].numpy()
+    np.testing.assert_allclose(out, ref, rtol=0, atol=1e-12)
+
+
+# ----------------------------------------------- P1 / P2 special cases
+
+def test_p1_full_density_equals_dense():
+    Q, K, V = tiny_case(n=40, d=5, seed=13)
+    res, _, _ = run_head(Q, K, V, 0.8, density=1.0, n_probes=0)
+    dense, _ = orc.dense_attention(Q, K, V, 0.8)
+    np.testing.assert_allclose(res.S, dense, rtol=0, atol=1e-12)
+    np.testing.assert_allclose(res.O, dense, rtol=0, atol=1e-12)
+    assert res.density == 1.0
+
+
+def test_p1_single_group_with_probes_equals_dense():
+    Q, K, V = tiny_case(n=40, d=5, seed=14)
+    res, _, _ = run_head(Q, K, V, 0.8, n_groups=1, density=0.3, n_probes=6, rank=3)
+    dense, _ = orc.dense_attention(Q, K, V, 0.8)
+    np.testing.assert_allclose(res.O, dense, rtol=0, atol=1e-12)
+    assert res.U.shape[1] == 0   # zero residuals -> empty subspace
+
+
+def test_p2_zero_probes_or_rank_gives_sparse_output():
+    Q, K, V = tiny_case(n=40, d=5, seed=15)
+    res, _, _ = run_head(Q, K, V, 0.8, n_probes=0)
+    assert np.array_equal(res.O, res.S)
+    res2, _, _ = run_head(Q, K, V, 0.8, n_probes=5, rank=0)
+    unprobed = np.setdiff1d(np.arange(40), res2.probe_tokens)
+    assert np.array_equal(res2.O[unprobed], res2.S[unprobed])
+    dense, _ = orc.dense_attention(Q, K, V, 0.8, rows=res2.probe_tokens)
+    np.testing.assert_allclose(res2.O[res2.probe_tokens], dense, rtol=0, atol=1e-13)
+
+
+# ----------------------------------------------- P3 normal equations
+
+def test_p3_normal_equations():
+    Q, K, V = tiny_case(n=64, d=6, seed=17)
+    res, _, _ = run_head(Q, K, V, 0.8, n_probes=10, rank=4)
+    Rp = res.O_probe - res.S[res.probe_tokens]
+    Y = Rp @ res.U
+    r = orc.normal_equation_residual(res.S[res.probe_tokens], Y, res.w, 1e-3, res.Theta)
+    assert r <= 1e-12
+
+
+# ----------------------------------------------- P4 permutation equivariance
+
+def test_p4_permutation_equivariance():
+    Q, K, V = tiny_case(n=64, d=6, seed=19)
+    res, sidx, iidx = run_head(Q, K, V, 0.8, n_probes=6, rank=3)
+    rng = np.random.default_rng(77)
+    pi = rng.permutation(64)           # new token t holds old token pi[t]
+    inv = np.argsort(pi)
+    kw = dict(q_block=8, n_groups=6, kmeans_iters=4, density=0.5, n_probes=6, rank=3,
+              ridge_lambda=1e-3)
+    res2 = orc.sparsepr_head(Q[pi], K[pi], V[pi], 0.8, sample_idx=inv[sidx], init_idx=inv[iidx],
+                             **kw)
+    np.testing.assert_allclose(res2.O, res.O[pi], rtol=0, atol=1e-10)
+    assert np.array_equal(res2.labels, res.labels[pi])
+    assert res2.executed_pairs == res.executed_pairs
+
+
+# ----------------------------------------------- P7 identities I1, I2
+
+def test_p7_metric_form_kmeans_identity():
+    Q, K, V = tiny_case(n=60, d=5, seed=21)
+    rng = np.random.default_rng(3)
+    sidx = rng.choice(60, 15, replace=False)
+    iidx = rng.choice(60, 6, replace=False)
+    R = orc.key_responses(Q, K, 0.7, sidx)
+    km = orc.kmeans(R, iidx, 5)
+    M = orc.sampled_metric(Q, 0.7, sidx)
+    lab2, kbar2 = orc.kmeans_metric_form(K, M, iidx, 5)
+    assert np.array_equal(km.labels, lab2)
+    # response-space centroids are the responses of the key-space centroids
+    Qs = Q[sidx]
+    np.testing.assert_allclose(km.centroids, 0.7 * kbar2 @ Qs.T, rtol=0, atol=1e-12)
+
+
+def test_p7_block_score_identity():
+    Q, K, V = tiny_case(n=50, d=6, seed=23)
+    res, _, _ = run_head(Q, K, V, 0.9)
+    alt = orc.block_scores_mean_query(Q, res.blocks, res.kbar, 0.9)
+    np.testing.assert_allclose(res.sigma, alt, rtol=0, atol=1e-12)
+
+
+# ----------------------------------------------- P8 / P9 closed forms
+
+def test_p8_planted_affine_residual():
+    rng = np.random.default_rng(31)
+    m, d, k = 80, 10, 3
+    U0, _ = np.linalg.qr(rng.standard_normal((d, k)))
+    A0 = rng.standard_normal((k, d))
+    c0 = rng.standard_normal(k)
+    S = rng.standard_normal((m, d))
+    R = (S @ A0.T + c0) @ U0.T
+    w = rng.random(m)
+    w /= w.sum()
+    U, _ = orc.residual_subspace(R, w, k)
+    np.testing.assert_allclose(U @ U.T, U0 @ U0.T, rtol=0, atol=1e-8)
+    Th = orc.ridge_fit(S, R @ U, w, 1e-12)
+    Snew = rng.standard_normal((7, d))
+    pred = orc.predicted_residual(Snew, U, Th)
+    np.testing.assert_allclose(pred, (Snew @ A0.T + c0) @ U0.T, rtol=0, atol=1e-8)
+
+
+def test_p9_interpolation_small_probe_count():
+    rng = np.random.default_rng(37)
+    m, d = 7, 8                         # m <= d + 1
+    S = rng.standard_normal((m, d))
+    R = rng.standard_normal((m, d))
+    w = rng.random(m)
+    w /= w.sum()
+    U, _ = orc.residual_subspace(R, w, d)   # k_eff = m >= rank(R)
+    Th = orc.ridge_fit(S, R @ U, w, 1e-13)
+    np.testing.assert_allclose(orc.predicted_residual(S, U, Th), R, rtol=0, atol=1e-8)
+
+
+# ----------------------------------------------- P10 Lloyd, P11 CSR
+
+def test_p10_lloyd_monotone_and_valid():
+    wl = configs.TINY
+    inp = wl.make_inputs()
+    R = orc.key_responses(inp.Q[0], inp.K[0], inp.scale[0], inp.sample_idx)
+    km = orc.kmeans(R, inp.init_idx, 8)
+    obj = np.array(km.objective)
+    assert np.all(np.diff(obj) <= 1e-9 * obj[0])
+    assert km.labels.min() >= 0 and km.labels.max() < 32
+    _, goff, sizes = orc.group_members(km.labels, 32)
+    assert sizes.sum() == 2048 and goff[-1] == 2048
+
+
+def test_p11_csr_well_formed():
+    wl = configs.TINY
+    inp = wl.make_inputs()
+    p = wl.params
+    res = orc.sparsepr_head(inp.Q[0], inp.K[0], inp.V[0], inp.scale[0],
+                            sample_idx=inp.sample_idx, init_idx=inp.init_idx,
+                            q_block=p.q_block, n_groups=p.n_groups,
+                            kmeans_iters=p.kmeans_iters, density=p.density,
+                            n_probes=p.n_probes, rank=p.rank, ridge_lambda=p.ridge_lambda)
+    n = p.n_tokens
+    kappa = p.key_budget
+    assert np.all(np.diff(res.block_ptr) >= 1)
+    assert sorted(res.key_perm.tolist()) == list(range(n))
+    assert sorted(res.query_perm.tolist()) == list(range(n))
+    for b in range(len(res.blocks)):
+        gs = res.block_groups[res.block_ptr[b]:res.block_ptr[b + 1]]
+        assert np.all(np.diff(gs) > 0)
+        assert np.all(res.sizes[gs] > 0)
+        tot = int(res.sizes[gs].sum())
+        assert tot <= kappa or len(gs) == 1
+        # maximality: the next ranked group would not fit
+        cand = np.nonzero(res.sizes > 0)[0]
+        ranked = cand[np.lexsort((cand, -res.sigma[b][cand]))]
+        assert set(ranked[:len(gs)].tolist()) == set(gs.tolist())
+        if len(gs) < len(ranked):
+            assert tot + res.sizes[ranked[len(gs)]] > kappa
+    assert res.density <= p.density + 1e-12
+
+
+# ----------------------------------------------- P12 planted clusters (sanity)
+
+def test_p12_planted_clusters_sanity():
+    from sklearn.metrics import adjusted_rand_score
+    n, d = 400, 16
+    rng = np.random.default_rng(41)
+    mu = rng.standard_normal((8, d)) * 3
+    lab = rng.integers(0, 8, n)
+    Q = mu[lab] + 0.3 * rng.standard_normal((n, d))
+    K = mu[lab] + 0.3 * rng.standard_normal((n, d))
+    sidx = rng.choice(n, 64, replace=False)
+    init = np.array([np.nonzero(lab == c)[0][0] for c in range(8)])
+    R = orc.key_responses(Q, K, 0.25, sidx)
+    km = orc.kmeans(R, init, 8)
+    assert adjusted_rand_score(lab, km.labels) > 0.95
+
+
+# ----------------------------------------------- P13 LSE merge
+
+def test_p13_lse_merge_of_disjoint_supports():
+    Q, K, V = tiny_case(n=50, d=6, seed=43)
+    a, la = orc.softmax_attention(Q[:9], K[:20], V[:20], 0.7)
+    b, lb = orc.softmax_attention(Q[:9], K[20:], V[20:], 0.7)
+    full, lf = orc.softmax_attention(Q[:9], K, V, 0.7)
+    lt = np.logaddexp(la, lb)
+    merged = np.exp(la - lt)[:, None] * a + np.exp(lb - lt)[:, None] * b
+    np.testing.assert_allclose(merged, full, rtol=0, atol=1e-12)
+    np.testing.assert_allclose(lt, lf, rtol=0, atol=1e-12)
+
+
+# ----------------------------------------------- random-block variant
+
+def test_random_block_variant_groups_are_near_equal_runs():
+    n, G = 37, 5
+    perm = np.random.default_rng(0).permutation(n)
+    lab = orc.random_block_labels(perm, G)
+    sizes = np.bincount(lab, minlength=G)
+    assert sizes.tolist() == [(g + 1) * n // G - g * n // G for g in range(G)]
+    for g in range(G):
+        assert set(np.nonzero(lab == g)[0].tolist()) == set(perm[g * n // G:(g + 1) * n // G].tolist())
+
+
+def test_random_block_head_runs_and_is_valid():
+    Q, K, V = tiny_case(n=48, d=6, seed=45)
+    kp = np.random.default_rng(1).permutation(48)
+    qp = np.random.default_rng(2).permutation(48)
+    res = orc.sparsepr_head(Q, K, V, 0.7, q_block=8, n_groups=6, kmeans_iters=4, density=0.5,
+                            n_probes=5, rank=3, ridge_lambda=1e-3, partition_mode=1,
+                            rand_key_perm=kp, rand_query_perm=qp)
+    assert np.array_equal(res.query_perm, qp)
+    assert np.all(np.isfinite(res.O))
+
+
+# ----------------------------------------------- P14 direction (report only)
+
+def test_p14_reconstruction_direction_report(capsys):
+    wl = configs.TINY
+    inp = wl.make_inputs()
+    p = wl.params
+    res = orc.sparsepr_head(inp.Q[0], inp.K[0], inp.V[0], inp.scale[0],
+                            sample_idx=inp.sample_idx, init_idx=inp.init_idx,
+                            q_block=p.q_block, n_groups=p.n_groups, kmeans_iters=p.kmeans_iters,
+                            density=p.density, n_probes=p.n_probes, rank=p.rank,
+                            ridge_lambda=p.ridge_lambda)
+    dense, _ = orc.dense_attention(inp.Q[0], inp.K[0], inp.V[0], inp.scale[0])
+    unp = np.setdiff1d(np.arange(p.n_tokens), res.probe_tokens)
+    e = orc.relative_l2_rows(res.O[unp], dense[unp])
+    e0 = orc.relative_l2_rows(res.S[unp], dense[unp])
+    print(f"tiny: SparsePR mean {e.mean():.4g} p99 {np.percentile(e, 99):.4g}; "
+          f"hard-drop mean {e0.mean():.4g}; density {res.density:.4f}")
+    assert np.isfinite(e).all()
