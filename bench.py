@@ -1,0 +1,270 @@
+"""Benchmark of one SparsePR call on one MI355X.
+
+A step is one whole call (partition, route, attend, probe_fit, apply) on
+synthetic inputs already resident in HBM. Prints ONE JSON line: executed-pair
+TFLOP/s of the call (value), call ms, the build's dense attention ms and the
+speedup, per-stage ms, the block-sparse kernel's roofline, and the fp64
+oracle timed on a bounded sample on the host cores.
+
+    python bench.py [--config hunyuan] [--steps 10] [--warmup 3] [--gpus 1]
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+METRIC = "SparsePR call ms & speedup vs dense at 22% density; executed-pair TFLOP/s"
+PEAK_BF16_TFLOPS = 2500.0
+PEAK_HBM_GBS = 8000.0
+
+
+def log(msg):
+    print(msg, file=sys.stderr, flush=True)
+
+
+def source_hash(path):
+    with open(path, "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()[:16]
+
+
+def load_traffic(workload):
+    """HBM traffic of the block-sparse kernel from committed rocprofv3 PMC
+    summaries, valid only while the kernel source is unchanged."""
+    path = os.path.join(ROOT, "profiles", f"attend_traffic_{workload}.json")
+    if not os.path.exists(path):
+        return None
+    rec = json.load(open(path))
+    src = os.path.join(ROOT, "free_block_sparse_rcp_amd", "csrc", "attention.hip")
+    if rec.get("attention_hip_sha256_16") != source_hash(src):
+        return None
+    return rec.get("bytes_per_launch")
+
+
+def cpu_baseline(wl, inp, block_stride):
+    """The fp64 oracle, as it stands, on head 0 of the same workload: every
+    stage in the pages' order; the block-sparse attention step runs on every
+    `block_stride`-th query block and its time is scaled by executed pairs."""
+    import numpy as np
+    from oracle import sparsepr_oracle as orc
+    try:
+        from threadpoolctl import threadpool_info
+        cores = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    except Exception:  # pragma: no cover
+        cores = os.cpu_count() or 1
+    p = wl.params
+    Q, K, V = (x[0].astype(np.float64) for x in (inp.Q, inp.K, inp.V))
+    tau = float(inp.scale[0])
+    N = p.n_tokens
+    t = {}
+    t0 = time.perf_counter()
+    if p.partition_mode == 0:
+        R = orc.key_responses(Q, K, tau, inp.sample_idx)
+        labels = orc.kmeans(R, inp.init_idx, p.kmeans_iters).labels
+        del R
+    else:
+        labels = orc.random_block_labels(inp.rand_key_perm, p.n_groups)
+    key_perm, group_off, sizes = orc.group_members(labels, p.n_groups)
+    kbar, _ = orc.key_centroids(K, labels, p.n_groups)
+    t["partition"] = time.perf_counter() - t0
+    t0 = time.perf_counter()
+    C = orc.query_coordinates(Q, kbar, tau)
+    g1, v = orc.dominant_groups(C, sizes)
+    qperm = orc.query_order(g1, v) if p.partition_mode == 0 else np.asarray(inp.rand_query_perm)
+    blocks = orc.query_blocks(qperm, p.q_block)
+    sigma = orc.block_scores(C, blocks)
+    del C
+    bptr, bgrp = orc.route(sigma, sizes, orc.key_budget(N, p.density, p.n_probes))
+    ksets = orc.block_key_sets(bptr, bgrp, key_perm, group_off)
+    t["route"] = time.perf_counter() - t0
+    E = orc.executed_pairs(blocks, ksets, p.n_probes, N)
+    sp_all = E - p.n_probes * N
+    sel = list(range(0, len(blocks), block_stride))
+    sp_sample = sum(len(blocks[b]) * len(ksets[b]) for b in sel)
+    t0 = time.perf_counter()
+    S, _ = orc.sparse_attention(Q, K, V, tau, [blocks[b] for b in sel], [ksets[b] for b in sel])
+    t["attend_sampled"] = time.perf_counter() - t0
+    t["attend_scaled"] = t["attend_sampled"] * sp_all / max(sp_sample, 1)
+    t0 = time.perf_counter()
+    ptok = qperm[orc.probe_positions(N, p.n_probes)]
+    Op, _ = orc.dense_attention(Q, K, V, tau, rows=ptok)
+    w = orc.probe_weights(Op)
+    Rp = Op - S[ptok]
+    U, _ = orc.residual_subspace(Rp, w, p.rank)
+    Th = orc.ridge_fit(S[ptok], Rp @ U, w, p.ridge_lambda)
+    O = S + orc.predicted_residual(S, U, Th)
+    O[ptok] = Op
+    t["probe_fit_apply"] = time.perf_counter() - t0
+    total = t["partition"] + t["route"] + t["attend_scaled"] + t["probe_fit_apply"]
+    tflops = 4.0 * p.head_dim * E / total / 1e12
+    spent = t["partition"] + t["route"] + t["attend_sampled"] + t["probe_fit_apply"]
+    return {"value": tflops, "unit": "TFLOP/s", "cores": int(cores), "kind": "oracle",
+            "sample": f"head 0 of {p.heads}: every oracle stage in order; sparse attention on "
+                      f"{len(sel)} of {len(blocks)} query blocks (every {block_stride}th), time "
+                      f"scaled by executed pairs; {spent:.1f} s of CPU time",
+            "stage_seconds": t, "call_ms_scaled_all_heads": total * 1e3 * p.heads}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=10)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--config", default="hunyuan")
+    ap.add_argument("--cpu-block-stride", type=int, default=0,
+                    help="oracle samples every n-th query block (0: chosen by workload size)")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-dense", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py runs on one GPU only: the operator is per call and per head, and this "
+              f"build has no multi-GPU path (asked for --gpus {args.gpus}).", file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+    from free_block_sparse_rcp_amd import binding, configs
+
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(1)
+    binding.load()
+    wl = configs.get(args.config)
+    p = wl.params
+    dev = torch.device("cuda:0")
+    log(f"[bench] generating {wl.name}")
+    t0 = time.perf_counter()
+    inp = wl.make_inputs()
+    log(f"[bench] inputs ready in {time.perf_counter() - t0:.1f} s")
+    dt = binding.torch_dtype(p)
+    Q, K, V = (torch.from_numpy(x).to(dev, dt) for x in (inp.Q, inp.K, inp.V))
+    scale = torch.from_numpy(inp.scale).to(dev)
+    op = binding.SparsePR(p, dev)
+    idx = op.upload_indices(inp.sample_idx, inp.init_idx, inp.rand_key_perm, inp.rand_query_perm)
+    b = op.buffers
+    O_dense = torch.empty_like(Q)
+    lse_dense = torch.empty(p.heads, p.n_tokens, dtype=torch.float32, device=dev)
+
+    stages = ("partition", "route", "attend", "probe_fit", "apply")
+
+    def one_call(ev=None):
+        if ev is not None:
+            ev[0].record()
+        binding.partition(p, Q, K, V, scale, idx.get("sample_idx"), idx.get("init_idx"), b,
+                          rand_key_perm=idx.get("rand_key_perm"))
+        if ev is not None:
+            ev[1].record()
+        binding.route(p, Q, scale, b, rand_query_perm=idx.get("rand_query_perm"))
+        if ev is not None:
+            ev[2].record()
+        binding.attend(p, Q, scale, b)
+        if ev is not None:
+            ev[3].record()
+        binding.probe_fit(p, Q, scale, b)
+        if ev is not None:
+            ev[4].record()
+        binding.apply(p, b)
+        if ev is not None:
+            ev[5].record()
+
+    log(f"[bench] warmup {args.warmup}")
+    for _ in range(args.warmup):
+        one_call()
+        if not args.no_dense:
+            binding.dense_attention(p, Q, K, V, scale, O_dense, lse_dense)
+    torch.cuda.synchronize()
+
+    # timed region: K whole calls, events between stages (on the library's stream)
+    log(f"[bench] timing {args.steps} calls")
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(6)] for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    w0 = time.perf_counter()
+    for s in range(args.steps):
+        one_call(evs[s])
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - w0
+    stage_ms = {n: float(np.mean([evs[s][i].elapsed_time(evs[s][i + 1]) for s in range(args.steps)]))
+                for i, n in enumerate(stages)}
+    call_ms = float(np.mean([evs[s][0].elapsed_time(evs[s][5]) for s in range(args.steps)]))
+
+    dense_ms = None
+    if not args.no_dense:
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        e0.record()
+        for _ in range(args.steps):
+            binding.dense_attention(p, Q, K, V, scale, O_dense, lse_dense)
+        e1.record()
+        torch.cuda.synchronize()
+        dense_ms = e0.elapsed_time(e1) / args.steps
+
+    E = int(b.executed_pairs.sum().item())
+    H, N, D = p.heads, p.n_tokens, p.head_dim
+    sparse_pairs = E - H * p.n_probes * N
+    call_tflops = 4.0 * D * E / (call_ms * 1e-3) / 1e12
+    attend_tflops = 4.0 * D * sparse_pairs / (stage_ms["attend"] * 1e-3) / 1e12
+    density = E / (H * float(N) ** 2)
+
+    # quality on this synthetic call, against the build's own dense output
+    quality = None
+    if not args.no_dense:
+        with torch.no_grad():
+            ref = O_dense.float()
+            S_tok = torch.empty_like(b.S)
+            S_tok.scatter_(1, b.query_perm.long()[:, :, None].expand(-1, -1, D), b.S)
+            mask = torch.ones(H, N, dtype=torch.bool, device=dev)
+            pos = torch.tensor([((2 * i + 1) * N) // (2 * p.n_probes) for i in range(p.n_probes)],
+                               dtype=torch.long, device=dev)
+            if p.n_probes:
+                mask.scatter_(1, b.query_perm.long().gather(1, pos[None].expand(H, -1)), False)
+            rn = ref.norm(dim=2)
+            e = ((b.O.float() - ref).norm(dim=2) / rn)[mask]
+            e0 = ((S_tok - ref).norm(dim=2) / rn)[mask]
+            quality = {"reference": "this build's dense kernel (bf16 output)",
+                       "rel_l2_mean_unprobed": float(e.mean()),
+                       "rel_l2_p99_unprobed": float(torch.quantile(e[:1_000_000].float(), 0.99)),
+                       "hard_drop_rel_l2_mean": float(e0.mean())}
+
+    traffic = load_traffic(wl.name)
+    roofline = {"bound": "mfma", "kernel": "k_attn_mfma (sparsepr_attend)",
+                "achieved": attend_tflops, "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+                "frac": attend_tflops / PEAK_BF16_TFLOPS, "traffic": traffic,
+                "algorithmic_flops_per_launch": 4.0 * D * sparse_pairs,
+                "launch_ms": stage_ms["attend"]}
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        stride = args.cpu_block_stride or max(1, int(round(4.0 * N / 118800)))
+        log(f"[bench] cpu baseline (oracle), head 0, block stride {stride}")
+        sub = inp if H == 1 else wl.make_inputs([0])
+        cpu = cpu_baseline(wl, sub, stride)
+
+    out = {
+        "metric": METRIC, "value": call_tflops, "unit": "TFLOP/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": call_ms,
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": p.dtype,
+        "data": "synthetic",
+        "config": {"workload": wl.name, "heads": H, "n_tokens": N, "head_dim": D,
+                   "density_target": p.density, "n_probes": p.n_probes, "n_groups": p.n_groups,
+                   "n_samples": p.n_samples, "kmeans_iters": p.kmeans_iters,
+                   "q_block": p.q_block, "rank": p.rank, "ridge_lambda": p.ridge_lambda},
+        "call_ms": call_ms, "dense_ms": dense_ms,
+        "speedup_vs_dense": (dense_ms / call_ms) if dense_ms else None,
+        "attend_speedup_vs_dense": (dense_ms / stage_ms["attend"]) if dense_ms else None,
+        "stage_ms": stage_ms, "wall_ms_per_step": wall * 1e3 / args.steps,
+        "executed_pairs": E, "realized_density": density,
+        "dense_tflops": (4.0 * D * H * float(N) ** 2 / (dense_ms * 1e-3) / 1e12) if dense_ms else None,
+        "quality": quality, "roofline": roofline, "cpu_baseline": cpu,
+    }
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,293 @@
+"""ctypes binding of ``libsparsepr.so`` (declared in ``include/sparsepr.h``).
+
+Argument marshalling only: torch tensors are used for device memory and the
+current HIP stream; every step of the operator runs in the library's kernels.
+Loading fails loudly when the library has not been built.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from dataclasses import dataclass
+from typing import Dict, Optional
+
+import numpy as np
+import torch
+
+from . import build as _build
+from .configs import Params
+
+_c_i32 = ctypes.c_int32
+_c_p = ctypes.c_void_p
+_c_sz = ctypes.c_size_t
+
+SPARSEPR_F32 = 0
+SPARSEPR_BF16 = 1
+STATUS = {0: "SPARSEPR_OK", 1: "SPARSEPR_ERR_INVALID_ARG", 2: "SPARSEPR_ERR_UNSUPPORTED",
+          3: "SPARSEPR_ERR_WORKSPACE", 4: "SPARSEPR_ERR_HIP"}
+
+# every entry point declared in include/sparsepr.h
+EXPORTS = ("sparsepr_abi_version", "sparsepr_status_string", "sparsepr_last_error",
+           "sparsepr_workspace_bytes", "sparsepr_partition", "sparsepr_route", "sparsepr_attend",
+           "sparsepr_probe_fit", "sparsepr_apply", "sparsepr_dense_attention")
+
+
+class CParams(ctypes.Structure):
+    _fields_ = [("heads", _c_i32), ("n_tokens", _c_i32), ("head_dim", _c_i32), ("dtype", _c_i32),
+                ("q_block", _c_i32), ("n_groups", _c_i32), ("n_samples", _c_i32),
+                ("kmeans_iters", _c_i32), ("density", ctypes.c_double), ("n_probes", _c_i32),
+                ("rank", _c_i32), ("ridge_lambda", ctypes.c_double), ("partition_mode", _c_i32),
+                ("reserved", _c_i32)]
+
+
+class SparsePRError(RuntimeError):
+    def __init__(self, status: int, message: str):
+        super().__init__(f"{STATUS.get(status, status)}: {message}")
+        self.status = status
+
+
+_LIB = None
+
+
+def load(path: Optional[str] = None) -> ctypes.CDLL:
+    """Load the HIP library (once). Raises if it is missing."""
+    global _LIB
+    if _LIB is not None:
+        return _LIB
+    path = path or _build.lib_path()
+    if not os.path.exists(path):
+        raise FileNotFoundError(
+            f"{path} not found: build the HIP library with `python -m free_block_sparse_rcp_amd.build`")
+    lib = ctypes.CDLL(path)
+    lib.sparsepr_abi_version.restype = _c_i32
+    lib.sparsepr_status_string.restype = ctypes.c_char_p
+    lib.sparsepr_status_string.argtypes = [_c_i32]
+    lib.sparsepr_last_error.restype = ctypes.c_char_p
+    lib.sparsepr_workspace_bytes.argtypes = [ctypes.POINTER(CParams), ctypes.POINTER(_c_sz)]
+    lib.sparsepr_workspace_bytes.restype = _c_i32
+    pp = ctypes.POINTER(CParams)
+    lib.sparsepr_partition.argtypes = [pp] + [_c_p] * 14 + [_c_p, _c_sz, _c_p]
+    lib.sparsepr_route.argtypes = [pp] + [_c_p] * 13 + [_c_p, _c_sz, _c_p]
+    lib.sparsepr_attend.argtypes = [pp] + [_c_p] * 10 + [_c_p]
+    lib.sparsepr_probe_fit.argtypes = [pp] + [_c_p] * 10 + [_c_p, _c_sz, _c_p]
+    lib.sparsepr_apply.argtypes = [pp] + [_c_p] * 7 + [_c_p]
+    lib.sparsepr_dense_attention.argtypes = [pp] + [_c_p] * 6 + [_c_p]
+    for name in ("sparsepr_partition", "sparsepr_route", "sparsepr_attend", "sparsepr_probe_fit",
+                 "sparsepr_apply", "sparsepr_dense_attention"):
+        getattr(lib, name).restype = _c_i32
+    if lib.sparsepr_abi_version() != 1:
+        raise RuntimeError("libsparsepr ABI version mismatch")
+    _LIB = lib
+    return lib
+
+
+def loaded_path() -> Optional[str]:
+    return _build.lib_path() if _LIB is not None else None
+
+
+def _check(status: int) -> None:
+    if status != 0:
+        msg = load().sparsepr_last_error().decode()
+        raise SparsePRError(status, msg)
+
+
+def c_params(p: Params) -> CParams:
+    return CParams(p.heads, p.n_tokens, p.head_dim, SPARSEPR_BF16 if p.dtype == "bf16" else SPARSEPR_F32,
+                   p.q_block, p.n_groups, p.n_samples, p.kmeans_iters, float(p.density), p.n_probes,
+                   p.rank, float(p.ridge_lambda), p.partition_mode, 0)
+
+
+def _ptr(t: Optional[torch.Tensor]):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(device) -> ctypes.c_void_p:
+    return ctypes.c_void_p(torch.cuda.current_stream(device).cuda_stream)
+
+
+def torch_dtype(p: Params):
+    return torch.bfloat16 if p.dtype == "bf16" else torch.float32
+
+
+def workspace_bytes(p: Params) -> int:
+    n = _c_sz(0)
+    _check(load().sparsepr_workspace_bytes(ctypes.byref(c_params(p)), ctypes.byref(n)))
+    return int(n.value)
+
+
+def _check_tensor(name, t, shape, dtype, device):
+    if t is None:
+        raise ValueError(f"{name} is required")
+    if tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} has shape {tuple(t.shape)}, expected {tuple(shape)}")
+    if t.dtype != dtype:
+        raise ValueError(f"{name} has dtype {t.dtype}, expected {dtype}")
+    if t.device != device:
+        raise ValueError(f"{name} is on {t.device}, expected {device}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+
+
+def index_tensor(a, n: int, length: int, name: str, device, distinct: bool = False) -> torch.Tensor:
+    """Validate an index array on the host and upload it as int32."""
+    arr = np.asarray(a.cpu().numpy() if isinstance(a, torch.Tensor) else a).astype(np.int64).ravel()
+    if arr.size != length:
+        raise ValueError(f"{name} must have {length} entries (got {arr.size})")
+    if arr.size and (arr.min() < 0 or arr.max() >= n):
+        raise ValueError(f"{name} entries must lie in [0, {n})")
+    if distinct and np.unique(arr).size != arr.size:
+        raise ValueError(f"{name} entries must be distinct")
+    return torch.from_numpy(arr.astype(np.int32)).to(device)
+
+
+@dataclass
+class Buffers:
+    """Every device buffer of one call; reused across calls of the same shape."""
+
+    key_label: torch.Tensor
+    key_perm: torch.Tensor
+    group_off: torch.Tensor
+    key_centroid: torch.Tensor
+    Kp: torch.Tensor
+    Vp: torch.Tensor
+    query_perm: torch.Tensor
+    block_ptr: torch.Tensor
+    block_groups: torch.Tensor
+    executed_pairs: torch.Tensor
+    S: torch.Tensor
+    lse: torch.Tensor
+    O_probe: torch.Tensor
+    U: torch.Tensor
+    Theta: torch.Tensor
+    rank_eff: torch.Tensor
+    O: torch.Tensor
+    workspace: torch.Tensor
+
+
+def alloc_buffers(p: Params, device) -> Buffers:
+    H, N, D, G = p.heads, p.n_tokens, p.head_dim, p.n_groups
+    nb = p.n_blocks
+    dt = torch_dtype(p)
+    i32 = dict(dtype=torch.int32, device=device)
+    f32 = dict(dtype=torch.float32, device=device)
+    return Buffers(
+        key_label=torch.empty(H, N, **i32), key_perm=torch.empty(H, N, **i32),
+        group_off=torch.empty(H, G + 1, **i32), key_centroid=torch.empty(H, G, D, **f32),
+        Kp=torch.empty(H, N, D, dtype=dt, device=device),
+        Vp=torch.empty(H, N, D, dtype=dt, device=device),
+        query_perm=torch.empty(H, N, **i32), block_ptr=torch.empty(H, nb + 1, **i32),
+        block_groups=torch.empty(H, nb * G, **i32),
+        executed_pairs=torch.empty(H, dtype=torch.int64, device=device),
+        S=torch.empty(H, N, D, **f32), lse=torch.empty(H, N, **f32),
+        O_probe=torch.empty(H, max(p.n_probes, 1), D, **f32),
+        U=torch.empty(H, D, max(p.rank, 1), **f32),
+        Theta=torch.empty(H, D + 1, max(p.rank, 1), **f32),
+        rank_eff=torch.empty(H, **i32), O=torch.empty(H, N, D, dtype=dt, device=device),
+        workspace=torch.empty(workspace_bytes(p), dtype=torch.uint8, device=device))
+
+
+# ------------------------------------------------------------ stage calls
+
+def partition(p: Params, Q, K, V, scale, sample_idx, init_idx, b: Buffers, rand_key_perm=None,
+              dbg_assign_scores: Optional[torch.Tensor] = None) -> None:
+    lib = load()
+    cp = c_params(p)
+    _check(lib.sparsepr_partition(
+        ctypes.byref(cp), _ptr(Q), _ptr(K), _ptr(V), _ptr(scale), _ptr(sample_idx), _ptr(init_idx),
+        _ptr(rand_key_perm), _ptr(b.key_label), _ptr(b.key_perm), _ptr(b.group_off),
+        _ptr(b.key_centroid), _ptr(b.Kp), _ptr(b.Vp), _ptr(dbg_assign_scores),
+        _ptr(b.workspace), b.workspace.numel(), _stream(K.device)))
+
+
+def route(p: Params, Q, scale, b: Buffers, rand_query_perm=None, dbg_coords=None,
+          dbg_dominant=None, dbg_dominant_val=None, dbg_block_score=None) -> None:
+    lib = load()
+    cp = c_params(p)
+    _check(lib.sparsepr_route(
+        ctypes.byref(cp), _ptr(Q), _ptr(scale), _ptr(b.key_centroid), _ptr(b.group_off),
+        _ptr(rand_query_perm), _ptr(b.query_perm), _ptr(b.block_ptr), _ptr(b.block_groups),
+        _ptr(b.executed_pairs), _ptr(dbg_coords), _ptr(dbg_dominant), _ptr(dbg_dominant_val),
+        _ptr(dbg_block_score), _ptr(b.workspace), b.workspace.numel(), _stream(Q.device)))
+
+
+def attend(p: Params, Q, scale, b: Buffers) -> None:
+    lib = load()
+    cp = c_params(p)
+    _check(lib.sparsepr_attend(
+        ctypes.byref(cp), _ptr(Q), _ptr(b.Kp), _ptr(b.Vp), _ptr(scale), _ptr(b.group_off),
+        _ptr(b.query_perm), _ptr(b.block_ptr), _ptr(b.block_groups), _ptr(b.S), _ptr(b.lse),
+        _stream(Q.device)))
+
+
+def probe_fit(p: Params, Q, scale, b: Buffers, K=None, V=None) -> None:
+    lib = load()
+    cp = c_params(p)
+    K = b.Kp if K is None else K
+    V = b.Vp if V is None else V
+    _check(lib.sparsepr_probe_fit(
+        ctypes.byref(cp), _ptr(Q), _ptr(K), _ptr(V), _ptr(scale), _ptr(b.query_perm), _ptr(b.S),
+        _ptr(b.O_probe), _ptr(b.U), _ptr(b.Theta), _ptr(b.rank_eff), _ptr(b.workspace),
+        b.workspace.numel(), _stream(Q.device)))
+
+
+def apply(p: Params, b: Buffers) -> None:
+    lib = load()
+    cp = c_params(p)
+    _check(lib.sparsepr_apply(
+        ctypes.byref(cp), _ptr(b.S), _ptr(b.query_perm), _ptr(b.O_probe), _ptr(b.U),
+        _ptr(b.Theta), _ptr(b.rank_eff), _ptr(b.O), _stream(b.S.device)))
+
+
+def dense_attention(p: Params, Q, K, V, scale, O=None, lse=None):
+    lib = load()
+    cp = c_params(p)
+    if O is None:
+        O = torch.empty_like(Q)
+    if lse is None:
+        lse = torch.empty(p.heads, p.n_tokens, dtype=torch.float32, device=Q.device)
+    _check(lib.sparsepr_dense_attention(ctypes.byref(cp), _ptr(Q), _ptr(K), _ptr(V), _ptr(scale),
+                                        _ptr(O), _ptr(lse), _stream(Q.device)))
+    return O, lse
+
+
+class SparsePR:
+    """One SparsePR operator of a fixed shape with preallocated buffers.
+
+    ``run`` enqueues the five stages on the current stream; the result is
+    ``buffers.O`` (token order) once the stream has been synchronised.
+    """
+
+    def __init__(self, p: Params, device="cuda"):
+        load()
+        self.p = p
+        self.device = torch.device(device)
+        self.buffers = alloc_buffers(p, self.device)
+
+    def upload_indices(self, sample_idx=None, init_idx=None, rand_key_perm=None,
+                       rand_query_perm=None) -> Dict[str, torch.Tensor]:
+        p, dev = self.p, self.device
+        out = {}
+        if p.partition_mode == 0:
+            out["sample_idx"] = index_tensor(sample_idx, p.n_tokens, p.n_samples, "sample_idx", dev, True)
+            out["init_idx"] = index_tensor(init_idx, p.n_tokens, p.n_groups, "init_idx", dev, True)
+        else:
+            out["rand_key_perm"] = index_tensor(rand_key_perm, p.n_tokens, p.n_tokens, "rand_key_perm", dev, True)
+            out["rand_query_perm"] = index_tensor(rand_query_perm, p.n_tokens, p.n_tokens, "rand_query_perm", dev, True)
+        return out
+
+    def check_inputs(self, Q, K, V, scale):
+        p = self.p
+        shp = (p.heads, p.n_tokens, p.head_dim)
+        for name, t in (("Q", Q), ("K", K), ("V", V)):
+            _check_tensor(name, t, shp, torch_dtype(p), self.device)
+        _check_tensor("scale", scale, (p.heads,), torch.float32, self.device)
+
+    def run(self, Q, K, V, scale, idx: Dict[str, torch.Tensor]) -> torch.Tensor:
+        p, b = self.p, self.buffers
+        partition(p, Q, K, V, scale, idx.get("sample_idx"), idx.get("init_idx"), b,
+                  rand_key_perm=idx.get("rand_key_perm"))
+        route(p, Q, scale, b, rand_query_perm=idx.get("rand_query_perm"))
+        attend(p, Q, scale, b)
+        probe_fit(p, Q, scale, b)
+        apply(p, b)
+        return b.O

@@ -1,0 +1,432 @@
+// C-ABI of the SparsePR operator: host-side validation, workspace layout and
+// the stage launch sequences. Every check happens before the first launch.
+#include <algorithm>
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+
+#include "internal.hpp"
+
+namespace spr {
+
+static thread_local char g_last_error[512] = "";
+
+static int32_t fail(int32_t code, const char* fmt, ...) __attribute__((format(printf, 2, 3)));
+static int32_t fail(int32_t code, const char* fmt, ...) {
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(g_last_error, sizeof(g_last_error), fmt, ap);
+  va_end(ap);
+  return code;
+}
+
+static size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
+
+struct Bump {
+  size_t off = 0;
+  size_t take(size_t bytes) {
+    const size_t o = align256(off);
+    off = o + bytes;
+    return o;
+  }
+};
+
+static int bits_for(int n) {
+  int b = 0;
+  while ((1 << b) < n) ++b;
+  return b;
+}
+
+PartitionWs partition_ws(const Dims& d) {
+  Bump b;
+  PartitionWs L;
+  const size_t H = d.H, G = d.G, D = d.D;
+  const size_t nbk = size_t(1) << d.gbits;
+  L.M = b.take(H * D * D * sizeof(double));
+  L.P = b.take(H * G * D * sizeof(float));
+  L.Phl = b.take(H * G * D * 2 * sizeof(uint16_t));
+  L.bvec = b.take(H * G * sizeof(float));
+  L.counts = b.take(H * nbk * d.nchunk * sizeof(int32_t));
+  L.totals = b.take(H * nbk * sizeof(int32_t));
+  L.starts = b.take(H * nbk * sizeof(int32_t));
+  L.partial = b.take(H * (G + d.ntile64) * D * sizeof(float));
+  L.end = align256(b.off);
+  return L;
+}
+
+RouteWs route_ws(const Dims& d) {
+  Bump b;
+  RouteWs L;
+  const size_t H = d.H, N = d.N, G = d.G, nb = d.nb;
+  const size_t nbk = std::max<size_t>(256, size_t(1) << d.gbits);
+  L.keysA = b.take(H * N * 8);
+  L.keysB = b.take(H * N * 8);
+  L.valsA = b.take(H * N * 4);
+  L.valsB = b.take(H * N * 4);
+  L.counts = b.take(H * nbk * d.nchunk * 4);
+  L.totals = b.take(H * nbk * 4);
+  L.starts = b.take(H * nbk * 4);
+  L.qbar = b.take(H * nb * d.D * 4);
+  L.sigma = b.take(H * nb * G * 4);
+  L.sel = b.take(H * nb * G * 4);
+  L.selcnt = b.take(H * nb * 4);
+  L.blkkeys = b.take(H * nb * 8);
+  L.end = align256(b.off);
+  return L;
+}
+
+ProbeWs probe_ws(const Dims& d) {
+  Bump b;
+  ProbeWs L;
+  const size_t H = d.H, m = d.m;
+  L.opart = b.take(H * d.nsplit * m * d.D * 4);
+  L.lsepart = b.take(H * d.nsplit * m * 4);
+  L.fit_per_head = fit_ws_per_head(d);
+  L.fit = b.take(H * L.fit_per_head);
+  L.end = align256(b.off);
+  return L;
+}
+
+// Validation of the parameters; `full` also checks the fields that only the
+// sparse stages use.
+static int32_t make_dims(const sparsepr_params* p, bool full, Dims* d) {
+  if (p == nullptr) return fail(SPARSEPR_ERR_INVALID_ARG, "params is NULL");
+  if (p->heads < 1) return fail(SPARSEPR_ERR_INVALID_ARG, "heads must be >= 1 (got %d)", p->heads);
+  if (p->n_tokens < 1) return fail(SPARSEPR_ERR_INVALID_ARG, "n_tokens must be >= 1 (got %d)", p->n_tokens);
+  if (p->head_dim != 64 && p->head_dim != 128)
+    return fail(SPARSEPR_ERR_UNSUPPORTED, "head_dim must be 64 or 128 (got %d)", p->head_dim);
+  if (p->dtype != SPARSEPR_F32 && p->dtype != SPARSEPR_BF16)
+    return fail(SPARSEPR_ERR_INVALID_ARG, "dtype must be SPARSEPR_F32 or SPARSEPR_BF16 (got %d)", p->dtype);
+  if (p->q_block != 64 && p->q_block != 128)
+    return fail(SPARSEPR_ERR_UNSUPPORTED, "q_block must be 64 or 128 (got %d)", p->q_block);
+  if ((int64_t)p->heads * p->n_tokens * p->head_dim > (int64_t(1) << 40))
+    return fail(SPARSEPR_ERR_UNSUPPORTED, "H*N*d too large");
+  if ((int64_t)p->n_tokens * p->head_dim >= (int64_t(1) << 31))
+    return fail(SPARSEPR_ERR_UNSUPPORTED, "N*d must fit in 31 bits");
+  d->H = p->heads;
+  d->N = p->n_tokens;
+  d->D = p->head_dim;
+  d->bf16 = p->dtype == SPARSEPR_BF16;
+  d->BQ = p->q_block;
+  d->nb = (d->N + d->BQ - 1) / d->BQ;
+  d->nchunk = (d->N + 255) / 256;
+  d->ntile64 = (d->N + 63) / 64;
+  d->G = 1;
+  d->S = 1;
+  d->T = 1;
+  d->m = 0;
+  d->k = 0;
+  d->mode = 0;
+  d->rho = 1.0;
+  d->lam = 1.0;
+  d->kappa = d->N;
+  d->gbits = 0;
+  d->nsplit = 1;
+  d->split_len = d->N;
+  if (!full) return SPARSEPR_OK;
+  if (p->reserved != 0) return fail(SPARSEPR_ERR_INVALID_ARG, "reserved must be 0");
+  if (p->partition_mode != SPARSEPR_RESPONSE_COUPLED && p->partition_mode != SPARSEPR_RANDOM_BLOCK)
+    return fail(SPARSEPR_ERR_INVALID_ARG, "partition_mode must be 0 or 1 (got %d)", p->partition_mode);
+  if (p->n_groups < 1 || p->n_groups > 1024 || p->n_groups > p->n_tokens)
+    return fail(SPARSEPR_ERR_INVALID_ARG, "n_groups must be in [1, min(N, 1024)] (got %d)", p->n_groups);
+  if (p->partition_mode == SPARSEPR_RESPONSE_COUPLED) {
+    if (p->n_samples < 1 || p->n_samples > p->n_tokens)
+      return fail(SPARSEPR_ERR_INVALID_ARG, "n_samples must be in [1, N] (got %d)", p->n_samples);
+    if (p->kmeans_iters < 1)
+      return fail(SPARSEPR_ERR_INVALID_ARG, "kmeans_iters must be >= 1 (got %d)", p->kmeans_iters);
+  }
+  if (!(p->density > 0.0 && p->density <= 1.0))
+    return fail(SPARSEPR_ERR_INVALID_ARG, "density must be in (0, 1] (got %g)", p->density);
+  if (p->n_probes < 0 || p->n_probes > p->n_tokens)
+    return fail(SPARSEPR_ERR_INVALID_ARG, "n_probes must be in [0, N] (got %d)", p->n_probes);
+  if (p->rank < 0 || p->rank > p->head_dim)
+    return fail(SPARSEPR_ERR_INVALID_ARG, "rank must be in [0, d] (got %d)", p->rank);
+  if (!(p->ridge_lambda > 0.0) || !std::isfinite(p->ridge_lambda))
+    return fail(SPARSEPR_ERR_INVALID_ARG, "ridge_lambda must be > 0 (got %g)", p->ridge_lambda);
+  const double kap = std::floor(p->density * (double)p->n_tokens - (double)p->n_probes);
+  if (kap < 1.0)
+    return fail(SPARSEPR_ERR_INVALID_ARG,
+                "key budget floor(density*N - n_probes) = %.0f must be >= 1", kap);
+  d->G = p->n_groups;
+  d->S = p->n_samples;
+  d->T = p->kmeans_iters;
+  d->m = p->n_probes;
+  d->k = p->rank;
+  d->mode = p->partition_mode;
+  d->rho = p->density;
+  d->lam = p->ridge_lambda;
+  d->kappa = (int64_t)kap;
+  d->gbits = bits_for(d->G);
+  if (d->m > 0) {
+    const int nqb = (d->m + d->BQ - 1) / d->BQ;
+    const int items = d->H * nqb;
+    int nsplit = (1024 + items - 1) / items;
+    nsplit = std::max(1, std::min(nsplit, (d->N + 255) / 256));
+    int len = (d->N + nsplit - 1) / nsplit;
+    len = (len + 63) / 64 * 64;
+    d->split_len = len;
+    d->nsplit = (d->N + len - 1) / len;
+  }
+  return SPARSEPR_OK;
+}
+
+static size_t total_ws(const Dims& d) {
+  return std::max(partition_ws(d).end, std::max(route_ws(d).end, probe_ws(d).end));
+}
+
+#define SPR_REQUIRE(ptr, name) \
+  if ((ptr) == nullptr) return fail(SPARSEPR_ERR_INVALID_ARG, "%s is NULL", name)
+
+static int32_t check_ws(const Dims& d, const void* ws, size_t ws_bytes) {
+  const size_t need = total_ws(d);
+  if (ws == nullptr || ws_bytes < need)
+    return fail(SPARSEPR_ERR_WORKSPACE, "workspace of %zu bytes needed (got %zu%s)", need, ws_bytes,
+                ws == nullptr ? ", NULL" : "");
+  return SPARSEPR_OK;
+}
+
+static int32_t hip_status(hipError_t e, const char* stage) {
+  if (e == hipSuccess) {
+    g_last_error[0] = 0;
+    return SPARSEPR_OK;
+  }
+  return fail(SPARSEPR_ERR_HIP, "%s: %s", stage, hipGetErrorString(e));
+}
+
+}  // namespace spr
+
+using namespace spr;
+
+extern "C" {
+
+int32_t sparsepr_abi_version(void) { return SPARSEPR_ABI_VERSION; }
+
+const char* sparsepr_status_string(int32_t status) {
+  switch (status) {
+    case SPARSEPR_OK: return "SPARSEPR_OK";
+    case SPARSEPR_ERR_INVALID_ARG: return "SPARSEPR_ERR_INVALID_ARG";
+    case SPARSEPR_ERR_UNSUPPORTED: return "SPARSEPR_ERR_UNSUPPORTED";
+    case SPARSEPR_ERR_WORKSPACE: return "SPARSEPR_ERR_WORKSPACE";
+    case SPARSEPR_ERR_HIP: return "SPARSEPR_ERR_HIP";
+    default: return "SPARSEPR_UNKNOWN_STATUS";
+  }
+}
+
+const char* sparsepr_last_error(void) { return g_last_error; }
+
+int32_t sparsepr_workspace_bytes(const sparsepr_params* params, size_t* bytes) {
+  Dims d;
+  const int32_t s = make_dims(params, true, &d);
+  if (s != SPARSEPR_OK) return s;
+  SPR_REQUIRE(bytes, "bytes");
+  *bytes = total_ws(d);
+  return SPARSEPR_OK;
+}
+
+int32_t sparsepr_partition(const sparsepr_params* params, const void* Q, const void* K,
+                           const void* V, const float* scale, const int32_t* sample_idx,
+                           const int32_t* init_idx, const int32_t* rand_key_perm,
+                           int32_t* key_label, int32_t* key_perm, int32_t* group_off,
+                           float* key_centroid, void* Kp, void* Vp, float* dbg_assign_scores,
+                           void* workspace, size_t workspace_bytes, void* stream) {
+  Dims d;
+  int32_t s = make_dims(params, true, &d);
+  if (s != SPARSEPR_OK) return s;
+  SPR_REQUIRE(K, "K");
+  SPR_REQUIRE(V, "V");
+  if (d.mode == SPARSEPR_RESPONSE_COUPLED) {
+    SPR_REQUIRE(Q, "Q");
+    SPR_REQUIRE(scale, "scale");
+    SPR_REQUIRE(sample_idx, "sample_idx");
+    SPR_REQUIRE(init_idx, "init_idx");
+  } else {
+    SPR_REQUIRE(rand_key_perm, "rand_key_perm");
+  }
+  SPR_REQUIRE(key_label, "key_label");
+  SPR_REQUIRE(key_perm, "key_perm");
+  SPR_REQUIRE(group_off, "group_off");
+  SPR_REQUIRE(key_centroid, "key_centroid");
+  SPR_REQUIRE(Kp, "Kp");
+  SPR_REQUIRE(Vp, "Vp");
+  if ((s = check_ws(d, workspace, workspace_bytes)) != SPARSEPR_OK) return s;
+  return hip_status(launch_partition(d, Q, K, V, scale, sample_idx, init_idx, rand_key_perm,
+                                     key_label, key_perm, group_off, key_centroid, Kp, Vp,
+                                     dbg_assign_scores, static_cast<char*>(workspace),
+                                     static_cast<hipStream_t>(stream)),
+                    "sparsepr_partition");
+}
+
+int32_t sparsepr_route(const sparsepr_params* params, const void* Q, const float* scale,
+                       const float* key_centroid, const int32_t* group_off,
+                       const int32_t* rand_query_perm, int32_t* query_perm, int32_t* block_ptr,
+                       int32_t* block_groups, int64_t* executed_pairs, float* dbg_coords,
+                       int32_t* dbg_dominant, float* dbg_dominant_val, float* dbg_block_score,
+                       void* workspace, size_t workspace_bytes, void* stream) {
+  Dims d;
+  int32_t s = make_dims(params, true, &d);
+  if (s != SPARSEPR_OK) return s;
+  SPR_REQUIRE(Q, "Q");
+  SPR_REQUIRE(scale, "scale");
+  SPR_REQUIRE(key_centroid, "key_centroid");
+  SPR_REQUIRE(group_off, "group_off");
+  if (d.mode == SPARSEPR_RANDOM_BLOCK) SPR_REQUIRE(rand_query_perm, "rand_query_perm");
+  SPR_REQUIRE(query_perm, "query_perm");
+  SPR_REQUIRE(block_ptr, "block_ptr");
+  SPR_REQUIRE(block_groups, "block_groups");
+  SPR_REQUIRE(executed_pairs, "executed_pairs");
+  if ((s = check_ws(d, workspace, workspace_bytes)) != SPARSEPR_OK) return s;
+  return hip_status(launch_route(d, Q, scale, key_centroid, group_off, rand_query_perm,
+                                 query_perm, block_ptr, block_groups, executed_pairs, dbg_coords,
+                                 dbg_dominant, dbg_dominant_val, dbg_block_score,
+                                 static_cast<char*>(workspace), static_cast<hipStream_t>(stream)),
+                    "sparsepr_route");
+}
+
+int32_t sparsepr_attend(const sparsepr_params* params, const void* Q, const void* Kp,
+                        const void* Vp, const float* scale, const int32_t* group_off,
+                        const int32_t* query_perm, const int32_t* block_ptr,
+                        const int32_t* block_groups, float* S_out, float* lse, void* stream) {
+  Dims d;
+  int32_t s = make_dims(params, true, &d);
+  if (s != SPARSEPR_OK) return s;
+  SPR_REQUIRE(Q, "Q");
+  SPR_REQUIRE(Kp, "Kp");
+  SPR_REQUIRE(Vp, "Vp");
+  SPR_REQUIRE(scale, "scale");
+  SPR_REQUIRE(group_off, "group_off");
+  SPR_REQUIRE(query_perm, "query_perm");
+  SPR_REQUIRE(block_ptr, "block_ptr");
+  SPR_REQUIRE(block_groups, "block_groups");
+  SPR_REQUIRE(S_out, "S_out");
+  SPR_REQUIRE(lse, "lse");
+  AttnArgs a{};
+  a.Q = Q;
+  a.K = Kp;
+  a.V = Vp;
+  a.scale = scale;
+  a.H = d.H;
+  a.N = d.N;
+  a.m = d.m;
+  a.nsplit = 1;
+  a.split_len = d.N;
+  a.G = d.G;
+  a.nb = d.nb;
+  a.query_perm = query_perm;
+  a.block_ptr = block_ptr;
+  a.block_groups = block_groups;
+  a.group_off = group_off;
+  a.out = S_out;
+  a.lse = lse;
+  return hip_status(launch_attention(d, ATTN_SPARSE, a, static_cast<hipStream_t>(stream)),
+                    "sparsepr_attend");
+}
+
+int32_t sparsepr_probe_fit(const sparsepr_params* params, const void* Q, const void* K,
+                           const void* V, const float* scale, const int32_t* query_perm,
+                           const float* S_out, float* O_probe, float* U, float* Theta,
+                           int32_t* rank_eff, void* workspace, size_t workspace_bytes,
+                           void* stream) {
+  Dims d;
+  int32_t s = make_dims(params, true, &d);
+  if (s != SPARSEPR_OK) return s;
+  SPR_REQUIRE(rank_eff, "rank_eff");
+  if (d.m > 0) {
+    SPR_REQUIRE(Q, "Q");
+    SPR_REQUIRE(K, "K");
+    SPR_REQUIRE(V, "V");
+    SPR_REQUIRE(scale, "scale");
+    SPR_REQUIRE(query_perm, "query_perm");
+    SPR_REQUIRE(S_out, "S_out");
+    SPR_REQUIRE(O_probe, "O_probe");
+  }
+  if (d.k > 0) {
+    SPR_REQUIRE(U, "U");
+    SPR_REQUIRE(Theta, "Theta");
+  }
+  if ((s = check_ws(d, workspace, workspace_bytes)) != SPARSEPR_OK) return s;
+  const hipStream_t st = static_cast<hipStream_t>(stream);
+  const ProbeWs L = probe_ws(d);
+  char* ws = static_cast<char*>(workspace);
+  hipError_t e = hipSuccess;
+  if (d.m > 0) {
+    AttnArgs a{};
+    a.Q = Q;
+    a.K = K;
+    a.V = V;
+    a.scale = scale;
+    a.H = d.H;
+    a.N = d.N;
+    a.m = d.m;
+    a.nsplit = d.nsplit;
+    a.split_len = d.split_len;
+    a.G = d.G;
+    a.nb = d.nb;
+    a.query_perm = query_perm;
+    a.opart = reinterpret_cast<float*>(ws + L.opart);
+    a.lsepart = reinterpret_cast<float*>(ws + L.lsepart);
+    e = launch_attention(d, ATTN_PROBE, a, st);
+    if (e == hipSuccess) e = launch_probe_merge(d, a.opart, a.lsepart, O_probe, st);
+  }
+  if (e == hipSuccess) {
+    if (d.m > 0 && d.k > 0) {
+      e = launch_fit(d, S_out, O_probe, U, Theta, rank_eff, ws + L.fit, st);
+    } else {
+      e = launch_fill_i32(rank_eff, (size_t)d.H, 0, st);
+      if (e == hipSuccess && d.k > 0) e = launch_fill_f32(U, (size_t)d.H * d.D * d.k, 0.f, st);
+      if (e == hipSuccess && d.k > 0)
+        e = launch_fill_f32(Theta, (size_t)d.H * (d.D + 1) * d.k, 0.f, st);
+    }
+  }
+  return hip_status(e, "sparsepr_probe_fit");
+}
+
+int32_t sparsepr_apply(const sparsepr_params* params, const float* S_out,
+                       const int32_t* query_perm, const float* O_probe, const float* U,
+                       const float* Theta, const int32_t* rank_eff, void* O, void* stream) {
+  Dims d;
+  int32_t s = make_dims(params, true, &d);
+  if (s != SPARSEPR_OK) return s;
+  SPR_REQUIRE(S_out, "S_out");
+  SPR_REQUIRE(query_perm, "query_perm");
+  SPR_REQUIRE(rank_eff, "rank_eff");
+  SPR_REQUIRE(O, "O");
+  if (d.m > 0) SPR_REQUIRE(O_probe, "O_probe");
+  if (d.k > 0) {
+    SPR_REQUIRE(U, "U");
+    SPR_REQUIRE(Theta, "Theta");
+  }
+  return hip_status(launch_apply(d, S_out, query_perm, O_probe, U, Theta, rank_eff, O,
+                                 static_cast<hipStream_t>(stream)),
+                    "sparsepr_apply");
+}
+
+int32_t sparsepr_dense_attention(const sparsepr_params* params, const void* Q, const void* K,
+                                 const void* V, const float* scale, void* O, float* lse,
+                                 void* stream) {
+  Dims d;
+  int32_t s = make_dims(params, false, &d);
+  if (s != SPARSEPR_OK) return s;
+  SPR_REQUIRE(Q, "Q");
+  SPR_REQUIRE(K, "K");
+  SPR_REQUIRE(V, "V");
+  SPR_REQUIRE(scale, "scale");
+  SPR_REQUIRE(O, "O");
+  AttnArgs a{};
+  a.Q = Q;
+  a.K = K;
+  a.V = V;
+  a.scale = scale;
+  a.H = d.H;
+  a.N = d.N;
+  a.nsplit = 1;
+  a.split_len = d.N;
+  a.G = 1;
+  a.nb = d.nb;
+  a.out = O;
+  a.lse = lse;
+  return hip_status(launch_attention(d, ATTN_DENSE, a, static_cast<hipStream_t>(stream)),
+                    "sparsepr_dense_attention");
+}
+
+}  // extern "C"

@@ -1,0 +1,518 @@
+// Attention kernels: block-sparse over routed key groups, dense, and the
+// split-key pass for the exact probe rows (arxivdaily 2608.18484, English
+// abstract: attention only between selected groups; exact attention on a
+// small set of query rows).
+//
+// bf16 path (gfx950 MFMA, v_mfma_f32_32x32x16_bf16). One workgroup owns one
+// query block of BQ rows; each wavefront owns 32 query rows. Keys stream in
+// tiles of 64 through double-buffered LDS. The product is formed transposed,
+// S^T = K Q^T, so each lane holds the logits of ONE query (lane % 32) for 16
+// keys of each 32-key half: the online-softmax statistics are per-lane
+// scalars, and the probabilities are already in the B-operand layout of
+// O^T = V^T P^T. V stays row-major in LDS (chunks XOR-swizzled) and is read
+// transposed with ds_read_b64_tr_b16. The key list of a block is the
+// concatenation of its routed groups' ranges in the group-contiguous Kp/Vp;
+// tiles run across group boundaries, so only the block's last tile is ragged.
+#include "common.hpp"
+#include "internal.hpp"
+
+namespace spr {
+
+constexpr int kMaxRanges = 1024;
+
+template <int D>
+__device__ __forceinline__ int v_swizzle(int r) {
+  return D == 128 ? 4 * (r & 3) : 4 * ((r >> 1) & 1);
+}
+
+// Decoded work item of one workgroup.
+struct Item {
+  int h, b, sp;
+};
+
+template <int MODE>
+__device__ __forceinline__ Item decode_item(const AttnArgs& a, int nqb) {
+  const int total = (MODE == ATTN_PROBE ? nqb * a.nsplit : nqb) * a.H;
+  const int L = xcd_remap(blockIdx.x, total);
+  Item it;
+  if (MODE == ATTN_PROBE) {
+    const int per = nqb * a.nsplit;
+    it.h = L / per;
+    const int r = L % per;
+    it.b = r / a.nsplit;
+    it.sp = r % a.nsplit;
+  } else {
+    it.h = L / nqb;
+    it.b = L % nqb;
+    it.sp = 0;
+  }
+  return it;
+}
+
+// Token of query row qi of the work item; sets *pos to the output row.
+template <int MODE, int BQ>
+__device__ __forceinline__ int query_token(const AttnArgs& a, const Item& it, int qi, int* pos,
+                                           bool* valid) {
+  if (MODE == ATTN_PROBE) {
+    const int pi = it.b * BQ + qi;
+    *valid = pi < a.m;
+    *pos = pi;
+    if (!*valid) return 0;
+    const int p = (int)(((2LL * pi + 1) * a.N) / (2LL * a.m));
+    return clamp_idx(a.query_perm[(size_t)it.h * a.N + p], a.N);
+  }
+  const int p = it.b * BQ + qi;
+  *pos = p;
+  *valid = p < a.N;
+  if (!*valid) return 0;
+  if (MODE == ATTN_SPARSE) return clamp_idx(a.query_perm[(size_t)it.h * a.N + p], a.N);
+  return p;
+}
+
+// Fills r_start / r_cum (exclusive prefix, r_cum[ng] = total) in LDS and
+// returns the number of ranges. Contains __syncthreads().
+template <int MODE, int NT>
+__device__ __forceinline__ int build_ranges(const AttnArgs& a, const Item& it, int* r_start,
+                                            int* r_cum, int* tmp) {
+  const int t = threadIdx.x;
+  if (MODE != ATTN_SPARSE) {
+    if (t == 0) {
+      int lo = 0, hi = a.N;
+      if (MODE == ATTN_PROBE) {
+        lo = it.sp * a.split_len;
+        hi = min(a.N, lo + a.split_len);
+      }
+      r_start[0] = lo;
+      r_cum[0] = 0;
+      r_cum[1] = hi - lo;
+    }
+    __syncthreads();
+    return 1;
+  }
+  const int32_t* bp = a.block_ptr + (size_t)it.h * (a.nb + 1);
+  const int p0 = bp[it.b];
+  int ng = bp[it.b + 1] - p0;
+  ng = ng < 0 ? 0 : (ng > kMaxRanges ? kMaxRanges : ng);
+  const int32_t* grp = a.block_groups + (size_t)it.h * a.nb * a.G + p0;
+  const int32_t* off = a.group_off + (size_t)it.h * (a.G + 1);
+  int carry = 0;
+  for (int base = 0; base < ng; base += NT) {
+    const int i = base + t;
+    int len = 0;
+    if (i < ng) {
+      const int g = clamp_idx(grp[i], a.G);
+      const int st = off[g];
+      len = off[g + 1] - st;
+      if (len < 0) len = 0;
+      r_start[i] = st;
+    }
+    int tot;
+    const int ex = block_exclusive_scan<NT>(len, tmp, &tot);
+    if (i < ng) r_cum[i] = carry + ex;
+    carry += tot;
+  }
+  if (t == 0) r_cum[ng] = carry;
+  __syncthreads();
+  return ng;
+}
+
+// Row of Kp/Vp at key position p of the block's list (cursor advances
+// monotonically across tiles).
+__device__ __forceinline__ int key_row(int p, int total, int ng, const int* r_start,
+                                       const int* r_cum, int& cur) {
+  if (p >= total) return r_start[0];
+  while (cur + 1 < ng && r_cum[cur + 1] <= p) ++cur;
+  return r_start[cur] + (p - r_cum[cur]);
+}
+
+template <int D, int BQ, int MODE>
+__global__ __launch_bounds__(BQ * 2) void k_attn_mfma(AttnArgs a) {
+  constexpr int NT = BQ * 2;
+  constexpr int KT = 64;
+  constexpr int ROWB = D * 2;
+  constexpr int CPR = ROWB / 16;
+  constexpr int TPR = NT / KT;
+  constexpr int CPT = CPR / TPR;
+  constexpr int KPITCH = ROWB + 16;
+  constexpr int VPITCH = ROWB;
+  constexpr int NDT = D / 32;   // 32-wide output d tiles
+  constexpr int NKK = D / 16;   // k-steps of the QK^T product
+  __shared__ __attribute__((aligned(16))) char lds_k[2][KT * KPITCH];
+  __shared__ __attribute__((aligned(16))) char lds_v[2][KT * VPITCH];
+  __shared__ int r_start[kMaxRanges + 1];
+  __shared__ int r_cum[kMaxRanges + 2];
+  __shared__ int tmp[NT];
+
+  const int nqb = MODE == ATTN_PROBE ? (a.m + BQ - 1) / BQ : a.nb;
+  const Item it = decode_item<MODE>(a, nqb);
+  const int t = threadIdx.x;
+  const int lane = t & 63, w = t >> 6;
+  const int hl = lane >> 5;       // which half of the wave
+  const int ql = lane & 31;       // query within the wave
+  const size_t hoff = (size_t)it.h * a.N * D;
+  const uint16_t* Qh = static_cast<const uint16_t*>(a.Q) + hoff;
+  const char* Kh = static_cast<const char*>(a.K) + hoff * 2;
+  const char* Vh = static_cast<const char*>(a.V) + hoff * 2;
+
+  const int ng = build_ranges<MODE, NT>(a, it, r_start, r_cum, tmp);
+  const int total = r_cum[ng];
+
+  // Q operand: B of S^T = K Q^T; lane holds query ql, d = 16 kk + 8 hl + 0..7
+  int qpos;
+  bool qvalid;
+  const int qtok = query_token<MODE, BQ>(a, it, w * 32 + ql, &qpos, &qvalid);
+  bf16x8 qreg[NKK];
+#pragma unroll
+  for (int kk = 0; kk < NKK; ++kk)
+    qreg[kk] = *reinterpret_cast<const bf16x8*>(Qh + (size_t)qtok * D + 16 * kk + 8 * hl);
+
+  const float c = a.scale[it.h] * kLog2e;
+  float m_run = -__builtin_inff();
+  float l_run = 0.f;
+  f32x16 acc_o[NDT];
+#pragma unroll
+  for (int dt = 0; dt < NDT; ++dt)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) acc_o[dt][r] = 0.f;
+
+  const int ntiles = (total + KT - 1) / KT;
+  const int lrow = t / TPR;       // row this thread loads
+  const int lch0 = t % TPR;       // first chunk; chunks lch0 + TPR*u
+  int cursor = 0;
+  uint4 kreg[CPT], vreg[CPT];
+
+  auto load_tile = [&](int tile) {
+    const int row = key_row(tile * KT + lrow, total, ng, r_start, r_cum, cursor);
+#pragma unroll
+    for (int u = 0; u < CPT; ++u) {
+      const int ch = lch0 + TPR * u;
+      kreg[u] = *reinterpret_cast<const uint4*>(Kh + (size_t)row * ROWB + ch * 16);
+      vreg[u] = *reinterpret_cast<const uint4*>(Vh + (size_t)row * ROWB + ch * 16);
+    }
+  };
+  auto store_tile = [&](int buf) {
+#pragma unroll
+    for (int u = 0; u < CPT; ++u) {
+      const int ch = lch0 + TPR * u;
+      *reinterpret_cast<uint4*>(&lds_k[buf][lrow * KPITCH + ch * 16]) = kreg[u];
+      *reinterpret_cast<uint4*>(&lds_v[buf][lrow * VPITCH + ((ch ^ v_swizzle<D>(lrow)) * 16)]) = vreg[u];
+    }
+  };
+
+  if (ntiles > 0) {
+    load_tile(0);
+    store_tile(0);
+  }
+  __syncthreads();
+
+  for (int tile = 0; tile < ntiles; ++tile) {
+    const int buf = tile & 1;
+    const bool more = tile + 1 < ntiles;
+    if (more) load_tile(tile + 1);
+
+    // ---- S^T = K Q^T for the 64-key tile (two 32-key halves)
+    f32x16 s[2];
+#pragma unroll
+    for (int kt = 0; kt < 2; ++kt) {
+#pragma unroll
+      for (int r = 0; r < 16; ++r) s[kt][r] = 0.f;
+      const char* krow = &lds_k[buf][(32 * kt + ql) * KPITCH];
+#pragma unroll
+      for (int kk = 0; kk < NKK; ++kk) {
+        const bf16x8 kop = *reinterpret_cast<const bf16x8*>(krow + (16 * kk + 8 * hl) * 2);
+        s[kt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kop, qreg[kk], s[kt], 0, 0, 0);
+      }
+    }
+    // ---- online softmax (log2 domain), lazy rescale
+    const int kbase = tile * KT;
+    float mx = -__builtin_inff();
+#pragma unroll
+    for (int kt = 0; kt < 2; ++kt)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int kp = kbase + 32 * kt + 8 * (r >> 2) + 4 * hl + (r & 3);
+        const float x = kp < total ? s[kt][r] * c : -__builtin_inff();
+        s[kt][r] = x;
+        mx = fmaxf(mx, x);
+      }
+    mx = fmaxf(mx, __shfl_xor(mx, 32));
+    const float m_new = fmaxf(m_run, mx);
+    const bool need = m_new > m_run + 8.0f;
+    if (__any(need)) {
+      const float alpha = need ? __builtin_amdgcn_exp2f(m_run - m_new) : 1.0f;
+      l_run *= alpha;
+#pragma unroll
+      for (int dt = 0; dt < NDT; ++dt)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) acc_o[dt][r] *= alpha;
+      if (need) m_run = m_new;
+    }
+    bf16x8 pk[2][2];
+#pragma unroll
+    for (int kt = 0; kt < 2; ++kt)
+#pragma unroll
+      for (int hf = 0; hf < 2; ++hf) {
+        float pv[8];
+#pragma unroll
+        for (int q = 0; q < 8; ++q) {
+          pv[q] = __builtin_amdgcn_exp2f(s[kt][8 * hf + q] - m_run);
+          l_run += pv[q];
+        }
+#pragma unroll
+        for (int q = 0; q < 8; q += 2) {
+          const f32x2 f = {pv[q], pv[q + 1]};
+          const bf16x2 bb = __builtin_convertvector(f, bf16x2);
+          pk[kt][hf][q] = bb[0];
+          pk[kt][hf][q + 1] = bb[1];
+        }
+      }
+    // ---- O^T += V^T P^T; V^T operand via transposing LDS reads
+    const int grp = lane >> 4, gl = lane & 15;
+#pragma unroll
+    for (int kt = 0; kt < 2; ++kt)
+#pragma unroll
+      for (int hf = 0; hf < 2; ++hf) {
+        const int chunk = 32 * kt + 16 * hf;
+#pragma unroll
+        for (int dt = 0; dt < NDT; ++dt) {
+          const int d = 32 * dt + 16 * (grp & 1) + 4 * (gl & 3);
+          const int r1 = chunk + 4 * (grp >> 1) + (gl >> 2);
+          const int r2 = r1 + 8;
+          const char* p1 = &lds_v[buf][r1 * VPITCH + (((d >> 3) ^ v_swizzle<D>(r1)) * 16) + (d & 4) * 2];
+          const char* p2 = &lds_v[buf][r2 * VPITCH + (((d >> 3) ^ v_swizzle<D>(r2)) * 16) + (d & 4) * 2];
+          const s16x4 v1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+              (__attribute__((address_space(3))) s16x4*)(p1));
+          const s16x4 v2 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+              (__attribute__((address_space(3))) s16x4*)(p2));
+          const s16x8 vv = __builtin_shufflevector(v1, v2, 0, 1, 2, 3, 4, 5, 6, 7);
+          acc_o[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, vv),
+                                                              pk[kt][hf], acc_o[dt], 0, 0, 0);
+        }
+      }
+    if (more) store_tile(buf ^ 1);
+    __syncthreads();
+  }
+
+  // ---- epilogue
+  const float l_tot = l_run + __shfl_xor(l_run, 32);
+  const float inv = l_tot > 0.f ? 1.0f / l_tot : 0.f;
+  const float lse = l_tot > 0.f ? (m_run + log2f(l_tot)) * kLn2 : -__builtin_inff();
+  if (!qvalid) return;
+  if (MODE == ATTN_PROBE) {
+    float* op = a.opart + (((size_t)it.h * a.nsplit + it.sp) * a.m + qpos) * D;
+#pragma unroll
+    for (int dt = 0; dt < NDT; ++dt)
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const int d0 = 32 * dt + 8 * j + 4 * hl;
+        const f32x4 v = {acc_o[dt][4 * j] * inv, acc_o[dt][4 * j + 1] * inv,
+                         acc_o[dt][4 * j + 2] * inv, acc_o[dt][4 * j + 3] * inv};
+        *reinterpret_cast<f32x4*>(op + d0) = v;
+      }
+    if (hl == 0) a.lsepart[((size_t)it.h * a.nsplit + it.sp) * a.m + qpos] = lse;
+  } else if (MODE == ATTN_SPARSE) {
+    float* out = static_cast<float*>(a.out) + hoff + (size_t)qpos * D;
+#pragma unroll
+    for (int dt = 0; dt < NDT; ++dt)
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const int d0 = 32 * dt + 8 * j + 4 * hl;
+        const f32x4 v = {acc_o[dt][4 * j] * inv, acc_o[dt][4 * j + 1] * inv,
+                         acc_o[dt][4 * j + 2] * inv, acc_o[dt][4 * j + 3] * inv};
+        *reinterpret_cast<f32x4*>(out + d0) = v;
+      }
+  } else {
+    uint16_t* out = static_cast<uint16_t*>(a.out) + hoff + (size_t)qpos * D;
+#pragma unroll
+    for (int dt = 0; dt < NDT; ++dt)
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const int d0 = 32 * dt + 8 * j + 4 * hl;
+        const f32x2 f0 = {acc_o[dt][4 * j] * inv, acc_o[dt][4 * j + 1] * inv};
+        const f32x2 f1 = {acc_o[dt][4 * j + 2] * inv, acc_o[dt][4 * j + 3] * inv};
+        const bf16x2 b0 = __builtin_convertvector(f0, bf16x2);
+        const bf16x2 b1 = __builtin_convertvector(f1, bf16x2);
+        const bf16x4 bv = {b0[0], b0[1], b1[0], b1[1]};
+        *reinterpret_cast<bf16x4*>(out + d0) = bv;
+      }
+  }
+  if (MODE != ATTN_PROBE) {
+    if (hl == 0 && a.lse != nullptr) a.lse[(size_t)it.h * a.N + qpos] = lse;
+  }
+}
+
+// fp32 path: 64 query rows per workgroup, 4 lanes per query (dims 4u + lane%4),
+// key tiles of 32 rows in LDS; online softmax per tile.
+template <int D, int MODE>
+__global__ __launch_bounds__(256) void k_attn_valu(AttnArgs a, int BQ) {
+  constexpr int NT = 256;
+  constexpr int KT = 32;
+  constexpr int DU = D / 4;
+  __shared__ float kt_s[KT][D];
+  __shared__ float vt_s[KT][D];
+  __shared__ int r_start[kMaxRanges + 1];
+  __shared__ int r_cum[kMaxRanges + 2];
+  __shared__ int tmp[NT];
+  const int sub_per_block = BQ / 64;
+  const int nqb = MODE == ATTN_PROBE ? (a.m + BQ - 1) / BQ : a.nb;
+  const int total_items = (MODE == ATTN_PROBE ? nqb * a.nsplit : nqb) * a.H * sub_per_block;
+  const int Lw = xcd_remap(blockIdx.x, total_items);
+  const int sub = Lw % sub_per_block;
+  const int L = Lw / sub_per_block;
+  Item it;
+  if (MODE == ATTN_PROBE) {
+    const int per = nqb * a.nsplit;
+    it.h = L / per;
+    it.b = (L % per) / a.nsplit;
+    it.sp = (L % per) % a.nsplit;
+  } else {
+    it.h = L / nqb;
+    it.b = L % nqb;
+    it.sp = 0;
+  }
+  const int t = threadIdx.x;
+  const int qq = t & 3;
+  const int qi = sub * 64 + (t >> 2);
+  const size_t hoff = (size_t)it.h * a.N * D;
+  const float* Qh = static_cast<const float*>(a.Q) + hoff;
+  const float* Kh = static_cast<const float*>(a.K) + hoff;
+  const float* Vh = static_cast<const float*>(a.V) + hoff;
+
+  const int ng = build_ranges<MODE, NT>(a, it, r_start, r_cum, tmp);
+  const int total = r_cum[ng];
+  int qpos;
+  bool qvalid;
+  int qtok;
+  if (MODE == ATTN_PROBE) {
+    const int pi = it.b * BQ + qi;
+    qvalid = pi < a.m;
+    qpos = pi;
+    qtok = qvalid ? clamp_idx(a.query_perm[(size_t)it.h * a.N +
+                                           (int)(((2LL * pi + 1) * a.N) / (2LL * a.m))], a.N) : 0;
+  } else {
+    qpos = it.b * BQ + qi;
+    qvalid = qpos < a.N;
+    qtok = !qvalid ? 0 : (MODE == ATTN_SPARSE ? clamp_idx(a.query_perm[(size_t)it.h * a.N + qpos], a.N) : qpos);
+  }
+  float q[DU], o[DU];
+#pragma unroll
+  for (int u = 0; u < DU; ++u) {
+    q[u] = Qh[(size_t)qtok * D + 4 * u + qq];
+    o[u] = 0.f;
+  }
+  const float c = a.scale[it.h] * kLog2e;
+  float m_run = -__builtin_inff(), l_run = 0.f;
+  int cursor = 0;
+  const int ntiles = (total + KT - 1) / KT;
+  for (int tile = 0; tile < ntiles; ++tile) {
+    __syncthreads();
+    for (int f = t; f < KT * DU; f += NT) {
+      const int r = f / DU, c4 = f % DU;
+      // rows are visited in increasing order by each thread, so the cursor is monotone
+      const int row = key_row(tile * KT + r, total, ng, r_start, r_cum, cursor);
+      *reinterpret_cast<f32x4*>(&kt_s[r][4 * c4]) = *reinterpret_cast<const f32x4*>(Kh + (size_t)row * D + 4 * c4);
+      *reinterpret_cast<f32x4*>(&vt_s[r][4 * c4]) = *reinterpret_cast<const f32x4*>(Vh + (size_t)row * D + 4 * c4);
+    }
+    __syncthreads();
+    float x[KT];
+    float mx = -__builtin_inff();
+#pragma unroll
+    for (int j = 0; j < KT; ++j) {
+      float part = 0.f;
+#pragma unroll
+      for (int u = 0; u < DU; ++u) part = fmaf(q[u], kt_s[j][4 * u + qq], part);
+      part += __shfl_xor(part, 1);
+      part += __shfl_xor(part, 2);
+      x[j] = (tile * KT + j < total) ? part * c : -__builtin_inff();
+      mx = fmaxf(mx, x[j]);
+    }
+    const float m_new = fmaxf(m_run, mx);
+    const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
+    l_run *= alpha;
+#pragma unroll
+    for (int u = 0; u < DU; ++u) o[u] *= alpha;
+    m_run = m_new;
+#pragma unroll
+    for (int j = 0; j < KT; ++j) {
+      const float p = __builtin_amdgcn_exp2f(x[j] - m_run);
+      l_run += p;
+#pragma unroll
+      for (int u = 0; u < DU; ++u) o[u] = fmaf(p, vt_s[j][4 * u + qq], o[u]);
+    }
+  }
+  const float inv = l_run > 0.f ? 1.0f / l_run : 0.f;
+  const float lse = l_run > 0.f ? (m_run + log2f(l_run)) * kLn2 : -__builtin_inff();
+  if (!qvalid) return;
+  if (MODE == ATTN_PROBE) {
+    float* op = a.opart + (((size_t)it.h * a.nsplit + it.sp) * a.m + qpos) * D;
+#pragma unroll
+    for (int u = 0; u < DU; ++u) op[4 * u + qq] = o[u] * inv;
+    if (qq == 0) a.lsepart[((size_t)it.h * a.nsplit + it.sp) * a.m + qpos] = lse;
+  } else {
+    float* out = static_cast<float*>(a.out) + hoff + (size_t)qpos * D;
+#pragma unroll
+    for (int u = 0; u < DU; ++u) out[4 * u + qq] = o[u] * inv;
+    if (qq == 0 && a.lse != nullptr) a.lse[(size_t)it.h * a.N + qpos] = lse;
+  }
+}
+
+// O_probe = LSE-weighted merge of the split partials. grid (m, H), block D.
+template <int D>
+__global__ void k_probe_merge(const float* opart, const float* lsepart, int m, int nsplit,
+                              float* O_probe) {
+  const int i = blockIdx.x, h = blockIdx.y, e = threadIdx.x;
+  float mx = -__builtin_inff();
+  for (int s = 0; s < nsplit; ++s) mx = fmaxf(mx, lsepart[((size_t)h * nsplit + s) * m + i]);
+  float wsum = 0.f, acc = 0.f;
+  for (int s = 0; s < nsplit; ++s) {
+    const float ls = lsepart[((size_t)h * nsplit + s) * m + i];
+    const float wgt = ls == -__builtin_inff() ? 0.f : expf(ls - mx);
+    wsum += wgt;
+    acc += wgt * opart[(((size_t)h * nsplit + s) * m + i) * D + e];
+  }
+  O_probe[((size_t)h * m + i) * D + e] = wsum > 0.f ? acc / wsum : 0.f;
+}
+
+hipError_t launch_attention(const Dims& d, AttnMode mode, const AttnArgs& a, hipStream_t st) {
+  const int nqb = mode == ATTN_PROBE ? (d.m + d.BQ - 1) / d.BQ : (d.N + d.BQ - 1) / d.BQ;
+  const int items = (mode == ATTN_PROBE ? nqb * d.nsplit : nqb) * d.H;
+  AttnArgs aa = a;
+  aa.nb = mode == ATTN_PROBE ? a.nb : nqb;
+  if (d.bf16) {
+#define SPR_MFMA(DD, BB)                                                                    \
+  do {                                                                                      \
+    if (mode == ATTN_SPARSE) k_attn_mfma<DD, BB, ATTN_SPARSE><<<items, BB * 2, 0, st>>>(aa); \
+    else if (mode == ATTN_DENSE) k_attn_mfma<DD, BB, ATTN_DENSE><<<items, BB * 2, 0, st>>>(aa); \
+    else k_attn_mfma<DD, BB, ATTN_PROBE><<<items, BB * 2, 0, st>>>(aa);                     \
+  } while (0)
+    if (d.D == 128) {
+      if (d.BQ == 128) SPR_MFMA(128, 128); else SPR_MFMA(128, 64);
+    } else {
+      if (d.BQ == 128) SPR_MFMA(64, 128); else SPR_MFMA(64, 64);
+    }
+#undef SPR_MFMA
+  } else {
+    const int witems = items * (d.BQ / 64);
+#define SPR_VALU(DD)                                                                        \
+  do {                                                                                      \
+    if (mode == ATTN_SPARSE) k_attn_valu<DD, ATTN_SPARSE><<<witems, 256, 0, st>>>(aa, d.BQ); \
+    else if (mode == ATTN_DENSE) k_attn_valu<DD, ATTN_DENSE><<<witems, 256, 0, st>>>(aa, d.BQ); \
+    else k_attn_valu<DD, ATTN_PROBE><<<witems, 256, 0, st>>>(aa, d.BQ);                     \
+  } while (0)
+    if (d.D == 128) SPR_VALU(128); else SPR_VALU(64);
+#undef SPR_VALU
+  }
+  return hipGetLastError();
+}
+
+hipError_t launch_probe_merge(const Dims& d, const float* opart, const float* lsepart,
+                              float* O_probe, hipStream_t st) {
+  if (d.m == 0) return hipSuccess;
+  if (d.D == 128)
+    k_probe_merge<128><<<dim3(d.m, d.H), 128, 0, st>>>(opart, lsepart, d.m, d.nsplit, O_probe);
+  else
+    k_probe_merge<64><<<dim3(d.m, d.H), 64, 0, st>>>(opart, lsepart, d.m, d.nsplit, O_probe);
+  return hipGetLastError();
+}
+
+}  // namespace spr

@@ -1,0 +1,108 @@
+// Shared device helpers for the SparsePR gfx950 kernels.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace spr {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+typedef short s16x8 __attribute__((ext_vector_type(8)));
+
+constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kLn2 = 0.6931471805599453f;
+
+__device__ __forceinline__ float bf16_to_f32(uint16_t b) {
+  return __uint_as_float(static_cast<uint32_t>(b) << 16);
+}
+
+// Round-to-nearest-even conversion (v_cvt_pk_bf16_f32 on gfx950).
+__device__ __forceinline__ uint16_t f32_to_bf16(float f) {
+  __bf16 h = static_cast<__bf16>(f);
+  return __builtin_bit_cast(uint16_t, h);
+}
+
+// Element access for the two storage types of Q/K/V/S/O.
+template <bool BF16>
+struct Elt;
+template <>
+struct Elt<true> {
+  using T = uint16_t;
+  static __device__ __forceinline__ float ld(const T* p, size_t i) { return bf16_to_f32(p[i]); }
+  static __device__ __forceinline__ void st(T* p, size_t i, float v) { p[i] = f32_to_bf16(v); }
+};
+template <>
+struct Elt<false> {
+  using T = float;
+  static __device__ __forceinline__ float ld(const T* p, size_t i) { return p[i]; }
+  static __device__ __forceinline__ void st(T* p, size_t i, float v) { p[i] = v; }
+};
+
+__device__ __forceinline__ int clamp_idx(int i, int n) { return i < 0 ? 0 : (i >= n ? n - 1 : i); }
+
+// Orderable bit pattern of a float: ascending uint order == ascending value.
+// -0.0 is folded onto +0.0 so that equal values give equal keys.
+__device__ __forceinline__ uint32_t float_order_bits(float f) {
+  if (f == 0.0f) f = 0.0f;
+  uint32_t u = __float_as_uint(f);
+  return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+}
+// Key that sorts floats in DESCENDING order when sorted ascending.
+__device__ __forceinline__ uint32_t float_desc_bits(float f) { return ~float_order_bits(f); }
+
+// Workgroups are dispatched round-robin over the 8 XCDs; this maps the
+// dispatch id to a logical id so that each XCD receives one contiguous run of
+// logical work items (neighbouring blocks share keys, so they share its L2).
+__device__ __forceinline__ int xcd_remap(int w, int total) {
+  const int q = total / 8, rem = total % 8;
+  const int xcd = w % 8, idx = w / 8;
+  return xcd < rem ? xcd * (q + 1) + idx : rem * (q + 1) + (xcd - rem) * q + idx;
+}
+
+__device__ __forceinline__ uint64_t lanemask_lt() {
+  const int lane = __lane_id();
+  return lane == 0 ? 0ull : (~0ull >> (64 - lane));
+}
+
+// Exclusive scan of one int per thread across a workgroup of NT threads.
+// `tmp` must hold NT ints of shared memory. Returns the exclusive prefix and
+// writes the total to *total. Contains __syncthreads().
+template <int NT>
+__device__ __forceinline__ int block_exclusive_scan(int v, int* tmp, int* total) {
+  const int t = threadIdx.x;
+  tmp[t] = v;
+  __syncthreads();
+  for (int off = 1; off < NT; off <<= 1) {
+    int add = t >= off ? tmp[t - off] : 0;
+    __syncthreads();
+    tmp[t] += add;
+    __syncthreads();
+  }
+  int incl = tmp[t];
+  *total = tmp[NT - 1];
+  __syncthreads();
+  return incl - v;
+}
+
+template <int NT>
+__device__ __forceinline__ double block_sum_f64(double v, double* tmp) {
+  const int t = threadIdx.x;
+  tmp[t] = v;
+  __syncthreads();
+  for (int off = NT / 2; off > 0; off >>= 1) {
+    if (t < off) tmp[t] += tmp[t + off];
+    __syncthreads();
+  }
+  double r = tmp[0];
+  __syncthreads();
+  return r;
+}
+
+}  // namespace spr

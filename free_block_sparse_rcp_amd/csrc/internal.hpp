@@ -1,0 +1,99 @@
+// Host-side launchers shared between the C-ABI (api.hip) and the kernel files.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+#include "../../include/sparsepr.h"
+
+namespace spr {
+
+// Sizes derived from sparsepr_params, computed once per call on the host.
+struct Dims {
+  int H, N, D, G, S, T, BQ, nb, m, k;
+  bool bf16;
+  int mode;
+  double rho, lam;
+  int64_t kappa;
+  int nchunk;     // ceil(N / 256): chunks of the counting-sort passes
+  int ntile64;    // ceil(N / 64)
+  int gbits;      // bits needed for a group index (0 when G == 1)
+  int nsplit;     // probe attention: key splits
+  int split_len;  // probe attention: keys per split (multiple of 64)
+};
+
+// ---- workspace layout (byte offsets; one workspace serves every stage)
+struct PartitionWs {
+  size_t M, P, Phl, bvec, counts, totals, starts, partial, end;
+};
+struct RouteWs {
+  size_t keysA, keysB, valsA, valsB, counts, totals, starts, qbar, sigma, sel, selcnt, blkkeys,
+      end;
+};
+struct ProbeWs {
+  size_t opart, lsepart, fit, fit_per_head, end;
+};
+PartitionWs partition_ws(const Dims& d);
+RouteWs route_ws(const Dims& d);
+ProbeWs probe_ws(const Dims& d);
+size_t fit_ws_per_head(const Dims& d);
+
+// ---- partition.hip
+hipError_t launch_partition(const Dims& d, const void* Q, const void* K, const void* V,
+                            const float* scale, const int32_t* sample_idx, const int32_t* init_idx,
+                            const int32_t* rand_key_perm, int32_t* key_label, int32_t* key_perm,
+                            int32_t* group_off, float* kbar, void* Kp, void* Vp, float* dbg,
+                            char* ws, hipStream_t st);
+
+// counting-sort pass used by partition (labels) and route (query keys)
+hipError_t launch_sort_pass_u32(const Dims& d, const int32_t* keys_in, int bits,
+                                const int32_t* vals_in, int32_t* vals_out, int32_t* counts,
+                                int32_t* totals, int32_t* starts, int32_t* group_off_out,
+                                hipStream_t st);
+hipError_t launch_sort_pass_u64(const Dims& d, const uint64_t* keys_in, uint64_t* keys_out,
+                                int shift, int bits, const int32_t* vals_in, int32_t* vals_out,
+                                int32_t* counts, int32_t* totals, int32_t* starts, hipStream_t st);
+
+// fills by kernel (no memset nodes, so callers may capture the stream)
+hipError_t launch_fill_i32(int32_t* p, size_t n, int32_t v, hipStream_t st);
+hipError_t launch_fill_f32(float* p, size_t n, float v, hipStream_t st);
+
+// ---- route.hip
+hipError_t launch_route(const Dims& d, const void* Q, const float* scale, const float* kbar,
+                        const int32_t* group_off, const int32_t* rand_query_perm,
+                        int32_t* query_perm, int32_t* block_ptr, int32_t* block_groups,
+                        int64_t* executed_pairs, float* dbg_coords, int32_t* dbg_dom,
+                        float* dbg_domval, float* dbg_sigma, char* ws, hipStream_t st);
+
+// ---- attention.hip
+enum AttnMode { ATTN_SPARSE = 0, ATTN_DENSE = 1, ATTN_PROBE = 2 };
+struct AttnArgs {
+  const void* Q;
+  const void* K;
+  const void* V;
+  const float* scale;
+  int H, N, m, nsplit, split_len, G, nb;
+  const int32_t* query_perm;   // sparse / probe
+  const int32_t* block_ptr;    // sparse
+  const int32_t* block_groups; // sparse
+  const int32_t* group_off;    // sparse
+  void* out;                   // sparse: S_out fp32 (query order); dense: O dtype (token order)
+  float* lse;                  // sparse / dense (may be null for dense)
+  float* opart;                // probe: [H, nsplit, m, D] fp32
+  float* lsepart;              // probe: [H, nsplit, m]
+};
+hipError_t launch_attention(const Dims& d, AttnMode mode, const AttnArgs& a, hipStream_t st);
+hipError_t launch_probe_merge(const Dims& d, const float* opart, const float* lsepart,
+                              float* O_probe, hipStream_t st);
+
+// ---- fit.hip
+hipError_t launch_fit(const Dims& d, const float* S_out, const float* O_probe, float* U,
+                      float* Theta, int32_t* rank_eff, char* fit_ws, hipStream_t st);
+
+// ---- apply.hip
+hipError_t launch_apply(const Dims& d, const float* S_out, const int32_t* query_perm,
+                        const float* O_probe, const float* U, const float* Theta,
+                        const int32_t* rank_eff, void* O, hipStream_t st);
+
+}  // namespace spr

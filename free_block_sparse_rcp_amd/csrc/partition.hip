@@ -1,0 +1,554 @@
+// Response-coupled partitioning of the keys (arxivdaily 2608.18484, English
+// abstract: keys grouped by how they respond to sampled queries; cpu3d
+// summary: paired K/V groups).
+//
+// Lloyd k-means of the key response profiles r_j = tau * Q_s k_j is run with
+// key-space centroids kbar_g: since profiles are linear in k,
+//   ||r_j - c_g||^2 - ||r_j||^2 = kbar_g^T M kbar_g - 2 k_j^T (M kbar_g),
+//   M = tau^2 Q_s^T Q_s,
+// so each assignment is a [N x d] x [d x G] contraction plus a bias and a
+// row-wise argmin. Every reduction runs in a fixed order, so labels and
+// centroids are bit-identical from run to run.
+#include "common.hpp"
+#include "internal.hpp"
+
+namespace spr {
+
+// ---------------------------------------------------------------- metric M
+// M[h] = tau_h^2 * sum_s q_s q_s^T in fp64. grid (H, D/16), block 256.
+template <bool BF16, int D>
+__global__ __launch_bounds__(256) void k_metric(const void* Qv, const float* scale,
+                                                const int32_t* sample_idx, int S, int N,
+                                                double* M) {
+  using E = Elt<BF16>;
+  const typename E::T* Q = static_cast<const typename E::T*>(Qv) + (size_t)blockIdx.x * N * D;
+  __shared__ float xs[32][D];
+  const int t = threadIdx.x;
+  const int i = blockIdx.y * 16 + t / 16;
+  const int jl = t % 16;
+  constexpr int U = D / 16;
+  double acc[U];
+#pragma unroll
+  for (int u = 0; u < U; ++u) acc[u] = 0.0;
+  for (int s0 = 0; s0 < S; s0 += 32) {
+    const int ns = min(32, S - s0);
+    for (int e = t; e < 32 * D; e += 256) {
+      const int ss = e / D, c = e % D;
+      xs[ss][c] = ss < ns ? E::ld(Q, (size_t)clamp_idx(sample_idx[s0 + ss], N) * D + c) : 0.f;
+    }
+    __syncthreads();
+    for (int ss = 0; ss < ns; ++ss) {
+      const double xi = xs[ss][i];
+#pragma unroll
+      for (int u = 0; u < U; ++u) acc[u] += xi * (double)xs[ss][jl + 16 * u];
+    }
+    __syncthreads();
+  }
+  const double tau = scale[blockIdx.x];
+  double* Mh = M + (size_t)blockIdx.x * D * D;
+#pragma unroll
+  for (int u = 0; u < U; ++u) Mh[(size_t)i * D + jl + 16 * u] = tau * tau * acc[u];
+}
+
+// kbar[h][g] = K[h][init_idx[g]]. grid (G, H), block D.
+template <bool BF16, int D>
+__global__ void k_centroid_init(const void* Kv, const int32_t* init_idx, int N, int G,
+                                float* kbar) {
+  using E = Elt<BF16>;
+  const int g = blockIdx.x, h = blockIdx.y, e = threadIdx.x;
+  const typename E::T* K = static_cast<const typename E::T*>(Kv) + (size_t)h * N * D;
+  kbar[((size_t)h * G + g) * D + e] = E::ld(K, (size_t)clamp_idx(init_idx[g], N) * D + e);
+}
+
+// P_g = M kbar_g (fp64 accumulate), b_g = kbar_g^T M kbar_g. Stores P in fp32
+// and as a bf16 hi/lo pair. grid (G, H), block D.
+template <int D>
+__global__ void k_centroid_prep(const double* M, const float* kbar, int G, float* P,
+                                uint16_t* Phl, float* bvec) {
+  const int g = blockIdx.x, h = blockIdx.y, e = threadIdx.x;
+  __shared__ double kb[D];
+  __shared__ double red[D];
+  const float* kg = kbar + ((size_t)h * G + g) * D;
+  kb[e] = kg[e];
+  __syncthreads();
+  const double* Mh = M + (size_t)h * D * D;
+  double p = 0.0;
+  for (int j = 0; j < D; ++j) p += Mh[(size_t)j * D + e] * kb[j];  // M symmetric: column e
+  const size_t o = ((size_t)h * G + g) * D + e;
+  P[o] = (float)p;
+  const uint16_t hi = f32_to_bf16((float)p);
+  const uint16_t lo = f32_to_bf16((float)(p - (double)bf16_to_f32(hi)));
+  Phl[2 * o] = hi;
+  Phl[2 * o + 1] = lo;
+  const double bsum = block_sum_f64<D>(kb[e] * p, red);
+  if (e == 0) bvec[(size_t)h * G + g] = (float)bsum;
+}
+
+// ------------------------------------------------- row x centroid argselect
+// MODE 0 (assign): score(j,g) = b_g - 2 * (x_j . P_g), argmin, lowest g wins.
+// MODE 1 (coords): score(q,g) = tau * (x_q . P_g) over non-empty g, argmax.
+// One workgroup = 64 rows; 256 threads, each 4 rows x 4 groups per chunk of
+// 64 groups. fp32 dot products accumulated in increasing dimension order.
+template <bool BF16, int D, int MODE>
+__global__ __launch_bounds__(256) void k_rowvec_argsel(const void* Xv, const float* P,
+                                                       const float* bvec, const float* scale,
+                                                       const int32_t* group_off, int N, int G,
+                                                       int32_t* best_idx, float* best_val,
+                                                       float* dbg) {
+  using E = Elt<BF16>;
+  const int h = blockIdx.y;
+  const int r0 = blockIdx.x * 64;
+  const int t = threadIdx.x;
+  const typename E::T* X = static_cast<const typename E::T*>(Xv) + (size_t)h * N * D;
+  __shared__ float xs[64][D + 1];
+  __shared__ float ps[64][D + 1];
+  __shared__ float bs[64];
+  __shared__ int ok[64];
+  __shared__ float rv[16][64];
+  __shared__ int rg[16][64];
+  for (int idx = t; idx < 64 * D; idx += 256) {
+    const int r = idx / D, c = idx % D;
+    xs[r][c] = (r0 + r < N) ? E::ld(X, (size_t)(r0 + r) * D + c) : 0.f;
+  }
+  const float tau = MODE == 1 ? scale[h] : 0.f;
+  const int ki = t % 16, gi = t / 16;
+  float best[4];
+  int bestg[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    best[i] = MODE == 0 ? __builtin_inff() : -__builtin_inff();
+    bestg[i] = G;  // sentinel: replaced by the first finite candidate
+  }
+  for (int g0 = 0; g0 < G; g0 += 64) {
+    __syncthreads();
+    for (int idx = t; idx < 64 * D; idx += 256) {
+      const int r = idx / D, c = idx % D;
+      ps[r][c] = (g0 + r < G) ? P[((size_t)h * G + g0 + r) * D + c] : 0.f;
+    }
+    if (t < 64) {
+      const int g = g0 + t;
+      if (MODE == 0) {
+        bs[t] = g < G ? bvec[(size_t)h * G + g] : 0.f;
+        ok[t] = g < G;
+      } else {
+        ok[t] = g < G && group_off[(size_t)h * (G + 1) + g + 1] > group_off[(size_t)h * (G + 1) + g];
+      }
+    }
+    __syncthreads();
+    float acc[4][4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+      for (int j = 0; j < 4; ++j) acc[i][j] = 0.f;
+    for (int e = 0; e < D; ++e) {
+      float a[4], p[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) a[i] = xs[ki + 16 * i][e];
+#pragma unroll
+      for (int j = 0; j < 4; ++j) p[j] = ps[gi + 16 * j][e];
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) acc[i][j] = fmaf(a[i], p[j], acc[i][j]);
+    }
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int gl = gi + 16 * j;
+      const int g = g0 + gl;
+      if (g >= G) continue;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int row = r0 + ki + 16 * i;
+        float s;
+        if (MODE == 0) {
+          s = bs[gl] - 2.0f * acc[i][j];
+        } else {
+          s = ok[gl] ? tau * acc[i][j] : -__builtin_inff();
+        }
+        if (dbg != nullptr && row < N) dbg[((size_t)h * N + row) * G + g] = s;
+        if (MODE == 0) {
+          if (s < best[i]) { best[i] = s; bestg[i] = g; }
+        } else if (ok[gl]) {
+          if (s > best[i]) { best[i] = s; bestg[i] = g; }
+        }
+      }
+    }
+  }
+  __syncthreads();
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    rv[gi][ki + 16 * i] = best[i];
+    rg[gi][ki + 16 * i] = bestg[i];
+  }
+  __syncthreads();
+  if (t < 64 && r0 + t < N) {
+    float bv = rv[0][t];
+    int bg = rg[0][t];
+    for (int q = 1; q < 16; ++q) {
+      const float s = rv[q][t];
+      const int g = rg[q][t];
+      if (g == G) continue;
+      const bool better = MODE == 0 ? (s < bv || (s == bv && g < bg)) : (s > bv || (s == bv && g < bg));
+      if (bg == G || better) { bv = s; bg = g; }
+    }
+    if (bg == G) bg = 0;  // only if every score was NaN
+    best_idx[(size_t)h * N + r0 + t] = bg;
+    if (best_val) best_val[(size_t)h * N + r0 + t] = bv;
+  }
+}
+
+// ------------------------------------------------ stable counting-sort pass
+__device__ __forceinline__ uint32_t digit_of(int32_t key, int shift, uint32_t mask) {
+  return (static_cast<uint32_t>(key) >> shift) & mask;
+}
+__device__ __forceinline__ uint32_t digit_of(uint64_t key, int shift, uint32_t mask) {
+  return static_cast<uint32_t>(key >> shift) & mask;
+}
+
+// counts layout [H][nbuckets][nchunk]; chunks of 256 elements. grid (nchunk, H).
+template <typename KeyT>
+__global__ __launch_bounds__(256) void k_digit_hist(const KeyT* keys, int N, int nchunk,
+                                                    int shift, int bits, int32_t* counts) {
+  __shared__ int hist[1024];
+  const int nbuckets = 1 << bits;
+  const uint32_t mask = nbuckets - 1;
+  const int h = blockIdx.y, c = blockIdx.x, t = threadIdx.x;
+  for (int b = t; b < nbuckets; b += 256) hist[b] = 0;
+  __syncthreads();
+  const int i = c * 256 + t;
+  if (i < N) atomicAdd(&hist[digit_of(keys[(size_t)h * N + i], shift, mask)], 1);
+  __syncthreads();
+  for (int b = t; b < nbuckets; b += 256) counts[((size_t)h * nbuckets + b) * nchunk + c] = hist[b];
+}
+
+// Exclusive scan over the chunks of each bucket, in place. grid (nbuckets, H).
+__global__ __launch_bounds__(256) void k_scan_chunks(int32_t* counts, int nchunk, int nbuckets,
+                                                     int32_t* totals) {
+  __shared__ int tmp[256];
+  const int h = blockIdx.y, b = blockIdx.x;
+  int32_t* row = counts + ((size_t)h * nbuckets + b) * nchunk;
+  int carry = 0;
+  for (int base = 0; base < nchunk; base += 256) {
+    const int i = base + threadIdx.x;
+    const int v = i < nchunk ? row[i] : 0;
+    int tot;
+    const int ex = block_exclusive_scan<256>(v, tmp, &tot);
+    if (i < nchunk) row[i] = carry + ex;
+    carry += tot;
+  }
+  if (threadIdx.x == 0) totals[(size_t)h * nbuckets + b] = carry;
+}
+
+// Exclusive scan over buckets; optionally the group offsets. grid (H), block 1024.
+__global__ __launch_bounds__(1024) void k_scan_buckets(const int32_t* totals, int nbuckets,
+                                                       int32_t* starts, int32_t* group_off, int G,
+                                                       int N) {
+  __shared__ int tmp[1024];
+  const int h = blockIdx.x, t = threadIdx.x;
+  const int v = t < nbuckets ? totals[(size_t)h * nbuckets + t] : 0;
+  int tot;
+  const int ex = block_exclusive_scan<1024>(v, tmp, &tot);
+  if (t < nbuckets) starts[(size_t)h * nbuckets + t] = ex;
+  if (group_off != nullptr) {
+    if (t < G) group_off[(size_t)h * (G + 1) + t] = ex;
+    if (t == 0) group_off[(size_t)h * (G + 1) + G] = N;
+  }
+}
+
+// Stable scatter: in-chunk rank from wavefront ballots over the digit bits,
+// then per-wave digit counts in LDS. grid (nchunk, H).
+template <typename KeyT, bool WRITE_KEYS>
+__global__ __launch_bounds__(256) void k_digit_scatter(const KeyT* keys_in, KeyT* keys_out,
+                                                       const int32_t* vals_in, int32_t* vals_out,
+                                                       int N, int nchunk, int shift, int bits,
+                                                       const int32_t* counts,
+                                                       const int32_t* starts) {
+  __shared__ int wcnt[4 * 1024];
+  const int nbuckets = 1 << bits;
+  const uint32_t mask = nbuckets - 1;
+  const int h = blockIdx.y, c = blockIdx.x, t = threadIdx.x, w = t >> 6;
+  for (int b = t; b < 4 * nbuckets; b += 256) wcnt[b] = 0;
+  __syncthreads();
+  const int i = c * 256 + t;
+  const bool valid = i < N;
+  const KeyT key = valid ? keys_in[(size_t)h * N + i] : KeyT(0);
+  const uint32_t dg = digit_of(key, shift, mask);
+  uint64_t match = __ballot(valid);
+  for (int bit = 0; bit < bits; ++bit) {
+    const bool set = (dg >> bit) & 1u;
+    const uint64_t bb = __ballot(valid && set);
+    match &= set ? bb : ~bb;
+  }
+  const uint64_t lt = lanemask_lt();
+  const int rank = __popcll(match & lt);
+  if (valid && (match & lt) == 0) wcnt[w * nbuckets + dg] = __popcll(match);
+  __syncthreads();
+  if (valid) {
+    int before = 0;
+    for (int ww = 0; ww < w; ++ww) before += wcnt[ww * nbuckets + dg];
+    const int pos = starts[(size_t)h * nbuckets + dg] +
+                    counts[((size_t)h * nbuckets + dg) * nchunk + c] + before + rank;
+    if (WRITE_KEYS) keys_out[(size_t)h * N + pos] = key;
+    vals_out[(size_t)h * N + pos] = vals_in ? vals_in[(size_t)h * N + i] : i;
+  }
+}
+
+// ------------------------------------------------ deterministic group means
+// Tile c = positions [64c, 64c+64) of the group-contiguous order. Each run of
+// one group inside a tile is summed (fixed order) into partial[g + c]; the
+// index g + c is unique because tiles and groups both advance along the order.
+// grid (ntile64, H), block D.
+template <bool BF16, int D>
+__global__ void k_seg_partial(const void* Kv, const int32_t* key_perm, const int32_t* labels,
+                              int N, int G, int ntile, float* partial) {
+  using E = Elt<BF16>;
+  const int c = blockIdx.x, h = blockIdx.y, e = threadIdx.x;
+  const typename E::T* K = static_cast<const typename E::T*>(Kv) + (size_t)h * N * D;
+  float* part = partial + (size_t)h * (G + ntile) * D;
+  __shared__ int skey[64];
+  __shared__ int slab[64];
+  const int p0 = c * 64, n = min(N, p0 + 64) - p0;
+  if (e < n) {
+    const int key = clamp_idx(key_perm[(size_t)h * N + p0 + e], N);
+    skey[e] = key;
+    slab[e] = labels[(size_t)h * N + key];
+  }
+  __syncthreads();
+  int cur = -1;
+  float acc = 0.f;
+  for (int pp = 0; pp < n; pp += 8) {
+    float vals[8];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) vals[u] = (pp + u < n) ? E::ld(K, (size_t)skey[pp + u] * D + e) : 0.f;
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+      if (pp + u < n) {
+        const int g = slab[pp + u];
+        if (g != cur) {
+          if (cur >= 0) part[(size_t)(cur + c) * D + e] = acc;
+          cur = g;
+          acc = 0.f;
+        }
+        acc += vals[u];
+      }
+    }
+  }
+  if (cur >= 0) part[(size_t)(cur + c) * D + e] = acc;
+}
+
+// kbar_g = (sum of the group's tile partials, in tile order) / n_g for
+// non-empty groups; empty groups keep kbar. grid (G, H), block D.
+template <int D>
+__global__ void k_seg_final(const float* partial, const int32_t* group_off, int G, int ntile,
+                            float* kbar) {
+  const int g = blockIdx.x, h = blockIdx.y, e = threadIdx.x;
+  const int off = group_off[(size_t)h * (G + 1) + g];
+  const int end = group_off[(size_t)h * (G + 1) + g + 1];
+  if (end <= off) return;
+  const float* part = partial + (size_t)h * (G + ntile) * D;
+  float s = 0.f;
+  for (int c = off / 64; c <= (end - 1) / 64; ++c) s += part[(size_t)(g + c) * D + e];
+  kbar[((size_t)h * G + g) * D + e] = s / (float)(end - off);
+}
+
+// Random-block variant: label of key perm[i] is the run g with
+// floor(gN/G) <= i < floor((g+1)N/G). grid (ceil(N/256), H).
+__global__ void k_random_labels(const int32_t* perm, int N, int G, int32_t* labels) {
+  const int i = blockIdx.x * 256 + threadIdx.x;
+  if (i >= N) return;
+  int64_t g = ((int64_t)i * G) / N;
+  while (g + 1 < G && ((g + 1) * (int64_t)N) / G <= i) ++g;
+  while (g > 0 && (g * (int64_t)N) / G > i) --g;
+  labels[(size_t)blockIdx.y * N + clamp_idx(perm[i], N)] = (int32_t)g;
+}
+
+__global__ void k_fill_i32(int32_t* p, size_t n, int32_t v) {
+  const size_t i = (size_t)blockIdx.x * 256 + threadIdx.x;
+  if (i < n) p[i] = v;
+}
+__global__ void k_fill_f32(float* p, size_t n, float v) {
+  const size_t i = (size_t)blockIdx.x * 256 + threadIdx.x;
+  if (i < n) p[i] = v;
+}
+
+// Kp[i] = K[key_perm[i]], Vp[i] = V[key_perm[i]]: 16-byte copies.
+// grid (ceil(N * CPR / 256), H) where CPR = row bytes / 16.
+template <int ROWB>
+__global__ void k_gather_rows(const char* K, const char* V, const int32_t* perm, int N, char* Kp,
+                              char* Vp) {
+  constexpr int CPR = ROWB / 16;
+  const size_t f = (size_t)blockIdx.x * 256 + threadIdx.x;
+  const int h = blockIdx.y;
+  if (f >= (size_t)N * CPR) return;
+  const int i = (int)(f / CPR), ch = (int)(f % CPR);
+  const int src = clamp_idx(perm[(size_t)h * N + i], N);
+  const size_t hb = (size_t)h * N * ROWB;
+  const uint4 kv = *reinterpret_cast<const uint4*>(K + hb + (size_t)src * ROWB + ch * 16);
+  const uint4 vv = *reinterpret_cast<const uint4*>(V + hb + (size_t)src * ROWB + ch * 16);
+  *reinterpret_cast<uint4*>(Kp + hb + (size_t)i * ROWB + ch * 16) = kv;
+  *reinterpret_cast<uint4*>(Vp + hb + (size_t)i * ROWB + ch * 16) = vv;
+}
+
+// ------------------------------------------------------------- launchers
+#define SPR_CHECK_LAUNCH()                              \
+  do {                                                  \
+    hipError_t e__ = hipGetLastError();                 \
+    if (e__ != hipSuccess) return e__;                  \
+  } while (0)
+
+hipError_t launch_sort_pass_u32(const Dims& d, const int32_t* keys_in, int bits,
+                                const int32_t* vals_in, int32_t* vals_out, int32_t* counts,
+                                int32_t* totals, int32_t* starts, int32_t* group_off_out,
+                                hipStream_t st) {
+  const int nb = 1 << bits;
+  k_digit_hist<int32_t><<<dim3(d.nchunk, d.H), 256, 0, st>>>(keys_in, d.N, d.nchunk, 0, bits,
+                                                              counts);
+  SPR_CHECK_LAUNCH();
+  k_scan_chunks<<<dim3(nb, d.H), 256, 0, st>>>(counts, d.nchunk, nb, totals);
+  SPR_CHECK_LAUNCH();
+  k_scan_buckets<<<d.H, 1024, 0, st>>>(totals, nb, starts, group_off_out, d.G, d.N);
+  SPR_CHECK_LAUNCH();
+  k_digit_scatter<int32_t, false><<<dim3(d.nchunk, d.H), 256, 0, st>>>(
+      keys_in, nullptr, vals_in, vals_out, d.N, d.nchunk, 0, bits, counts, starts);
+  SPR_CHECK_LAUNCH();
+  return hipSuccess;
+}
+
+hipError_t launch_sort_pass_u64(const Dims& d, const uint64_t* keys_in, uint64_t* keys_out,
+                                int shift, int bits, const int32_t* vals_in, int32_t* vals_out,
+                                int32_t* counts, int32_t* totals, int32_t* starts,
+                                hipStream_t st) {
+  const int nb = 1 << bits;
+  k_digit_hist<uint64_t><<<dim3(d.nchunk, d.H), 256, 0, st>>>(keys_in, d.N, d.nchunk, shift,
+                                                               bits, counts);
+  SPR_CHECK_LAUNCH();
+  k_scan_chunks<<<dim3(nb, d.H), 256, 0, st>>>(counts, d.nchunk, nb, totals);
+  SPR_CHECK_LAUNCH();
+  k_scan_buckets<<<d.H, 1024, 0, st>>>(totals, nb, starts, nullptr, d.G, d.N);
+  SPR_CHECK_LAUNCH();
+  if (keys_out != nullptr) {
+    k_digit_scatter<uint64_t, true><<<dim3(d.nchunk, d.H), 256, 0, st>>>(
+        keys_in, keys_out, vals_in, vals_out, d.N, d.nchunk, shift, bits, counts, starts);
+  } else {
+    k_digit_scatter<uint64_t, false><<<dim3(d.nchunk, d.H), 256, 0, st>>>(
+        keys_in, nullptr, vals_in, vals_out, d.N, d.nchunk, shift, bits, counts, starts);
+  }
+  SPR_CHECK_LAUNCH();
+  return hipSuccess;
+}
+
+template <bool BF16, int D>
+static hipError_t partition_impl(const Dims& d, const void* Q, const void* K, const void* V,
+                                 const float* scale, const int32_t* sample_idx,
+                                 const int32_t* init_idx, const int32_t* rand_key_perm,
+                                 int32_t* key_label, int32_t* key_perm, int32_t* group_off,
+                                 float* kbar, void* Kp, void* Vp, float* dbg, char* ws,
+                                 hipStream_t st) {
+  const PartitionWs L = partition_ws(d);
+  double* M = reinterpret_cast<double*>(ws + L.M);
+  float* P = reinterpret_cast<float*>(ws + L.P);
+  uint16_t* Phl = reinterpret_cast<uint16_t*>(ws + L.Phl);
+  float* bvec = reinterpret_cast<float*>(ws + L.bvec);
+  int32_t* counts = reinterpret_cast<int32_t*>(ws + L.counts);
+  int32_t* totals = reinterpret_cast<int32_t*>(ws + L.totals);
+  int32_t* starts = reinterpret_cast<int32_t*>(ws + L.starts);
+  float* partial = reinterpret_cast<float*>(ws + L.partial);
+  const dim3 rows64((d.N + 63) / 64, d.H);
+  const dim3 per_group(d.G, d.H);
+
+  auto regroup = [&]() -> hipError_t {
+    hipError_t e = launch_sort_pass_u32(d, key_label, d.gbits, nullptr, key_perm, counts, totals,
+                                        starts, group_off, st);
+    if (e != hipSuccess) return e;
+    k_seg_partial<BF16, D><<<dim3(d.ntile64, d.H), D, 0, st>>>(K, key_perm, key_label, d.N, d.G,
+                                                                d.ntile64, partial);
+    SPR_CHECK_LAUNCH();
+    k_seg_final<D><<<per_group, D, 0, st>>>(partial, group_off, d.G, d.ntile64, kbar);
+    SPR_CHECK_LAUNCH();
+    return hipSuccess;
+  };
+
+  if (d.mode == SPARSEPR_RESPONSE_COUPLED) {
+    k_metric<BF16, D><<<dim3(d.H, D / 16), 256, 0, st>>>(Q, scale, sample_idx, d.S, d.N, M);
+    SPR_CHECK_LAUNCH();
+    k_centroid_init<BF16, D><<<per_group, D, 0, st>>>(K, init_idx, d.N, d.G, kbar);
+    SPR_CHECK_LAUNCH();
+    for (int it = 0; it < d.T; ++it) {
+      k_centroid_prep<D><<<per_group, D, 0, st>>>(M, kbar, d.G, P, Phl, bvec);
+      SPR_CHECK_LAUNCH();
+      float* dbg_it = (it == d.T - 1) ? dbg : nullptr;
+      k_rowvec_argsel<BF16, D, 0><<<rows64, 256, 0, st>>>(K, P, bvec, nullptr, nullptr, d.N, d.G,
+                                                           key_label, nullptr, dbg_it);
+      SPR_CHECK_LAUNCH();
+      hipError_t e = regroup();
+      if (e != hipSuccess) return e;
+    }
+  } else {
+    const size_t nl = (size_t)d.H * d.N;
+    k_fill_i32<<<(unsigned)((nl + 255) / 256), 256, 0, st>>>(key_label, nl, 0);
+    SPR_CHECK_LAUNCH();
+    const size_t nk = (size_t)d.H * d.G * D;
+    k_fill_f32<<<(unsigned)((nk + 255) / 256), 256, 0, st>>>(kbar, nk, 0.f);
+    SPR_CHECK_LAUNCH();
+    k_random_labels<<<dim3((d.N + 255) / 256, d.H), 256, 0, st>>>(rand_key_perm, d.N, d.G,
+                                                                   key_label);
+    SPR_CHECK_LAUNCH();
+    hipError_t e = regroup();
+    if (e != hipSuccess) return e;
+  }
+  constexpr int ROWB = D * (BF16 ? 2 : 4);
+  const size_t nchunks = (size_t)d.N * (ROWB / 16);
+  k_gather_rows<ROWB><<<dim3((unsigned)((nchunks + 255) / 256), d.H), 256, 0, st>>>(
+      static_cast<const char*>(K), static_cast<const char*>(V), key_perm, d.N,
+      static_cast<char*>(Kp), static_cast<char*>(Vp));
+  SPR_CHECK_LAUNCH();
+  return hipSuccess;
+}
+
+hipError_t launch_partition(const Dims& d, const void* Q, const void* K, const void* V,
+                            const float* scale, const int32_t* sample_idx, const int32_t* init_idx,
+                            const int32_t* rand_key_perm, int32_t* key_label, int32_t* key_perm,
+                            int32_t* group_off, float* kbar, void* Kp, void* Vp, float* dbg,
+                            char* ws, hipStream_t st) {
+#define SPR_PART(B, DD)                                                                       \
+  return partition_impl<B, DD>(d, Q, K, V, scale, sample_idx, init_idx, rand_key_perm,        \
+                               key_label, key_perm, group_off, kbar, Kp, Vp, dbg, ws, st)
+  if (d.bf16) {
+    if (d.D == 128) SPR_PART(true, 128);
+    SPR_PART(true, 64);
+  } else {
+    if (d.D == 128) SPR_PART(false, 128);
+    SPR_PART(false, 64);
+  }
+#undef SPR_PART
+}
+
+hipError_t launch_fill_i32(int32_t* p, size_t n, int32_t v, hipStream_t st) {
+  if (n == 0) return hipSuccess;
+  k_fill_i32<<<(unsigned)((n + 255) / 256), 256, 0, st>>>(p, n, v);
+  return hipGetLastError();
+}
+hipError_t launch_fill_f32(float* p, size_t n, float v, hipStream_t st) {
+  if (n == 0) return hipSuccess;
+  k_fill_f32<<<(unsigned)((n + 255) / 256), 256, 0, st>>>(p, n, v);
+  return hipGetLastError();
+}
+
+// Coordinates argmax is shared with route.hip through this launcher.
+hipError_t launch_coords_valu(const Dims& d, const void* Q, const float* kbar, const float* scale,
+                              const int32_t* group_off, int32_t* g1, float* v, float* dbg,
+                              hipStream_t st) {
+  const dim3 rows64((d.N + 63) / 64, d.H);
+#define SPR_COORD(B, DD)                                                                        \
+  k_rowvec_argsel<B, DD, 1><<<rows64, 256, 0, st>>>(Q, kbar, nullptr, scale, group_off, d.N, d.G, \
+                                                    g1, v, dbg)
+  if (d.bf16) {
+    if (d.D == 128) SPR_COORD(true, 128); else SPR_COORD(true, 64);
+  } else {
+    if (d.D == 128) SPR_COORD(false, 128); else SPR_COORD(false, 64);
+  }
+#undef SPR_COORD
+  return hipGetLastError();
+}
+
+}  // namespace spr

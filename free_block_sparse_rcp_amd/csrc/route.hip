@@ -1,0 +1,293 @@
+// Query coordinates, query grouping and shared routing (arxivdaily
+// 2608.18484, English abstract: queries grouped by their responses to the
+// key-group centroids for shared sparse routing; peercurrent abstract: the
+// centroids induce query-response coordinates).
+#include "common.hpp"
+#include "internal.hpp"
+
+namespace spr {
+
+hipError_t launch_coords_valu(const Dims& d, const void* Q, const float* kbar, const float* scale,
+                              const int32_t* group_off, int32_t* g1, float* v, float* dbg,
+                              hipStream_t st);
+
+// Sort key of a query: (dominant group ascending, value descending); the
+// stable passes keep token order for equal keys. grid (ceil(N/256), H).
+__global__ void k_make_qkeys(const int32_t* g1, const float* v, int N, uint64_t* keys,
+                             int32_t* dbg_dom, float* dbg_val) {
+  const int i = blockIdx.x * 256 + threadIdx.x;
+  if (i >= N) return;
+  const size_t o = (size_t)blockIdx.y * N + i;
+  const int g = g1[o];
+  const float x = v[o];
+  keys[o] = (static_cast<uint64_t>(static_cast<uint32_t>(g)) << 32) | float_desc_bits(x);
+  if (dbg_dom) dbg_dom[o] = g;
+  if (dbg_val) dbg_val[o] = x;
+}
+
+__global__ void k_copy_perm(const int32_t* perm, int N, int32_t* out) {
+  const int i = blockIdx.x * 256 + threadIdx.x;
+  if (i < N) out[(size_t)blockIdx.y * N + i] = clamp_idx(perm[i], N);
+}
+
+// qbar_b = mean of the block's queries (fixed order). grid (nb, H), block D.
+template <bool BF16, int D>
+__global__ void k_block_means(const void* Qv, const int32_t* query_perm, int N, int BQ,
+                              float* qbar) {
+  using E = Elt<BF16>;
+  const int b = blockIdx.x, h = blockIdx.y, e = threadIdx.x;
+  const typename E::T* Q = static_cast<const typename E::T*>(Qv) + (size_t)h * N * D;
+  const int p0 = b * BQ, n = min(N, p0 + BQ) - p0;
+  float s = 0.f;
+  for (int i = 0; i < n; ++i) s += E::ld(Q, (size_t)clamp_idx(query_perm[(size_t)h * N + p0 + i], N) * D + e);
+  qbar[((size_t)h * gridDim.x + b) * D + e] = s / (float)n;
+}
+
+// sigma[b,g] = tau * qbar_b . kbar_g over non-empty groups (-inf for empty).
+// grid (nb, H), block 256.
+template <int D>
+__global__ __launch_bounds__(256) void k_block_scores(const float* qbar, const float* kbar,
+                                                      const float* scale, const int32_t* group_off,
+                                                      int G, float* sigma, float* dbg) {
+  const int b = blockIdx.x, h = blockIdx.y, nb = gridDim.x;
+  __shared__ float qb[D];
+  for (int e = threadIdx.x; e < D; e += 256) qb[e] = qbar[((size_t)h * nb + b) * D + e];
+  __syncthreads();
+  const float tau = scale[h];
+  const int32_t* off = group_off + (size_t)h * (G + 1);
+  for (int g = threadIdx.x; g < G; g += 256) {
+    float s;
+    if (off[g + 1] > off[g]) {
+      const float* kg = kbar + ((size_t)h * G + g) * D;
+      float acc = 0.f;
+      for (int e = 0; e < D; ++e) acc = fmaf(qb[e], kg[e], acc);
+      s = tau * acc;
+    } else {
+      s = -__builtin_inff();
+    }
+    sigma[((size_t)h * nb + b) * G + g] = s;
+    if (dbg) dbg[((size_t)h * nb + b) * G + g] = s;
+  }
+}
+
+// Per block: rank non-empty groups by (sigma desc, g asc) with a bitonic sort
+// in LDS, take the longest ranked prefix with total size <= kappa (at least
+// one group), and list the chosen groups in ascending g.
+// grid (nb, H), block 256; G <= 1024.
+__global__ __launch_bounds__(256) void k_block_select(const float* sigma,
+                                                      const int32_t* group_off, int G,
+                                                      int64_t kappa, int32_t* sel,
+                                                      int32_t* selcnt, int64_t* blkkeys) {
+  constexpr int NT = 256;
+  const int b = blockIdx.x, h = blockIdx.y, nb = gridDim.x, t = threadIdx.x;
+  __shared__ uint64_t key[1024];
+  __shared__ int flag[1024];
+  __shared__ int tmp[NT];
+  __shared__ int s_keys;
+  int GP = 1;
+  while (GP < G) GP <<= 1;
+  const int32_t* off = group_off + (size_t)h * (G + 1);
+  const float* sg = sigma + ((size_t)h * nb + b) * G;
+  for (int i = t; i < GP; i += NT) {
+    uint64_t k = ~0ull;
+    if (i < G && off[i + 1] > off[i]) k = (static_cast<uint64_t>(float_desc_bits(sg[i])) << 32) | (uint32_t)i;
+    key[i] = k;
+    if (i < G) flag[i] = 0;
+  }
+  __syncthreads();
+  for (int k = 2; k <= GP; k <<= 1) {
+    for (int j = k >> 1; j > 0; j >>= 1) {
+      for (int i = t; i < GP; i += NT) {
+        const int ixj = i ^ j;
+        if (ixj > i) {
+          const uint64_t a = key[i], c = key[ixj];
+          const bool up = (i & k) == 0;
+          if ((a > c) == up) {
+            key[i] = c;
+            key[ixj] = a;
+          }
+        }
+      }
+      __syncthreads();
+    }
+  }
+  // inclusive prefix of sizes in ranked order; each thread owns E consecutive entries
+  const int E = (GP + NT - 1) / NT;
+  int loc[4];
+  int own = 0;
+  for (int u = 0; u < E; ++u) {
+    const int i = t * E + u;
+    int sz = 0;
+    if (i < GP && key[i] != ~0ull) {
+      const int g = (int)(key[i] & 0xffffffffu);
+      sz = off[g + 1] - off[g];
+    }
+    loc[u] = sz;
+    own += sz;
+  }
+  int total;
+  const int ex = block_exclusive_scan<NT>(own, tmp, &total);
+  int fits = 0;
+  int incl = ex;
+  int inclv[4];
+  for (int u = 0; u < E; ++u) {
+    const int i = t * E + u;
+    incl += loc[u];
+    inclv[u] = incl;
+    if (i < GP && key[i] != ~0ull && (int64_t)incl <= kappa) ++fits;
+  }
+  int nfit;
+  (void)block_exclusive_scan<NT>(fits, tmp, &nfit);
+  const int count = nfit > 0 ? nfit : 1;
+  for (int u = 0; u < E; ++u)
+    if (t * E + u == count - 1) s_keys = inclv[u];
+  for (int i = t; i < count; i += NT) flag[(int)(key[i] & 0xffffffffu)] = 1;
+  __syncthreads();
+  // ascending compaction of the chosen groups
+  int32_t* out = sel + ((size_t)h * nb + b) * G;
+  int base = 0;
+  for (int g0 = 0; g0 < G; g0 += NT) {
+    const int g = g0 + t;
+    const int f = g < G ? flag[g] : 0;
+    int tot;
+    const int ex = block_exclusive_scan<NT>(f, tmp, &tot);
+    if (f) out[base + ex] = g;
+    base += tot;
+  }
+  if (t == 0) {
+    selcnt[(size_t)h * nb + b] = count;
+    blkkeys[(size_t)h * nb + b] = s_keys;
+  }
+}
+
+// block_ptr = exclusive scan of the per-block counts; executed pairs =
+// sum_b n_b |K(b)| + m N. grid (H), block 1024.
+__global__ __launch_bounds__(1024) void k_csr_scan(const int32_t* selcnt, const int64_t* blkkeys,
+                                                   int nb, int N, int BQ, int m,
+                                                   int32_t* block_ptr, int64_t* executed) {
+  constexpr int NT = 1024;
+  __shared__ int tmp[NT];
+  __shared__ long long red[NT];
+  const int h = blockIdx.x, t = threadIdx.x;
+  int carry = 0;
+  long long pairs = 0;
+  for (int base = 0; base < nb; base += NT) {
+    const int b = base + t;
+    const int v = b < nb ? selcnt[(size_t)h * nb + b] : 0;
+    int tot;
+    const int ex = block_exclusive_scan<NT>(v, tmp, &tot);
+    if (b < nb) {
+      block_ptr[(size_t)h * (nb + 1) + b] = carry + ex;
+      const int nrow = min(N, (b + 1) * BQ) - b * BQ;
+      pairs += (long long)nrow * blkkeys[(size_t)h * nb + b];
+    }
+    carry += tot;
+  }
+  red[t] = pairs;
+  __syncthreads();
+  for (int o = NT / 2; o > 0; o >>= 1) {
+    if (t < o) red[t] += red[t + o];
+    __syncthreads();
+  }
+  if (t == 0) {
+    block_ptr[(size_t)h * (nb + 1) + nb] = carry;
+    executed[h] = red[0] + (long long)m * N;
+  }
+}
+
+// Copy each block's chosen groups into the CSR. grid (nb, H), block 256.
+__global__ void k_csr_copy(const int32_t* sel, const int32_t* selcnt, const int32_t* block_ptr,
+                           int G, int32_t* block_groups) {
+  const int b = blockIdx.x, h = blockIdx.y, nb = gridDim.x;
+  const int cnt = selcnt[(size_t)h * nb + b];
+  const int p = block_ptr[(size_t)h * (nb + 1) + b];
+  const int32_t* src = sel + ((size_t)h * nb + b) * G;
+  int32_t* dst = block_groups + (size_t)h * nb * G + p;
+  for (int i = threadIdx.x; i < cnt; i += 256) dst[i] = src[i];
+}
+
+#define SPR_CHECK_LAUNCH()                              \
+  do {                                                  \
+    hipError_t e__ = hipGetLastError();                 \
+    if (e__ != hipSuccess) return e__;                  \
+  } while (0)
+
+hipError_t launch_route(const Dims& d, const void* Q, const float* scale, const float* kbar,
+                        const int32_t* group_off, const int32_t* rand_query_perm,
+                        int32_t* query_perm, int32_t* block_ptr, int32_t* block_groups,
+                        int64_t* executed_pairs, float* dbg_coords, int32_t* dbg_dom,
+                        float* dbg_domval, float* dbg_sigma, char* ws, hipStream_t st) {
+  const RouteWs L = route_ws(d);
+  uint64_t* keysA = reinterpret_cast<uint64_t*>(ws + L.keysA);
+  uint64_t* keysB = reinterpret_cast<uint64_t*>(ws + L.keysB);
+  int32_t* valsA = reinterpret_cast<int32_t*>(ws + L.valsA);
+  int32_t* valsB = reinterpret_cast<int32_t*>(ws + L.valsB);
+  int32_t* counts = reinterpret_cast<int32_t*>(ws + L.counts);
+  int32_t* totals = reinterpret_cast<int32_t*>(ws + L.totals);
+  int32_t* starts = reinterpret_cast<int32_t*>(ws + L.starts);
+  float* qbar = reinterpret_cast<float*>(ws + L.qbar);
+  float* sigma = reinterpret_cast<float*>(ws + L.sigma);
+  int32_t* sel = reinterpret_cast<int32_t*>(ws + L.sel);
+  int32_t* selcnt = reinterpret_cast<int32_t*>(ws + L.selcnt);
+  int64_t* blkkeys = reinterpret_cast<int64_t*>(ws + L.blkkeys);
+  const dim3 rows256((d.N + 255) / 256, d.H);
+  const bool response = d.mode == SPARSEPR_RESPONSE_COUPLED;
+
+  if (response || dbg_coords || dbg_dom || dbg_domval) {
+    // g1 -> valsA, v -> valsB (reinterpreted) before the sort reuses them
+    int32_t* g1 = valsA;
+    float* v = reinterpret_cast<float*>(valsB);
+    hipError_t e = launch_coords_valu(d, Q, kbar, scale, group_off, g1, v, dbg_coords, st);
+    if (e != hipSuccess) return e;
+    k_make_qkeys<<<rows256, 256, 0, st>>>(g1, v, d.N, keysA, dbg_dom, dbg_domval);
+    SPR_CHECK_LAUNCH();
+  }
+  if (response) {
+    // LSD radix sort: 4 passes over the value key (8 bits each), then the group bits.
+    const int npass = 4 + (d.gbits > 0 ? 1 : 0);
+    uint64_t* kin = keysA;
+    uint64_t* kout = keysB;
+    const int32_t* vin = nullptr;
+    int32_t* vbuf[2] = {valsA, valsB};
+    for (int ps = 0; ps < npass; ++ps) {
+      const bool last = ps == npass - 1;
+      const int shift = ps < 4 ? 8 * ps : 32;
+      const int bits = ps < 4 ? 8 : d.gbits;
+      int32_t* vout = last ? query_perm : vbuf[ps & 1];
+      hipError_t e = launch_sort_pass_u64(d, kin, last ? nullptr : kout, shift, bits, vin, vout,
+                                          counts, totals, starts, st);
+      if (e != hipSuccess) return e;
+      vin = vout;
+      uint64_t* tk = kin;
+      kin = kout;
+      kout = tk;
+    }
+  } else {
+    k_copy_perm<<<rows256, 256, 0, st>>>(rand_query_perm, d.N, query_perm);
+    SPR_CHECK_LAUNCH();
+  }
+  const dim3 blocks(d.nb, d.H);
+#define SPR_MEANS(B, DD) k_block_means<B, DD><<<blocks, DD, 0, st>>>(Q, query_perm, d.N, d.BQ, qbar)
+  if (d.bf16) {
+    if (d.D == 128) SPR_MEANS(true, 128); else SPR_MEANS(true, 64);
+  } else {
+    if (d.D == 128) SPR_MEANS(false, 128); else SPR_MEANS(false, 64);
+  }
+#undef SPR_MEANS
+  SPR_CHECK_LAUNCH();
+  if (d.D == 128)
+    k_block_scores<128><<<blocks, 256, 0, st>>>(qbar, kbar, scale, group_off, d.G, sigma, dbg_sigma);
+  else
+    k_block_scores<64><<<blocks, 256, 0, st>>>(qbar, kbar, scale, group_off, d.G, sigma, dbg_sigma);
+  SPR_CHECK_LAUNCH();
+  k_block_select<<<blocks, 256, 0, st>>>(sigma, group_off, d.G, d.kappa, sel, selcnt, blkkeys);
+  SPR_CHECK_LAUNCH();
+  k_csr_scan<<<d.H, 1024, 0, st>>>(selcnt, blkkeys, d.nb, d.N, d.BQ, d.m, block_ptr,
+                                    executed_pairs);
+  SPR_CHECK_LAUNCH();
+  k_csr_copy<<<blocks, 256, 0, st>>>(sel, selcnt, block_ptr, d.G, block_groups);
+  SPR_CHECK_LAUNCH();
+  return hipSuccess;
+}
+
+}  // namespace spr

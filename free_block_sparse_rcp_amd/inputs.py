@@ -26,6 +26,8 @@ exact bf16 values, which is what both the GPU path and the oracle consume.
 """
 from __future__ import annotations
 
+import os
+from concurrent.futures import ThreadPoolExecutor
 from dataclasses import dataclass
 from typing import Optional, Sequence
 
@@ -148,7 +150,8 @@ def gen_g2(grid, d: int, n_heads: int, n_samples: int, n_groups: int, seed: int,
     Q = np.empty((len(heads), n, d), dtype=np.float32)
     K = np.empty_like(Q)
     V = np.empty_like(Q)
-    for i, h in enumerate(heads):
+
+    def one_head(i, h):
         rng = np.random.default_rng(streams[h])
         a = rng.standard_normal((64, d)) / 8.0
         a2 = a + 0.25 * rng.standard_normal((64, d)) / 8.0
@@ -166,6 +169,11 @@ def gen_g2(grid, d: int, n_heads: int, n_samples: int, n_groups: int, seed: int,
         Q[i] = round_to_dtype(q, dtype)
         K[i] = round_to_dtype(k, dtype)
         V[i] = round_to_dtype(v, dtype)
+
+    # heads draw from independent streams, so they can be generated concurrently
+    workers = max(1, min(len(heads), 8, os.cpu_count() or 1))
+    with ThreadPoolExecutor(workers) as ex:
+        list(ex.map(lambda ih: one_head(*ih), enumerate(heads)))
     kp, qp = random_block_perms(seed, n)
     sc = np.asarray([scales[h] for h in heads], dtype=np.float32)
     return Inputs(Q=Q, K=K, V=V, scale=sc, sample_idx=sample_idx, init_idx=init_idx,

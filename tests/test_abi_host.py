@@ -1,0 +1,128 @@
+"""Host-only checks of the C-ABI library: it loads, exports every function
+that include/sparsepr.h declares, and its validation returns the documented
+status codes before anything is launched (no GPU is needed or touched)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+from free_block_sparse_rcp_amd import binding, build, configs
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "sparsepr.h")
+
+
+def declared_functions():
+    src = open(HEADER).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"\b(sparsepr_[a-z_]+)\s*\(", src)))
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(build.lib_path()):
+        pytest.skip("libsparsepr.so not built (run python -m free_block_sparse_rcp_amd.build)")
+    return binding.load()
+
+
+def test_header_declares_the_five_stages_and_helpers():
+    names = declared_functions()
+    for n in ("sparsepr_partition", "sparsepr_route", "sparsepr_attend", "sparsepr_probe_fit",
+              "sparsepr_apply", "sparsepr_dense_attention", "sparsepr_workspace_bytes"):
+        assert n in names
+    assert sorted(binding.EXPORTS) == names
+
+
+def test_library_exports_every_declared_symbol(lib):
+    for n in declared_functions():
+        assert hasattr(lib, n), n
+    assert lib.sparsepr_abi_version() == 1
+
+
+def test_status_strings(lib):
+    for code, name in binding.STATUS.items():
+        assert lib.sparsepr_status_string(code).decode() == name
+    assert lib.sparsepr_status_string(99).decode() == "SPARSEPR_UNKNOWN_STATUS"
+
+
+def test_params_struct_layout_matches_header():
+    assert ctypes.sizeof(binding.CParams) == 64
+    assert binding.CParams.density.offset == 32
+    assert binding.CParams.ridge_lambda.offset == 48
+
+
+def _ws(lib, p):
+    n = ctypes.c_size_t(0)
+    st = lib.sparsepr_workspace_bytes(ctypes.byref(p), ctypes.byref(n))
+    return st, n.value
+
+
+@pytest.mark.parametrize("name", ["tiny", "wan", "hunyuan", "cosmos", "sweep"])
+def test_workspace_bytes_for_every_workload(lib, name):
+    p = binding.c_params(configs.get(name).params)
+    st, n = _ws(lib, p)
+    assert st == 0 and n > 0
+    assert n < 64 * 2**30
+
+
+BAD = [
+    ("heads", 0, 1), ("n_tokens", 0, 1), ("head_dim", 96, 2), ("dtype", 7, 1), ("q_block", 32, 2),
+    ("n_groups", 0, 1), ("n_groups", 2000, 1), ("n_samples", 0, 1), ("kmeans_iters", 0, 1),
+    ("density", 0.0, 1), ("density", 1.5, 1), ("n_probes", -1, 1), ("rank", 200, 1),
+    ("ridge_lambda", 0.0, 1), ("partition_mode", 3, 1), ("reserved", 1, 1),
+]
+
+
+@pytest.mark.parametrize("field,value,code", BAD)
+def test_invalid_params_are_rejected_on_host(lib, field, value, code):
+    p = binding.c_params(configs.TINY.params)
+    setattr(p, field, value)
+    st, _ = _ws(lib, p)
+    assert st == code
+    assert lib.sparsepr_last_error().decode() != ""
+
+
+def test_budget_below_one_key_is_rejected(lib):
+    p = binding.c_params(configs.TINY.params)
+    p.density = 0.03          # 0.03 * 2048 - 64 < 1
+    st, _ = _ws(lib, p)
+    assert st == 1 and "key budget" in lib.sparsepr_last_error().decode()
+
+
+def test_null_pointers_and_small_workspace_are_rejected(lib):
+    p = binding.c_params(configs.TINY.params)
+    fake = ctypes.c_void_p(0x1000)   # never dereferenced: validation fails first
+    # partition with K missing
+    st = lib.sparsepr_partition(ctypes.byref(p), fake, None, fake, fake, fake, fake, None, fake,
+                                fake, fake, fake, fake, fake, None, fake, 1 << 40, None)
+    assert st == 1 and "K is NULL" in lib.sparsepr_last_error().decode()
+    # workspace too small
+    st = lib.sparsepr_partition(ctypes.byref(p), fake, fake, fake, fake, fake, fake, None, fake,
+                                fake, fake, fake, fake, fake, None, fake, 16, None)
+    assert st == 3
+    # route without the random-block permutation in random-block mode
+    p.partition_mode = 1
+    st = lib.sparsepr_route(ctypes.byref(p), fake, fake, fake, fake, None, fake, fake, fake, fake,
+                            None, None, None, None, fake, 1 << 40, None)
+    assert st == 1 and "rand_query_perm" in lib.sparsepr_last_error().decode()
+    # attend with no lse
+    p.partition_mode = 0
+    st = lib.sparsepr_attend(ctypes.byref(p), fake, fake, fake, fake, fake, fake, fake, fake, fake,
+                             None, None)
+    assert st == 1
+    # dense attention validates only the shape fields
+    q = binding.c_params(configs.TINY.params)
+    q.head_dim = 80
+    st = lib.sparsepr_dense_attention(ctypes.byref(q), fake, fake, fake, fake, fake, None, None)
+    assert st == 2
+
+
+def test_index_validation_in_binding():
+    import numpy as np
+    with pytest.raises(ValueError):
+        binding.index_tensor(np.array([0, 5]), 5, 2, "x", "cpu")
+    with pytest.raises(ValueError):
+        binding.index_tensor(np.array([1, 1]), 5, 2, "x", "cpu", distinct=True)
+    t = binding.index_tensor(np.array([4, 0]), 5, 2, "x", "cpu", distinct=True)
+    assert t.dtype.is_floating_point is False and t.tolist() == [4, 0]

@@ -1,0 +1,382 @@
+"""GPU parity of every stage against the fp64 oracle, through the C-ABI.
+
+Protocol:
+  (i)   index stages bit-exact: the oracle's selection functions, fed the
+        fp32 scores the kernels dumped, reproduce labels, groups, query order,
+        routed groups and pair counts exactly;
+  (ii)  value stages: the oracle run in fp64 on the GPU's own indices matches
+        within relative L2 1e-4 (fp32 path) or 2e-2 (bf16 path);
+  (iii) per-query relative error against dense agrees with the oracle's
+        (oracle output rounded to the output dtype) within 1e-3 absolute;
+  (iv)  the oracle's own independent run is compared for information only.
+"""
+import math
+from dataclasses import replace
+
+import numpy as np
+import pytest
+import torch
+
+from oracle import sparsepr_oracle as orc
+from free_block_sparse_rcp_amd import binding, configs
+
+from _gpu_util import bf16_round, csr_lists, rel_l2, run_pipeline, small_bf16
+
+pytestmark = pytest.mark.gpu
+
+TOL = {"f32": 1e-4, "bf16": 2e-2}
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _need_gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    binding.load()
+
+
+WORKLOADS = {
+    "tiny": configs.TINY,
+    "bf16_d128": small_bf16(),
+    "bf16_d64_bq64": small_bf16(name="bf16_d64_bq64", d=64, BQ=64, G=48, k=16, seed=12),
+    "bf16_mixed_temp": small_bf16(name="bf16_mixed", heads=2, seed=13,
+                                  scales=[2.0 / math.sqrt(128), 0.3 / math.sqrt(128)],
+                                  smoothing=True, m=96, k=24),
+}
+
+_RUNS = {}
+
+
+def get_run(name):
+    if name not in _RUNS:
+        print(f"[gpu] running pipeline {name}", flush=True)
+        _RUNS[name] = run_pipeline(WORKLOADS[name])
+    return _RUNS[name]
+
+
+def head_arrays(r, h):
+    p = r.p
+    out = {n: r.np(n)[h] for n in ("key_label", "key_perm", "group_off", "key_centroid",
+                                   "query_perm", "block_ptr", "lse", "O_probe", "U", "Theta",
+                                   "rank_eff", "executed_pairs")}
+    out["S"] = r.np("S")[h]
+    out["O"] = r.np("O")[h]
+    out["Kp"] = r.np("Kp")[h]
+    out["block_groups"] = r.np("block_groups")[h]
+    for k in ("assign", "coords", "dom", "domval", "sigma"):
+        if k in r.dbg:
+            out[k] = r.np(k)[h]
+    return out
+
+
+def oracle_on_gpu_indices(Q, K, V, tau, p, g):
+    """Steps after routing, in fp64, on the GPU's groups, order and routes."""
+    N = p.n_tokens
+    qperm = g["query_perm"].astype(np.int64)
+    blocks = orc.query_blocks(qperm, p.q_block)
+    bp = g["block_ptr"].astype(np.int64)
+    bg = g["block_groups"][:bp[-1]].astype(np.int64)
+    ksets = orc.block_key_sets(bp, bg, g["key_perm"].astype(np.int64), g["group_off"].astype(np.int64))
+    S, lse = orc.sparse_attention(Q, K, V, tau, blocks, ksets)
+    ptok = qperm[orc.probe_positions(N, p.n_probes)]
+    if p.n_probes:
+        Op, _ = orc.dense_attention(Q, K, V, tau, rows=ptok)
+    else:
+        Op = np.zeros((0, p.head_dim))
+    w = orc.probe_weights(Op)
+    Rp = Op - S[ptok]
+    if p.n_probes:
+        U, ev = orc.residual_subspace(Rp, w, p.rank)
+    else:
+        U, ev = np.zeros((p.head_dim, 0)), np.zeros(p.head_dim)
+    Th = orc.ridge_fit(S[ptok], Rp @ U, w, p.ridge_lambda) if U.shape[1] else np.zeros((p.head_dim + 1, 0))
+    O = S + orc.predicted_residual(S, U, Th)
+    O[ptok] = Op
+    E = orc.executed_pairs(blocks, ksets, p.n_probes, N)
+    return dict(S=S, lse=lse, O=O, Op=Op, ptok=ptok, U=U, ev=ev, Th=Th, blocks=blocks, ksets=ksets,
+                E=E)
+
+
+def to_token_order(x_query_order, qperm):
+    out = np.empty_like(x_query_order)
+    out[qperm] = x_query_order
+    return out
+
+
+# ------------------------------------------------------------ (i) index parity
+
+@pytest.mark.parametrize("name", list(WORKLOADS))
+def test_partition_index_parity(name):
+    r = get_run(name)
+    p = r.p
+    for h in range(p.heads):
+        g = head_arrays(r, h)
+        assert np.array_equal(orc.argmin_lowest(g["assign"]), g["key_label"])
+        kp, goff, sizes = orc.group_members(g["key_label"], p.n_groups)
+        assert np.array_equal(kp, g["key_perm"])
+        assert np.array_equal(goff, g["group_off"])
+        # paired K/V groups: Kp rows are K rows in group order (bit-exact)
+        assert np.array_equal(g["Kp"], r.inp.K[h][kp])
+
+
+@pytest.mark.parametrize("name", list(WORKLOADS))
+def test_route_index_parity(name):
+    r = get_run(name)
+    p = r.p
+    for h in range(p.heads):
+        g = head_arrays(r, h)
+        sizes = np.diff(g["group_off"])
+        g1, v = orc.dominant_groups(g["coords"], sizes)
+        assert np.array_equal(g1, g["dom"])
+        assert np.array_equal(v.astype(np.float32), g["domval"])
+        assert np.array_equal(orc.query_order(g["dom"], g["domval"]), g["query_perm"])
+        ptr, grp = orc.route(g["sigma"], sizes, p.key_budget)
+        assert np.array_equal(ptr, g["block_ptr"])
+        assert np.array_equal(grp, g["block_groups"][:ptr[-1]])
+        blocks = orc.query_blocks(g["query_perm"], p.q_block)
+        ksets = orc.block_key_sets(ptr, grp, g["key_perm"], g["group_off"])
+        assert int(g["executed_pairs"]) == orc.executed_pairs(blocks, ksets, p.n_probes, p.n_tokens)
+
+
+def test_every_kmeans_iteration_tiny():
+    wl = configs.TINY
+    inp = wl.make_inputs()
+    prev_centroids = inp.K[0][inp.init_idx].astype(np.float64)
+    Qs = inp.Q[0][inp.sample_idx].astype(np.float64)
+    tau = float(inp.scale[0])
+    R = orc.key_responses(inp.Q[0], inp.K[0], tau, inp.sample_idx)
+    r2 = (R * R).sum(1)
+    for T in range(1, wl.params.kmeans_iters + 1):
+        print(f"[gpu] tiny k-means T={T}", flush=True)
+        r = run_pipeline(wl, p=replace(wl.params, kmeans_iters=T), inp=inp)
+        scores = r.np("assign")[0]
+        labels = r.np("key_label")[0]
+        assert np.array_equal(orc.argmin_lowest(scores), labels)
+        # value parity of the dumped scores: ||r - c||^2 - ||r||^2 with the
+        # previous iteration's GPU centroids
+        C = tau * prev_centroids @ Qs.T
+        ref = orc.squared_distances(R, C) - r2[:, None]
+        scale_ref = (C * C).sum(1)[None, :] + 2 * np.abs(R @ C.T)
+        assert np.all(np.abs(scores - ref) <= 1e-5 * scale_ref + 1e-6)
+        prev_centroids = r.np("key_centroid")[0].astype(np.float64)
+
+
+# ------------------------------------------------------------ (ii) value parity
+
+@pytest.mark.parametrize("name", list(WORKLOADS))
+def test_partition_and_route_values(name):
+    r = get_run(name)
+    p = r.p
+    tol = 1e-5
+    for h in range(p.heads):
+        g = head_arrays(r, h)
+        K = r.inp.K[h].astype(np.float64)
+        Q = r.inp.Q[h].astype(np.float64)
+        tau = float(r.inp.scale[h])
+        sizes = np.diff(g["group_off"])
+        kbar, _ = orc.key_centroids(K, g["key_label"], p.n_groups)
+        ne = sizes > 0
+        assert rel_l2(g["key_centroid"][ne], kbar[ne]) < tol
+        C = orc.query_coordinates(Q, g["key_centroid"].astype(np.float64), tau)
+        assert rel_l2(g["coords"][:, ne], C[:, ne]) < tol
+        assert np.all(np.isneginf(g["coords"][:, ~ne]))
+        blocks = orc.query_blocks(g["query_perm"], p.q_block)
+        sig = orc.block_scores(C, blocks)
+        assert rel_l2(g["sigma"][:, ne], sig[:, ne]) < tol
+
+
+@pytest.mark.parametrize("name", list(WORKLOADS))
+def test_attend_probe_fit_apply_values(name):
+    r = get_run(name)
+    p = r.p
+    tol = TOL[p.dtype]
+    for h in range(p.heads):
+        g = head_arrays(r, h)
+        Q, K, V = (x[h].astype(np.float64) for x in (r.inp.Q, r.inp.K, r.inp.V))
+        tau = float(r.inp.scale[h])
+        o = oracle_on_gpu_indices(Q, K, V, tau, p, g)
+        qperm = g["query_perm"]
+        S_tok = to_token_order(g["S"], qperm)
+        assert rel_l2(S_tok, o["S"]) < tol, "sparse attention"
+        lse_tok = to_token_order(g["lse"], qperm)
+        assert np.max(np.abs(lse_tok - o["lse"])) < (1e-4 if p.dtype == "f32" else 2e-2)
+        assert int(g["executed_pairs"]) == o["E"]
+        if p.n_probes:
+            assert rel_l2(g["O_probe"], o["Op"]) < tol, "probe rows"
+        assert rel_l2(g["O"], o["O"]) < tol, "final output"
+
+
+@pytest.mark.parametrize("name", list(WORKLOADS))
+def test_fit_matches_oracle_on_gpu_inputs(name):
+    """The fit alone: oracle fit on the GPU's probe inputs (S as stored, O_probe)."""
+    r = get_run(name)
+    p = r.p
+    for h in range(p.heads):
+        g = head_arrays(r, h)
+        N = p.n_tokens
+        pos = orc.probe_positions(N, p.n_probes)
+        Sp = g["S"][pos].astype(np.float64)
+        Op = g["O_probe"].astype(np.float64)
+        w = orc.probe_weights(Op)
+        Rp = Op - Sp
+        U, ev = orc.residual_subspace(Rp, w, p.rank)
+        keff = int(g["rank_eff"])
+        assert keff == U.shape[1]
+        Ug = g["U"][:, :keff].astype(np.float64)
+        Thg = g["Theta"][:, :keff].astype(np.float64)
+        # orthonormal basis of the same subspace
+        assert np.max(np.abs(Ug.T @ Ug - np.eye(keff))) < 1e-5
+        gap = (ev[keff - 1] - ev[keff]) / max(ev[0], 1e-300) if keff < len(ev) else 1.0
+        if gap > 1e-4:
+            assert np.max(np.abs(Ug @ Ug.T - U @ U.T)) < 1e-3
+        # normal equations satisfied by the GPU's Theta in its own basis
+        res = orc.normal_equation_residual(Sp, Rp @ Ug, w, p.ridge_lambda, Thg)
+        assert res < 1e-4
+        Th = orc.ridge_fit(Sp, Rp @ U, w, p.ridge_lambda)
+        S_all = g["S"].astype(np.float64)
+        if gap > 1e-4:
+            assert rel_l2(orc.predicted_residual(S_all, Ug, Thg),
+                          orc.predicted_residual(S_all, U, Th)) < 1e-3
+
+
+# ------------------------------------------------------------ (iii) per-query error
+
+@pytest.mark.parametrize("name", list(WORKLOADS))
+def test_per_query_error_agreement(name):
+    r = get_run(name)
+    p = r.p
+    rng = np.random.default_rng(5)
+    for h in range(p.heads):
+        g = head_arrays(r, h)
+        Q, K, V = (x[h].astype(np.float64) for x in (r.inp.Q, r.inp.K, r.inp.V))
+        tau = float(r.inp.scale[h])
+        o = oracle_on_gpu_indices(Q, K, V, tau, p, g)
+        unprobed = np.setdiff1d(np.arange(p.n_tokens), o["ptok"])
+        rows = unprobed if unprobed.size <= 2048 else np.sort(rng.choice(unprobed, 2048, replace=False))
+        dense, _ = orc.dense_attention(Q, K, V, tau, rows=rows)
+        O_or = o["O"][rows]
+        if p.dtype == "bf16":
+            O_or = bf16_round(O_or)
+        e_gpu = orc.relative_l2_rows(g["O"][rows], dense)
+        e_or = orc.relative_l2_rows(O_or, dense)
+        dd = np.abs(e_gpu - e_or)
+        e_hd = orc.relative_l2_rows(to_token_order(g["S"], g["query_perm"])[rows], dense)
+        print(f"[{name} h{h}] mean err {e_gpu.mean():.4g} (oracle {e_or.mean():.4g}); "
+              f"hard-drop {e_hd.mean():.4g}; |de| mean {dd.mean():.2e} p99 "
+              f"{np.percentile(dd, 99):.2e} max {dd.max():.2e}; "
+              f"density {int(g['executed_pairs']) / p.n_tokens**2:.4f}")
+        # the pages' metric: mean relative error over unprobed queries
+        assert abs(e_gpu.mean() - e_or.mean()) <= 1e-3
+        if p.dtype == "f32":
+            assert dd.max() <= 1e-3
+
+
+# ------------------------------------------------------------ (iv) independent
+
+@pytest.mark.parametrize("name", ["tiny", "bf16_d128"])
+def test_independent_oracle_run_report(name):
+    r = get_run(name)
+    p = r.p
+    h = 0
+    g = head_arrays(r, h)
+    res = orc.sparsepr_head(r.inp.Q[h], r.inp.K[h], r.inp.V[h], float(r.inp.scale[h]),
+                            sample_idx=r.inp.sample_idx, init_idx=r.inp.init_idx,
+                            q_block=p.q_block, n_groups=p.n_groups, kmeans_iters=p.kmeans_iters,
+                            density=p.density, n_probes=p.n_probes, rank=p.rank,
+                            ridge_lambda=p.ridge_lambda)
+    agree = float(np.mean(res.labels == g["key_label"]))
+    print(f"[{name}] independent oracle: label agreement {agree:.4f}, "
+          f"output rel L2 {rel_l2(g['O'], res.O):.3g}")
+    assert agree > 0.5
+
+
+# ------------------------------------------------------------ dense kernel
+
+@pytest.mark.parametrize("dtype,d,bq,n", [("f32", 64, 64, 1000), ("f32", 128, 128, 777),
+                                          ("bf16", 128, 128, 3045), ("bf16", 64, 64, 1500),
+                                          ("bf16", 128, 64, 200)])
+def test_dense_attention(dtype, d, bq, n):
+    rng = np.random.default_rng(n + d)
+    H = 2
+    from free_block_sparse_rcp_amd.inputs import round_to_dtype
+    Q = round_to_dtype(rng.standard_normal((H, n, d)), dtype)
+    K = round_to_dtype(rng.standard_normal((H, n, d)), dtype)
+    V = round_to_dtype(rng.standard_normal((H, n, d)), dtype)
+    sc = np.array([1.3 / math.sqrt(d), 0.4 / math.sqrt(d)], np.float32)
+    p = configs.Params(heads=H, n_tokens=n, head_dim=d, dtype=dtype, q_block=bq, n_groups=1,
+                       n_samples=1, kmeans_iters=1, density=1.0, n_probes=0, rank=0,
+                       ridge_lambda=1.0)
+    tdt = binding.torch_dtype(p)
+    tq, tk, tv = (torch.from_numpy(x).to("cuda", tdt) for x in (Q, K, V))
+    O, lse = binding.dense_attention(p, tq, tk, tv, torch.from_numpy(sc).cuda())
+    torch.cuda.synchronize()
+    O = O.float().cpu().numpy()
+    lse = lse.cpu().numpy()
+    for h in range(H):
+        ref, rl = orc.dense_attention(Q[h], K[h], V[h], float(sc[h]))
+        # bf16: output storage (~1.7e-3) plus bf16 probabilities in P V
+        assert rel_l2(O[h], ref) < (5e-3 if dtype == "bf16" else TOL[dtype])
+        assert np.max(np.abs(lse[h] - rl)) < 1e-4
+
+
+# ------------------------------------------------------------ variants and edges
+
+def test_random_block_variant():
+    wl = small_bf16(name="rb", mode=1, seed=14)
+    r = run_pipeline(wl)
+    p = r.p
+    for h in range(p.heads):
+        g = head_arrays(r, h)
+        lab = orc.random_block_labels(r.inp.rand_key_perm, p.n_groups)
+        assert np.array_equal(lab, g["key_label"])
+        assert np.array_equal(g["query_perm"], r.inp.rand_query_perm)
+        sizes = np.diff(g["group_off"])
+        ptr, grp = orc.route(g["sigma"], sizes, p.key_budget)
+        assert np.array_equal(ptr, g["block_ptr"])
+        Q, K, V = (x[h].astype(np.float64) for x in (r.inp.Q, r.inp.K, r.inp.V))
+        o = oracle_on_gpu_indices(Q, K, V, float(r.inp.scale[h]), p, g)
+        assert rel_l2(g["O"], o["O"]) < TOL["bf16"]
+
+
+def test_full_density_equals_dense():
+    wl = small_bf16(name="full", rho=1.0, m=0, k=0, G=16, seed=15)
+    r = run_pipeline(wl)
+    p = r.p
+    for h in range(p.heads):
+        g = head_arrays(r, h)
+        assert int(g["executed_pairs"]) == p.n_tokens ** 2
+        Q, K, V = (x[h].astype(np.float64) for x in (r.inp.Q, r.inp.K, r.inp.V))
+        dense, _ = orc.dense_attention(Q, K, V, float(r.inp.scale[h]))
+        assert rel_l2(g["O"], dense) < 5e-3
+
+
+def test_zero_probes_output_is_sparse_output():
+    wl = small_bf16(name="m0", m=0, seed=16)
+    r = run_pipeline(wl)
+    for h in range(r.p.heads):
+        g = head_arrays(r, h)
+        assert int(g["rank_eff"]) == 0
+        assert np.array_equal(g["O"], bf16_round(to_token_order(g["S"], g["query_perm"])))
+
+
+def test_many_probes():
+    wl = replace(configs.TINY, params=replace(configs.TINY.params, n_probes=1024, density=1.0))
+    r = run_pipeline(wl)
+    p = r.p
+    g = head_arrays(r, 0)
+    Q, K, V = (x[0].astype(np.float64) for x in (r.inp.Q, r.inp.K, r.inp.V))
+    o = oracle_on_gpu_indices(Q, K, V, float(r.inp.scale[0]), p, g)
+    dense, _ = orc.dense_attention(Q, K, V, float(r.inp.scale[0]), rows=o["ptok"])
+    assert rel_l2(g["O"][o["ptok"]], dense) < 1e-4
+    assert rel_l2(g["O"], o["O"]) < 1e-4
+
+
+def test_determinism():
+    wl = WORKLOADS["bf16_d128"]
+    a = get_run("bf16_d128")
+    b = run_pipeline(wl, inp=a.inp)
+    for n in ("key_label", "key_perm", "group_off", "query_perm", "block_ptr", "executed_pairs",
+              "S", "lse", "O", "O_probe", "U", "Theta", "rank_eff"):
+        assert np.array_equal(a.np(n), b.np(n)), n
+    ptr = a.np("block_ptr")
+    for h in range(a.p.heads):
+        assert np.array_equal(a.np("block_groups")[h][:ptr[h][-1]], b.np("block_groups")[h][:ptr[h][-1]])
