@@ -18,12 +18,29 @@
 
 namespace spr {
 
-constexpr int kMaxRanges = 1024;
+// Routed groups that are adjacent in the group-contiguous key order are merged
+// into one range; with at most 1024 groups there are at most 512 ranges.
+constexpr int kMaxRanges = 512;
+constexpr int kMaxGroups = 1024;
 
+// LDS tiles hold 64 key rows with padded pitches: K rows at 2D+16 bytes (MFMA
+// A-operand reads of 16 consecutive rows hit distinct banks), V rows at 2D+64
+// bytes (the transposing ds_read_b64_tr_b16 reads 4 rows x 64 bytes per 32
+// lanes, and the pitch puts those rows on disjoint banks). Both keep every
+// LDS read address affine in the loop indices.
 template <int D>
-__device__ __forceinline__ int v_swizzle(int r) {
-  return D == 128 ? 4 * (r & 3) : 4 * ((r >> 1) & 1);
-}
+struct TileGeom {
+  static constexpr int ROWB = 2 * D;
+  static constexpr int KP = ROWB + 16;
+  static constexpr int VP = ROWB + 64;
+  static constexpr int KCH = KP / 16;          // 16-byte chunks per padded K row
+  static constexpr int VCH = VP / 16;
+  static constexpr int KBYTES = 64 * KP;
+  static constexpr int VBYTES = 64 * VP;
+  static constexpr int KINS = KBYTES / 1024;   // 1 KB direct loads per tile
+  static constexpr int VINS = VBYTES / 1024;
+  static_assert(KBYTES % 1024 == 0 && VBYTES % 1024 == 0, "tiles must be whole 1 KB loads");
+};
 
 // Decoded work item of one workgroup.
 struct Item {
@@ -92,28 +109,35 @@ __device__ __forceinline__ int build_ranges(const AttnArgs& a, const Item& it, i
   const int32_t* bp = a.block_ptr + (size_t)it.h * (a.nb + 1);
   const int p0 = bp[it.b];
   int ng = bp[it.b + 1] - p0;
-  ng = ng < 0 ? 0 : (ng > kMaxRanges ? kMaxRanges : ng);
+  ng = ng < 0 ? 0 : (ng > kMaxGroups ? kMaxGroups : ng);
   const int32_t* grp = a.block_groups + (size_t)it.h * a.nb * a.G + p0;
   const int32_t* off = a.group_off + (size_t)it.h * (a.G + 1);
-  int carry = 0;
+  int carry_len = 0, carry_rng = 0;
   for (int base = 0; base < ng; base += NT) {
     const int i = base + t;
-    int len = 0;
+    int len = 0, st = 0, fresh = 0;
     if (i < ng) {
       const int g = clamp_idx(grp[i], a.G);
-      const int st = off[g];
-      len = off[g + 1] - st;
-      if (len < 0) len = 0;
-      r_start[i] = st;
+      st = off[g];
+      len = max(0, off[g + 1] - st);
+      // a range starts unless this group begins where the previous one ended
+      fresh = (i == 0) || (off[clamp_idx(grp[i - 1], a.G) + 1] != st);
     }
-    int tot;
-    const int ex = block_exclusive_scan<NT>(len, tmp, &tot);
-    if (i < ng) r_cum[i] = carry + ex;
-    carry += tot;
+    int tot_len, tot_rng;
+    const int ex_len = block_exclusive_scan<NT>(len, tmp, &tot_len);
+    const int ex_rng = block_exclusive_scan<NT>(fresh, tmp, &tot_rng);
+    const int ri = carry_rng + ex_rng;
+    if (i < ng && fresh && ri < kMaxRanges) {
+      r_start[ri] = st;
+      r_cum[ri] = carry_len + ex_len;
+    }
+    carry_len += tot_len;
+    carry_rng += tot_rng;
   }
-  if (t == 0) r_cum[ng] = carry;
+  const int nr = carry_rng < kMaxRanges ? carry_rng : kMaxRanges;
+  if (t == 0) r_cum[nr] = carry_len;
   __syncthreads();
-  return ng;
+  return nr;
 }
 
 // Row of Kp/Vp at key position p of the block's list (cursor advances
@@ -125,20 +149,114 @@ __device__ __forceinline__ int key_row(int p, int total, int ng, const int* r_st
   return r_start[cur] + (p - r_cum[cur]);
 }
 
-template <int D, int BQ, int MODE>
-__global__ __launch_bounds__(BQ * 2) void k_attn_mfma(AttnArgs a) {
-  constexpr int NT = BQ * 2;
+// One 64-key tile of the flash loop: S^T = K Q^T, online softmax, O^T += V^T P^T.
+// Ktile / Vtile point at distinct __shared__ buffers, so the compiler can see
+// that these reads do not alias the direct loads filling the other buffer.
+template <int D>
+__device__ __forceinline__ void attn_tile(const char* __restrict__ kb, const char* __restrict__ vb,
+                                          const bf16x8* qreg, f32x16* acc_o, float& m_run,
+                                          float& l_run, float c, int kbase, int total, int hl) {
+  using TG = TileGeom<D>;
   constexpr int KT = 64;
-  constexpr int ROWB = D * 2;
-  constexpr int CPR = ROWB / 16;
-  constexpr int TPR = NT / KT;
-  constexpr int CPT = CPR / TPR;
-  constexpr int KPITCH = ROWB + 16;
-  constexpr int VPITCH = ROWB;
-  constexpr int NDT = D / 32;   // 32-wide output d tiles
-  constexpr int NKK = D / 16;   // k-steps of the QK^T product
-  __shared__ __attribute__((aligned(16))) char lds_k[2][KT * KPITCH];
-  __shared__ __attribute__((aligned(16))) char lds_v[2][KT * VPITCH];
+  constexpr int NDT = D / 32;
+  constexpr int NKK = D / 16;
+  f32x16 s[2];
+#pragma unroll
+  for (int kt = 0; kt < 2; ++kt) {
+#pragma unroll
+    for (int r = 0; r < 16; ++r) s[kt][r] = 0.f;
+#pragma unroll
+    for (int kk = 0; kk < NKK; ++kk) {
+      const bf16x8 kop = *reinterpret_cast<const bf16x8*>(kb + 32 * kt * TG::KP + 32 * kk);
+      s[kt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kop, qreg[kk], s[kt], 0, 0, 0);
+    }
+  }
+  // online softmax in log2 units; the max is only re-based when it grows by > 8
+  if (kbase + KT > total) {
+#pragma unroll
+    for (int kt = 0; kt < 2; ++kt)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int kp = kbase + 32 * kt + 8 * (r >> 2) + 4 * hl + (r & 3);
+        if (kp >= total) s[kt][r] = -__builtin_inff();
+      }
+  }
+  float mx = -__builtin_inff();
+#pragma unroll
+  for (int kt = 0; kt < 2; ++kt)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[kt][r]);
+  mx = fmaxf(mx, __shfl_xor(mx, 32)) * c;
+  const float m_new = fmaxf(m_run, mx);
+  const bool need = m_new > m_run + 8.0f;
+  if (__any(need)) {
+    const float alpha = need ? __builtin_amdgcn_exp2f(m_run - m_new) : 1.0f;
+    l_run *= alpha;
+#pragma unroll
+    for (int dt = 0; dt < NDT; ++dt)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) acc_o[dt][r] *= alpha;
+    if (need) m_run = m_new;
+  }
+  const float neg_m = -m_run;
+  bf16x8 pk[2][2];
+#pragma unroll
+  for (int kt = 0; kt < 2; ++kt)
+#pragma unroll
+    for (int hf = 0; hf < 2; ++hf) {
+      float pv[8];
+#pragma unroll
+      for (int q = 0; q < 8; ++q) {
+        pv[q] = __builtin_amdgcn_exp2f(fmaf(s[kt][8 * hf + q], c, neg_m));
+        l_run += pv[q];
+      }
+#pragma unroll
+      for (int q = 0; q < 8; q += 2) {
+        const f32x2 f = {pv[q], pv[q + 1]};
+        const bf16x2 bb = __builtin_convertvector(f, bf16x2);
+        pk[kt][hf][q] = bb[0];
+        pk[kt][hf][q + 1] = bb[1];
+      }
+    }
+  // V^T operand via transposing LDS reads
+#pragma unroll
+  for (int kt = 0; kt < 2; ++kt)
+#pragma unroll
+    for (int hf = 0; hf < 2; ++hf) {
+      const int chunk = 32 * kt + 16 * hf;
+#pragma unroll
+      for (int dt = 0; dt < NDT; ++dt) {
+        const char* p1 = vb + chunk * TG::VP + 64 * dt;
+        const char* p2 = p1 + 8 * TG::VP;
+        const s16x4 v1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+            (__attribute__((address_space(3))) s16x4*)(p1));
+        const s16x4 v2 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+            (__attribute__((address_space(3))) s16x4*)(p2));
+        const s16x8 vv = __builtin_shufflevector(v1, v2, 0, 1, 2, 3, 4, 5, 6, 7);
+        acc_o[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, vv),
+                                                            pk[kt][hf], acc_o[dt], 0, 0, 0);
+      }
+    }
+}
+
+template <int D, int BQ, int MODE>
+__global__ __launch_bounds__(BQ * 2) __attribute__((amdgpu_waves_per_eu(2, 2)))
+void k_attn_mfma(AttnArgs a) {
+  using TG = TileGeom<D>;
+  constexpr int NT = BQ * 2;
+  constexpr int NW = BQ / 32;
+  constexpr int KT = 64;
+  constexpr int ROWB = TG::ROWB;
+  constexpr int CPR = ROWB / 16;             // data chunks per row
+  constexpr int NDT = D / 32;                // 32-wide output d tiles
+  constexpr int NKK = D / 16;                // k-steps of the QK^T product
+  constexpr int KINS_W = (TG::KINS + NW - 1) / NW;
+  constexpr int VINS_W = (TG::VINS + NW - 1) / NW;
+  __shared__ __attribute__((aligned(1024))) char lds_k0[TG::KBYTES];
+  __shared__ __attribute__((aligned(1024))) char lds_k1[TG::KBYTES];
+  __shared__ __attribute__((aligned(1024))) char lds_v0[TG::VBYTES];
+  __shared__ __attribute__((aligned(1024))) char lds_v1[TG::VBYTES];
+  __shared__ int ridx[2][KT];
   __shared__ int r_start[kMaxRanges + 1];
   __shared__ int r_cum[kMaxRanges + 2];
   __shared__ int tmp[NT];
@@ -167,7 +285,7 @@ __global__ __launch_bounds__(BQ * 2) void k_attn_mfma(AttnArgs a) {
     qreg[kk] = *reinterpret_cast<const bf16x8*>(Qh + (size_t)qtok * D + 16 * kk + 8 * hl);
 
   const float c = a.scale[it.h] * kLog2e;
-  float m_run = -__builtin_inff();
+  float m_run = -__builtin_inff();   // running max of the scaled logits (log2 units)
   float l_run = 0.f;
   f32x16 acc_o[NDT];
 #pragma unroll
@@ -176,120 +294,61 @@ __global__ __launch_bounds__(BQ * 2) void k_attn_mfma(AttnArgs a) {
     for (int r = 0; r < 16; ++r) acc_o[dt][r] = 0.f;
 
   const int ntiles = (total + KT - 1) / KT;
-  const int lrow = t / TPR;       // row this thread loads
-  const int lch0 = t % TPR;       // first chunk; chunks lch0 + TPR*u
   int cursor = 0;
-  uint4 kreg[CPT], vreg[CPT];
-
-  auto load_tile = [&](int tile) {
-    const int row = key_row(tile * KT + lrow, total, ng, r_start, r_cum, cursor);
+  // wave 0 writes the Kp/Vp row of each of a tile's 64 key positions
+  auto fill_rows = [&](int tile) {
+    if (w == 0 && tile < ntiles) ridx[tile & 1][lane] = key_row(tile * KT + lane, total, ng, r_start, r_cum, cursor);
+  };
+  // direct global->LDS loads: 1 KB per wave instruction, lane i -> chunk 64u + i of the tile
+  auto issue_tile = [&](int tile, char* kdst, char* vdst) {
+    const int* rows = ridx[tile & 1];
 #pragma unroll
-    for (int u = 0; u < CPT; ++u) {
-      const int ch = lch0 + TPR * u;
-      kreg[u] = *reinterpret_cast<const uint4*>(Kh + (size_t)row * ROWB + ch * 16);
-      vreg[u] = *reinterpret_cast<const uint4*>(Vh + (size_t)row * ROWB + ch * 16);
+    for (int j = 0; j < KINS_W; ++j) {
+      const int u = w + NW * j;
+      if (u < TG::KINS) {
+        const int q = 64 * u + lane;
+        const int r = q / TG::KCH, cc = q - r * TG::KCH;
+        const char* src = Kh + (size_t)rows[r] * ROWB + (cc < CPR ? cc : 0) * 16;
+        __builtin_amdgcn_global_load_lds(
+            src, (__attribute__((address_space(3))) void*)(kdst + u * 1024), 16, 0, 0);
+      }
+    }
+#pragma unroll
+    for (int j = 0; j < VINS_W; ++j) {
+      const int u = w + NW * j;
+      if (u < TG::VINS) {
+        const int q = 64 * u + lane;
+        const int r = q / TG::VCH, cc = q - r * TG::VCH;
+        const char* src = Vh + (size_t)rows[r] * ROWB + (cc < CPR ? cc : 0) * 16;
+        __builtin_amdgcn_global_load_lds(
+            src, (__attribute__((address_space(3))) void*)(vdst + u * 1024), 16, 0, 0);
+      }
     }
   };
-  auto store_tile = [&](int buf) {
-#pragma unroll
-    for (int u = 0; u < CPT; ++u) {
-      const int ch = lch0 + TPR * u;
-      *reinterpret_cast<uint4*>(&lds_k[buf][lrow * KPITCH + ch * 16]) = kreg[u];
-      *reinterpret_cast<uint4*>(&lds_v[buf][lrow * VPITCH + ((ch ^ v_swizzle<D>(lrow)) * 16)]) = vreg[u];
-    }
-  };
 
-  if (ntiles > 0) {
-    load_tile(0);
-    store_tile(0);
-  }
+  fill_rows(0);
+  fill_rows(1);
+  __syncthreads();
+  if (ntiles > 0) issue_tile(0, lds_k0, lds_v0);
+  __builtin_amdgcn_s_waitcnt(0);
   __syncthreads();
 
-  for (int tile = 0; tile < ntiles; ++tile) {
-    const int buf = tile & 1;
-    const bool more = tile + 1 < ntiles;
-    if (more) load_tile(tile + 1);
-
-    // ---- S^T = K Q^T for the 64-key tile (two 32-key halves)
-    f32x16 s[2];
-#pragma unroll
-    for (int kt = 0; kt < 2; ++kt) {
-#pragma unroll
-      for (int r = 0; r < 16; ++r) s[kt][r] = 0.f;
-      const char* krow = &lds_k[buf][(32 * kt + ql) * KPITCH];
-#pragma unroll
-      for (int kk = 0; kk < NKK; ++kk) {
-        const bf16x8 kop = *reinterpret_cast<const bf16x8*>(krow + (16 * kk + 8 * hl) * 2);
-        s[kt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kop, qreg[kk], s[kt], 0, 0, 0);
-      }
-    }
-    // ---- online softmax (log2 domain), lazy rescale
-    const int kbase = tile * KT;
-    float mx = -__builtin_inff();
-#pragma unroll
-    for (int kt = 0; kt < 2; ++kt)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int kp = kbase + 32 * kt + 8 * (r >> 2) + 4 * hl + (r & 3);
-        const float x = kp < total ? s[kt][r] * c : -__builtin_inff();
-        s[kt][r] = x;
-        mx = fmaxf(mx, x);
-      }
-    mx = fmaxf(mx, __shfl_xor(mx, 32));
-    const float m_new = fmaxf(m_run, mx);
-    const bool need = m_new > m_run + 8.0f;
-    if (__any(need)) {
-      const float alpha = need ? __builtin_amdgcn_exp2f(m_run - m_new) : 1.0f;
-      l_run *= alpha;
-#pragma unroll
-      for (int dt = 0; dt < NDT; ++dt)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) acc_o[dt][r] *= alpha;
-      if (need) m_run = m_new;
-    }
-    bf16x8 pk[2][2];
-#pragma unroll
-    for (int kt = 0; kt < 2; ++kt)
-#pragma unroll
-      for (int hf = 0; hf < 2; ++hf) {
-        float pv[8];
-#pragma unroll
-        for (int q = 0; q < 8; ++q) {
-          pv[q] = __builtin_amdgcn_exp2f(s[kt][8 * hf + q] - m_run);
-          l_run += pv[q];
-        }
-#pragma unroll
-        for (int q = 0; q < 8; q += 2) {
-          const f32x2 f = {pv[q], pv[q + 1]};
-          const bf16x2 bb = __builtin_convertvector(f, bf16x2);
-          pk[kt][hf][q] = bb[0];
-          pk[kt][hf][q + 1] = bb[1];
-        }
-      }
-    // ---- O^T += V^T P^T; V^T operand via transposing LDS reads
-    const int grp = lane >> 4, gl = lane & 15;
-#pragma unroll
-    for (int kt = 0; kt < 2; ++kt)
-#pragma unroll
-      for (int hf = 0; hf < 2; ++hf) {
-        const int chunk = 32 * kt + 16 * hf;
-#pragma unroll
-        for (int dt = 0; dt < NDT; ++dt) {
-          const int d = 32 * dt + 16 * (grp & 1) + 4 * (gl & 3);
-          const int r1 = chunk + 4 * (grp >> 1) + (gl >> 2);
-          const int r2 = r1 + 8;
-          const char* p1 = &lds_v[buf][r1 * VPITCH + (((d >> 3) ^ v_swizzle<D>(r1)) * 16) + (d & 4) * 2];
-          const char* p2 = &lds_v[buf][r2 * VPITCH + (((d >> 3) ^ v_swizzle<D>(r2)) * 16) + (d & 4) * 2];
-          const s16x4 v1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-              (__attribute__((address_space(3))) s16x4*)(p1));
-          const s16x4 v2 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-              (__attribute__((address_space(3))) s16x4*)(p2));
-          const s16x8 vv = __builtin_shufflevector(v1, v2, 0, 1, 2, 3, 4, 5, 6, 7);
-          acc_o[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, vv),
-                                                              pk[kt][hf], acc_o[dt], 0, 0, 0);
-        }
-      }
-    if (more) store_tile(buf ^ 1);
+  const int grp = lane >> 4, gl = lane & 15;
+  // per-lane LDS byte offsets (the tile loop adds only compile-time constants)
+  const int koff = ql * TG::KP + hl * 16;
+  const int voff = (4 * (grp >> 1) + (gl >> 2)) * TG::VP + (16 * (grp & 1) + 4 * (gl & 3)) * 2;
+  // two tiles per trip: even tiles live in buffer 0, odd tiles in buffer 1
+  for (int tile = 0; tile < ntiles; tile += 2) {
+    if (tile + 1 < ntiles) issue_tile(tile + 1, lds_k1, lds_v1);
+    fill_rows(tile + 2);
+    attn_tile<D>(lds_k0 + koff, lds_v0 + voff, qreg, acc_o, m_run, l_run, c, tile * KT, total, hl);
+    __builtin_amdgcn_s_waitcnt(0);
+    __syncthreads();
+    if (tile + 1 >= ntiles) break;
+    if (tile + 2 < ntiles) issue_tile(tile + 2, lds_k0, lds_v0);
+    fill_rows(tile + 3);
+    attn_tile<D>(lds_k1 + koff, lds_v1 + voff, qreg, acc_o, m_run, l_run, c, (tile + 1) * KT, total, hl);
+    __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
   }
 
