@@ -122,6 +122,9 @@ def main():
                     help="oracle samples every n-th query block (0: chosen by workload size)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-dense", action="store_true")
+    ap.add_argument("--calibration-copy-mib", type=int, default=0,
+                    help="also run one plain device copy of this many MiB (a known-size "
+                         "kernel for scaling the FETCH_SIZE / WRITE_SIZE counters)")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only: the operator is per call and per head, and this "
@@ -173,6 +176,14 @@ def main():
         binding.apply(p, b)
         if ev is not None:
             ev[5].record()
+
+    if args.calibration_copy_mib:
+        n = args.calibration_copy_mib * (1 << 20) // 4
+        src = torch.ones(n, dtype=torch.float32, device=dev)
+        dst = torch.empty_like(src)
+        torch.neg(src, out=dst)   # reads and writes exactly n * 4 bytes
+        torch.cuda.synchronize()
+        del src, dst
 
     log(f"[bench] warmup {args.warmup}")
     for _ in range(args.warmup):

@@ -55,6 +55,11 @@ def build(verbose: bool = True) -> str:
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"link failed:\n{r.stdout}{r.stderr}")
+    # a kernel whose host stub was not instantiated links fine and fails at dlopen
+    r = subprocess.run([sys.executable, "-c", f"import ctypes; ctypes.CDLL({tmp!r})"],
+                       capture_output=True, text=True)
+    if r.returncode != 0:
+        raise RuntimeError(f"built library does not load:\n{r.stderr}")
     os.replace(tmp, lib_path())
     if verbose:
         print(f"built {lib_path()}")

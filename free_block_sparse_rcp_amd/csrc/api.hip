@@ -51,6 +51,7 @@ PartitionWs partition_ws(const Dims& d) {
   L.totals = b.take(H * nbk * sizeof(int32_t));
   L.starts = b.take(H * nbk * sizeof(int32_t));
   L.partial = b.take(H * (G + d.ntile64) * D * sizeof(float));
+  L.best = b.take(H * (size_t)d.N * sizeof(unsigned long long));
   L.end = align256(b.off);
   return L;
 }
@@ -72,6 +73,8 @@ RouteWs route_ws(const Dims& d) {
   L.sel = b.take(H * nb * G * 4);
   L.selcnt = b.take(H * nb * 4);
   L.blkkeys = b.take(H * nb * 8);
+  L.chl = b.take(H * G * d.D * 2 * 2);
+  L.best = b.take(H * N * 8);
   L.end = align256(b.off);
   return L;
 }

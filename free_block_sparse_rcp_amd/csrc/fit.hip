@@ -54,10 +54,10 @@ __device__ int sturm_count(const double* a, const double* b2, int n, double x, d
 
 // Per-head scratch layout (doubles) in the workspace.
 struct FitScratch {
-  double *R, *S, *w, *X, *lu, *Y, *rhs;
+  double *R, *S, *w, *X, *hv, *Y, *rhs;
 };
 __host__ __device__ inline size_t fit_doubles_per_head(int m, int D, int k) {
-  return (size_t)2 * m * D + m + (size_t)D * k + (size_t)4 * k * D + (size_t)m * k +
+  return (size_t)2 * m * D + m + (size_t)D * k + (size_t)D * D + (size_t)m * k +
          (size_t)(D + 1) * k + 64;
 }
 __device__ inline FitScratch fit_scratch(double* base, int m, int D, int k) {
@@ -66,8 +66,8 @@ __device__ inline FitScratch fit_scratch(double* base, int m, int D, int k) {
   f.S = f.R + (size_t)m * D;
   f.w = f.S + (size_t)m * D;
   f.X = f.w + m;
-  f.lu = f.X + (size_t)D * k;
-  f.Y = f.lu + (size_t)4 * k * D;
+  f.hv = f.X + (size_t)D * k;
+  f.Y = f.hv + (size_t)D * D;
   f.rhs = f.Y + (size_t)m * k;
   return f;
 }
@@ -123,13 +123,36 @@ __global__ __launch_bounds__(kFitThreads) void k_fit(const float* S_out_in, cons
   const double wsum = wg_sum(wpart, red);
   for (int i = t; i < m; i += NT) f.w[i] = wsum > 0.0 ? f.w[i] / wsum : 0.0;
   __syncthreads();
-  // ---- Sigma = sum_i w_i r_i r_i^T into LDS
+  // ---- Sigma = sum_i w_i r_i r_i^T into LDS, 8 x 8 tiles per thread
   double* A = big;
-  for (int idx = t; idx < D * D; idx += NT) {
-    const int ra = idx / D, cb = idx % D;
-    double s = 0.0;
-    for (int i = 0; i < m; ++i) s += f.w[i] * f.R[(size_t)i * D + ra] * f.R[(size_t)i * D + cb];
-    A[ra * PA + cb] = s;
+  {
+    constexpr int NTB = D / 8;
+    for (int tile = t; tile < NTB * NTB; tile += NT) {
+      const int a0 = 8 * (tile / NTB), b0 = 8 * (tile % NTB);
+      double acc[8][8];
+#pragma unroll
+      for (int i = 0; i < 8; ++i)
+#pragma unroll
+        for (int j = 0; j < 8; ++j) acc[i][j] = 0.0;
+      for (int i = 0; i < m; ++i) {
+        const double wi = f.w[i];
+        const double* Ri = f.R + (size_t)i * D;
+        double ra[8], rb[8];
+#pragma unroll
+        for (int u = 0; u < 8; ++u) {
+          ra[u] = wi * Ri[a0 + u];
+          rb[u] = Ri[b0 + u];
+        }
+#pragma unroll
+        for (int u = 0; u < 8; ++u)
+#pragma unroll
+          for (int v = 0; v < 8; ++v) acc[u][v] += ra[u] * rb[v];
+      }
+#pragma unroll
+      for (int u = 0; u < 8; ++u)
+#pragma unroll
+        for (int v = 0; v < 8; ++v) A[(a0 + u) * PA + b0 + v] = acc[u][v];
+    }
   }
   __syncthreads();
   double trpart = 0.0;
@@ -226,60 +249,82 @@ __global__ __launch_bounds__(kFitThreads) void k_fit(const float* S_out_in, cons
     if (r < keff && sub == 0) lam_top[r] = 0.5 * (lo + hi);
   }
   __syncthreads();
-  // ---- inverse iteration on the tridiagonal, one thread per eigenvector
+  // ---- reflectors to the workspace; the LDS block is reused from here on
+  for (int idx = t; idx < D * D; idx += NT) {
+    const int i = idx / D, k = idx % D;
+    if (i > k && k < D - 2) f.hv[(size_t)i * D + k] = A[i * PA + k];
+  }
+  __syncthreads();
+  // ---- inverse iteration on the tridiagonal, one thread per eigenvector,
+  // factors in LDS interleaved across the batch ([i][r]) so lanes hit distinct banks
   const double pe = 2.2e-16 * fmax(tnorm, 1e-300);
-  for (int r = t; r < keff; r += NT) {
-    const double lam = lam_top[r];
-    double* U1 = f.lu + (size_t)r * 4 * D;
-    double* U2 = U1 + D;
-    double* U3 = U2 + D;
-    double* RR = U3 + D;
-    double* x = f.X;  // column r, layout [D][kmax]
-    for (int i = 0; i < D; ++i) {
-      const uint32_t hsh = (uint32_t)(i * 2654435761u) ^ (uint32_t)(r * 40503u + 12345u);
-      x[(size_t)i * kmax + r] = 0.5 + (double)(hsh % 1000u) / 1000.0;
-    }
-    for (int pass = 0; pass < 3; ++pass) {
-      double cd = dg[0] - lam, cu = D > 1 ? od[0] : 0.0, cu2 = 0.0, cr = x[r];
-      for (int i = 0; i < D - 1; ++i) {
-        const double nl = od[i], nd = dg[i + 1] - lam, nu = (i + 1 < D - 1) ? od[i + 1] : 0.0;
-        const double nr = x[(size_t)(i + 1) * kmax + r];
-        if (fabs(cd) >= fabs(nl)) {
-          if (cd == 0.0) cd = pe;
-          const double mlt = nl / cd;
-          U1[i] = cd; U2[i] = cu; U3[i] = cu2; RR[i] = cr;
-          cd = nd - mlt * cu;
-          cu = nu - mlt * cu2;
-          cu2 = 0.0;
-          cr = nr - mlt * cr;
-        } else {
-          const double mlt = cd / nl;
-          U1[i] = nl; U2[i] = nd; U3[i] = nu; RR[i] = nr;
-          const double ncd = cu - mlt * nd;
-          const double ncu = cu2 - mlt * nu;
-          cr = cr - mlt * nr;
-          cd = ncd;
-          cu = ncu;
-          cu2 = 0.0;
+  constexpr int KB = D / 4;   // 4 arrays of D x KB doubles fit the (D+1)(D+2) LDS block
+  static_assert(4 * D * KB <= (D + 1) * (D + 2), "inverse-iteration batch exceeds LDS");
+  for (int b0 = 0; b0 < keff; b0 += KB) {
+    const int nbt = min(KB, keff - b0);
+    double* U1 = big;
+    double* U2 = U1 + D * KB;
+    double* U3 = U2 + D * KB;
+    double* Z = U3 + D * KB;
+    if (t < nbt) {
+      const int r = b0 + t;
+      const double lam = lam_top[r];
+      for (int i = 0; i < D; ++i) {
+        const uint32_t hsh = (uint32_t)(i * 2654435761u) ^ (uint32_t)(r * 40503u + 12345u);
+        Z[i * KB + t] = 0.5 + (double)(hsh % 1000u) / 1000.0;
+      }
+      for (int pass = 0; pass < 3; ++pass) {
+        double cd = dg[0] - lam, cu = od[0], cu2 = 0.0, cr = Z[t];
+        for (int i = 0; i < D - 1; ++i) {
+          const double nl = od[i], nd = dg[i + 1] - lam, nu = (i + 1 < D - 1) ? od[i + 1] : 0.0;
+          const double nr = Z[(i + 1) * KB + t];
+          if (fabs(cd) >= fabs(nl)) {
+            if (cd == 0.0) cd = pe;
+            const double mlt = nl / cd;
+            U1[i * KB + t] = cd; U2[i * KB + t] = cu; U3[i * KB + t] = cu2; Z[i * KB + t] = cr;
+            cd = nd - mlt * cu;
+            cu = nu - mlt * cu2;
+            cu2 = 0.0;
+            cr = nr - mlt * cr;
+          } else {
+            const double mlt = cd / nl;
+            U1[i * KB + t] = nl; U2[i * KB + t] = nd; U3[i * KB + t] = nu; Z[i * KB + t] = nr;
+            const double ncd = cu - mlt * nd;
+            const double ncu = cu2 - mlt * nu;
+            cr = cr - mlt * nr;
+            cd = ncd;
+            cu = ncu;
+            cu2 = 0.0;
+          }
         }
+        if (fabs(cd) < pe) cd = cd < 0.0 ? -pe : pe;
+        double y1 = cr / cd, y2 = 0.0;
+        double nrm = y1 * y1;
+        Z[(D - 1) * KB + t] = y1;
+        for (int i = D - 2; i >= 0; --i) {
+          const double y = (Z[i * KB + t] - U2[i * KB + t] * y1 - U3[i * KB + t] * y2) / U1[i * KB + t];
+          Z[i * KB + t] = y;
+          nrm += y * y;
+          y2 = y1;
+          y1 = y;
+        }
+        const double inv = 1.0 / sqrt(nrm);
+        for (int i = 0; i < D; ++i) Z[i * KB + t] *= inv;
       }
-      if (fabs(cd) < pe) cd = cd < 0.0 ? -pe : pe;
-      U1[D - 1] = cd;
-      RR[D - 1] = cr;
-      double y1 = RR[D - 1] / U1[D - 1];
-      double y2 = 0.0;
-      double nrm = y1 * y1;
-      x[(size_t)(D - 1) * kmax + r] = y1;
-      for (int i = D - 2; i >= 0; --i) {
-        const double y = (RR[i] - U2[i] * y1 - U3[i] * y2) / U1[i];
-        x[(size_t)i * kmax + r] = y;
-        nrm += y * y;
-        y2 = y1;
-        y1 = y;
-      }
-      const double inv = 1.0 / sqrt(nrm);
-      for (int i = 0; i < D; ++i) x[(size_t)i * kmax + r] *= inv;
     }
+    __syncthreads();
+    for (int idx = t; idx < D * nbt; idx += NT) {
+      const int i = idx / nbt, r = idx % nbt;
+      f.X[(size_t)i * kmax + b0 + r] = Z[i * KB + r];
+    }
+    __syncthreads();
+  }
+  // ---- eigenvector block in LDS: X[e][r], pitch keff + 1
+  const int PXK = keff + 1;
+  double* X = big;
+  for (int idx = t; idx < D * keff; idx += NT) {
+    const int e = idx / keff, r = idx % keff;
+    X[e * PXK + r] = f.X[(size_t)e * kmax + r];
   }
   __syncthreads();
   // ---- classical Gram-Schmidt, twice, in eigenvalue order
@@ -287,29 +332,29 @@ __global__ __launch_bounds__(kFitThreads) void k_fit(const float* S_out_in, cons
     for (int pass = 0; pass < 2; ++pass) {
       for (int i0 = 0; i0 < j; i0 += NT / 8) {
         const int i = i0 + t / 8, sub = t % 8;
-        double s = 0.0;
+        double sacc = 0.0;
         if (i < j)
-          for (int e = sub; e < D; e += 8) s += f.X[(size_t)e * kmax + i] * f.X[(size_t)e * kmax + j];
-        s += __shfl_xor(s, 1);
-        s += __shfl_xor(s, 2);
-        s += __shfl_xor(s, 4);
-        if (i < j && sub == 0) dots[i] = s;
+          for (int e = sub; e < D; e += 8) sacc += X[e * PXK + i] * X[e * PXK + j];
+        sacc += __shfl_xor(sacc, 1);
+        sacc += __shfl_xor(sacc, 2);
+        sacc += __shfl_xor(sacc, 4);
+        if (i < j && sub == 0) dots[i] = sacc;
       }
       __syncthreads();
       for (int e = t; e < D; e += NT) {
-        double x = f.X[(size_t)e * kmax + j];
-        for (int i = 0; i < j; ++i) x -= dots[i] * f.X[(size_t)e * kmax + i];
-        f.X[(size_t)e * kmax + j] = x;
+        double x = X[e * PXK + j];
+        for (int i = 0; i < j; ++i) x -= dots[i] * X[e * PXK + i];
+        X[e * PXK + j] = x;
       }
       __syncthreads();
     }
     double part = 0.0;
     for (int e = t; e < D; e += NT) {
-      const double x = f.X[(size_t)e * kmax + j];
+      const double x = X[e * PXK + j];
       part += x * x;
     }
     const double nrm = sqrt(wg_sum(part, red));
-    for (int e = t; e < D; e += NT) f.X[(size_t)e * kmax + j] /= nrm;
+    for (int e = t; e < D; e += NT) X[e * PXK + j] /= nrm;
     __syncthreads();
   }
   // ---- back-transform through the reflectors: X <- H_0 H_1 ... H_{D-3} X
@@ -317,27 +362,31 @@ __global__ __launch_bounds__(kFitThreads) void k_fit(const float* S_out_in, cons
     const double bk = beta[k];
     if (bk == 0.0) continue;
     const int L = D - k - 1;
+    for (int i = t; i < L; i += NT) vv[i] = f.hv[(size_t)(k + 1 + i) * D + k];
+    __syncthreads();
     for (int c0 = 0; c0 < keff; c0 += NT / 8) {
       const int cc = c0 + t / 8, sub = t % 8;
-      double s = 0.0;
+      double sacc = 0.0;
       if (cc < keff)
-        for (int i = sub; i < L; i += 8) s += A[(k + 1 + i) * PA + k] * f.X[(size_t)(k + 1 + i) * kmax + cc];
-      s += __shfl_xor(s, 1);
-      s += __shfl_xor(s, 2);
-      s += __shfl_xor(s, 4);
-      if (cc < keff && sub == 0) dots[cc] = bk * s;
+        for (int i = sub; i < L; i += 8) sacc += vv[i] * X[(k + 1 + i) * PXK + cc];
+      sacc += __shfl_xor(sacc, 1);
+      sacc += __shfl_xor(sacc, 2);
+      sacc += __shfl_xor(sacc, 4);
+      if (cc < keff && sub == 0) dots[cc] = bk * sacc;
     }
     __syncthreads();
     for (int idx = t; idx < L * keff; idx += NT) {
       const int i = idx / keff, cc = idx % keff;
-      f.X[(size_t)(k + 1 + i) * kmax + cc] -= dots[cc] * A[(k + 1 + i) * PA + k];
+      X[(k + 1 + i) * PXK + cc] -= dots[cc] * vv[i];
     }
     __syncthreads();
   }
   for (int idx = t; idx < D * keff; idx += NT) {
     const int e = idx / keff, cc = idx % keff;
-    Uh[(size_t)e * kmax + cc] = (float)f.X[(size_t)e * kmax + cc];
+    f.X[(size_t)e * kmax + cc] = X[e * PXK + cc];
+    Uh[(size_t)e * kmax + cc] = (float)X[e * PXK + cc];
   }
+  __syncthreads();
   // ---- Y = R U
   for (int idx = t; idx < m * keff; idx += NT) {
     const int i = idx / keff, cc = idx % keff;
@@ -348,16 +397,38 @@ __global__ __launch_bounds__(kFitThreads) void k_fit(const float* S_out_in, cons
   __syncthreads();
   // ---- normal equations in LDS (the eigen matrix is no longer needed)
   double* Xn = big;
-  for (int idx = t; idx < NX * NX; idx += NT) {
-    const int ra = idx / NX, cb = idx % NX;
-    double s = 0.0;
-    for (int i = 0; i < m; ++i) {
-      const double xa = ra < D ? f.S[(size_t)i * D + ra] : 1.0;
-      const double xb = cb < D ? f.S[(size_t)i * D + cb] : 1.0;
-      s += f.w[i] * xa * xb;
+  {
+    constexpr int NTB = (NX + 7) / 8;
+    for (int tile = t; tile < NTB * NTB; tile += NT) {
+      const int a0 = 8 * (tile / NTB), b0 = 8 * (tile % NTB);
+      double acc[8][8];
+#pragma unroll
+      for (int i = 0; i < 8; ++i)
+#pragma unroll
+        for (int j = 0; j < 8; ++j) acc[i][j] = 0.0;
+      for (int i = 0; i < m; ++i) {
+        const double wi = f.w[i];
+        const double* Si = f.S + (size_t)i * D;
+        double xa[8], xb[8];
+#pragma unroll
+        for (int u = 0; u < 8; ++u) {
+          const int a = a0 + u, b = b0 + u;
+          xa[u] = wi * (a < D ? Si[a] : (a == D ? 1.0 : 0.0));
+          xb[u] = b < D ? Si[b] : (b == D ? 1.0 : 0.0);
+        }
+#pragma unroll
+        for (int u = 0; u < 8; ++u)
+#pragma unroll
+          for (int v = 0; v < 8; ++v) acc[u][v] += xa[u] * xb[v];
+      }
+#pragma unroll
+      for (int u = 0; u < 8; ++u)
+#pragma unroll
+        for (int v = 0; v < 8; ++v) {
+          const int a = a0 + u, b = b0 + v;
+          if (a < NX && b < NX) Xn[a * PX + b] = acc[u][v] + ((a == b && a < D) ? lambda : 0.0);
+        }
     }
-    if (ra == cb && ra < D) s += lambda;
-    Xn[ra * PX + cb] = s;
   }
   for (int idx = t; idx < NX * keff; idx += NT) {
     const int ra = idx / keff, cc = idx % keff;

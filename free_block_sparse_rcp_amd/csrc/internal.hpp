@@ -25,11 +25,11 @@ struct Dims {
 
 // ---- workspace layout (byte offsets; one workspace serves every stage)
 struct PartitionWs {
-  size_t M, P, Phl, bvec, counts, totals, starts, partial, end;
+  size_t M, P, Phl, bvec, counts, totals, starts, partial, best, end;
 };
 struct RouteWs {
   size_t keysA, keysB, valsA, valsB, counts, totals, starts, qbar, sigma, sel, selcnt, blkkeys,
-      end;
+      chl, best, end;
 };
 struct ProbeWs {
   size_t opart, lsepart, fit, fit_per_head, end;
@@ -54,6 +54,15 @@ hipError_t launch_sort_pass_u32(const Dims& d, const int32_t* keys_in, int bits,
 hipError_t launch_sort_pass_u64(const Dims& d, const uint64_t* keys_in, uint64_t* keys_out,
                                 int shift, int bits, const int32_t* vals_in, int32_t* vals_out,
                                 int32_t* counts, int32_t* totals, int32_t* starts, hipStream_t st);
+
+// row x centroid arg-selection on MFMA (bf16 rows): mode 0 argmin of
+// b - 2 x.P, mode 1 argmax of tau x.P over non-empty groups
+hipError_t launch_rowvec_mfma(const Dims& d, int mode, const void* X, const uint16_t* Phl,
+                              const float* bvec, const float* scale, const int32_t* group_off,
+                              unsigned long long* best, float* dbg, hipStream_t st);
+hipError_t launch_best_to_label(const Dims& d, const unsigned long long* best, bool descending,
+                                int32_t* label, float* value, hipStream_t st);
+hipError_t launch_split_hilo(const float* src, size_t rows, int D, uint16_t* dst, hipStream_t st);
 
 // fills by kernel (no memset nodes, so callers may capture the stream)
 hipError_t launch_fill_i32(int32_t* p, size_t n, int32_t v, hipStream_t st);

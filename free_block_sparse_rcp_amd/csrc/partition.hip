@@ -61,7 +61,8 @@ __global__ void k_centroid_init(const void* Kv, const int32_t* init_idx, int N, 
 }
 
 // P_g = M kbar_g (fp64 accumulate), b_g = kbar_g^T M kbar_g. Stores P in fp32
-// and as a bf16 hi/lo pair. grid (G, H), block D.
+// and as a bf16 pair P ~ hi + lo (rows [H][G][2][D]), so that a bf16 MFMA with
+// exact bf16 keys recovers the product to ~2^-18 relative. grid (G, H), block D.
 template <int D>
 __global__ void k_centroid_prep(const double* M, const float* kbar, int G, float* P,
                                 uint16_t* Phl, float* bvec) {
@@ -78,8 +79,9 @@ __global__ void k_centroid_prep(const double* M, const float* kbar, int G, float
   P[o] = (float)p;
   const uint16_t hi = f32_to_bf16((float)p);
   const uint16_t lo = f32_to_bf16((float)(p - (double)bf16_to_f32(hi)));
-  Phl[2 * o] = hi;
-  Phl[2 * o + 1] = lo;
+  uint16_t* ph = Phl + ((size_t)h * G + g) * 2 * D;
+  ph[e] = hi;
+  ph[D + e] = lo;
   const double bsum = block_sum_f64<D>(kb[e] * p, red);
   if (e == 0) bvec[(size_t)h * G + g] = (float)bsum;
 }
@@ -195,6 +197,216 @@ __global__ __launch_bounds__(256) void k_rowvec_argsel(const void* Xv, const flo
     best_idx[(size_t)h * N + r0 + t] = bg;
     if (best_val) best_val[(size_t)h * N + r0 + t] = bv;
   }
+}
+
+// ------------------------------------------------ row x centroid argselect, MFMA
+// Same scores as k_rowvec_argsel for bf16 rows, on v_mfma_f32_32x32x16_bf16:
+// the centroid-side vectors are split P = hi + lo (bf16) and both halves are
+// multiplied by the exact bf16 rows with fp32 accumulation. The product is
+// formed transposed (groups x keys) so that each lane holds one key and 16
+// groups. Each workgroup covers 256 groups (8 waves x 32, operands held in
+// registers) for a chunk of 512 keys streamed through padded LDS tiles; the
+// per-key winner over its groups is merged into best[h][key] with a 64-bit
+// atomicMin on (orderable score << 32 | g), which is order independent, so
+// results are deterministic and ties go to the lowest g.
+//   MODE 0 (assign): score = b_g - 2 k.P_g, minimised.
+//   MODE 1 (coords): score = tau q.kbar_g over non-empty groups, maximised.
+constexpr int kRvWaves = 8;
+constexpr int kRvKeys = 2048;
+constexpr int kRvTile = 64;
+
+template <int D, int MODE>
+__global__ __launch_bounds__(kRvWaves * 64) void k_rowvec_mfma(
+    const uint16_t* X, const uint16_t* Phl, const float* bvec, const float* scale,
+    const int32_t* group_off, int N, int G, int nkc, unsigned long long* best, float* dbg) {
+  constexpr int NKK = D / 16;
+  constexpr int KP = 2 * D + 16;
+  constexpr int KCH = KP / 16;
+  constexpr int TILEB = kRvTile * KP;
+  constexpr int NINS = (TILEB + 1023) / 1024;
+  __shared__ __attribute__((aligned(1024))) char kt0[NINS * 1024];
+  __shared__ __attribute__((aligned(1024))) char kt1[NINS * 1024];
+  __shared__ unsigned long long red[kRvWaves][kRvTile];
+  const int h = blockIdx.y;
+  const int kc = blockIdx.x % nkc, gt = blockIdx.x / nkc;
+  const int t = threadIdx.x, w = t >> 6, lane = t & 63, hl = lane >> 5, ql = lane & 31;
+  const uint16_t* Xh = X + (size_t)h * N * D;
+  // A operands: 32 groups of this wave, rows of hi and lo
+  const int gA = gt * (32 * kRvWaves) + 32 * w + ql;
+  bf16x8 phi[NKK], plo[NKK];
+  {
+    const bool ok = gA < G;
+    const uint16_t* ph = Phl + ((size_t)h * G + (ok ? gA : 0)) * 2 * D;
+#pragma unroll
+    for (int kk = 0; kk < NKK; ++kk) {
+      phi[kk] = *reinterpret_cast<const bf16x8*>(ph + 16 * kk + 8 * hl);
+      plo[kk] = *reinterpret_cast<const bf16x8*>(ph + D + 16 * kk + 8 * hl);
+      if (!ok) {
+        phi[kk] = bf16x8{};
+        plo[kk] = bf16x8{};
+      }
+    }
+  }
+  // output rows of this lane: groups g(r) = base + 8(r/4) + 4 hl + r%4
+  const int gbase = gt * (32 * kRvWaves) + 32 * w + 4 * hl;
+  float bias[16];
+  uint32_t okmask = 0;
+#pragma unroll
+  for (int r = 0; r < 16; ++r) {
+    const int g = gbase + 8 * (r >> 2) + (r & 3);
+    bool ok = g < G;
+    if (MODE == 0) {
+      bias[r] = ok ? bvec[(size_t)h * G + g] : 0.f;
+    } else {
+      bias[r] = 0.f;
+      if (ok) ok = group_off[(size_t)h * (G + 1) + g + 1] > group_off[(size_t)h * (G + 1) + g];
+    }
+    okmask |= (ok ? 1u : 0u) << r;
+  }
+  const float tau = MODE == 1 ? scale[h] : 0.f;
+  const int k0 = kc * kRvKeys, k1 = min(N, k0 + kRvKeys);
+  const int ntile = (k1 - k0 + kRvTile - 1) / kRvTile;
+
+  auto issue = [&](int tile, char* dst) {
+#pragma unroll
+    for (int u0 = 0; u0 < NINS; u0 += kRvWaves) {
+      const int u = u0 + w;
+      const int q = 64 * u + lane;
+      if (u < NINS && q * 16 < TILEB) {
+        const int r = q / KCH, cc = q - r * KCH;
+        const int key = min(k0 + tile * kRvTile + r, N - 1);
+        const uint16_t* src = Xh + (size_t)key * D + (cc < D / 8 ? cc : 0) * 8;
+        __builtin_amdgcn_global_load_lds(src, (__attribute__((address_space(3))) void*)(dst + u * 1024),
+                                         16, 0, 0);
+      }
+    }
+  };
+  auto compute = [&](int tile, const char* __restrict__ buf) {
+    f32x16 acc[2];
+#pragma unroll
+    for (int hk = 0; hk < 2; ++hk)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) acc[hk][r] = 0.f;
+    const char* kb = buf + ql * KP + hl * 16;
+#pragma unroll
+    for (int kk = 0; kk < NKK; ++kk) {
+#pragma unroll
+      for (int hk = 0; hk < 2; ++hk) {
+        const bf16x8 kop = *reinterpret_cast<const bf16x8*>(kb + 32 * hk * KP + 32 * kk);
+        acc[hk] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(phi[kk], kop, acc[hk], 0, 0, 0);
+        acc[hk] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(plo[kk], kop, acc[hk], 0, 0, 0);
+      }
+    }
+#pragma unroll
+    for (int hk = 0; hk < 2; ++hk) {
+      const int key = k0 + tile * kRvTile + 32 * hk + ql;
+      const bool kvalid = key < k1;
+      unsigned long long bk = ~0ull;
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int g = gbase + 8 * (r >> 2) + (r & 3);
+        const bool ok = (okmask >> r) & 1u;
+        float sc;
+        if (MODE == 0) sc = bias[r] - 2.0f * acc[hk][r];
+        else sc = ok ? tau * acc[hk][r] : -__builtin_inff();
+        if (dbg != nullptr && kvalid && g < G) dbg[((size_t)h * N + key) * G + g] = sc;
+        if (ok) {
+          const uint32_t ob = MODE == 0 ? float_order_bits(sc) : float_desc_bits(sc);
+          const unsigned long long pk = (static_cast<unsigned long long>(ob) << 32) | (uint32_t)g;
+          bk = pk < bk ? pk : bk;
+        }
+      }
+      const unsigned long long other = __shfl_xor(bk, 32);
+      bk = other < bk ? other : bk;
+      if (hl == 0) red[w][32 * hk + ql] = bk;
+    }
+    lds_barrier();
+    if (w == 0) {
+      const int key = k0 + tile * kRvTile + lane;
+      unsigned long long m = red[0][lane];
+#pragma unroll
+      for (int ww = 1; ww < kRvWaves; ++ww) m = red[ww][lane] < m ? red[ww][lane] : m;
+      if (key < k1 && m != ~0ull) atomicMin(&best[(size_t)h * N + key], m);
+    }
+  };
+
+  if (ntile > 0) issue(0, kt0);
+  __builtin_amdgcn_s_waitcnt(0);
+  __syncthreads();
+  for (int tile = 0; tile < ntile; tile += 2) {
+    if (tile + 1 < ntile) issue(tile + 1, kt1);
+    compute(tile, kt0);
+    __builtin_amdgcn_s_waitcnt(0);
+    __syncthreads();
+    if (tile + 1 >= ntile) break;
+    if (tile + 2 < ntile) issue(tile + 2, kt0);
+    compute(tile + 1, kt1);
+    __builtin_amdgcn_s_waitcnt(0);
+    __syncthreads();
+  }
+}
+
+__global__ void k_fill_u64(unsigned long long* p, size_t n, unsigned long long v) {
+  const size_t i = (size_t)blockIdx.x * 256 + threadIdx.x;
+  if (i < n) p[i] = v;
+}
+
+// best -> label (and, for coordinates, the winning value as fp32).
+__global__ void k_best_to_label(const unsigned long long* best, size_t n, int descending,
+                                int32_t* label, float* value) {
+  const size_t i = (size_t)blockIdx.x * 256 + threadIdx.x;
+  if (i >= n) return;
+  const unsigned long long b = best[i];
+  label[i] = b == ~0ull ? 0 : (int32_t)(b & 0xffffffffu);
+  if (value != nullptr) {
+    uint32_t ob = (uint32_t)(b >> 32);
+    if (descending) ob = ~ob;
+    const uint32_t bits = (ob & 0x80000000u) ? (ob & 0x7fffffffu) : ~ob;
+    value[i] = __uint_as_float(bits);
+  }
+}
+
+// hi/lo bf16 split of fp32 rows: dst[row][0][:] = hi, dst[row][1][:] = lo.
+__global__ void k_split_hilo(const float* src, size_t rows, int D, uint16_t* dst) {
+  const size_t i = (size_t)blockIdx.x * 256 + threadIdx.x;
+  if (i >= rows * D) return;
+  const size_t r = i / D, e = i % D;
+  const float x = src[i];
+  const uint16_t hi = f32_to_bf16(x);
+  dst[r * 2 * D + e] = hi;
+  dst[r * 2 * D + D + e] = f32_to_bf16(x - bf16_to_f32(hi));
+}
+
+hipError_t launch_rowvec_mfma(const Dims& d, int mode, const void* X, const uint16_t* Phl,
+                              const float* bvec, const float* scale, const int32_t* group_off,
+                              unsigned long long* best, float* dbg, hipStream_t st) {
+  const size_t n = (size_t)d.H * d.N;
+  k_fill_u64<<<(unsigned)((n + 255) / 256), 256, 0, st>>>(best, n, ~0ull);
+  const int nkc = (d.N + kRvKeys - 1) / kRvKeys;
+  const int ngt = (d.G + 32 * kRvWaves - 1) / (32 * kRvWaves);
+  const dim3 grid(nkc * ngt, d.H);
+  const uint16_t* Xb = static_cast<const uint16_t*>(X);
+  if (d.D == 128) {
+    if (mode == 0) k_rowvec_mfma<128, 0><<<grid, kRvWaves * 64, 0, st>>>(Xb, Phl, bvec, scale, group_off, d.N, d.G, nkc, best, dbg);
+    else k_rowvec_mfma<128, 1><<<grid, kRvWaves * 64, 0, st>>>(Xb, Phl, bvec, scale, group_off, d.N, d.G, nkc, best, dbg);
+  } else {
+    if (mode == 0) k_rowvec_mfma<64, 0><<<grid, kRvWaves * 64, 0, st>>>(Xb, Phl, bvec, scale, group_off, d.N, d.G, nkc, best, dbg);
+    else k_rowvec_mfma<64, 1><<<grid, kRvWaves * 64, 0, st>>>(Xb, Phl, bvec, scale, group_off, d.N, d.G, nkc, best, dbg);
+  }
+  return hipGetLastError();
+}
+
+hipError_t launch_best_to_label(const Dims& d, const unsigned long long* best, bool descending,
+                                int32_t* label, float* value, hipStream_t st) {
+  const size_t n = (size_t)d.H * d.N;
+  k_best_to_label<<<(unsigned)((n + 255) / 256), 256, 0, st>>>(best, n, descending ? 1 : 0, label, value);
+  return hipGetLastError();
+}
+
+hipError_t launch_split_hilo(const float* src, size_t rows, int D, uint16_t* dst, hipStream_t st) {
+  const size_t n = rows * D;
+  k_split_hilo<<<(unsigned)((n + 255) / 256), 256, 0, st>>>(src, rows, D, dst);
+  return hipGetLastError();
 }
 
 // ------------------------------------------------ stable counting-sort pass
@@ -314,23 +526,22 @@ __global__ void k_seg_partial(const void* Kv, const int32_t* key_perm, const int
     slab[e] = labels[(size_t)h * N + key];
   }
   __syncthreads();
+  // all 64 row loads are issued before any is consumed (one memory round trip)
+  float vals[64];
+#pragma unroll
+  for (int u = 0; u < 64; ++u) vals[u] = u < n ? E::ld(K, (size_t)skey[u] * D + e) : 0.f;
   int cur = -1;
   float acc = 0.f;
-  for (int pp = 0; pp < n; pp += 8) {
-    float vals[8];
 #pragma unroll
-    for (int u = 0; u < 8; ++u) vals[u] = (pp + u < n) ? E::ld(K, (size_t)skey[pp + u] * D + e) : 0.f;
-#pragma unroll
-    for (int u = 0; u < 8; ++u) {
-      if (pp + u < n) {
-        const int g = slab[pp + u];
-        if (g != cur) {
-          if (cur >= 0) part[(size_t)(cur + c) * D + e] = acc;
-          cur = g;
-          acc = 0.f;
-        }
-        acc += vals[u];
+  for (int u = 0; u < 64; ++u) {
+    if (u < n) {
+      const int g = slab[u];
+      if (g != cur) {
+        if (cur >= 0) part[(size_t)(cur + c) * D + e] = acc;
+        cur = g;
+        acc = 0.f;
       }
+      acc += vals[u];
     }
   }
   if (cur >= 0) part[(size_t)(cur + c) * D + e] = acc;
@@ -453,6 +664,7 @@ static hipError_t partition_impl(const Dims& d, const void* Q, const void* K, co
   int32_t* totals = reinterpret_cast<int32_t*>(ws + L.totals);
   int32_t* starts = reinterpret_cast<int32_t*>(ws + L.starts);
   float* partial = reinterpret_cast<float*>(ws + L.partial);
+  unsigned long long* best = reinterpret_cast<unsigned long long*>(ws + L.best);
   const dim3 rows64((d.N + 63) / 64, d.H);
   const dim3 per_group(d.G, d.H);
 
@@ -477,9 +689,15 @@ static hipError_t partition_impl(const Dims& d, const void* Q, const void* K, co
       k_centroid_prep<D><<<per_group, D, 0, st>>>(M, kbar, d.G, P, Phl, bvec);
       SPR_CHECK_LAUNCH();
       float* dbg_it = (it == d.T - 1) ? dbg : nullptr;
-      k_rowvec_argsel<BF16, D, 0><<<rows64, 256, 0, st>>>(K, P, bvec, nullptr, nullptr, d.N, d.G,
-                                                           key_label, nullptr, dbg_it);
-      SPR_CHECK_LAUNCH();
+      if (BF16) {
+        hipError_t e = launch_rowvec_mfma(d, 0, K, Phl, bvec, nullptr, nullptr, best, dbg_it, st);
+        if (e == hipSuccess) e = launch_best_to_label(d, best, false, key_label, nullptr, st);
+        if (e != hipSuccess) return e;
+      } else {
+        k_rowvec_argsel<BF16, D, 0><<<rows64, 256, 0, st>>>(K, P, bvec, nullptr, nullptr, d.N, d.G,
+                                                             key_label, nullptr, dbg_it);
+        SPR_CHECK_LAUNCH();
+      }
       hipError_t e = regroup();
       if (e != hipSuccess) return e;
     }

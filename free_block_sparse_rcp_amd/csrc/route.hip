@@ -237,7 +237,17 @@ hipError_t launch_route(const Dims& d, const void* Q, const float* scale, const 
     // g1 -> valsA, v -> valsB (reinterpreted) before the sort reuses them
     int32_t* g1 = valsA;
     float* v = reinterpret_cast<float*>(valsB);
-    hipError_t e = launch_coords_valu(d, Q, kbar, scale, group_off, g1, v, dbg_coords, st);
+    hipError_t e;
+    if (d.bf16) {
+      uint16_t* chl = reinterpret_cast<uint16_t*>(ws + L.chl);
+      unsigned long long* best = reinterpret_cast<unsigned long long*>(ws + L.best);
+      e = launch_split_hilo(kbar, (size_t)d.H * d.G, d.D, chl, st);
+      if (e == hipSuccess)
+        e = launch_rowvec_mfma(d, 1, Q, chl, nullptr, scale, group_off, best, dbg_coords, st);
+      if (e == hipSuccess) e = launch_best_to_label(d, best, true, g1, v, st);
+    } else {
+      e = launch_coords_valu(d, Q, kbar, scale, group_off, g1, v, dbg_coords, st);
+    }
     if (e != hipSuccess) return e;
     k_make_qkeys<<<rows256, 256, 0, st>>>(g1, v, d.N, keysA, dbg_dom, dbg_domval);
     SPR_CHECK_LAUNCH();
