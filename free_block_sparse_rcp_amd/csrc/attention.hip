@@ -49,9 +49,20 @@ struct Item {
 
 template <int MODE>
 __device__ __forceinline__ Item decode_item(const AttnArgs& a, int nqb) {
+  Item it;
+  if (MODE != ATTN_PROBE && a.xcd_chunk > 0) {
+    // dispatch w runs on XCD w % 8; XCD x takes blocks [x c, x c + c) of every
+    // head, heads in order, so all XCDs stream the same head's keys together
+    const int c = a.xcd_chunk;
+    const int x = blockIdx.x & 7, i = blockIdx.x >> 3;
+    it.h = i / c;
+    it.b = x * c + i % c;
+    it.sp = 0;
+    if (it.b >= nqb) it.h = a.H;  // padding dispatch: no work
+    return it;
+  }
   const int total = (MODE == ATTN_PROBE ? nqb * a.nsplit : nqb) * a.H;
   const int L = xcd_remap(blockIdx.x, total);
-  Item it;
   if (MODE == ATTN_PROBE) {
     const int per = nqb * a.nsplit;
     it.h = L / per;
@@ -263,6 +274,7 @@ void k_attn_mfma(AttnArgs a) {
 
   const int nqb = MODE == ATTN_PROBE ? (a.m + BQ - 1) / BQ : a.nb;
   const Item it = decode_item<MODE>(a, nqb);
+  if (it.h >= a.H) return;
   const int t = threadIdx.x;
   const int lane = t & 63, w = t >> 6;
   const int hl = lane >> 5;       // which half of the wave
@@ -534,10 +546,16 @@ __global__ void k_probe_merge(const float* opart, const float* lsepart, int m, i
 
 hipError_t launch_attention(const Dims& d, AttnMode mode, const AttnArgs& a, hipStream_t st) {
   const int nqb = mode == ATTN_PROBE ? (d.m + d.BQ - 1) / d.BQ : (d.N + d.BQ - 1) / d.BQ;
-  const int items = (mode == ATTN_PROBE ? nqb * d.nsplit : nqb) * d.H;
+  int items = (mode == ATTN_PROBE ? nqb * d.nsplit : nqb) * d.H;
   AttnArgs aa = a;
   aa.nb = mode == ATTN_PROBE ? a.nb : nqb;
+  aa.xcd_chunk = 0;
   if (d.bf16) {
+    if (mode != ATTN_PROBE) {
+      // head-synchronous XCD mapping (padding dispatches exit at once)
+      aa.xcd_chunk = (nqb + 7) / 8;
+      items = 8 * aa.xcd_chunk * d.H;
+    }
 #define SPR_MFMA(DD, BB)                                                                    \
   do {                                                                                      \
     if (mode == ATTN_SPARSE) k_attn_mfma<DD, BB, ATTN_SPARSE><<<items, BB * 2, 0, st>>>(aa); \

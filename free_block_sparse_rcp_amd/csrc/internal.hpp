@@ -91,6 +91,7 @@ struct AttnArgs {
   float* lse;                  // sparse / dense (may be null for dense)
   float* opart;                // probe: [H, nsplit, m, D] fp32
   float* lsepart;              // probe: [H, nsplit, m]
+  int xcd_chunk;               // > 0: head-synchronous XCD mapping with this many blocks per XCD
 };
 hipError_t launch_attention(const Dims& d, AttnMode mode, const AttnArgs& a, hipStream_t st);
 hipError_t launch_probe_merge(const Dims& d, const float* opart, const float* lsepart,

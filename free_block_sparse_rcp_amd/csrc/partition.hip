@@ -226,10 +226,11 @@ __global__ __launch_bounds__(kRvWaves * 64) void k_rowvec_mfma(
   constexpr int NINS = (TILEB + 1023) / 1024;
   __shared__ __attribute__((aligned(1024))) char kt0[NINS * 1024];
   __shared__ __attribute__((aligned(1024))) char kt1[NINS * 1024];
-  __shared__ unsigned long long red[kRvWaves][kRvTile];
+  __shared__ unsigned long long red[2][kRvWaves][kRvTile];
   const int h = blockIdx.y;
   const int kc = blockIdx.x % nkc, gt = blockIdx.x / nkc;
-  const int t = threadIdx.x, w = t >> 6, lane = t & 63, hl = lane >> 5, ql = lane & 31;
+  const int t = threadIdx.x, lane = t & 63, hl = lane >> 5, ql = lane & 31;
+  const int w = __builtin_amdgcn_readfirstlane(t >> 6);
   const uint16_t* Xh = X + (size_t)h * N * D;
   // A operands: 32 groups of this wave, rows of hi and lo
   const int gA = gt * (32 * kRvWaves) + 32 * w + ql;
@@ -247,23 +248,23 @@ __global__ __launch_bounds__(kRvWaves * 64) void k_rowvec_mfma(
       }
     }
   }
-  // output rows of this lane: groups g(r) = base + 8(r/4) + 4 hl + r%4
+  // output rows of this lane: groups g(r) = base + 8(r/4) + 4 hl + r%4, increasing in r.
+  // Scores are minimised in the form  sgn * acc + bias  (MODE 0: -2 k.P_g + b_g;
+  // MODE 1: -tau q.kbar_g); slots that must never win get bias = +inf.
   const int gbase = gt * (32 * kRvWaves) + 32 * w + 4 * hl;
   float bias[16];
-  uint32_t okmask = 0;
 #pragma unroll
   for (int r = 0; r < 16; ++r) {
     const int g = gbase + 8 * (r >> 2) + (r & 3);
     bool ok = g < G;
     if (MODE == 0) {
-      bias[r] = ok ? bvec[(size_t)h * G + g] : 0.f;
+      bias[r] = ok ? bvec[(size_t)h * G + g] : __builtin_inff();
     } else {
-      bias[r] = 0.f;
       if (ok) ok = group_off[(size_t)h * (G + 1) + g + 1] > group_off[(size_t)h * (G + 1) + g];
+      bias[r] = ok ? 0.f : __builtin_inff();
     }
-    okmask |= (ok ? 1u : 0u) << r;
   }
-  const float tau = MODE == 1 ? scale[h] : 0.f;
+  const float sgn = MODE == 0 ? -2.0f : -scale[h];
   const int k0 = kc * kRvKeys, k1 = min(N, k0 + kRvKeys);
   const int ntile = (k1 - k0 + kRvTile - 1) / kRvTile;
 
@@ -281,6 +282,7 @@ __global__ __launch_bounds__(kRvWaves * 64) void k_rowvec_mfma(
       }
     }
   };
+  // scores of one tile; the per-key winner of this wave goes to red[tile & 1][w]
   auto compute = [&](int tile, const char* __restrict__ buf) {
     f32x16 acc[2];
 #pragma unroll
@@ -300,32 +302,42 @@ __global__ __launch_bounds__(kRvWaves * 64) void k_rowvec_mfma(
 #pragma unroll
     for (int hk = 0; hk < 2; ++hk) {
       const int key = k0 + tile * kRvTile + 32 * hk + ql;
-      const bool kvalid = key < k1;
-      unsigned long long bk = ~0ull;
+      float bs = __builtin_inff();
+      int br = -1;
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
-        const int g = gbase + 8 * (r >> 2) + (r & 3);
-        const bool ok = (okmask >> r) & 1u;
-        float sc;
-        if (MODE == 0) sc = bias[r] - 2.0f * acc[hk][r];
-        else sc = ok ? tau * acc[hk][r] : -__builtin_inff();
-        if (dbg != nullptr && kvalid && g < G) dbg[((size_t)h * N + key) * G + g] = sc;
-        if (ok) {
-          const uint32_t ob = MODE == 0 ? float_order_bits(sc) : float_desc_bits(sc);
-          const unsigned long long pk = (static_cast<unsigned long long>(ob) << 32) | (uint32_t)g;
-          bk = pk < bk ? pk : bk;
+        const float sc = fmaf(sgn, acc[hk][r], bias[r]);
+        if (sc < bs) {
+          bs = sc;
+          br = r;
         }
+      }
+      if (dbg != nullptr && key < k1) {
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int g = gbase + 8 * (r >> 2) + (r & 3);
+          const float sc = fmaf(sgn, acc[hk][r], bias[r]);
+          if (g < G) dbg[((size_t)h * N + key) * G + g] = MODE == 0 ? sc : -sc;
+        }
+      }
+      unsigned long long bk = ~0ull;
+      if (br >= 0) {
+        const int g = gbase + 8 * (br >> 2) + (br & 3);
+        const uint32_t ob = MODE == 0 ? float_order_bits(bs) : float_desc_bits(-bs);
+        bk = (static_cast<unsigned long long>(ob) << 32) | (uint32_t)g;
       }
       const unsigned long long other = __shfl_xor(bk, 32);
       bk = other < bk ? other : bk;
-      if (hl == 0) red[w][32 * hk + ql] = bk;
+      if (hl == 0) red[tile & 1][w][32 * hk + ql] = bk;
     }
-    lds_barrier();
-    if (w == 0) {
+  };
+  // after the barrier that ends a tile, one wave folds that tile's per-wave winners
+  auto merge = [&](int tile) {
+    if (w == (tile & (kRvWaves - 1))) {
       const int key = k0 + tile * kRvTile + lane;
-      unsigned long long m = red[0][lane];
+      unsigned long long m = red[tile & 1][0][lane];
 #pragma unroll
-      for (int ww = 1; ww < kRvWaves; ++ww) m = red[ww][lane] < m ? red[ww][lane] : m;
+      for (int ww = 1; ww < kRvWaves; ++ww) m = red[tile & 1][ww][lane] < m ? red[tile & 1][ww][lane] : m;
       if (key < k1 && m != ~0ull) atomicMin(&best[(size_t)h * N + key], m);
     }
   };
@@ -338,11 +350,13 @@ __global__ __launch_bounds__(kRvWaves * 64) void k_rowvec_mfma(
     compute(tile, kt0);
     __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
+    merge(tile);
     if (tile + 1 >= ntile) break;
     if (tile + 2 < ntile) issue(tile + 2, kt0);
     compute(tile + 1, kt1);
     __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
+    merge(tile + 1);
   }
 }
 

@@ -1,0 +1,272 @@
+"""GPU parity at the full workload sizes, in the launch configuration the
+benchmark times, checked on heads {0, H/2, H-1}.
+
+The full call is run twice: as the benchmark runs it (no debug dumps) and with
+every debug dump enabled; the two must agree bit for bit, so the dumps vouch
+for the benchmark's run. Then, per checked head:
+  * index stages exactly: labels are the lowest-index argmin of the dumped
+    assignment scores over all N keys, groups and Kp/Vp follow from the labels,
+    dominant groups / query order / routes follow from the dumped coordinates
+    and block scores, and the pair count follows from the routes;
+  * value stages against fp64 on samples the oracle computes one by one:
+    assignment scores (from the previous iteration's centroids, taken from a
+    run with one iteration fewer), centroids, coordinates and block scores,
+    sparse attention rows of the first, the ragged last and random blocks, all
+    probe rows, the fit on the GPU's probe inputs and the applied correction.
+"""
+import math
+from dataclasses import replace
+
+import numpy as np
+import pytest
+import torch
+
+from oracle import sparsepr_oracle as orc
+from free_block_sparse_rcp_amd import binding, configs
+
+from _gpu_util import bf16_round, rel_l2, run_pipeline
+
+pytestmark = pytest.mark.gpu
+
+ATTN_TOL = 2e-2      # bf16 operands and bf16 probabilities, fp32 accumulation
+SCORE_TOL = 1e-5     # fp32 scores from exact bf16 products (hi/lo split centroids)
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _need_gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    binding.load()
+
+
+def _sweep_point(rho, m, mode, name):
+    wl = configs.SWEEP
+    return replace(wl, name=name, params=replace(wl.params, density=rho, n_probes=m,
+                                                 partition_mode=mode))
+
+
+CASES = {
+    "wan": configs.WAN,
+    "hunyuan": configs.HUNYUAN,
+    "cosmos": configs.COSMOS,
+    "sweep": configs.SWEEP,
+    "sweep_rho15_m32_random": _sweep_point(0.15, 32, 1, "sweep_rho15_m32_random"),
+    "sweep_rho30_m256": _sweep_point(0.30, 256, 0, "sweep_rho30_m256"),
+}
+
+
+class FullRun:
+    """The benchmark-configuration run, its debug twin and (for k-means) the
+    run with one iteration fewer; host copies are made per head on demand."""
+
+    def __init__(self, name):
+        wl = CASES[name]
+        print(f"[gpu-full] {name}: generating inputs", flush=True)
+        self.wl = wl
+        self.p = wl.params
+        self.inp = wl.make_inputs()
+        print(f"[gpu-full] {name}: bench-configuration run", flush=True)
+        self.bench = run_pipeline(wl, dbg=False, inp=self.inp)
+        print(f"[gpu-full] {name}: debug run", flush=True)
+        self.dbg = run_pipeline(wl, dbg=True, inp=self.inp)
+        self.prev = None
+        if self.p.partition_mode == 0 and self.p.kmeans_iters > 1:
+            print(f"[gpu-full] {name}: run with T-1 k-means iterations", flush=True)
+            pp = replace(self.p, kmeans_iters=self.p.kmeans_iters - 1)
+            r = run_pipeline(wl, dbg=False, inp=self.inp, p=pp)
+            self.prev = r.b.key_centroid.detach().cpu().numpy()
+            del r
+        torch.cuda.synchronize()
+        H = self.p.heads
+        self.heads = sorted({0, H // 2, H - 1})
+
+    def get(self, name, h, which="dbg"):
+        r = self.dbg if which == "dbg" else self.bench
+        t = getattr(r.b, name) if hasattr(r.b, name) else r.dbg[name]
+        t = t[h]
+        if t.dtype == torch.bfloat16:
+            t = t.float()
+        return t.detach().cpu().numpy()
+
+
+@pytest.fixture(scope="module", params=list(CASES))
+def fr(request):
+    """One case at a time (a module-scoped parametrized fixture groups the
+    tests by case), freed before the next case is built."""
+    run = FullRun(request.param)
+    yield run
+    del run
+    torch.cuda.synchronize()
+    torch.cuda.empty_cache()
+
+
+def block_keys(bp, bg, key_perm, group_off, b):
+    gs = bg[bp[b]:bp[b + 1]]
+    return np.concatenate([key_perm[group_off[g]:group_off[g + 1]] for g in gs]) if len(gs) else \
+        np.zeros(0, np.int64)
+
+
+def test_debug_run_matches_bench_run(fr):
+    name = fr.wl.name
+    a, b = fr.bench.b, fr.dbg.b
+    for n in ("key_label", "key_perm", "group_off", "key_centroid", "Kp", "Vp", "query_perm",
+              "block_ptr", "executed_pairs", "S", "lse", "O_probe", "U", "Theta", "rank_eff", "O"):
+        assert torch.equal(getattr(a, n), getattr(b, n)), n
+    ptr = a.block_ptr.cpu().numpy()
+    ga, gb = a.block_groups.cpu().numpy(), b.block_groups.cpu().numpy()
+    for h in range(fr.p.heads):
+        assert np.array_equal(ga[h][:ptr[h][-1]], gb[h][:ptr[h][-1]])
+
+
+def test_partition_full(fr):
+    name = fr.wl.name
+    p = fr.p
+    rng = np.random.default_rng(21)
+    for h in fr.heads:
+        print(f"[gpu-full] {name} partition head {h}", flush=True)
+        lab = fr.get("key_label", h)
+        if p.partition_mode == 0:
+            scores = fr.get("assign", h)
+            assert np.array_equal(orc.argmin_lowest(scores), lab)
+        else:
+            assert np.array_equal(orc.random_block_labels(fr.inp.rand_key_perm, p.n_groups), lab)
+        kp, goff, sizes = orc.group_members(lab, p.n_groups)
+        assert np.array_equal(kp, fr.get("key_perm", h))
+        assert np.array_equal(goff, fr.get("group_off", h))
+        # paired K/V groups, bit-exact, compared on the device
+        idx = torch.from_numpy(kp).to(fr.dbg.K.device)
+        assert torch.equal(fr.dbg.b.Kp[h], fr.dbg.K[h].index_select(0, idx))
+        assert torch.equal(fr.dbg.b.Vp[h], fr.dbg.V[h].index_select(0, idx))
+        K = fr.inp.K[h].astype(np.float64)
+        kbar, _ = orc.key_centroids(K, lab, p.n_groups)
+        ne = sizes > 0
+        assert rel_l2(fr.get("key_centroid", h)[ne], kbar[ne]) < SCORE_TOL
+        if fr.prev is not None:
+            # dumped scores of the last iteration against fp64 from the previous centroids
+            keys = np.sort(rng.choice(p.n_tokens, 4096, replace=False))
+            tau = float(fr.inp.scale[h])
+            Qs = fr.inp.Q[h][fr.inp.sample_idx].astype(np.float64)
+            R = tau * K[keys] @ Qs.T
+            C = tau * fr.prev[h].astype(np.float64) @ Qs.T
+            ref = orc.squared_distances(R, C) - (R * R).sum(1)[:, None]
+            scale_ref = (C * C).sum(1)[None, :] + 2 * np.abs(R @ C.T)
+            assert np.all(np.abs(scores[keys] - ref) <= SCORE_TOL * scale_ref + 1e-6)
+
+
+def test_route_full(fr):
+    name = fr.wl.name
+    p = fr.p
+    rng = np.random.default_rng(22)
+    for h in fr.heads:
+        print(f"[gpu-full] {name} route head {h}", flush=True)
+        goff = fr.get("group_off", h)
+        sizes = np.diff(goff)
+        qperm = fr.get("query_perm", h)
+        sigma = fr.get("sigma", h)
+        if p.partition_mode == 0:
+            coords = fr.get("coords", h)
+            g1, v = orc.dominant_groups(coords, sizes)
+            assert np.array_equal(g1, fr.get("dom", h))
+            assert np.array_equal(v.astype(np.float32), fr.get("domval", h))
+            assert np.array_equal(orc.query_order(fr.get("dom", h), fr.get("domval", h)), qperm)
+            # coordinate values on sampled queries
+            Q = fr.inp.Q[h].astype(np.float64)
+            tau = float(fr.inp.scale[h])
+            kb = fr.get("key_centroid", h).astype(np.float64)
+            ne = sizes > 0
+            rows = np.sort(rng.choice(p.n_tokens, 4096, replace=False))
+            C = orc.query_coordinates(Q[rows], kb, tau)
+            assert rel_l2(coords[rows][:, ne], C[:, ne]) < SCORE_TOL
+            assert np.all(np.isneginf(coords[rows][:, ~ne]))
+        else:
+            assert np.array_equal(qperm, fr.inp.rand_query_perm)
+            Q = fr.inp.Q[h].astype(np.float64)
+            tau = float(fr.inp.scale[h])
+            kb = fr.get("key_centroid", h).astype(np.float64)
+            ne = sizes > 0
+        # block scores on sampled blocks (first, last, random)
+        nb = p.n_blocks
+        blks = np.unique(np.concatenate([[0, nb - 1], rng.choice(nb, min(nb, 48), replace=False)]))
+        for b in blks:
+            qb = qperm[b * p.q_block:(b + 1) * p.q_block]
+            ref = orc.query_coordinates(Q[qb], kb, tau).mean(axis=0)
+            assert rel_l2(sigma[b][ne], ref[ne]) < SCORE_TOL, f"block {b}"
+        bp, bg = orc.route(sigma, sizes, p.key_budget)
+        assert np.array_equal(bp, fr.get("block_ptr", h))
+        assert np.array_equal(bg, fr.get("block_groups", h)[:bp[-1]])
+        # pair accounting (exact): sum over blocks of rows x routed keys, plus m N
+        rows_b = np.minimum(p.q_block, p.n_tokens - np.arange(nb) * p.q_block)
+        keys_b = np.array([sizes[bg[bp[b]:bp[b + 1]]].sum() for b in range(nb)], np.int64)
+        E = int((rows_b * keys_b).sum()) + p.n_probes * p.n_tokens
+        assert int(fr.get("executed_pairs", h)) == E
+
+
+def test_attention_rows_full(fr):
+    name = fr.wl.name
+    p = fr.p
+    rng = np.random.default_rng(23)
+    nb = p.n_blocks
+    for h in fr.heads:
+        print(f"[gpu-full] {name} attention head {h}", flush=True)
+        qperm = fr.get("query_perm", h)
+        kp = fr.get("key_perm", h).astype(np.int64)
+        goff = fr.get("group_off", h).astype(np.int64)
+        bp = fr.get("block_ptr", h).astype(np.int64)
+        bg = fr.get("block_groups", h).astype(np.int64)
+        S = fr.get("S", h)
+        lse = fr.get("lse", h)
+        Q, K, V = (x[h] for x in (fr.inp.Q, fr.inp.K, fr.inp.V))
+        tau = float(fr.inp.scale[h])
+        got, ref, got_l, ref_l = [], [], [], []
+        for b in np.unique(np.concatenate([[0, nb - 1], rng.choice(nb, 6, replace=False)])):
+            pos = np.arange(b * p.q_block, min(p.n_tokens, (b + 1) * p.q_block))
+            if b not in (0, nb - 1):
+                pos = np.sort(rng.choice(pos, min(len(pos), 32), replace=False))
+            keys = block_keys(bp, bg, kp, goff, b)
+            o, l = orc.softmax_attention(Q[qperm[pos]], K[keys], V[keys], tau)
+            got.append(S[pos]); ref.append(o); got_l.append(lse[pos]); ref_l.append(l)
+        got, ref = np.concatenate(got), np.concatenate(ref)
+        assert rel_l2(got, ref) < ATTN_TOL
+        assert np.max(np.abs(np.concatenate(got_l) - np.concatenate(ref_l))) < ATTN_TOL
+
+
+def test_probes_fit_apply_full(fr):
+    name = fr.wl.name
+    p = fr.p
+    N = p.n_tokens
+    rng = np.random.default_rng(24)
+    for h in fr.heads:
+        print(f"[gpu-full] {name} probes/fit/apply head {h}", flush=True)
+        qperm = fr.get("query_perm", h)
+        Q, K, V = (x[h] for x in (fr.inp.Q, fr.inp.K, fr.inp.V))
+        tau = float(fr.inp.scale[h])
+        pos = orc.probe_positions(N, p.n_probes)
+        ptok = qperm[pos]
+        Op = fr.get("O_probe", h)[:p.n_probes]
+        ref, _ = orc.dense_attention(Q, K, V, tau, rows=ptok)
+        assert rel_l2(Op, ref) < ATTN_TOL, "probe rows"
+        # fit on the GPU's probe inputs
+        S = fr.get("S", h)
+        Sp = S[pos].astype(np.float64)
+        Op64 = Op.astype(np.float64)
+        w = orc.probe_weights(Op64)
+        Rp = Op64 - Sp
+        U, ev = orc.residual_subspace(Rp, w, p.rank)
+        keff = int(fr.get("rank_eff", h))
+        assert keff == U.shape[1]
+        Ug = fr.get("U", h)[:, :keff].astype(np.float64)
+        Thg = fr.get("Theta", h)[:, :keff].astype(np.float64)
+        assert np.max(np.abs(Ug.T @ Ug - np.eye(keff))) < 1e-5
+        gap = (ev[keff - 1] - ev[keff]) / max(ev[0], 1e-300) if keff < len(ev) else 1.0
+        if gap > 1e-4:
+            assert np.max(np.abs(Ug @ Ug.T - U @ U.T)) < 1e-3
+        assert orc.normal_equation_residual(Sp, Rp @ Ug, w, p.ridge_lambda, Thg) < 1e-4
+        # apply on sampled rows (token order): s + U Theta^T [s; 1], probe rows exact
+        O = fr.get("O", h)
+        rows_q = np.sort(rng.choice(N, 4096, replace=False))
+        s_rows = S[rows_q].astype(np.float64)
+        expect = s_rows + orc.predicted_residual(s_rows, Ug, Thg)
+        is_probe = np.isin(rows_q, pos)
+        expect[is_probe] = Op64[np.searchsorted(pos, rows_q[is_probe])]
+        assert rel_l2(O[qperm[rows_q]], expect) < 5e-3
+        assert np.array_equal(O[ptok], bf16_round(Op))
