@@ -70,7 +70,7 @@ def load(path: Optional[str] = None) -> ctypes.CDLL:
     lib.sparsepr_route.argtypes = [pp] + [_c_p] * 13 + [_c_p, _c_sz, _c_p]
     lib.sparsepr_attend.argtypes = [pp] + [_c_p] * 10 + [_c_p]
     lib.sparsepr_probe_fit.argtypes = [pp] + [_c_p] * 10 + [_c_p, _c_sz, _c_p]
-    lib.sparsepr_apply.argtypes = [pp] + [_c_p] * 7 + [_c_p]
+    lib.sparsepr_apply.argtypes = [pp] + [_c_p] * 7 + [_c_p, _c_sz, _c_p]
     lib.sparsepr_dense_attention.argtypes = [pp] + [_c_p] * 6 + [_c_p]
     for name in ("sparsepr_partition", "sparsepr_route", "sparsepr_attend", "sparsepr_probe_fit",
                  "sparsepr_apply", "sparsepr_dense_attention"):
@@ -235,7 +235,8 @@ def apply(p: Params, b: Buffers) -> None:
     cp = c_params(p)
     _check(lib.sparsepr_apply(
         ctypes.byref(cp), _ptr(b.S), _ptr(b.query_perm), _ptr(b.O_probe), _ptr(b.U),
-        _ptr(b.Theta), _ptr(b.rank_eff), _ptr(b.O), _stream(b.S.device)))
+        _ptr(b.Theta), _ptr(b.rank_eff), _ptr(b.O), _ptr(b.workspace), b.workspace.numel(),
+        _stream(b.S.device)))
 
 
 def dense_attention(p: Params, Q, K, V, scale, O=None, lse=None):

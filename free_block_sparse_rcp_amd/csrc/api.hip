@@ -91,6 +91,16 @@ ProbeWs probe_ws(const Dims& d) {
   return L;
 }
 
+ApplyWs apply_ws(const Dims& d) {
+  Bump b;
+  ApplyWs L;
+  const size_t H = d.H, D = d.D;
+  L.wt = b.take(H * 2 * D * D * 2);
+  L.bias = b.take(H * D * 4);
+  L.end = align256(b.off);
+  return L;
+}
+
 // Validation of the parameters; `full` also checks the fields that only the
 // sparse stages use.
 static int32_t make_dims(const sparsepr_params* p, bool full, Dims* d) {
@@ -175,7 +185,8 @@ static int32_t make_dims(const sparsepr_params* p, bool full, Dims* d) {
 }
 
 static size_t total_ws(const Dims& d) {
-  return std::max(partition_ws(d).end, std::max(route_ws(d).end, probe_ws(d).end));
+  return std::max(std::max(partition_ws(d).end, route_ws(d).end),
+                  std::max(probe_ws(d).end, apply_ws(d).end));
 }
 
 #define SPR_REQUIRE(ptr, name) \
@@ -386,7 +397,8 @@ int32_t sparsepr_probe_fit(const sparsepr_params* params, const void* Q, const v
 
 int32_t sparsepr_apply(const sparsepr_params* params, const float* S_out,
                        const int32_t* query_perm, const float* O_probe, const float* U,
-                       const float* Theta, const int32_t* rank_eff, void* O, void* stream) {
+                       const float* Theta, const int32_t* rank_eff, void* O, void* workspace,
+                       size_t workspace_bytes, void* stream) {
   Dims d;
   int32_t s = make_dims(params, true, &d);
   if (s != SPARSEPR_OK) return s;
@@ -399,8 +411,9 @@ int32_t sparsepr_apply(const sparsepr_params* params, const float* S_out,
     SPR_REQUIRE(U, "U");
     SPR_REQUIRE(Theta, "Theta");
   }
+  if ((s = check_ws(d, workspace, workspace_bytes)) != SPARSEPR_OK) return s;
   return hip_status(launch_apply(d, S_out, query_perm, O_probe, U, Theta, rank_eff, O,
-                                 static_cast<hipStream_t>(stream)),
+                                 static_cast<char*>(workspace), static_cast<hipStream_t>(stream)),
                     "sparsepr_apply");
 }
 

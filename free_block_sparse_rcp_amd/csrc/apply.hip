@@ -146,18 +146,192 @@ __global__ __launch_bounds__(256) void k_apply(const float* S, const int32_t* qu
   }
 }
 
+// bf16 path on MFMA. The correction is linear in [s; 1], so it is folded into
+// one matrix per head, W = Theta U^T ((d+1) x d): o = s + s W[:d] + W[d].
+// k_apply_weights forms W^T once per head (fp32, stored as bf16 hi + lo parts)
+// and the bias W[d]; k_apply_mfma copies them into LDS and runs the product
+// O^T = W^T S^T as v_mfma_f32_32x32x16_bf16 with S split into hi + lo too
+// (hi*hi + lo*hi + hi*lo; the dropped lo*lo term is ~2^-16 relative), so the
+// correction keeps near-fp32 accuracy. Each wave takes 32 query positions at a
+// time; s is re-read in the output layout for the final sum.
+constexpr int kApplyTilesPerWg = 128;  // 32-row tiles per workgroup
+
+// grid (H), block 256. wt: [H][2][d][d] bf16 (hi, lo) of W^T; bias: [H][d].
+// Entry (e, a) of W^T (a = d is the bias) accumulates in LDS over chunks of
+// 32 rank columns staged in LDS.
+template <int D>
+__global__ __launch_bounds__(256) void k_apply_weights(const float* U, const float* Theta,
+                                                       const int32_t* rank_eff, int kmax,
+                                                       uint16_t* wt, float* bias) {
+  constexpr int CJ = 32;
+  constexpr int UP = CJ + 1;
+  constexpr int NE = D * (D + 1);
+  __shared__ float ust[D * UP];
+  __shared__ float tst[(D + 1) * UP];
+  __shared__ float wacc[NE];
+  const int h = blockIdx.x, t = threadIdx.x;
+  int keff = rank_eff[h];
+  keff = keff < 0 ? 0 : (keff > kmax ? kmax : keff);
+  const float* Uh = U + (size_t)h * D * kmax;
+  const float* Th = Theta + (size_t)h * (D + 1) * kmax;
+  for (int i = t; i < NE; i += 256) wacc[i] = 0.f;
+  for (int j0 = 0; j0 < keff; j0 += CJ) {
+    __syncthreads();
+    for (int i = t; i < D * CJ; i += 256) {
+      const int r = i / CJ, j = i % CJ;
+      ust[r * UP + j] = j0 + j < keff ? Uh[(size_t)r * kmax + j0 + j] : 0.f;
+    }
+    for (int i = t; i < (D + 1) * CJ; i += 256) {
+      const int r = i / CJ, j = i % CJ;
+      tst[r * UP + j] = j0 + j < keff ? Th[(size_t)r * kmax + j0 + j] : 0.f;
+    }
+    __syncthreads();
+#pragma unroll 1
+    for (int idx = t; idx < NE; idx += 256) {
+      const int e = idx % D, aa = idx / D;
+      float s = wacc[idx];
+#pragma unroll 8
+      for (int j = 0; j < CJ; ++j) s = fmaf(ust[e * UP + j], tst[aa * UP + j], s);
+      wacc[idx] = s;
+    }
+  }
+  __syncthreads();
+  uint16_t* whi = wt + (size_t)h * 2 * D * D;
+  uint16_t* wlo = whi + D * D;
+  for (int idx = t; idx < NE; idx += 256) {
+    const int e = idx % D, aa = idx / D;
+    const float v = wacc[idx];
+    if (aa == D) {
+      bias[(size_t)h * D + e] = v;
+    } else {
+      const uint16_t hi = f32_to_bf16(v);
+      whi[e * D + aa] = hi;
+      wlo[e * D + aa] = f32_to_bf16(v - bf16_to_f32(hi));
+    }
+  }
+}
+
+template <int D>
+__global__ __launch_bounds__(256) void k_apply_mfma(const float* S, const int32_t* query_perm,
+                                                    const float* O_probe, const uint16_t* wt,
+                                                    const float* bias, int N, int m,
+                                                    int wg_per_head, uint16_t* O) {
+  constexpr int WP = D + 8;            // bf16 elements per LDS row of W^T (conflict-free b128 reads)
+  constexpr int NKK = D / 16, NDT = D / 32;
+  constexpr int CPR = D / 8;           // 16-byte chunks per row
+  __shared__ __attribute__((aligned(16))) uint16_t wt_hi[D * WP];
+  __shared__ __attribute__((aligned(16))) uint16_t wt_lo[D * WP];
+  __shared__ float wbias[D];
+  const int h = blockIdx.x / wg_per_head, part = blockIdx.x % wg_per_head;
+  const int t = threadIdx.x, lane = t & 63, hl = lane >> 5, ql = lane & 31;
+  const int w = __builtin_amdgcn_readfirstlane(t >> 6);
+  {
+    const uint16_t* src = wt + (size_t)h * 2 * D * D;
+    for (int i = t; i < 2 * D * CPR; i += 256) {
+      const int arr = i / (D * CPR), rem = i % (D * CPR);
+      const int r = rem / CPR, c = rem % CPR;
+      const u32x4 v = *reinterpret_cast<const u32x4*>(src + (size_t)arr * D * D + r * D + 8 * c);
+      *reinterpret_cast<u32x4*>((arr ? wt_lo : wt_hi) + r * WP + 8 * c) = v;
+    }
+    if (t < D) wbias[t] = bias[(size_t)h * D + t];
+  }
+  __syncthreads();
+
+  const int ntile = (N + 31) / 32;
+  const int t0 = part * kApplyTilesPerWg, t1 = min(ntile, t0 + kApplyTilesPerWg);
+  const float* Sh = S + (size_t)h * N * D;
+  uint16_t* Oh = O + (size_t)h * N * D;
+  for (int tile = t0 + w; tile < t1; tile += 4) {
+    const int pos = tile * 32 + ql;
+    const bool valid = pos < N;
+    const float* srow = Sh + (size_t)(valid ? pos : 0) * D;
+    bf16x8 shi[NKK], slo[NKK];
+#pragma unroll
+    for (int kk = 0; kk < NKK; ++kk) {
+      f32x4 x0 = {0.f, 0.f, 0.f, 0.f}, x1 = x0;
+      if (valid) {
+        x0 = *reinterpret_cast<const f32x4*>(srow + 16 * kk + 8 * hl);
+        x1 = *reinterpret_cast<const f32x4*>(srow + 16 * kk + 8 * hl + 4);
+      }
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        const __bf16 h0 = static_cast<__bf16>(x0[u]);
+        const __bf16 h1 = static_cast<__bf16>(x1[u]);
+        shi[kk][u] = h0;
+        shi[kk][4 + u] = h1;
+        slo[kk][u] = static_cast<__bf16>(x0[u] - static_cast<float>(h0));
+        slo[kk][4 + u] = static_cast<__bf16>(x1[u] - static_cast<float>(h1));
+      }
+    }
+    const int tok = valid ? clamp_idx(query_perm[(size_t)h * N + pos], N) : 0;
+    const int pi = valid ? probe_index(pos, N, m) : -1;
+    // W fragments are re-read from LDS every tile: kept opaque so that the
+    // compiler does not hoist all of them into registers (occupancy)
+    int woff = ql * WP + 8 * hl;
+    asm volatile("" : "+v"(woff));
+#pragma unroll
+    for (int nt = 0; nt < NDT; ++nt) {
+      f32x16 acc;
+#pragma unroll
+      for (int r = 0; r < 16; ++r) acc[r] = 0.f;
+      const uint16_t* whr = wt_hi + 32 * nt * WP + woff;
+      const uint16_t* wlr = wt_lo + 32 * nt * WP + woff;
+#pragma unroll
+      for (int kk = 0; kk < NKK; ++kk) {
+        const bf16x8 ahi = *reinterpret_cast<const bf16x8*>(whr + 16 * kk);
+        const bf16x8 alo = *reinterpret_cast<const bf16x8*>(wlr + 16 * kk);
+        acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ahi, shi[kk], acc, 0, 0, 0);
+        acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(alo, shi[kk], acc, 0, 0, 0);
+        acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ahi, slo[kk], acc, 0, 0, 0);
+      }
+      if (!valid) continue;
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const int d0 = 32 * nt + 8 * q + 4 * hl;
+        f32x4 v;
+        if (pi >= 0) {
+          v = *reinterpret_cast<const f32x4*>(O_probe + ((size_t)h * m + pi) * D + d0);
+        } else {
+          v = *reinterpret_cast<const f32x4*>(srow + d0);
+#pragma unroll
+          for (int u = 0; u < 4; ++u) v[u] += acc[4 * q + u] + wbias[d0 + u];
+        }
+        const f32x2 f0 = {v[0], v[1]};
+        const f32x2 f1 = {v[2], v[3]};
+        const bf16x2 b0 = __builtin_convertvector(f0, bf16x2);
+        const bf16x2 b1 = __builtin_convertvector(f1, bf16x2);
+        const bf16x4 bv = {b0[0], b0[1], b1[0], b1[1]};
+        *reinterpret_cast<bf16x4*>(Oh + (size_t)tok * D + d0) = bv;
+      }
+    }
+  }
+}
+
 hipError_t launch_apply(const Dims& d, const float* S_out, const int32_t* query_perm,
                         const float* O_probe, const float* U, const float* Theta,
-                        const int32_t* rank_eff, void* O, hipStream_t st) {
+                        const int32_t* rank_eff, void* O, char* ws, hipStream_t st) {
+  if (d.bf16) {
+    const ApplyWs L = apply_ws(d);
+    uint16_t* wt = reinterpret_cast<uint16_t*>(ws + L.wt);
+    float* bias = reinterpret_cast<float*>(ws + L.bias);
+    const int wgph = ((d.N + 31) / 32 + kApplyTilesPerWg - 1) / kApplyTilesPerWg;
+    uint16_t* Ob = static_cast<uint16_t*>(O);
+    if (d.D == 128) {
+      k_apply_weights<128><<<d.H, 256, 0, st>>>(U, Theta, rank_eff, d.k, wt, bias);
+      k_apply_mfma<128><<<d.H * wgph, 256, 0, st>>>(S_out, query_perm, O_probe, wt, bias, d.N,
+                                                    d.m, wgph, Ob);
+    } else {
+      k_apply_weights<64><<<d.H, 256, 0, st>>>(U, Theta, rank_eff, d.k, wt, bias);
+      k_apply_mfma<64><<<d.H * wgph, 256, 0, st>>>(S_out, query_perm, O_probe, wt, bias, d.N,
+                                                   d.m, wgph, Ob);
+    }
+    return hipGetLastError();
+  }
   const dim3 grid((d.N + kApplyRows - 1) / kApplyRows, d.H);
 #define SPR_APPLY(B, DD)                                                                   \
   k_apply<B, DD><<<grid, 256, 0, st>>>(S_out, query_perm, O_probe, U, Theta, rank_eff, d.N, \
                                         d.m, d.k, O)
-  if (d.bf16) {
-    if (d.D == 128) SPR_APPLY(true, 128); else SPR_APPLY(true, 64);
-  } else {
-    if (d.D == 128) SPR_APPLY(false, 128); else SPR_APPLY(false, 64);
-  }
+  if (d.D == 128) SPR_APPLY(false, 128); else SPR_APPLY(false, 64);
 #undef SPR_APPLY
   return hipGetLastError();
 }

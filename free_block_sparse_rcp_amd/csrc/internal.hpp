@@ -34,9 +34,13 @@ struct RouteWs {
 struct ProbeWs {
   size_t opart, lsepart, fit, fit_per_head, end;
 };
+struct ApplyWs {
+  size_t wt, bias, end;   // W^T as bf16 hi/lo [H][2][d][d]; bias [H][d] fp32
+};
 PartitionWs partition_ws(const Dims& d);
 RouteWs route_ws(const Dims& d);
 ProbeWs probe_ws(const Dims& d);
+ApplyWs apply_ws(const Dims& d);
 size_t fit_ws_per_head(const Dims& d);
 
 // ---- partition.hip
@@ -104,6 +108,6 @@ hipError_t launch_fit(const Dims& d, const float* S_out, const float* O_probe, f
 // ---- apply.hip
 hipError_t launch_apply(const Dims& d, const float* S_out, const int32_t* query_perm,
                         const float* O_probe, const float* U, const float* Theta,
-                        const int32_t* rank_eff, void* O, hipStream_t st);
+                        const int32_t* rank_eff, void* O, char* ws, hipStream_t st);
 
 }  // namespace spr

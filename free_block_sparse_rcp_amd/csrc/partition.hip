@@ -521,44 +521,71 @@ __global__ __launch_bounds__(256) void k_digit_scatter(const KeyT* keys_in, KeyT
 
 // ------------------------------------------------ deterministic group means
 // Tile c = positions [64c, 64c+64) of the group-contiguous order. Each run of
-// one group inside a tile is summed (fixed order) into partial[g + c]; the
-// index g + c is unique because tiles and groups both advance along the order.
-// grid (ntile64, H), block D.
+// one group inside a tile is summed (rows in order, per column) into
+// partial[g + c]; the index g + c is unique because tiles and groups both
+// advance along the order. The tile's 64 rows are gathered with 16-byte loads
+// into LDS as fp32; the group of a position follows from group_off.
+// grid (ntile64, H), block 256.
 template <bool BF16, int D>
-__global__ void k_seg_partial(const void* Kv, const int32_t* key_perm, const int32_t* labels,
-                              int N, int G, int ntile, float* partial) {
-  using E = Elt<BF16>;
-  const int c = blockIdx.x, h = blockIdx.y, e = threadIdx.x;
-  const typename E::T* K = static_cast<const typename E::T*>(Kv) + (size_t)h * N * D;
+__global__ __launch_bounds__(256) void k_seg_partial(const void* Kv, const int32_t* key_perm,
+                                                     const int32_t* group_off, int N, int G,
+                                                     int ntile, float* partial) {
+  using T = typename Elt<BF16>::T;
+  constexpr int ROWB = D * (int)sizeof(T);
+  constexpr int CPR = ROWB / 16;              // 16-byte chunks per row
+  constexpr int EPC = 16 / (int)sizeof(T);    // elements per chunk
+  constexpr int PITCH = D + 4;                // floats; rows stay 16-byte aligned
+  __shared__ __attribute__((aligned(16))) float tile[64 * PITCH];
+  __shared__ int srow[64];
+  const int c = blockIdx.x, h = blockIdx.y, t = threadIdx.x;
+  const char* K = static_cast<const char*>(Kv) + (size_t)h * N * ROWB;
+  const int32_t* off = group_off + (size_t)h * (G + 1);
   float* part = partial + (size_t)h * (G + ntile) * D;
-  __shared__ int skey[64];
-  __shared__ int slab[64];
   const int p0 = c * 64, n = min(N, p0 + 64) - p0;
-  if (e < n) {
-    const int key = clamp_idx(key_perm[(size_t)h * N + p0 + e], N);
-    skey[e] = key;
-    slab[e] = labels[(size_t)h * N + key];
-  }
+  if (t < n) srow[t] = clamp_idx(key_perm[(size_t)h * N + p0 + t], N);
   __syncthreads();
-  // all 64 row loads are issued before any is consumed (one memory round trip)
-  float vals[64];
+  for (int i = t; i < n * CPR; i += 256) {
+    const int r = i / CPR, cc = i - r * CPR;
+    const u32x4 raw = *reinterpret_cast<const u32x4*>(K + (size_t)srow[r] * ROWB + cc * 16);
+    float* dst = tile + r * PITCH + cc * EPC;
+    if (BF16) {
+      f32x4 lo, hi;
 #pragma unroll
-  for (int u = 0; u < 64; ++u) vals[u] = u < n ? E::ld(K, (size_t)skey[u] * D + e) : 0.f;
-  int cur = -1;
-  float acc = 0.f;
-#pragma unroll
-  for (int u = 0; u < 64; ++u) {
-    if (u < n) {
-      const int g = slab[u];
-      if (g != cur) {
-        if (cur >= 0) part[(size_t)(cur + c) * D + e] = acc;
-        cur = g;
-        acc = 0.f;
+      for (int j = 0; j < 2; ++j) {
+        lo[2 * j] = __uint_as_float(raw[j] << 16);
+        lo[2 * j + 1] = __uint_as_float(raw[j] & 0xffff0000u);
+        hi[2 * j] = __uint_as_float(raw[2 + j] << 16);
+        hi[2 * j + 1] = __uint_as_float(raw[2 + j] & 0xffff0000u);
       }
-      acc += vals[u];
+      *reinterpret_cast<f32x4*>(dst) = lo;
+      *reinterpret_cast<f32x4*>(dst + 4) = hi;
+    } else {
+      *reinterpret_cast<f32x4*>(dst) = __builtin_bit_cast(f32x4, raw);
     }
   }
-  if (cur >= 0) part[(size_t)(cur + c) * D + e] = acc;
+  __syncthreads();
+  if (t >= D || n <= 0) return;
+  // group of position p0: the last g with off[g] <= p0 (runs of empty groups skipped)
+  int lo = 0, hi = G;   // invariant off[lo] <= p0 < off[hi] (off[G] = N > p0)
+  while (hi - lo > 1) {
+    const int mid = (lo + hi) >> 1;
+    if (off[mid] <= p0) lo = mid; else hi = mid;
+  }
+  int g = lo, end = off[g + 1];
+  float acc = 0.f;
+  for (int r = 0; r < n; ++r) {
+    const int pos = p0 + r;
+    if (pos >= end) {
+      part[(size_t)(g + c) * D + t] = acc;
+      acc = 0.f;
+      do {
+        ++g;
+        end = off[g + 1];
+      } while (pos >= end);
+    }
+    acc += tile[r * PITCH + t];
+  }
+  part[(size_t)(g + c) * D + t] = acc;
 }
 
 // kbar_g = (sum of the group's tile partials, in tile order) / n_g for
@@ -686,8 +713,8 @@ static hipError_t partition_impl(const Dims& d, const void* Q, const void* K, co
     hipError_t e = launch_sort_pass_u32(d, key_label, d.gbits, nullptr, key_perm, counts, totals,
                                         starts, group_off, st);
     if (e != hipSuccess) return e;
-    k_seg_partial<BF16, D><<<dim3(d.ntile64, d.H), D, 0, st>>>(K, key_perm, key_label, d.N, d.G,
-                                                                d.ntile64, partial);
+    k_seg_partial<BF16, D><<<dim3(d.ntile64, d.H), 256, 0, st>>>(K, key_perm, group_off, d.N, d.G,
+                                                                  d.ntile64, partial);
     SPR_CHECK_LAUNCH();
     k_seg_final<D><<<per_group, D, 0, st>>>(partial, group_off, d.G, d.ntile64, kbar);
     SPR_CHECK_LAUNCH();

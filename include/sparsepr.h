@@ -243,11 +243,15 @@ int32_t sparsepr_probe_fit(const sparsepr_params* params, const void* Q, const v
  *   O[q] = s_i + U Theta^T [s_i; 1]   if i is not a probe position,
  *   O[q] = O_probe[probe index]       if it is.
  * Inputs : S_out [H,N,d] fp32; query_perm [H,N]; O_probe [H,m,d]; U; Theta;
- *          rank_eff [H]. Output: O [H,N,d] dtype in TOKEN ORDER.
+ *          rank_eff [H]; workspace (the shared one; this stage keeps the
+ *          per-head matrix Theta U^T there). Output: O [H,N,d] dtype in TOKEN
+ *          ORDER. Errors: as the other stages (NULL arguments, a workspace
+ *          smaller than sparsepr_workspace_bytes).
  */
 int32_t sparsepr_apply(const sparsepr_params* params, const float* S_out,
                        const int32_t* query_perm, const float* O_probe, const float* U,
-                       const float* Theta, const int32_t* rank_eff, void* O, void* stream);
+                       const float* Theta, const int32_t* rank_eff, void* O, void* workspace,
+                       size_t workspace_bytes, void* stream);
 
 /*
  * Exact softmax attention over all keys, the operator SparsePR replaces

@@ -111,6 +111,13 @@ def test_null_pointers_and_small_workspace_are_rejected(lib):
     st = lib.sparsepr_attend(ctypes.byref(p), fake, fake, fake, fake, fake, fake, fake, fake, fake,
                              None, None)
     assert st == 1
+    # apply: output missing, then a workspace too small for the per-head matrix
+    st = lib.sparsepr_apply(ctypes.byref(p), fake, fake, fake, fake, fake, fake, None, fake,
+                            1 << 40, None)
+    assert st == 1 and "O is NULL" in lib.sparsepr_last_error().decode()
+    st = lib.sparsepr_apply(ctypes.byref(p), fake, fake, fake, fake, fake, fake, fake, fake, 16,
+                            None)
+    assert st == 3
     # dense attention validates only the shape fields
     q = binding.c_params(configs.TINY.params)
     q.head_dim = 80
