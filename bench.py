@@ -48,6 +48,52 @@ def load_traffic(workload):
     return rec.get("bytes_per_launch")
 
 
+SPARSE_KERNEL = "k_attn_mfma<128, 128, 0>"   # sparsepr_attend's kernel (d=128, B_q=128)
+COPY_KERNEL = "neg_kernel"                    # the --calibration-copy-mib kernel
+
+
+def pmc_summary(fetch_csv, write_csv, workload, copy_mib):
+    """Per-launch HBM bytes of the block-sparse kernel from a FETCH_SIZE run and
+    a WRITE_SIZE run (rocprofv3 --pmc ... --output-format csv), each scaled by
+    what the same counter reports for the plain copy of copy_mib MiB (reads
+    and writes copy_mib MiB exactly). Writes profiles/attend_traffic_<workload>.json."""
+    import csv
+
+    def per_dispatch(path, counter):
+        vals = {"kernel": [], "copy": []}
+        for r in csv.DictReader(open(path)):
+            if r["Counter_Name"] != counter:
+                continue
+            if SPARSE_KERNEL in r["Kernel_Name"]:
+                vals["kernel"].append(float(r["Counter_Value"]))
+            elif COPY_KERNEL in r["Kernel_Name"]:
+                vals["copy"].append(float(r["Counter_Value"]))
+        if not vals["kernel"] or not vals["copy"]:
+            raise SystemExit(f"{path}: no {counter} rows for the kernel and the copy")
+        return sum(vals["kernel"]) / len(vals["kernel"]), sum(vals["copy"]) / len(vals["copy"]), \
+            len(vals["kernel"])
+
+    copy_kib = copy_mib * 1024.0
+    f_k, f_c, nf = per_dispatch(fetch_csv, "FETCH_SIZE")
+    w_k, w_c, nw = per_dispatch(write_csv, "WRITE_SIZE")
+    f_scale, w_scale = copy_kib / f_c, copy_kib / w_c
+    fetch_b = f_k * f_scale * 1024.0
+    write_b = w_k * w_scale * 1024.0
+    src = os.path.join(ROOT, "free_block_sparse_rcp_amd", "csrc", "attention.hip")
+    rec = {"workload": workload, "kernel": SPARSE_KERNEL,
+           "attention_hip_sha256_16": source_hash(src),
+           "fetch_kib_per_dispatch_raw": f_k, "write_kib_per_dispatch_raw": w_k,
+           "dispatches": {"fetch_run": nf, "write_run": nw},
+           "copy_mib": copy_mib, "copy_fetch_kib_raw": f_c, "copy_write_kib_raw": w_c,
+           "fetch_scale": f_scale, "write_scale": w_scale,
+           "fetch_bytes_per_launch": fetch_b, "write_bytes_per_launch": write_b,
+           "bytes_per_launch": fetch_b + write_b}
+    out = os.path.join(ROOT, "profiles", f"attend_traffic_{workload}.json")
+    with open(out, "w") as f:
+        json.dump(rec, f, indent=1)
+    print(json.dumps(rec))
+
+
 def cpu_baseline(wl, inp, block_stride):
     """The fp64 oracle, as it stands, on head 0 of the same workload: every
     stage in the pages' order; the block-sparse attention step runs on every
@@ -125,7 +171,15 @@ def main():
     ap.add_argument("--calibration-copy-mib", type=int, default=0,
                     help="also run one plain device copy of this many MiB (a known-size "
                          "kernel for scaling the FETCH_SIZE / WRITE_SIZE counters)")
+    ap.add_argument("--pmc-summary", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
+                    help="summarise two rocprofv3 PMC runs of this script (FETCH_SIZE, "
+                         "WRITE_SIZE) into profiles/attend_traffic_<workload>.json and exit")
     args = ap.parse_args()
+    if args.pmc_summary:
+        from free_block_sparse_rcp_amd import configs
+        pmc_summary(args.pmc_summary[0], args.pmc_summary[1], configs.get(args.config).name,
+                    args.calibration_copy_mib or 1024)
+        return
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only: the operator is per call and per head, and this "
               f"build has no multi-GPU path (asked for --gpus {args.gpus}).", file=sys.stderr)
