@@ -4,14 +4,16 @@
 // peercurrent abstract: an affine map, call-specific, restricted to the output
 // subspace seen in the probe residuals).
 //
-// One workgroup per head, all in fp64:
-//   r_i = o_i - s_i, w_i = ||o_i||^-2 / sum ||o||^-2, Sigma = sum w_i r_i r_i^T;
-//   top-k_eff eigenvectors of Sigma: Householder tridiagonalisation in LDS,
-//   eigenvalues by Sturm-count multisection, eigenvectors of the tridiagonal
-//   by inverse iteration, re-orthonormalised (classical Gram-Schmidt twice)
-//   and mapped back through the reflectors;
-//   Theta from (X^T W X + lambda I~) Theta = X^T W (R U), X = [s, 1], by
-//   Cholesky in LDS with an unpenalised bias row.
+// All in fp64, with X = [s, 1] and r_i = o_i - s_i for the m probe rows:
+//   k_fit_prep (many workgroups per head): w_i = ||o_i||^-2 / sum ||o||^-2,
+//     Sigma = sum w_i r_i r_i^T, the ridge Gram X^T W X + lambda I~ (bias row
+//     unpenalised) and X^T W R, a block of 8 rows per workgroup;
+//   k_fit (one workgroup per head): top-k_eff eigenvectors U of Sigma by
+//     Householder tridiagonalisation in LDS, Sturm-count multisection,
+//     inverse iteration on the tridiagonal, classical Gram-Schmidt twice and
+//     the back-transform through the reflectors; then the right-hand side
+//     X^T W (R U) = (X^T W R) U and Theta by a packed Cholesky factorisation
+//     in LDS with forward and backward substitution.
 #include "common.hpp"
 #include "internal.hpp"
 
@@ -25,16 +27,18 @@ __device__ __forceinline__ double wave_sum_f64(double v) {
   return v;
 }
 
-// Workgroup sum with two barriers (wave shuffles, then one LDS exchange).
-__device__ __forceinline__ double wg_sum(double v, double* red) {
+// Workgroup sum with one barrier. The wave partials go to one of two slots
+// that alternate between calls: a slot is rewritten only two calls later,
+// behind a barrier that every thread reaches after reading it.
+__device__ __forceinline__ double wg_sum1(double v, double* red2, int& slot) {
   v = wave_sum_f64(v);
-  const int w = threadIdx.x >> 6;
-  if ((threadIdx.x & 63) == 0) red[w] = v;
+  double* red = red2 + slot * (kFitThreads / 64);
+  if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = v;
   __syncthreads();
   double s = 0.0;
 #pragma unroll
   for (int i = 0; i < kFitThreads / 64; ++i) s += red[i];
-  __syncthreads();
+  slot ^= 1;
   return s;
 }
 
@@ -54,45 +58,141 @@ __device__ int sturm_count(const double* a, const double* b2, int n, double x, d
 
 // Per-head scratch layout (doubles) in the workspace.
 struct FitScratch {
-  double *R, *S, *w, *X, *hv, *Y, *rhs;
+  double *sig, *gram, *xtwr, *hv, *rhs;
 };
 __host__ __device__ inline size_t fit_doubles_per_head(int m, int D, int k) {
-  return (size_t)2 * m * D + m + (size_t)D * k + (size_t)D * D + (size_t)m * k +
-         (size_t)(D + 1) * k + 64;
+  const size_t NX = (size_t)D + 1;
+  (void)m;
+  return (size_t)D * D + NX * NX + NX * D + (size_t)D * D + NX * (size_t)(k > 0 ? k : 1) + 64;
 }
 __device__ inline FitScratch fit_scratch(double* base, int m, int D, int k) {
+  const size_t NX = (size_t)D + 1;
+  (void)m;
+  (void)k;
   FitScratch f;
-  f.R = base;
-  f.S = f.R + (size_t)m * D;
-  f.w = f.S + (size_t)m * D;
-  f.X = f.w + m;
-  f.hv = f.X + (size_t)D * k;
-  f.Y = f.hv + (size_t)D * D;
-  f.rhs = f.Y + (size_t)m * k;
+  f.sig = base;
+  f.gram = f.sig + (size_t)D * D;
+  f.xtwr = f.gram + NX * NX;
+  f.hv = f.xtwr + NX * D;
+  f.rhs = f.hv + (size_t)D * D;
   return f;
 }
 
+__device__ __forceinline__ int probe_pos(int i, int N, int m) {
+  return (int)(((2LL * i + 1) * N) / (2LL * m));
+}
+
+__device__ __forceinline__ double row_inv_norm2(const float* row, int D) {
+  double n2 = 0.0;
+  for (int e = 0; e < D; ++e) {
+    const double o = row[e];
+    n2 += o * o;
+  }
+  return n2 > 0.0 ? 1.0 / n2 : 0.0;
+}
+
+// ---------------------------------------------------------------- prep
+// grid (H, ceil((d+1)/8)), block 256. Workgroup b accumulates rows [8b, 8b+8)
+// of Sigma (rows < d), of X^T W R and of the Gram (rows < d+1) over chunks of
+// 256 probe rows staged in LDS.
 template <int D>
-__global__ __launch_bounds__(kFitThreads) void k_fit(const float* S_out_in, const float* O_probe,
-                                                     int N, int m, int kmax, double lambda,
-                                                     float* U_out, float* Th_out,
+__global__ __launch_bounds__(kFitThreads) void k_fit_prep(const float* S_out, const float* O_probe,
+                                                          int N, int m, int kmax, double lambda,
+                                                          double* scratch) {
+  constexpr int NT = kFitThreads;
+  constexpr int NX = D + 1;
+  constexpr int RB = 8;
+  constexpr int CH = 256;          // probe rows per chunk
+  __shared__ double ra[CH][RB];    // w_i * r_i[a] for the block's rows a
+  __shared__ double xa[CH][RB];    // w_i * x_i[a]
+  __shared__ double w_s[CH];
+  __shared__ int pos_s[CH];
+  __shared__ double red2[2 * NT / 64];
+  const int h = blockIdx.x, b = blockIdx.y, t = threadIdx.x;
+  const float* Sh = S_out + (size_t)h * N * D;
+  const float* Op = O_probe + (size_t)h * m * D;
+  FitScratch f = fit_scratch(scratch + (size_t)h * fit_doubles_per_head(m, D, kmax), m, D, kmax);
+  int slot = 0;
+  double wpart = 0.0;
+  for (int i = t; i < m; i += NT) wpart += row_inv_norm2(Op + (size_t)i * D, D);
+  const double wsum = wg_sum1(wpart, red2, slot);
+  const int a0 = RB * b;
+  for (int i0 = 0; i0 < m; i0 += CH) {
+    const int mi = min(CH, m - i0);
+    __syncthreads();
+    if (t < mi) {
+      const double wi = row_inv_norm2(Op + (size_t)(i0 + t) * D, D);
+      w_s[t] = wsum > 0.0 ? wi / wsum : 0.0;
+      pos_s[t] = probe_pos(i0 + t, N, m);
+    }
+    __syncthreads();
+    for (int idx = t; idx < mi * RB; idx += NT) {
+      const int i = idx / RB, u = idx % RB, a = a0 + u;
+      const int p = pos_s[i];
+      double rv = 0.0, xv = 0.0;
+      if (a < D) {
+        const double s = Sh[(size_t)p * D + a];
+        rv = (double)Op[(size_t)(i0 + i) * D + a] - s;
+        xv = s;
+      } else if (a == D) {
+        xv = 1.0;
+      }
+      ra[i][u] = w_s[i] * rv;
+      xa[i][u] = w_s[i] * xv;
+    }
+    __syncthreads();
+    // jobs: Sigma columns [0, D), X^T W R columns [D, 2D), Gram columns [2D, 2D + NX)
+    for (int job = t; job < 2 * D + NX; job += NT) {
+      const int kind = job < D ? 0 : (job < 2 * D ? 1 : 2);
+      const int c = kind == 0 ? job : (kind == 1 ? job - D : job - 2 * D);
+      double acc[RB];
+#pragma unroll
+      for (int u = 0; u < RB; ++u) acc[u] = 0.0;
+      for (int i = 0; i < mi; ++i) {
+        const int p = pos_s[i];
+        double col;
+        if (kind == 2) col = c < D ? (double)Sh[(size_t)p * D + c] : 1.0;
+        else col = (double)Op[(size_t)(i0 + i) * D + c] - (double)Sh[(size_t)p * D + c];
+        const double* rowv = kind == 0 ? ra[i] : xa[i];
+#pragma unroll
+        for (int u = 0; u < RB; ++u) acc[u] += rowv[u] * col;
+      }
+#pragma unroll
+      for (int u = 0; u < RB; ++u) {
+        const int a = a0 + u;
+        double* dst = nullptr;
+        if (kind == 0) dst = a < D ? f.sig + (size_t)a * D + c : nullptr;
+        else if (kind == 1) dst = a < NX ? f.xtwr + (size_t)a * D + c : nullptr;
+        else dst = a < NX ? f.gram + (size_t)a * NX + c : nullptr;
+        if (dst == nullptr) continue;
+        double v = (i0 == 0 ? 0.0 : *dst) + acc[u];
+        if (kind == 2 && i0 + mi == m && a == c && a < D) v += lambda;
+        *dst = v;
+      }
+    }
+  }
+}
+
+// ---------------------------------------------------------------- fit
+template <int D>
+__global__ __launch_bounds__(kFitThreads) void k_fit(int m, int kmax, float* U_out, float* Th_out,
                                                      int32_t* rank_eff, double* scratch) {
   constexpr int NT = kFitThreads;
-  constexpr int PA = D + 1;       // pitch of the eigen matrix
-  constexpr int PX = D + 2;       // pitch of the ridge matrix
-  constexpr int NX = D + 1;       // ridge unknowns (d weights + bias)
-  __shared__ double big[(D + 1) * (D + 2)];
-  __shared__ double dg[D], od[D], od2[D], beta[D], vv[D], pv[D];
+  constexpr int PA = D + 1;                // pitch of the eigen matrix
+  constexpr int NX = D + 1;                // ridge unknowns (d weights + bias)
+  constexpr int NP = NX * (NX + 1) / 2;    // packed lower triangle of the ridge matrix
+  constexpr int BIG = (D + 1) * (D + 2);
+  __shared__ double big[BIG];
+  __shared__ double dg[D], od[D], od2[D], beta[D], vv[D], pv[D], vn[D];
   __shared__ double lam_top[D];
-  __shared__ double red[NT / 64];
+  __shared__ double red2[2 * NT / 64];
   __shared__ double dots[D];
   const int h = blockIdx.x, t = threadIdx.x;
-  const float* S_out = S_out_in + (size_t)h * N * D;
-  const float* Op = O_probe + (size_t)h * m * D;
   float* Uh = U_out + (size_t)h * D * kmax;
   float* Th = Th_out + (size_t)h * (D + 1) * kmax;
-  int keff = min(kmax, min(m, D));
+  const int keff = min(kmax, min(m, D));
   FitScratch f = fit_scratch(scratch + (size_t)h * fit_doubles_per_head(m, D, kmax), m, D, kmax);
+  int slot = 0;
 
   for (int i = t; i < D * kmax; i += NT) Uh[i] = 0.f;
   for (int i = t; i < (D + 1) * kmax; i += NT) Th[i] = 0.f;
@@ -100,69 +200,18 @@ __global__ __launch_bounds__(kFitThreads) void k_fit(const float* S_out_in, cons
     if (t == 0) rank_eff[h] = 0;
     return;
   }
-  // ---- probes: residuals, weights
-  for (int idx = t; idx < m * D; idx += NT) {
-    const int i = idx / D, e = idx % D;
-    const int p = (int)(((2LL * i + 1) * N) / (2LL * m));
-    const double s = S_out[(size_t)p * D + e];
-    const double o = Op[(size_t)i * D + e];
-    f.S[idx] = s;
-    f.R[idx] = o - s;
-  }
-  double wpart = 0.0;
-  for (int i = t; i < m; i += NT) {
-    double n2 = 0.0;
-    for (int e = 0; e < D; ++e) {
-      const double o = Op[(size_t)i * D + e];
-      n2 += o * o;
-    }
-    const double wi = n2 > 0.0 ? 1.0 / n2 : 0.0;
-    f.w[i] = wi;
-    wpart += wi;
-  }
-  const double wsum = wg_sum(wpart, red);
-  for (int i = t; i < m; i += NT) f.w[i] = wsum > 0.0 ? f.w[i] / wsum : 0.0;
-  __syncthreads();
-  // ---- Sigma = sum_i w_i r_i r_i^T into LDS, 8 x 8 tiles per thread
   double* A = big;
-  {
-    constexpr int NTB = D / 8;
-    for (int tile = t; tile < NTB * NTB; tile += NT) {
-      const int a0 = 8 * (tile / NTB), b0 = 8 * (tile % NTB);
-      double acc[8][8];
-#pragma unroll
-      for (int i = 0; i < 8; ++i)
-#pragma unroll
-        for (int j = 0; j < 8; ++j) acc[i][j] = 0.0;
-      for (int i = 0; i < m; ++i) {
-        const double wi = f.w[i];
-        const double* Ri = f.R + (size_t)i * D;
-        double ra[8], rb[8];
-#pragma unroll
-        for (int u = 0; u < 8; ++u) {
-          ra[u] = wi * Ri[a0 + u];
-          rb[u] = Ri[b0 + u];
-        }
-#pragma unroll
-        for (int u = 0; u < 8; ++u)
-#pragma unroll
-          for (int v = 0; v < 8; ++v) acc[u][v] += ra[u] * rb[v];
-      }
-#pragma unroll
-      for (int u = 0; u < 8; ++u)
-#pragma unroll
-        for (int v = 0; v < 8; ++v) A[(a0 + u) * PA + b0 + v] = acc[u][v];
-    }
-  }
+  for (int idx = t; idx < D * D; idx += NT) A[(idx / D) * PA + idx % D] = f.sig[idx];
   __syncthreads();
   double trpart = 0.0;
   for (int i = t; i < D; i += NT) trpart += A[i * PA + i];
-  const double trace = wg_sum(trpart, red);
+  const double trace = wg_sum1(trpart, red2, slot);
   if (!(trace > 0.0)) {
     if (t == 0) rank_eff[h] = 0;
     return;
   }
-  // ---- Householder tridiagonalisation; reflector k stored in column k below the diagonal
+  // ---- Householder tridiagonalisation; reflector k stored in column k below
+  // the diagonal. Four barriers per step: two sums, q ready, update done.
   for (int k = 0; k < D - 2; ++k) {
     const int L = D - k - 1;
     double part = 0.0;
@@ -170,40 +219,45 @@ __global__ __launch_bounds__(kFitThreads) void k_fit(const float* S_out_in, cons
       const double x = A[(k + 1 + i) * PA + k];
       part += x * x;
     }
-    const double sig2 = wg_sum(part, red);
+    const double sig2 = wg_sum1(part, red2, slot);
     const double x0 = A[(k + 1) * PA + k];
     if (sig2 == 0.0) {
       if (t == 0) {
         beta[k] = 0.0;
         od[k] = x0;
       }
-      __syncthreads();
-      continue;
+      continue;   // nothing is updated in this step
     }
     const double alpha = -copysign(sqrt(x0 * x0 + sig2), x0);
     const double v0 = x0 - alpha;
     const double bk = 2.0 / (v0 * v0 + sig2);
-    for (int i = t; i < L; i += NT) vv[i] = i == 0 ? v0 : A[(k + 1 + i) * PA + k];
-    __syncthreads();
+    // p = beta A22 v with v_0 = v0, v_j = A[k+1+j][k]; two threads per row
+    const int i = t >> 1, half = t & 1;
+    double s = 0.0;
+    if (i < L) {
+      for (int j = half; j < L; j += 2) {
+        const double vj = j == 0 ? v0 : A[(k + 1 + j) * PA + k];
+        s += A[(k + 1 + j) * PA + (k + 1 + i)] * vj;
+      }
+    }
+    s += __shfl_xor(s, 1);
+    const double p_i = bk * s;
+    const double v_i = i == 0 ? v0 : (i < L ? A[(k + 1 + i) * PA + k] : 0.0);
+    const double vp = (half == 0 && i < L) ? v_i * p_i : 0.0;
+    const double K = 0.5 * bk * wg_sum1(vp, red2, slot);
+    if (half == 0 && i < L) {
+      pv[i] = p_i - K * v_i;   // q
+      vv[i] = v_i;
+    }
     if (t == 0) {
       beta[k] = bk;
       od[k] = alpha;
-      A[(k + 1) * PA + k] = v0;
+      A[(k + 1) * PA + k] = v0;   // x0 and the column are no longer read in this step
     }
-    // p = beta * A22 v (column access of the symmetric trailing block)
-    double vp = 0.0;
-    for (int i = t; i < L; i += NT) {
-      double s = 0.0;
-      for (int j = 0; j < L; ++j) s += A[(k + 1 + j) * PA + (k + 1 + i)] * vv[j];
-      pv[i] = bk * s;
-      vp += vv[i] * pv[i];
-    }
-    const double K = 0.5 * bk * wg_sum(vp, red);
-    for (int i = t; i < L; i += NT) pv[i] = pv[i] - K * vv[i];  // q
     __syncthreads();
     for (int idx = t; idx < L * L; idx += NT) {
-      const int i = idx / L, j = idx % L;
-      A[(k + 1 + i) * PA + (k + 1 + j)] -= vv[i] * pv[j] + pv[i] * vv[j];
+      const int i2 = idx / L, j2 = idx % L;
+      A[(k + 1 + i2) * PA + (k + 1 + j2)] -= vv[i2] * pv[j2] + pv[i2] * vv[j2];
     }
     __syncthreads();
   }
@@ -215,7 +269,8 @@ __global__ __launch_bounds__(kFitThreads) void k_fit(const float* S_out_in, cons
   __syncthreads();
   for (int i = t; i < D; i += NT) od2[i] = od[i] * od[i];
   __syncthreads();
-  // ---- eigenvalues r = 0..keff-1 from the top: 8-point multisection per eigenvalue
+  // ---- eigenvalues r = 0..keff-1 from the top: 8-point multisection per
+  // eigenvalue; 16 steps shrink the Gershgorin interval by 9^16 > 2^50
   double glo = 1e300, ghi = -1e300, maxb2 = 0.0, tnorm = 0.0;
   for (int i = 0; i < D; ++i) {
     const double bl = i > 0 ? fabs(od[i - 1]) : 0.0;
@@ -233,13 +288,13 @@ __global__ __launch_bounds__(kFitThreads) void k_fit(const float* S_out_in, cons
     const int r = base + t / 8, sub = t % 8;
     const int j = D - 1 - (r < keff ? r : 0);  // ascending eigenvalue index
     double lo = glo, hi = ghi;
-    for (int iter = 0; iter < 22; ++iter) {
+    for (int iter = 0; iter < 16; ++iter) {
       const double x = lo + (hi - lo) * (double)(sub + 1) / 9.0;
       const int cnt = sturm_count(dg, od2, D, x, pivmin);
       double nlo = lo, nhi = hi;
-      for (int s = 0; s < 8; ++s) {
-        const double xs = __shfl(x, (t & ~7) + s);
-        const int cs = __shfl(cnt, (t & ~7) + s);
+      for (int s8 = 0; s8 < 8; ++s8) {
+        const double xs = __shfl(x, (t & ~7) + s8);
+        const int cs = __shfl(cnt, (t & ~7) + s8);
         if (cs <= j) nlo = fmax(nlo, xs);
         else nhi = fmin(nhi, xs);
       }
@@ -256,10 +311,12 @@ __global__ __launch_bounds__(kFitThreads) void k_fit(const float* S_out_in, cons
   }
   __syncthreads();
   // ---- inverse iteration on the tridiagonal, one thread per eigenvector,
-  // factors in LDS interleaved across the batch ([i][r]) so lanes hit distinct banks
+  // factors in LDS interleaved across the batch ([i][r]) so lanes hit distinct
+  // banks; the vectors collect in the rhs scratch ([e][r], pitch kmax)
   const double pe = 2.2e-16 * fmax(tnorm, 1e-300);
-  constexpr int KB = D / 4;   // 4 arrays of D x KB doubles fit the (D+1)(D+2) LDS block
-  static_assert(4 * D * KB <= (D + 1) * (D + 2), "inverse-iteration batch exceeds LDS");
+  constexpr int KB = D / 4;   // 4 arrays of D x KB doubles fit the LDS block
+  static_assert(4 * D * KB <= BIG, "inverse-iteration batch exceeds LDS");
+  double* Xg = f.rhs;
   for (int b0 = 0; b0 < keff; b0 += KB) {
     const int nbt = min(KB, keff - b0);
     double* U1 = big;
@@ -315,7 +372,7 @@ __global__ __launch_bounds__(kFitThreads) void k_fit(const float* S_out_in, cons
     __syncthreads();
     for (int idx = t; idx < D * nbt; idx += NT) {
       const int i = idx / nbt, r = idx % nbt;
-      f.X[(size_t)i * kmax + b0 + r] = Z[i * KB + r];
+      Xg[(size_t)i * kmax + b0 + r] = Z[i * KB + r];
     }
     __syncthreads();
   }
@@ -324,7 +381,7 @@ __global__ __launch_bounds__(kFitThreads) void k_fit(const float* S_out_in, cons
   double* X = big;
   for (int idx = t; idx < D * keff; idx += NT) {
     const int e = idx / keff, r = idx % keff;
-    X[e * PXK + r] = f.X[(size_t)e * kmax + r];
+    X[e * PXK + r] = Xg[(size_t)e * kmax + r];
   }
   __syncthreads();
   // ---- classical Gram-Schmidt, twice, in eigenvalue order
@@ -353,134 +410,145 @@ __global__ __launch_bounds__(kFitThreads) void k_fit(const float* S_out_in, cons
       const double x = X[e * PXK + j];
       part += x * x;
     }
-    const double nrm = sqrt(wg_sum(part, red));
+    const double nrm = sqrt(wg_sum1(part, red2, slot));
     for (int e = t; e < D; e += NT) X[e * PXK + j] /= nrm;
     __syncthreads();
   }
-  // ---- back-transform through the reflectors: X <- H_0 H_1 ... H_{D-3} X
+  // ---- back-transform through the reflectors: X <- H_0 H_1 ... H_{D-3} X.
+  // The next reflector is fetched from the workspace while this one is applied.
+  for (int i = t; i < 2; i += NT) vv[i] = f.hv[(size_t)(D - 2 + i) * D + (D - 3)];
+  __syncthreads();
   for (int k = D - 3; k >= 0; --k) {
-    const double bk = beta[k];
-    if (bk == 0.0) continue;
     const int L = D - k - 1;
-    for (int i = t; i < L; i += NT) vv[i] = f.hv[(size_t)(k + 1 + i) * D + k];
-    __syncthreads();
+    double* vc = ((D - 3 - k) & 1) ? vn : vv;
+    double* vnx = ((D - 3 - k) & 1) ? vv : vn;
+    double nxt = 0.0;
+    if (k > 0 && t < L + 1) nxt = f.hv[(size_t)(k + t) * D + (k - 1)];
+    const double bk = beta[k];
     for (int c0 = 0; c0 < keff; c0 += NT / 8) {
       const int cc = c0 + t / 8, sub = t % 8;
       double sacc = 0.0;
-      if (cc < keff)
-        for (int i = sub; i < L; i += 8) sacc += vv[i] * X[(k + 1 + i) * PXK + cc];
+      if (cc < keff && bk != 0.0)
+        for (int i = sub; i < L; i += 8) sacc += vc[i] * X[(k + 1 + i) * PXK + cc];
       sacc += __shfl_xor(sacc, 1);
       sacc += __shfl_xor(sacc, 2);
       sacc += __shfl_xor(sacc, 4);
       if (cc < keff && sub == 0) dots[cc] = bk * sacc;
     }
     __syncthreads();
-    for (int idx = t; idx < L * keff; idx += NT) {
-      const int i = idx / keff, cc = idx % keff;
-      X[(k + 1 + i) * PXK + cc] -= dots[cc] * vv[i];
+    if (bk != 0.0) {
+      for (int idx = t; idx < L * keff; idx += NT) {
+        const int i = idx / keff, cc = idx % keff;
+        X[(k + 1 + i) * PXK + cc] -= dots[cc] * vc[i];
+      }
     }
+    if (k > 0 && t < L + 1) vnx[t] = nxt;
     __syncthreads();
   }
   for (int idx = t; idx < D * keff; idx += NT) {
     const int e = idx / keff, cc = idx % keff;
-    f.X[(size_t)e * kmax + cc] = X[e * PXK + cc];
     Uh[(size_t)e * kmax + cc] = (float)X[e * PXK + cc];
   }
-  __syncthreads();
-  // ---- Y = R U
-  for (int idx = t; idx < m * keff; idx += NT) {
-    const int i = idx / keff, cc = idx % keff;
-    double s = 0.0;
-    for (int e = 0; e < D; ++e) s += f.R[(size_t)i * D + e] * f.X[(size_t)e * kmax + cc];
-    f.Y[(size_t)i * kmax + cc] = s;
-  }
-  __syncthreads();
-  // ---- normal equations in LDS (the eigen matrix is no longer needed)
-  double* Xn = big;
+  // ---- right-hand side (X^T W R) U in 4 x 4 register tiles, into the
+  // workspace (it is copied behind the packed ridge matrix when it fits)
   {
-    constexpr int NTB = (NX + 7) / 8;
-    for (int tile = t; tile < NTB * NTB; tile += NT) {
-      const int a0 = 8 * (tile / NTB), b0 = 8 * (tile % NTB);
-      double acc[8][8];
+    const int ntr = (NX + 3) / 4, ntc = (keff + 3) / 4;
+    for (int tile = t; tile < ntr * ntc; tile += NT) {
+      const int r0 = 4 * (tile / ntc), c0 = 4 * (tile % ntc);
+      double acc[4][4];
 #pragma unroll
-      for (int i = 0; i < 8; ++i)
+      for (int u = 0; u < 4; ++u)
 #pragma unroll
-        for (int j = 0; j < 8; ++j) acc[i][j] = 0.0;
-      for (int i = 0; i < m; ++i) {
-        const double wi = f.w[i];
-        const double* Si = f.S + (size_t)i * D;
-        double xa[8], xb[8];
+        for (int v = 0; v < 4; ++v) acc[u][v] = 0.0;
+      for (int e = 0; e < D; ++e) {
+        double xr[4], uc[4];
 #pragma unroll
-        for (int u = 0; u < 8; ++u) {
-          const int a = a0 + u, b = b0 + u;
-          xa[u] = wi * (a < D ? Si[a] : (a == D ? 1.0 : 0.0));
-          xb[u] = b < D ? Si[b] : (b == D ? 1.0 : 0.0);
-        }
+        for (int u = 0; u < 4; ++u) xr[u] = r0 + u < NX ? f.xtwr[(size_t)(r0 + u) * D + e] : 0.0;
 #pragma unroll
-        for (int u = 0; u < 8; ++u)
+        for (int v = 0; v < 4; ++v) uc[v] = c0 + v < keff ? X[e * PXK + c0 + v] : 0.0;
 #pragma unroll
-          for (int v = 0; v < 8; ++v) acc[u][v] += xa[u] * xb[v];
+        for (int u = 0; u < 4; ++u)
+#pragma unroll
+          for (int v = 0; v < 4; ++v) acc[u][v] += xr[u] * uc[v];
       }
 #pragma unroll
-      for (int u = 0; u < 8; ++u)
+      for (int u = 0; u < 4; ++u)
 #pragma unroll
-        for (int v = 0; v < 8; ++v) {
-          const int a = a0 + u, b = b0 + v;
-          if (a < NX && b < NX) Xn[a * PX + b] = acc[u][v] + ((a == b && a < D) ? lambda : 0.0);
-        }
+        for (int v = 0; v < 4; ++v)
+          if (r0 + u < NX && c0 + v < keff) f.rhs[(size_t)(r0 + u) * kmax + c0 + v] = acc[u][v];
     }
-  }
-  for (int idx = t; idx < NX * keff; idx += NT) {
-    const int ra = idx / keff, cc = idx % keff;
-    double s = 0.0;
-    for (int i = 0; i < m; ++i) {
-      const double xa = ra < D ? f.S[(size_t)i * D + ra] : 1.0;
-      s += f.w[i] * xa * f.Y[(size_t)i * kmax + cc];
-    }
-    f.rhs[(size_t)ra * kmax + cc] = s;
   }
   __syncthreads();
-  // ---- Cholesky (lower, right-looking)
+  const bool rhs_lds = NP + NX * keff <= BIG;
+  double* rhs = rhs_lds ? big + NP : f.rhs;
+  const int rstride = rhs_lds ? keff : kmax;
+  // ---- packed ridge matrix P(i, j) = i (i + 1) / 2 + j, j <= i
+  for (int idx = t; idx < NX * NX; idx += NT) {
+    const int i = idx / NX, j = idx % NX;
+    if (j <= i) big[i * (i + 1) / 2 + j] = f.gram[idx];
+  }
+  if (rhs_lds)
+    for (int idx = t; idx < NX * keff; idx += NT) rhs[idx] = f.rhs[(size_t)(idx / keff) * kmax + idx % keff];
+  __syncthreads();
+  // ---- Cholesky, right-looking, one barrier per column: the trailing update
+  // uses the unscaled column j and 1/d_j; column j is scaled in the next step,
+  // when it is no longer read.
+  double dprev = 1.0;
   for (int j = 0; j < NX; ++j) {
-    if (t == 0) {
-      const double dj = Xn[j * PX + j];
-      Xn[j * PX + j] = sqrt(dj > 0.0 ? dj : 1e-300);
+    double dj = big[j * (j + 1) / 2 + j];
+    dj = dj > 0.0 ? dj : 1e-300;
+    const double rd = 1.0 / dj;
+    if (j > 0) {
+      const double sc = 1.0 / sqrt(dprev);
+      for (int i = j + t; i < NX; i += NT) big[i * (i + 1) / 2 + (j - 1)] *= sc;
+      if (t == 0) big[(j - 1) * j / 2 + (j - 1)] = sqrt(dprev);
     }
-    __syncthreads();
-    const double ljj = Xn[j * PX + j];
-    for (int i = j + 1 + t; i < NX; i += NT) Xn[i * PX + j] /= ljj;
-    __syncthreads();
     const int L = NX - j - 1;
     for (int idx = t; idx < L * L; idx += NT) {
       const int i = j + 1 + idx / L, l = j + 1 + idx % L;
-      if (l <= i) Xn[i * PX + l] -= Xn[i * PX + j] * Xn[l * PX + j];
+      if (l <= i) big[i * (i + 1) / 2 + l] -= big[i * (i + 1) / 2 + j] * big[l * (l + 1) / 2 + j] * rd;
     }
+    dprev = dj;
     __syncthreads();
   }
-  // ---- forward then backward substitution, parallel over right-hand sides
-  for (int i = 0; i < NX; ++i) {
-    const double lii = Xn[i * PX + i];
-    for (int cc = t; cc < keff; cc += NT) f.rhs[(size_t)i * kmax + cc] /= lii;
-    __syncthreads();
-    for (int idx = t; idx < (NX - i - 1) * keff; idx += NT) {
-      const int l = i + 1 + idx / keff, cc = idx % keff;
-      f.rhs[(size_t)l * kmax + cc] -= Xn[l * PX + i] * f.rhs[(size_t)i * kmax + cc];
+  if (t == 0) big[(NX - 1) * NX / 2 + (NX - 1)] = sqrt(dprev);
+  __syncthreads();
+  // ---- L y = b, then L^T x = y: four lanes per right-hand-side column, each
+  // column handled by one wave, so only wave-level ordering is needed
+  {
+    const int lane = t & 63, w = t >> 6;
+    const int part = lane & 3;
+    for (int cb = 0; cb < keff; cb += 64) {
+      const int cc = cb + 16 * w + (lane >> 2);
+      const bool on = cc < keff;
+      for (int i = 0; i < NX; ++i) {
+        double s = 0.0;
+        if (on)
+          for (int l = part; l < i; l += 4) s += big[i * (i + 1) / 2 + l] * rhs[(size_t)l * rstride + cc];
+        s += __shfl_xor(s, 1);
+        s += __shfl_xor(s, 2);
+        if (on && part == 0)
+          rhs[(size_t)i * rstride + cc] = (rhs[(size_t)i * rstride + cc] - s) / big[i * (i + 1) / 2 + i];
+        if (rhs_lds) __builtin_amdgcn_wave_barrier();
+        else __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "workgroup");
+      }
+      for (int i = NX - 1; i >= 0; --i) {
+        double s = 0.0;
+        if (on)
+          for (int l = i + 1 + part; l < NX; l += 4) s += big[l * (l + 1) / 2 + i] * rhs[(size_t)l * rstride + cc];
+        s += __shfl_xor(s, 1);
+        s += __shfl_xor(s, 2);
+        if (on && part == 0)
+          rhs[(size_t)i * rstride + cc] = (rhs[(size_t)i * rstride + cc] - s) / big[i * (i + 1) / 2 + i];
+        if (rhs_lds) __builtin_amdgcn_wave_barrier();
+        else __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "workgroup");
+      }
     }
-    __syncthreads();
   }
-  for (int i = NX - 1; i >= 0; --i) {
-    const double lii = Xn[i * PX + i];
-    for (int cc = t; cc < keff; cc += NT) f.rhs[(size_t)i * kmax + cc] /= lii;
-    __syncthreads();
-    for (int idx = t; idx < i * keff; idx += NT) {
-      const int l = idx / keff, cc = idx % keff;
-      f.rhs[(size_t)l * kmax + cc] -= Xn[i * PX + l] * f.rhs[(size_t)i * kmax + cc];
-    }
-    __syncthreads();
-  }
+  __syncthreads();
   for (int idx = t; idx < NX * keff; idx += NT) {
     const int ra = idx / keff, cc = idx % keff;
-    Th[(size_t)ra * kmax + cc] = (float)f.rhs[(size_t)ra * kmax + cc];
+    Th[(size_t)ra * kmax + cc] = (float)rhs[(size_t)ra * rstride + cc];
   }
   if (t == 0) rank_eff[h] = keff;
 }
@@ -492,10 +560,15 @@ size_t fit_ws_per_head(const Dims& d) {
 hipError_t launch_fit(const Dims& d, const float* S_out, const float* O_probe, float* U,
                       float* Theta, int32_t* rank_eff, char* fit_ws, hipStream_t st) {
   double* scratch = reinterpret_cast<double*>(fit_ws);
-#define SPR_FIT(DD)                                                                       \
-  k_fit<DD><<<d.H, kFitThreads, 0, st>>>(S_out, O_probe, d.N, d.m, d.k, d.lam, U, Theta, \
-                                         rank_eff, scratch)
-  if (d.D == 128) SPR_FIT(128); else SPR_FIT(64);
+  const dim3 pgrid(d.H, (d.D + 1 + 7) / 8);
+#define SPR_FIT(DD)                                                                         \
+  do {                                                                                      \
+    k_fit_prep<DD><<<pgrid, kFitThreads, 0, st>>>(S_out, O_probe, d.N, d.m, d.k, d.lam,     \
+                                                   scratch);                                \
+    k_fit<DD><<<d.H, kFitThreads, 0, st>>>(d.m, d.k, U, Theta, rank_eff, scratch);          \
+  } while (0)
+  if (d.D == 128) SPR_FIT(128);
+  else SPR_FIT(64);
 #undef SPR_FIT
   return hipGetLastError();
 }
