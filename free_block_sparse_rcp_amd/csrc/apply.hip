@@ -153,8 +153,10 @@ __global__ __launch_bounds__(256) void k_apply(const float* S, const int32_t* qu
 // O^T = W^T S^T as v_mfma_f32_32x32x16_bf16 with S split into hi + lo too
 // (hi*hi + lo*hi + hi*lo; the dropped lo*lo term is ~2^-16 relative), so the
 // correction keeps near-fp32 accuracy. Each wave takes 32 query positions at a
-// time; s is re-read in the output layout for the final sum.
+// time; s is re-read in the output layout for the final sum, and the output
+// tile is staged in LDS so that every row (token order) is written whole.
 constexpr int kApplyTilesPerWg = 128;  // 32-row tiles per workgroup
+constexpr int kApplyWaves = 8;
 
 // grid (H), block 256. wt: [H][2][d][d] bf16 (hi, lo) of W^T; bias: [H][d].
 // Entry (e, a) of W^T (a = d is the bias) accumulates in LDS over chunks of
@@ -212,22 +214,24 @@ __global__ __launch_bounds__(256) void k_apply_weights(const float* U, const flo
 }
 
 template <int D>
-__global__ __launch_bounds__(256) void k_apply_mfma(const float* S, const int32_t* query_perm,
+__global__ __launch_bounds__(kApplyWaves * 64) void k_apply_mfma(const float* S, const int32_t* query_perm,
                                                     const float* O_probe, const uint16_t* wt,
                                                     const float* bias, int N, int m,
                                                     int wg_per_head, uint16_t* O) {
   constexpr int WP = D + 8;            // bf16 elements per LDS row of W^T (conflict-free b128 reads)
   constexpr int NKK = D / 16, NDT = D / 32;
   constexpr int CPR = D / 8;           // 16-byte chunks per row
+  constexpr int OP = D + 8;            // bf16 elements per staged output row
   __shared__ __attribute__((aligned(16))) uint16_t wt_hi[D * WP];
   __shared__ __attribute__((aligned(16))) uint16_t wt_lo[D * WP];
   __shared__ float wbias[D];
+  __shared__ __attribute__((aligned(16))) uint16_t ostage[kApplyWaves][32 * OP];
   const int h = blockIdx.x / wg_per_head, part = blockIdx.x % wg_per_head;
   const int t = threadIdx.x, lane = t & 63, hl = lane >> 5, ql = lane & 31;
   const int w = __builtin_amdgcn_readfirstlane(t >> 6);
   {
     const uint16_t* src = wt + (size_t)h * 2 * D * D;
-    for (int i = t; i < 2 * D * CPR; i += 256) {
+    for (int i = t; i < 2 * D * CPR; i += kApplyWaves * 64) {
       const int arr = i / (D * CPR), rem = i % (D * CPR);
       const int r = rem / CPR, c = rem % CPR;
       const u32x4 v = *reinterpret_cast<const u32x4*>(src + (size_t)arr * D * D + r * D + 8 * c);
@@ -241,7 +245,8 @@ __global__ __launch_bounds__(256) void k_apply_mfma(const float* S, const int32_
   const int t0 = part * kApplyTilesPerWg, t1 = min(ntile, t0 + kApplyTilesPerWg);
   const float* Sh = S + (size_t)h * N * D;
   uint16_t* Oh = O + (size_t)h * N * D;
-  for (int tile = t0 + w; tile < t1; tile += 4) {
+  uint16_t* stg = ostage[w];
+  for (int tile = t0 + w; tile < t1; tile += kApplyWaves) {
     const int pos = tile * 32 + ql;
     const bool valid = pos < N;
     const float* srow = Sh + (size_t)(valid ? pos : 0) * D;
@@ -263,7 +268,6 @@ __global__ __launch_bounds__(256) void k_apply_mfma(const float* S, const int32_
         slo[kk][4 + u] = static_cast<__bf16>(x1[u] - static_cast<float>(h1));
       }
     }
-    const int tok = valid ? clamp_idx(query_perm[(size_t)h * N + pos], N) : 0;
     const int pi = valid ? probe_index(pos, N, m) : -1;
     // W fragments are re-read from LDS every tile: kept opaque so that the
     // compiler does not hoist all of them into registers (occupancy)
@@ -301,9 +305,24 @@ __global__ __launch_bounds__(256) void k_apply_mfma(const float* S, const int32_
         const bf16x2 b0 = __builtin_convertvector(f0, bf16x2);
         const bf16x2 b1 = __builtin_convertvector(f1, bf16x2);
         const bf16x4 bv = {b0[0], b0[1], b1[0], b1[1]};
-        *reinterpret_cast<bf16x4*>(Oh + (size_t)tok * D + d0) = bv;
+        *reinterpret_cast<bf16x4*>(stg + ql * OP + d0) = bv;
       }
     }
+    // whole output rows from the wave's staged tile: 16-byte pieces, one row per D/8 lanes
+    __builtin_amdgcn_wave_barrier();
+    constexpr int LPR = D / 8;          // lanes per row
+    constexpr int RPI = 64 / LPR;       // rows per store instruction
+#pragma unroll
+    for (int r0 = 0; r0 < 32; r0 += RPI) {
+      const int r = r0 + lane / LPR, c = lane % LPR;
+      const int rpos = tile * 32 + r;
+      if (rpos < N) {
+        const int rtok = clamp_idx(query_perm[(size_t)h * N + rpos], N);
+        const u32x4 v = *reinterpret_cast<const u32x4*>(stg + r * OP + 8 * c);
+        *reinterpret_cast<u32x4*>(Oh + (size_t)rtok * D + 8 * c) = v;
+      }
+    }
+    __builtin_amdgcn_wave_barrier();
   }
 }
 
@@ -318,11 +337,11 @@ hipError_t launch_apply(const Dims& d, const float* S_out, const int32_t* query_
     uint16_t* Ob = static_cast<uint16_t*>(O);
     if (d.D == 128) {
       k_apply_weights<128><<<d.H, 256, 0, st>>>(U, Theta, rank_eff, d.k, wt, bias);
-      k_apply_mfma<128><<<d.H * wgph, 256, 0, st>>>(S_out, query_perm, O_probe, wt, bias, d.N,
+      k_apply_mfma<128><<<d.H * wgph, kApplyWaves * 64, 0, st>>>(S_out, query_perm, O_probe, wt, bias, d.N,
                                                     d.m, wgph, Ob);
     } else {
       k_apply_weights<64><<<d.H, 256, 0, st>>>(U, Theta, rank_eff, d.k, wt, bias);
-      k_apply_mfma<64><<<d.H * wgph, 256, 0, st>>>(S_out, query_perm, O_probe, wt, bias, d.N,
+      k_apply_mfma<64><<<d.H * wgph, kApplyWaves * 64, 0, st>>>(S_out, query_perm, O_probe, wt, bias, d.N,
                                                    d.m, wgph, Ob);
     }
     return hipGetLastError();

@@ -231,21 +231,19 @@ __global__ __launch_bounds__(kFitThreads) void k_fit(int m, int kmax, float* U_o
     const double alpha = -copysign(sqrt(x0 * x0 + sig2), x0);
     const double v0 = x0 - alpha;
     const double bk = 2.0 / (v0 * v0 + sig2);
-    // p = beta A22 v with v_0 = v0, v_j = A[k+1+j][k]; two threads per row
-    const int i = t >> 1, half = t & 1;
+    // p = beta A22 v with v_0 = v0, v_j = A[k+1+j][k]; one thread per row, so
+    // every step of the sum reads one row of A22 across the wave
+    const int i = t;
     double s = 0.0;
     if (i < L) {
-      for (int j = half; j < L; j += 2) {
-        const double vj = j == 0 ? v0 : A[(k + 1 + j) * PA + k];
-        s += A[(k + 1 + j) * PA + (k + 1 + i)] * vj;
-      }
+      s = A[(k + 1) * PA + (k + 1 + i)] * v0;
+      for (int j = 1; j < L; ++j) s += A[(k + 1 + j) * PA + (k + 1 + i)] * A[(k + 1 + j) * PA + k];
     }
-    s += __shfl_xor(s, 1);
     const double p_i = bk * s;
     const double v_i = i == 0 ? v0 : (i < L ? A[(k + 1 + i) * PA + k] : 0.0);
-    const double vp = (half == 0 && i < L) ? v_i * p_i : 0.0;
+    const double vp = i < L ? v_i * p_i : 0.0;
     const double K = 0.5 * bk * wg_sum1(vp, red2, slot);
-    if (half == 0 && i < L) {
+    if (i < L) {
       pv[i] = p_i - K * v_i;   // q
       vv[i] = v_i;
     }
