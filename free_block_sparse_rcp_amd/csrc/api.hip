@@ -68,7 +68,6 @@ RouteWs route_ws(const Dims& d) {
   L.counts = b.take(H * nbk * d.nchunk * 4);
   L.totals = b.take(H * nbk * 4);
   L.starts = b.take(H * nbk * 4);
-  L.qbar = b.take(H * nb * d.D * 4);
   L.sigma = b.take(H * nb * G * 4);
   L.sel = b.take(H * nb * G * 4);
   L.selcnt = b.take(H * nb * 4);

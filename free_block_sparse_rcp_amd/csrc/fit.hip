@@ -231,19 +231,35 @@ __global__ __launch_bounds__(kFitThreads) void k_fit(int m, int kmax, float* U_o
     const double alpha = -copysign(sqrt(x0 * x0 + sig2), x0);
     const double v0 = x0 - alpha;
     const double bk = 2.0 / (v0 * v0 + sig2);
-    // p = beta A22 v with v_0 = v0, v_j = A[k+1+j][k]; one thread per row, so
-    // every step of the sum reads one row of A22 across the wave
-    const int i = t;
+    // p = beta A22 v with v_0 = v0, v_j = A[k+1+j][k]. Row i of the product is
+    // split between two waves by halves of j; every step of a partial sum reads
+    // one row of A22 across the wave. v^T p comes from the partials directly.
+    const int i = t & (D - 1), half = t / D;
+    const int jm = (L + 1) / 2;
     double s = 0.0;
-    if (i < L) {
-      s = A[(k + 1) * PA + (k + 1 + i)] * v0;
-      for (int j = 1; j < L; ++j) s += A[(k + 1 + j) * PA + (k + 1 + i)] * A[(k + 1 + j) * PA + k];
+    if (i < L && half < 2) {
+      const int j0 = half * jm, j1 = half == 0 ? jm : L;
+      // four independent partial sums keep several LDS reads in flight
+      double s4[4] = {0.0, 0.0, 0.0, 0.0};
+      int j = j0;
+      if (j == 0) {
+        s4[0] = A[(k + 1) * PA + (k + 1 + i)] * v0;
+        j = 1;
+      }
+      for (; j + 3 < j1; j += 4) {
+#pragma unroll
+        for (int u = 0; u < 4; ++u)
+          s4[u] += A[(k + 1 + j + u) * PA + (k + 1 + i)] * A[(k + 1 + j + u) * PA + k];
+      }
+      for (; j < j1; ++j) s4[0] += A[(k + 1 + j) * PA + (k + 1 + i)] * A[(k + 1 + j) * PA + k];
+      s = (s4[0] + s4[1]) + (s4[2] + s4[3]);
     }
-    const double p_i = bk * s;
     const double v_i = i == 0 ? v0 : (i < L ? A[(k + 1 + i) * PA + k] : 0.0);
-    const double vp = i < L ? v_i * p_i : 0.0;
+    if (half == 1 && i < L) pv[i] = s;   // partial of the second half
+    const double vp = (i < L && half < 2) ? v_i * bk * s : 0.0;
     const double K = 0.5 * bk * wg_sum1(vp, red2, slot);
-    if (i < L) {
+    if (half == 0 && i < L) {
+      const double p_i = bk * (s + pv[i]);
       pv[i] = p_i - K * v_i;   // q
       vv[i] = v_i;
     }
@@ -253,9 +269,10 @@ __global__ __launch_bounds__(kFitThreads) void k_fit(int m, int kmax, float* U_o
       A[(k + 1) * PA + k] = v0;   // x0 and the column are no longer read in this step
     }
     __syncthreads();
-    for (int idx = t; idx < L * L; idx += NT) {
-      const int i2 = idx / L, j2 = idx % L;
-      A[(k + 1 + i2) * PA + (k + 1 + j2)] -= vv[i2] * pv[j2] + pv[i2] * vv[j2];
+    for (int i2 = t >> 5; i2 < L; i2 += NT / 32) {
+      const double vi2 = vv[i2], qi2 = pv[i2];
+      double* row = A + (k + 1 + i2) * PA + (k + 1);
+      for (int j2 = t & 31; j2 < L; j2 += 32) row[j2] -= vi2 * pv[j2] + qi2 * vv[j2];
     }
     __syncthreads();
   }
@@ -426,8 +443,16 @@ __global__ __launch_bounds__(kFitThreads) void k_fit(int m, int kmax, float* U_o
     for (int c0 = 0; c0 < keff; c0 += NT / 8) {
       const int cc = c0 + t / 8, sub = t % 8;
       double sacc = 0.0;
-      if (cc < keff && bk != 0.0)
-        for (int i = sub; i < L; i += 8) sacc += vc[i] * X[(k + 1 + i) * PXK + cc];
+      if (cc < keff && bk != 0.0) {
+        double s2[2] = {0.0, 0.0};
+        int i = sub;
+        for (; i + 8 < L; i += 16) {
+          s2[0] += vc[i] * X[(k + 1 + i) * PXK + cc];
+          s2[1] += vc[i + 8] * X[(k + 9 + i) * PXK + cc];
+        }
+        for (; i < L; i += 8) s2[0] += vc[i] * X[(k + 1 + i) * PXK + cc];
+        sacc = s2[0] + s2[1];
+      }
       sacc += __shfl_xor(sacc, 1);
       sacc += __shfl_xor(sacc, 2);
       sacc += __shfl_xor(sacc, 4);
@@ -435,9 +460,9 @@ __global__ __launch_bounds__(kFitThreads) void k_fit(int m, int kmax, float* U_o
     }
     __syncthreads();
     if (bk != 0.0) {
-      for (int idx = t; idx < L * keff; idx += NT) {
-        const int i = idx / keff, cc = idx % keff;
-        X[(k + 1 + i) * PXK + cc] -= dots[cc] * vc[i];
+      for (int cc = t & 31; cc < keff; cc += 32) {
+        const double dc = dots[cc];
+        for (int i = t >> 5; i < L; i += NT / 32) X[(k + 1 + i) * PXK + cc] -= dc * vc[i];
       }
     }
     if (k > 0 && t < L + 1) vnx[t] = nxt;
@@ -501,10 +526,10 @@ __global__ __launch_bounds__(kFitThreads) void k_fit(int m, int kmax, float* U_o
       for (int i = j + t; i < NX; i += NT) big[i * (i + 1) / 2 + (j - 1)] *= sc;
       if (t == 0) big[(j - 1) * j / 2 + (j - 1)] = sqrt(dprev);
     }
-    const int L = NX - j - 1;
-    for (int idx = t; idx < L * L; idx += NT) {
-      const int i = j + 1 + idx / L, l = j + 1 + idx % L;
-      if (l <= i) big[i * (i + 1) / 2 + l] -= big[i * (i + 1) / 2 + j] * big[l * (l + 1) / 2 + j] * rd;
+    for (int i = j + 1 + (t >> 5); i < NX; i += NT / 32) {
+      double* row = big + i * (i + 1) / 2;
+      const double lij = row[j] * rd;
+      for (int l = j + 1 + (t & 31); l <= i; l += 32) row[l] -= lij * big[l * (l + 1) / 2 + j];
     }
     dprev = dj;
     __syncthreads();
@@ -521,8 +546,17 @@ __global__ __launch_bounds__(kFitThreads) void k_fit(int m, int kmax, float* U_o
       const bool on = cc < keff;
       for (int i = 0; i < NX; ++i) {
         double s = 0.0;
-        if (on)
-          for (int l = part; l < i; l += 4) s += big[i * (i + 1) / 2 + l] * rhs[(size_t)l * rstride + cc];
+        if (on) {
+          const double* row = big + i * (i + 1) / 2;
+          double s2[2] = {0.0, 0.0};
+          int l = part;
+          for (; l + 4 < i; l += 8) {
+            s2[0] += row[l] * rhs[(size_t)l * rstride + cc];
+            s2[1] += row[l + 4] * rhs[(size_t)(l + 4) * rstride + cc];
+          }
+          for (; l < i; l += 4) s2[0] += row[l] * rhs[(size_t)l * rstride + cc];
+          s = s2[0] + s2[1];
+        }
         s += __shfl_xor(s, 1);
         s += __shfl_xor(s, 2);
         if (on && part == 0)
@@ -532,8 +566,16 @@ __global__ __launch_bounds__(kFitThreads) void k_fit(int m, int kmax, float* U_o
       }
       for (int i = NX - 1; i >= 0; --i) {
         double s = 0.0;
-        if (on)
-          for (int l = i + 1 + part; l < NX; l += 4) s += big[l * (l + 1) / 2 + i] * rhs[(size_t)l * rstride + cc];
+        if (on) {
+          double s2[2] = {0.0, 0.0};
+          int l = i + 1 + part;
+          for (; l + 4 < NX; l += 8) {
+            s2[0] += big[l * (l + 1) / 2 + i] * rhs[(size_t)l * rstride + cc];
+            s2[1] += big[(l + 4) * (l + 5) / 2 + i] * rhs[(size_t)(l + 4) * rstride + cc];
+          }
+          for (; l < NX; l += 4) s2[0] += big[l * (l + 1) / 2 + i] * rhs[(size_t)l * rstride + cc];
+          s = s2[0] + s2[1];
+        }
         s += __shfl_xor(s, 1);
         s += __shfl_xor(s, 2);
         if (on && part == 0)

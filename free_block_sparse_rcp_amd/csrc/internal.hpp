@@ -28,7 +28,7 @@ struct PartitionWs {
   size_t M, P, Phl, bvec, counts, totals, starts, partial, best, end;
 };
 struct RouteWs {
-  size_t keysA, keysB, valsA, valsB, counts, totals, starts, qbar, sigma, sel, selcnt, blkkeys,
+  size_t keysA, keysB, valsA, valsB, counts, totals, starts, sigma, sel, selcnt, blkkeys,
       chl, best, end;
 };
 struct ProbeWs {

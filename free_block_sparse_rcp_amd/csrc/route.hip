@@ -30,43 +30,97 @@ __global__ void k_copy_perm(const int32_t* perm, int N, int32_t* out) {
   if (i < N) out[(size_t)blockIdx.y * N + i] = clamp_idx(perm[i], N);
 }
 
-// qbar_b = mean of the block's queries (fixed order). grid (nb, H), block D.
-template <bool BF16, int D>
-__global__ void k_block_means(const void* Qv, const int32_t* query_perm, int N, int BQ,
-                              float* qbar) {
-  using E = Elt<BF16>;
-  const int b = blockIdx.x, h = blockIdx.y, e = threadIdx.x;
-  const typename E::T* Q = static_cast<const typename E::T*>(Qv) + (size_t)h * N * D;
-  const int p0 = b * BQ, n = min(N, p0 + BQ) - p0;
-  float s = 0.f;
-  for (int i = 0; i < n; ++i) s += E::ld(Q, (size_t)clamp_idx(query_perm[(size_t)h * N + p0 + i], N) * D + e);
-  qbar[((size_t)h * gridDim.x + b) * D + e] = s / (float)n;
-}
-
+// Mean query of each block and its scores against every group:
 // sigma[b,g] = tau * qbar_b . kbar_g over non-empty groups (-inf for empty).
-// grid (nb, H), block 256.
-template <int D>
-__global__ __launch_bounds__(256) void k_block_scores(const float* qbar, const float* kbar,
-                                                      const float* scale, const int32_t* group_off,
-                                                      int G, float* sigma, float* dbg) {
-  const int b = blockIdx.x, h = blockIdx.y, nb = gridDim.x;
-  __shared__ float qb[D];
-  for (int e = threadIdx.x; e < D; e += 256) qb[e] = qbar[((size_t)h * nb + b) * D + e];
-  __syncthreads();
+// A workgroup takes kRsBlocks consecutive blocks: their query rows are
+// gathered with 16-byte loads and summed per column (row groups combined in a
+// fixed order); the centroids are then staged in LDS kRsGroups rows at a time.
+// grid (ceil(nb / kRsBlocks), H), block 256.
+constexpr int kRsBlocks = 16;
+constexpr int kRsGroups = 64;
+
+template <bool BF16, int D>
+__global__ __launch_bounds__(256) void k_route_scores(const void* Qv, const int32_t* query_perm,
+                                                      const float* kbar, const float* scale,
+                                                      const int32_t* group_off, int N, int BQ,
+                                                      int nb, int G, float* sigma, float* dbg) {
+  using T = typename Elt<BF16>::T;
+  constexpr int ROWB = D * (int)sizeof(T);
+  constexpr int CPR = ROWB / 16;             // 16-byte chunks per row
+  constexpr int EPC = 16 / (int)sizeof(T);   // elements per chunk
+  constexpr int RG = 256 / CPR;              // row groups
+  constexpr int KP = D + 1;
+  constexpr int BPT = kRsBlocks / 4;         // blocks per thread in the scores
+  __shared__ float qb[kRsBlocks][D];
+  __shared__ float part[RG][D];
+  __shared__ float kt[kRsGroups * KP];
+  const int h = blockIdx.y, b0 = blockIdx.x * kRsBlocks, t = threadIdx.x;
+  const char* Q = static_cast<const char*>(Qv) + (size_t)h * N * ROWB;
+  const int32_t* qp = query_perm + (size_t)h * N;
+  const int nblk = min(kRsBlocks, nb - b0);
+  {
+    const int c = t % CPR, rg = t / CPR;
+    for (int j = 0; j < nblk; ++j) {
+      const int p0 = (b0 + j) * BQ, n = min(N, p0 + BQ) - p0;
+      float acc[EPC];
+#pragma unroll
+      for (int u = 0; u < EPC; ++u) acc[u] = 0.f;
+      for (int r = rg; r < n; r += RG) {
+        const int tok = clamp_idx(qp[p0 + r], N);
+        const u32x4 raw = *reinterpret_cast<const u32x4*>(Q + (size_t)tok * ROWB + c * 16);
+        if (BF16) {
+#pragma unroll
+          for (int u = 0; u < 4; ++u) {
+            acc[2 * u] += __uint_as_float(raw[u] << 16);
+            acc[2 * u + 1] += __uint_as_float(raw[u] & 0xffff0000u);
+          }
+        } else {
+#pragma unroll
+          for (int u = 0; u < 4; ++u) acc[u] += __uint_as_float(raw[u]);
+        }
+      }
+#pragma unroll
+      for (int u = 0; u < EPC; ++u) part[rg][c * EPC + u] = acc[u];
+      __syncthreads();
+      if (t < D) {
+        float s = 0.f;
+        for (int i = 0; i < RG; ++i) s += part[i][t];
+        qb[j][t] = s / (float)n;
+      }
+      __syncthreads();
+    }
+  }
   const float tau = scale[h];
   const int32_t* off = group_off + (size_t)h * (G + 1);
-  for (int g = threadIdx.x; g < G; g += 256) {
-    float s;
-    if (off[g + 1] > off[g]) {
-      const float* kg = kbar + ((size_t)h * G + g) * D;
-      float acc = 0.f;
-      for (int e = 0; e < D; ++e) acc = fmaf(qb[e], kg[e], acc);
-      s = tau * acc;
-    } else {
-      s = -__builtin_inff();
+  const int gl = t % kRsGroups, bq = t / kRsGroups;
+  for (int g0 = 0; g0 < G; g0 += kRsGroups) {
+    __syncthreads();
+    for (int i = t; i < kRsGroups * D; i += 256) {
+      const int row = i / D, e = i % D, g = g0 + row;
+      kt[row * KP + e] = g < G ? kbar[((size_t)h * G + g) * D + e] : 0.f;
     }
-    sigma[((size_t)h * nb + b) * G + g] = s;
-    if (dbg) dbg[((size_t)h * nb + b) * G + g] = s;
+    __syncthreads();
+    float acc[BPT];
+#pragma unroll
+    for (int u = 0; u < BPT; ++u) acc[u] = 0.f;
+    for (int e = 0; e < D; ++e) {
+      const float kv = kt[gl * KP + e];
+#pragma unroll
+      for (int u = 0; u < BPT; ++u) acc[u] = fmaf(qb[bq + 4 * u][e], kv, acc[u]);
+    }
+    const int g = g0 + gl;
+    if (g < G) {
+      const bool ne = off[g + 1] > off[g];
+#pragma unroll
+      for (int u = 0; u < BPT; ++u) {
+        const int j = bq + 4 * u;
+        if (j < nblk) {
+          const float sc = ne ? tau * acc[u] : -__builtin_inff();
+          sigma[((size_t)h * nb + b0 + j) * G + g] = sc;
+          if (dbg) dbg[((size_t)h * nb + b0 + j) * G + g] = sc;
+        }
+      }
+    }
   }
 }
 
@@ -225,7 +279,6 @@ hipError_t launch_route(const Dims& d, const void* Q, const float* scale, const 
   int32_t* counts = reinterpret_cast<int32_t*>(ws + L.counts);
   int32_t* totals = reinterpret_cast<int32_t*>(ws + L.totals);
   int32_t* starts = reinterpret_cast<int32_t*>(ws + L.starts);
-  float* qbar = reinterpret_cast<float*>(ws + L.qbar);
   float* sigma = reinterpret_cast<float*>(ws + L.sigma);
   int32_t* sel = reinterpret_cast<int32_t*>(ws + L.sel);
   int32_t* selcnt = reinterpret_cast<int32_t*>(ws + L.selcnt);
@@ -277,18 +330,16 @@ hipError_t launch_route(const Dims& d, const void* Q, const float* scale, const 
     SPR_CHECK_LAUNCH();
   }
   const dim3 blocks(d.nb, d.H);
-#define SPR_MEANS(B, DD) k_block_means<B, DD><<<blocks, DD, 0, st>>>(Q, query_perm, d.N, d.BQ, qbar)
+  const dim3 sblocks((d.nb + kRsBlocks - 1) / kRsBlocks, d.H);
+#define SPR_RS(B, DD)                                                                          \
+  k_route_scores<B, DD><<<sblocks, 256, 0, st>>>(Q, query_perm, kbar, scale, group_off, d.N,    \
+                                                  d.BQ, d.nb, d.G, sigma, dbg_sigma)
   if (d.bf16) {
-    if (d.D == 128) SPR_MEANS(true, 128); else SPR_MEANS(true, 64);
+    if (d.D == 128) SPR_RS(true, 128); else SPR_RS(true, 64);
   } else {
-    if (d.D == 128) SPR_MEANS(false, 128); else SPR_MEANS(false, 64);
+    if (d.D == 128) SPR_RS(false, 128); else SPR_RS(false, 64);
   }
-#undef SPR_MEANS
-  SPR_CHECK_LAUNCH();
-  if (d.D == 128)
-    k_block_scores<128><<<blocks, 256, 0, st>>>(qbar, kbar, scale, group_off, d.G, sigma, dbg_sigma);
-  else
-    k_block_scores<64><<<blocks, 256, 0, st>>>(qbar, kbar, scale, group_off, d.G, sigma, dbg_sigma);
+#undef SPR_RS
   SPR_CHECK_LAUNCH();
   k_block_select<<<blocks, 256, 0, st>>>(sigma, group_off, d.G, d.kappa, sel, selcnt, blkkeys);
   SPR_CHECK_LAUNCH();
