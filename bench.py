@@ -168,6 +168,10 @@ def main():
                     help="oracle samples every n-th query block (0: chosen by workload size)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-dense", action="store_true")
+    ap.add_argument("--overlap", action="store_true",
+                    help="attend the blocks holding probe rows first and run the probe fit on a "
+                         "second stream while the other blocks are attended (default: the five "
+                         "stages back to back on one stream)")
     ap.add_argument("--calibration-copy-mib", type=int, default=0,
                     help="also run one plain device copy of this many MiB (a known-size "
                          "kernel for scaling the FETCH_SIZE / WRITE_SIZE counters)")
@@ -211,25 +215,10 @@ def main():
 
     stages = ("partition", "route", "attend", "probe_fit", "apply")
 
+    overlap = args.overlap
+
     def one_call(ev=None):
-        if ev is not None:
-            ev[0].record()
-        binding.partition(p, Q, K, V, scale, idx.get("sample_idx"), idx.get("init_idx"), b,
-                          rand_key_perm=idx.get("rand_key_perm"))
-        if ev is not None:
-            ev[1].record()
-        binding.route(p, Q, scale, b, rand_query_perm=idx.get("rand_query_perm"))
-        if ev is not None:
-            ev[2].record()
-        binding.attend(p, Q, scale, b)
-        if ev is not None:
-            ev[3].record()
-        binding.probe_fit(p, Q, scale, b)
-        if ev is not None:
-            ev[4].record()
-        binding.apply(p, b)
-        if ev is not None:
-            ev[5].record()
+        op.run(Q, K, V, scale, idx, overlap=overlap, events=ev)
 
     if args.calibration_copy_mib:
         n = args.calibration_copy_mib * (1 << 20) // 4
@@ -246,18 +235,33 @@ def main():
             binding.dense_attention(p, Q, K, V, scale, O_dense, lse_dense)
     torch.cuda.synchronize()
 
-    # timed region: K whole calls, events between stages (on the library's stream)
-    log(f"[bench] timing {args.steps} calls")
-    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(6)] for _ in range(args.steps)]
+    # timed region: K whole calls, events between stages (on the library's streams)
+    log(f"[bench] timing {args.steps} calls ({'overlapped' if overlap else 'serial'})")
+    evs = [dict() for _ in range(args.steps)]
     torch.cuda.synchronize()
     w0 = time.perf_counter()
     for s in range(args.steps):
         one_call(evs[s])
     torch.cuda.synchronize()
     wall = time.perf_counter() - w0
-    stage_ms = {n: float(np.mean([evs[s][i].elapsed_time(evs[s][i + 1]) for s in range(args.steps)]))
-                for i, n in enumerate(stages)}
-    call_ms = float(np.mean([evs[s][0].elapsed_time(evs[s][5]) for s in range(args.steps)]))
+
+    def span(e, a, b):
+        return e[a].elapsed_time(e[b])
+
+    if overlap:
+        parts = {"partition": ("start", "partition"), "route": ("partition", "route"),
+                 "attend_probe_blocks": ("route", "attend_probe_blocks"),
+                 "attend_other_blocks": ("attend_probe_blocks", "attend"),
+                 "probe_fit": ("probe_fit_start", "probe_fit"), "apply": ("join", "apply")}
+    else:
+        parts = {"partition": ("start", "partition"), "route": ("partition", "route"),
+                 "attend": ("route", "attend"), "probe_fit": ("attend", "probe_fit"),
+                 "apply": ("probe_fit", "apply")}
+    stage_ms = {n: float(np.mean([span(e, a_, b_) for e in evs])) for n, (a_, b_) in parts.items()}
+    if overlap:
+        stage_ms["attend"] = stage_ms["attend_probe_blocks"] + stage_ms["attend_other_blocks"]
+    attend_launches = 2 if overlap else 1
+    call_ms = float(np.mean([span(e, "start", "apply") for e in evs]))
 
     dense_ms = None
     if not args.no_dense:
@@ -301,8 +305,9 @@ def main():
     roofline = {"bound": "mfma", "kernel": "k_attn_mfma (sparsepr_attend)",
                 "achieved": attend_tflops, "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
                 "frac": attend_tflops / PEAK_BF16_TFLOPS, "traffic": traffic,
-                "algorithmic_flops_per_launch": 4.0 * D * sparse_pairs,
-                "launch_ms": stage_ms["attend"]}
+                "algorithmic_flops_per_launch": 4.0 * D * sparse_pairs / attend_launches,
+                "launch_ms": stage_ms["attend"] / attend_launches,
+                "launches_per_call": attend_launches}
 
     cpu = None
     if not args.no_cpu_baseline:
@@ -324,6 +329,8 @@ def main():
         "speedup_vs_dense": (dense_ms / call_ms) if dense_ms else None,
         "attend_speedup_vs_dense": (dense_ms / stage_ms["attend"]) if dense_ms else None,
         "stage_ms": stage_ms, "wall_ms_per_step": wall * 1e3 / args.steps,
+        "pipeline": ("probe blocks attended first; probe fit on a second stream overlaps the "
+                     "attention of the other blocks" if overlap else "stages back to back"),
         "executed_pairs": E, "realized_density": density,
         "dense_tflops": (4.0 * D * H * float(N) ** 2 / (dense_ms * 1e-3) / 1e12) if dense_ms else None,
         "quality": quality, "roofline": roofline, "cpu_baseline": cpu,

@@ -29,7 +29,9 @@ STATUS = {0: "SPARSEPR_OK", 1: "SPARSEPR_ERR_INVALID_ARG", 2: "SPARSEPR_ERR_UNSU
 # every entry point declared in include/sparsepr.h
 EXPORTS = ("sparsepr_abi_version", "sparsepr_status_string", "sparsepr_last_error",
            "sparsepr_workspace_bytes", "sparsepr_partition", "sparsepr_route", "sparsepr_attend",
-           "sparsepr_probe_fit", "sparsepr_apply", "sparsepr_dense_attention")
+           "sparsepr_attend_subset", "sparsepr_probe_fit", "sparsepr_apply",
+           "sparsepr_dense_attention")
+BLOCKS_ALL, BLOCKS_WITH_PROBE, BLOCKS_WITHOUT_PROBE = 0, 1, 2
 
 
 class CParams(ctypes.Structure):
@@ -69,11 +71,12 @@ def load(path: Optional[str] = None) -> ctypes.CDLL:
     lib.sparsepr_partition.argtypes = [pp] + [_c_p] * 14 + [_c_p, _c_sz, _c_p]
     lib.sparsepr_route.argtypes = [pp] + [_c_p] * 13 + [_c_p, _c_sz, _c_p]
     lib.sparsepr_attend.argtypes = [pp] + [_c_p] * 10 + [_c_p]
+    lib.sparsepr_attend_subset.argtypes = [pp] + [_c_p] * 10 + [_c_i32, _c_p]
     lib.sparsepr_probe_fit.argtypes = [pp] + [_c_p] * 10 + [_c_p, _c_sz, _c_p]
     lib.sparsepr_apply.argtypes = [pp] + [_c_p] * 7 + [_c_p, _c_sz, _c_p]
     lib.sparsepr_dense_attention.argtypes = [pp] + [_c_p] * 6 + [_c_p]
-    for name in ("sparsepr_partition", "sparsepr_route", "sparsepr_attend", "sparsepr_probe_fit",
-                 "sparsepr_apply", "sparsepr_dense_attention"):
+    for name in ("sparsepr_partition", "sparsepr_route", "sparsepr_attend", "sparsepr_attend_subset",
+                 "sparsepr_probe_fit", "sparsepr_apply", "sparsepr_dense_attention"):
         getattr(lib, name).restype = _c_i32
     if lib.sparsepr_abi_version() != 1:
         raise RuntimeError("libsparsepr ABI version mismatch")
@@ -210,13 +213,15 @@ def route(p: Params, Q, scale, b: Buffers, rand_query_perm=None, dbg_coords=None
         _ptr(dbg_block_score), _ptr(b.workspace), b.workspace.numel(), _stream(Q.device)))
 
 
-def attend(p: Params, Q, scale, b: Buffers) -> None:
+def attend(p: Params, Q, scale, b: Buffers, subset: int = BLOCKS_ALL) -> None:
     lib = load()
     cp = c_params(p)
-    _check(lib.sparsepr_attend(
-        ctypes.byref(cp), _ptr(Q), _ptr(b.Kp), _ptr(b.Vp), _ptr(scale), _ptr(b.group_off),
-        _ptr(b.query_perm), _ptr(b.block_ptr), _ptr(b.block_groups), _ptr(b.S), _ptr(b.lse),
-        _stream(Q.device)))
+    args = (ctypes.byref(cp), _ptr(Q), _ptr(b.Kp), _ptr(b.Vp), _ptr(scale), _ptr(b.group_off),
+            _ptr(b.query_perm), _ptr(b.block_ptr), _ptr(b.block_groups), _ptr(b.S), _ptr(b.lse))
+    if subset == BLOCKS_ALL:
+        _check(lib.sparsepr_attend(*args, _stream(Q.device)))
+    else:
+        _check(lib.sparsepr_attend_subset(*args, subset, _stream(Q.device)))
 
 
 def probe_fit(p: Params, Q, scale, b: Buffers, K=None, V=None) -> None:
@@ -263,6 +268,7 @@ class SparsePR:
         self.p = p
         self.device = torch.device(device)
         self.buffers = alloc_buffers(p, self.device)
+        self._side = None
 
     def upload_indices(self, sample_idx=None, init_idx=None, rand_key_perm=None,
                        rand_query_perm=None) -> Dict[str, torch.Tensor]:
@@ -283,12 +289,57 @@ class SparsePR:
             _check_tensor(name, t, shp, torch_dtype(p), self.device)
         _check_tensor("scale", scale, (p.heads,), torch.float32, self.device)
 
-    def run(self, Q, K, V, scale, idx: Dict[str, torch.Tensor]) -> torch.Tensor:
+    def side_stream(self) -> torch.cuda.Stream:
+        """Second stream (default priority) for the probe fit."""
+        if self._side is None:
+            self._side = torch.cuda.Stream(device=self.device)
+        return self._side
+
+    def run(self, Q, K, V, scale, idx: Dict[str, torch.Tensor], overlap: bool = False,
+            events: Optional[Dict[str, torch.cuda.Event]] = None) -> torch.Tensor:
+        """One call on the current stream. With ``overlap``, the blocks that hold
+        probe rows are attended first, then the probe fit runs on a side stream
+        while the remaining blocks are attended; apply waits for both. ``events``
+        (optional) receives HIP events recorded between the stages."""
         p, b = self.p, self.buffers
+        main = torch.cuda.current_stream(self.device)
+
+        def mark(name, stream=None):
+            if events is not None:
+                ev = torch.cuda.Event(enable_timing=True)
+                ev.record(stream or main)
+                events[name] = ev
+
+        mark("start")
         partition(p, Q, K, V, scale, idx.get("sample_idx"), idx.get("init_idx"), b,
                   rand_key_perm=idx.get("rand_key_perm"))
+        mark("partition")
         route(p, Q, scale, b, rand_query_perm=idx.get("rand_query_perm"))
-        attend(p, Q, scale, b)
-        probe_fit(p, Q, scale, b)
+        mark("route")
+        if not overlap:
+            attend(p, Q, scale, b)
+            mark("attend")
+            probe_fit(p, Q, scale, b)
+            mark("probe_fit")
+            apply(p, b)
+            mark("apply")
+            return b.O
+        attend(p, Q, scale, b, subset=BLOCKS_WITH_PROBE)
+        mark("attend_probe_blocks")
+        fork = torch.cuda.Event()
+        fork.record(main)
+        side = self.side_stream()
+        side.wait_event(fork)
+        with torch.cuda.stream(side):
+            mark("probe_fit_start", side)
+            probe_fit(p, Q, scale, b)
+            mark("probe_fit", side)
+        join = torch.cuda.Event()
+        join.record(side)
+        attend(p, Q, scale, b, subset=BLOCKS_WITHOUT_PROBE)
+        mark("attend")
+        main.wait_event(join)
+        mark("join")
         apply(p, b)
+        mark("apply")
         return b.O

@@ -296,13 +296,16 @@ int32_t sparsepr_route(const sparsepr_params* params, const void* Q, const float
                     "sparsepr_route");
 }
 
-int32_t sparsepr_attend(const sparsepr_params* params, const void* Q, const void* Kp,
-                        const void* Vp, const float* scale, const int32_t* group_off,
-                        const int32_t* query_perm, const int32_t* block_ptr,
-                        const int32_t* block_groups, float* S_out, float* lse, void* stream) {
+int32_t sparsepr_attend_subset(const sparsepr_params* params, const void* Q, const void* Kp,
+                               const void* Vp, const float* scale, const int32_t* group_off,
+                               const int32_t* query_perm, const int32_t* block_ptr,
+                               const int32_t* block_groups, float* S_out, float* lse,
+                               int32_t subset, void* stream) {
   Dims d;
   int32_t s = make_dims(params, true, &d);
   if (s != SPARSEPR_OK) return s;
+  if (subset < SPARSEPR_BLOCKS_ALL || subset > SPARSEPR_BLOCKS_WITHOUT_PROBE)
+    return fail(SPARSEPR_ERR_INVALID_ARG, "subset must be 0, 1 or 2 (got %d)", subset);
   SPR_REQUIRE(Q, "Q");
   SPR_REQUIRE(Kp, "Kp");
   SPR_REQUIRE(Vp, "Vp");
@@ -331,8 +334,17 @@ int32_t sparsepr_attend(const sparsepr_params* params, const void* Q, const void
   a.group_off = group_off;
   a.out = S_out;
   a.lse = lse;
+  a.subset = subset;
   return hip_status(launch_attention(d, ATTN_SPARSE, a, static_cast<hipStream_t>(stream)),
                     "sparsepr_attend");
+}
+
+int32_t sparsepr_attend(const sparsepr_params* params, const void* Q, const void* Kp,
+                        const void* Vp, const float* scale, const int32_t* group_off,
+                        const int32_t* query_perm, const int32_t* block_ptr,
+                        const int32_t* block_groups, float* S_out, float* lse, void* stream) {
+  return sparsepr_attend_subset(params, Q, Kp, Vp, scale, group_off, query_perm, block_ptr,
+                                block_groups, S_out, lse, SPARSEPR_BLOCKS_ALL, stream);
 }
 
 int32_t sparsepr_probe_fit(const sparsepr_params* params, const void* Q, const void* K,

@@ -77,6 +77,19 @@ __device__ __forceinline__ Item decode_item(const AttnArgs& a, int nqb) {
   return it;
 }
 
+// Whether query block b (positions [b B_q, b B_q + B_q)) holds a probe
+// position p_i = floor((2i + 1) N / (2m)): the first probe at or after the
+// block start is i0 = ceil((2m lo - N) / (2N)).
+__device__ __forceinline__ bool block_has_probe(int b, int N, int m, int BQ) {
+  if (m <= 0) return false;
+  const int64_t lo = (int64_t)b * BQ;
+  const int64_t hi = lo + BQ < N ? lo + BQ : N;
+  const int64_t num = 2LL * m * lo - N;
+  const int64_t i0 = num <= 0 ? 0 : (num + 2LL * N - 1) / (2LL * N);
+  if (i0 >= m) return false;
+  return ((2 * i0 + 1) * (int64_t)N) / (2LL * m) < hi;
+}
+
 // Token of query row qi of the work item; sets *pos to the output row.
 template <int MODE, int BQ>
 __device__ __forceinline__ int query_token(const AttnArgs& a, const Item& it, int qi, int* pos,
@@ -275,6 +288,8 @@ void k_attn_mfma(AttnArgs a) {
   const int nqb = MODE == ATTN_PROBE ? (a.m + BQ - 1) / BQ : a.nb;
   const Item it = decode_item<MODE>(a, nqb);
   if (it.h >= a.H) return;
+  if (MODE == ATTN_SPARSE && a.subset != 0 && block_has_probe(it.b, a.N, a.m, BQ) != (a.subset == 1))
+    return;
   const int t = threadIdx.x;
   const int lane = t & 63, w = t >> 6;
   const int hl = lane >> 5;       // which half of the wave
@@ -441,6 +456,8 @@ __global__ __launch_bounds__(256) void k_attn_valu(AttnArgs a, int BQ) {
     it.b = L % nqb;
     it.sp = 0;
   }
+  if (MODE == ATTN_SPARSE && a.subset != 0 && block_has_probe(it.b, a.N, a.m, BQ) != (a.subset == 1))
+    return;
   const int t = threadIdx.x;
   const int qq = t & 3;
   const int qi = sub * 64 + (t >> 2);

@@ -96,6 +96,7 @@ struct AttnArgs {
   float* opart;                // probe: [H, nsplit, m, D] fp32
   float* lsepart;              // probe: [H, nsplit, m]
   int xcd_chunk;               // > 0: head-synchronous XCD mapping with this many blocks per XCD
+  int subset;                  // sparse: 0 all blocks, 1 blocks holding a probe row, 2 the others
 };
 hipError_t launch_attention(const Dims& d, AttnMode mode, const AttnArgs& a, hipStream_t st);
 hipError_t launch_probe_merge(const Dims& d, const float* opart, const float* lsepart,

@@ -207,6 +207,28 @@ int32_t sparsepr_attend(const sparsepr_params* params, const void* Q, const void
                         const int32_t* block_groups, float* S_out, float* lse, void* stream);
 
 /*
+ * Stage 3 on a subset of the query blocks, so that the probe fit can start
+ * before the whole sparse output exists (stage 4 reads S_out only at the probe
+ * positions p_i of its own description):
+ *   SPARSEPR_BLOCKS_ALL              every block (= sparsepr_attend);
+ *   SPARSEPR_BLOCKS_WITH_PROBE       only blocks holding some probe position;
+ *   SPARSEPR_BLOCKS_WITHOUT_PROBE    only the other blocks.
+ * Running subset 1 then subset 2 writes exactly what sparsepr_attend writes
+ * (the blocks are disjoint and each is computed the same way). Between the
+ * two, sparsepr_probe_fit may run on another stream; it touches the workspace
+ * and this stage does not. Errors: as sparsepr_attend, and
+ * SPARSEPR_ERR_INVALID_ARG for another subset value.
+ */
+#define SPARSEPR_BLOCKS_ALL 0
+#define SPARSEPR_BLOCKS_WITH_PROBE 1
+#define SPARSEPR_BLOCKS_WITHOUT_PROBE 2
+int32_t sparsepr_attend_subset(const sparsepr_params* params, const void* Q, const void* Kp,
+                               const void* Vp, const float* scale, const int32_t* group_off,
+                               const int32_t* query_perm, const int32_t* block_ptr,
+                               const int32_t* block_groups, float* S_out, float* lse,
+                               int32_t subset, void* stream);
+
+/*
  * Stage 4 - exact probe rows and the probe-fitted map (arxivdaily 2608.18484,
  * English abstract: exact attention on a few rows, weighted ridge fit of the
  * dense-minus-sparse differences; skillfed article and peercurrent abstract:

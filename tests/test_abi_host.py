@@ -111,6 +111,10 @@ def test_null_pointers_and_small_workspace_are_rejected(lib):
     st = lib.sparsepr_attend(ctypes.byref(p), fake, fake, fake, fake, fake, fake, fake, fake, fake,
                              None, None)
     assert st == 1
+    # attention on a block subset: the subset value is validated
+    st = lib.sparsepr_attend_subset(ctypes.byref(p), fake, fake, fake, fake, fake, fake, fake, fake,
+                                    fake, fake, 3, None)
+    assert st == 1 and "subset" in lib.sparsepr_last_error().decode()
     # apply: output missing, then a workspace too small for the per-head matrix
     st = lib.sparsepr_apply(ctypes.byref(p), fake, fake, fake, fake, fake, fake, None, fake,
                             1 << 40, None)

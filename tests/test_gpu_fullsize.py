@@ -270,3 +270,15 @@ def test_probes_fit_apply_full(fr):
         expect[is_probe] = Op64[np.searchsorted(pos, rows_q[is_probe])]
         assert rel_l2(O[qperm[rows_q]], expect) < 5e-3
         assert np.array_equal(O[ptok], bf16_round(Op))
+
+
+def test_overlapped_call_matches(fr):
+    """The benchmark's overlapped schedule (probe fit on a side stream while the
+    other blocks are attended) gives the same outputs, bit for bit."""
+    op = binding.SparsePR(fr.p, "cuda")
+    b = fr.bench
+    op.run(b.Q, b.K, b.V, b.scale, b.idx, overlap=True)
+    torch.cuda.synchronize()
+    for n in ("O", "S", "lse", "U", "Theta", "O_probe", "query_perm", "key_perm"):
+        assert torch.equal(getattr(op.buffers, n), getattr(b.b, n)), n
+    del op

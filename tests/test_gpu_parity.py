@@ -380,3 +380,42 @@ def test_determinism():
     ptr = a.np("block_ptr")
     for h in range(a.p.heads):
         assert np.array_equal(a.np("block_groups")[h][:ptr[h][-1]], b.np("block_groups")[h][:ptr[h][-1]])
+
+
+def test_attend_block_subsets_compose():
+    """Blocks holding probe rows, then the others, write exactly the full attention."""
+    r = run_pipeline(small_bf16(name="subsets", m=8, k=4, seed=17))   # 8 of 24 blocks hold probes
+    p, b = r.p, r.b
+    full_S, full_lse = b.S.clone(), b.lse.clone()
+    b.S.fill_(float("nan"))
+    b.lse.fill_(float("nan"))
+    binding.attend(p, r.Q, r.scale, b, subset=binding.BLOCKS_WITH_PROBE)
+    torch.cuda.synchronize()
+    # exactly the rows of blocks that hold a probe position are written
+    pos = orc.probe_positions(p.n_tokens, p.n_probes)
+    blocks = np.unique(pos // p.q_block)
+    written = ~torch.isnan(b.lse).cpu().numpy()[0]
+    expect = np.zeros(p.n_tokens, bool)
+    for blk in blocks:
+        expect[blk * p.q_block:(blk + 1) * p.q_block] = True
+    assert np.array_equal(written, expect)
+    binding.attend(p, r.Q, r.scale, b, subset=binding.BLOCKS_WITHOUT_PROBE)
+    torch.cuda.synchronize()
+    assert torch.equal(b.S, full_S) and torch.equal(b.lse, full_lse)
+
+
+def test_overlapped_call_equals_serial():
+    wl = WORKLOADS["bf16_d128"]
+    inp = get_run("bf16_d128").inp
+    p = wl.params
+    outs = []
+    for overlap in (False, True):
+        op = binding.SparsePR(p, "cuda")
+        Q, K, V = (torch.from_numpy(x).to("cuda", torch.bfloat16) for x in (inp.Q, inp.K, inp.V))
+        scale = torch.from_numpy(inp.scale).cuda()
+        idx = op.upload_indices(inp.sample_idx, inp.init_idx)
+        op.run(Q, K, V, scale, idx, overlap=overlap)
+        torch.cuda.synchronize()
+        outs.append({n: getattr(op.buffers, n).clone() for n in ("O", "S", "U", "Theta", "O_probe")})
+    for n in outs[0]:
+        assert torch.equal(outs[0][n], outs[1][n]), n
