@@ -210,7 +210,12 @@ __device__ __forceinline__ void attn_tile(const char* __restrict__ kb, const cha
   for (int kt = 0; kt < 2; ++kt)
 #pragma unroll
     for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[kt][r]);
-  mx = fmaxf(mx, __shfl_xor(mx, 32)) * c;
+  {
+    // lanes l and l ^ 32 hold the two halves of one query row
+    const auto sw = __builtin_amdgcn_permlane32_swap(__builtin_bit_cast(unsigned, mx),
+                                                     __builtin_bit_cast(unsigned, mx), false, false);
+    mx = fmaxf(__builtin_bit_cast(float, sw[0]), __builtin_bit_cast(float, sw[1])) * c;
+  }
   const float m_new = fmaxf(m_run, mx);
   const bool need = m_new > m_run + 8.0f;
   if (__any(need)) {
