@@ -50,7 +50,6 @@ PartitionWs partition_ws(const Dims& d) {
   L.counts = b.take(H * nbk * d.nchunk * sizeof(int32_t));
   L.totals = b.take(H * nbk * sizeof(int32_t));
   L.starts = b.take(H * nbk * sizeof(int32_t));
-  L.partial = b.take(H * (G + d.ntile64) * D * sizeof(float));
   L.best = b.take(H * (size_t)d.N * sizeof(unsigned long long));
   L.end = align256(b.off);
   return L;
@@ -123,7 +122,6 @@ static int32_t make_dims(const sparsepr_params* p, bool full, Dims* d) {
   d->BQ = p->q_block;
   d->nb = (d->N + d->BQ - 1) / d->BQ;
   d->nchunk = (d->N + 255) / 256;
-  d->ntile64 = (d->N + 63) / 64;
   d->G = 1;
   d->S = 1;
   d->T = 1;

@@ -17,7 +17,6 @@ struct Dims {
   double rho, lam;
   int64_t kappa;
   int nchunk;     // ceil(N / 256): chunks of the counting-sort passes
-  int ntile64;    // ceil(N / 64)
   int gbits;      // bits needed for a group index (0 when G == 1)
   int nsplit;     // probe attention: key splits
   int split_len;  // probe attention: keys per split (multiple of 64)
@@ -25,7 +24,7 @@ struct Dims {
 
 // ---- workspace layout (byte offsets; one workspace serves every stage)
 struct PartitionWs {
-  size_t M, P, Phl, bvec, counts, totals, starts, partial, best, end;
+  size_t M, P, Phl, bvec, counts, totals, starts, best, end;
 };
 struct RouteWs {
   size_t keysA, keysB, valsA, valsB, counts, totals, starts, sigma, sel, selcnt, blkkeys,

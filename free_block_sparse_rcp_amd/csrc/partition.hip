@@ -62,28 +62,59 @@ __global__ void k_centroid_init(const void* Kv, const int32_t* init_idx, int N, 
 
 // P_g = M kbar_g (fp64 accumulate), b_g = kbar_g^T M kbar_g. Stores P in fp32
 // and as a bf16 pair P ~ hi + lo (rows [H][G][2][D]), so that a bf16 MFMA with
-// exact bf16 keys recovers the product to ~2^-18 relative. grid (G, H), block D.
+// exact bf16 keys recovers the product to ~2^-18 relative. Eight groups per
+// workgroup, so that M is read once per eight groups: thread (e, set) forms
+// P_g[e] for its set's groups in increasing j, and b_g is reduced over e with a
+// pairwise tree. grid (ceil(G / 8), H), block 256.
+constexpr int kPrepGroups = 8;
+
 template <int D>
-__global__ void k_centroid_prep(const double* M, const float* kbar, int G, float* P,
-                                uint16_t* Phl, float* bvec) {
-  const int g = blockIdx.x, h = blockIdx.y, e = threadIdx.x;
-  __shared__ double kb[D];
-  __shared__ double red[D];
-  const float* kg = kbar + ((size_t)h * G + g) * D;
-  kb[e] = kg[e];
+__global__ __launch_bounds__(256) void k_centroid_prep_g8(const double* M, const float* kbar, int G,
+                                                          float* P, uint16_t* Phl, float* bvec) {
+  constexpr int NG = kPrepGroups;
+  constexpr int NSET = 256 / D;        // thread sets
+  constexpr int GPT = NG / NSET;       // groups per thread
+  __shared__ double kb[NG][D];
+  __shared__ double rb[NG][D];
+  const int h = blockIdx.y, g0 = blockIdx.x * NG, t = threadIdx.x;
+  for (int i = t; i < NG * D; i += 256) {
+    const int k = i / D, e = i - k * D;
+    kb[k][e] = g0 + k < G ? (double)kbar[((size_t)h * G + g0 + k) * D + e] : 0.0;
+  }
   __syncthreads();
+  const int e = t % D, set = t / D;
   const double* Mh = M + (size_t)h * D * D;
-  double p = 0.0;
-  for (int j = 0; j < D; ++j) p += Mh[(size_t)j * D + e] * kb[j];  // M symmetric: column e
-  const size_t o = ((size_t)h * G + g) * D + e;
-  P[o] = (float)p;
-  const uint16_t hi = f32_to_bf16((float)p);
-  const uint16_t lo = f32_to_bf16((float)(p - (double)bf16_to_f32(hi)));
-  uint16_t* ph = Phl + ((size_t)h * G + g) * 2 * D;
-  ph[e] = hi;
-  ph[D + e] = lo;
-  const double bsum = block_sum_f64<D>(kb[e] * p, red);
-  if (e == 0) bvec[(size_t)h * G + g] = (float)bsum;
+  double p[GPT];
+#pragma unroll
+  for (int k = 0; k < GPT; ++k) p[k] = 0.0;
+  for (int j = 0; j < D; ++j) {
+    const double m = Mh[(size_t)j * D + e];   // M symmetric: column e
+#pragma unroll
+    for (int k = 0; k < GPT; ++k) p[k] += m * kb[set * GPT + k][j];
+  }
+#pragma unroll
+  for (int k = 0; k < GPT; ++k) {
+    const int gl = set * GPT + k, g = g0 + gl;
+    rb[gl][e] = kb[gl][e] * p[k];
+    if (g < G) {
+      const size_t o = ((size_t)h * G + g) * D + e;
+      P[o] = (float)p[k];
+      const uint16_t hi = f32_to_bf16((float)p[k]);
+      const uint16_t lo = f32_to_bf16((float)(p[k] - (double)bf16_to_f32(hi)));
+      uint16_t* ph = Phl + ((size_t)h * G + g) * 2 * D;
+      ph[e] = hi;
+      ph[D + e] = lo;
+    }
+  }
+  __syncthreads();
+  for (int off = D / 2; off > 0; off >>= 1) {
+    for (int i = t; i < NG * off; i += 256) {
+      const int k = i / off, x = i - k * off;
+      rb[k][x] += rb[k][x + off];
+    }
+    __syncthreads();
+  }
+  if (t < NG && g0 + t < G) bvec[(size_t)h * G + g0 + t] = (float)rb[t][0];
 }
 
 // ------------------------------------------------- row x centroid argselect
@@ -520,87 +551,63 @@ __global__ __launch_bounds__(256) void k_digit_scatter(const KeyT* keys_in, KeyT
 }
 
 // ------------------------------------------------ deterministic group means
-// Tile c = positions [64c, 64c+64) of the group-contiguous order. Each run of
-// one group inside a tile is summed (rows in order, per column) into
-// partial[g + c]; the index g + c is unique because tiles and groups both
-// advance along the order. The tile's 64 rows are gathered with 16-byte loads
-// into LDS as fp32; the group of a position follows from group_off.
-// grid (ntile64, H), block 256.
+// kbar_g = mean of the rows of group g (positions [off_g, off_g+1) of the
+// group-contiguous order), for non-empty groups; empty groups keep kbar. Each
+// row is read once: a row is split into 16-byte chunks over CPR threads, and
+// the workgroup's 256 / CPR row slots take rows slot, slot + 256 / CPR, ... in
+// increasing order; the slots are then added in slot order, so the sum order is
+// fixed. grid (G, H), block 256.
 template <bool BF16, int D>
-__global__ __launch_bounds__(256) void k_seg_partial(const void* Kv, const int32_t* key_perm,
-                                                     const int32_t* group_off, int N, int G,
-                                                     int ntile, float* partial) {
+__global__ __launch_bounds__(256) void k_group_mean(const void* Kv, const int32_t* key_perm,
+                                                    const int32_t* group_off, int N, int G,
+                                                    float* kbar) {
   using T = typename Elt<BF16>::T;
   constexpr int ROWB = D * (int)sizeof(T);
-  constexpr int CPR = ROWB / 16;              // 16-byte chunks per row
+  constexpr int CPR = ROWB / 16;              // threads per row
   constexpr int EPC = 16 / (int)sizeof(T);    // elements per chunk
-  constexpr int PITCH = D + 4;                // floats; rows stay 16-byte aligned
-  __shared__ __attribute__((aligned(16))) float tile[64 * PITCH];
-  __shared__ int srow[64];
-  const int c = blockIdx.x, h = blockIdx.y, t = threadIdx.x;
-  const char* K = static_cast<const char*>(Kv) + (size_t)h * N * ROWB;
+  constexpr int RPP = 256 / CPR;              // rows per pass
+  constexpr int U = 4;                        // row loads in flight per thread
+  __shared__ float red[RPP * D];
+  const int g = blockIdx.x, h = blockIdx.y, t = threadIdx.x;
   const int32_t* off = group_off + (size_t)h * (G + 1);
-  float* part = partial + (size_t)h * (G + ntile) * D;
-  const int p0 = c * 64, n = min(N, p0 + 64) - p0;
-  if (t < n) srow[t] = clamp_idx(key_perm[(size_t)h * N + p0 + t], N);
-  __syncthreads();
-  for (int i = t; i < n * CPR; i += 256) {
-    const int r = i / CPR, cc = i - r * CPR;
-    const u32x4 raw = *reinterpret_cast<const u32x4*>(K + (size_t)srow[r] * ROWB + cc * 16);
-    float* dst = tile + r * PITCH + cc * EPC;
-    if (BF16) {
-      f32x4 lo, hi;
+  const int b = off[g], e = off[g + 1];
+  if (e <= b) return;
+  const int cc = t % CPR, slot = t / CPR;
+  const char* K = static_cast<const char*>(Kv) + (size_t)h * N * ROWB + cc * 16;
+  const int32_t* perm = key_perm + (size_t)h * N;
+  float acc[EPC];
 #pragma unroll
-      for (int j = 0; j < 2; ++j) {
-        lo[2 * j] = __uint_as_float(raw[j] << 16);
-        lo[2 * j + 1] = __uint_as_float(raw[j] & 0xffff0000u);
-        hi[2 * j] = __uint_as_float(raw[2 + j] << 16);
-        hi[2 * j + 1] = __uint_as_float(raw[2 + j] & 0xffff0000u);
+  for (int j = 0; j < EPC; ++j) acc[j] = 0.f;
+  auto add = [&](const u32x4 raw) {
+    if (BF16) {
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        acc[2 * j] += __uint_as_float(raw[j] << 16);
+        acc[2 * j + 1] += __uint_as_float(raw[j] & 0xffff0000u);
       }
-      *reinterpret_cast<f32x4*>(dst) = lo;
-      *reinterpret_cast<f32x4*>(dst + 4) = hi;
     } else {
-      *reinterpret_cast<f32x4*>(dst) = __builtin_bit_cast(f32x4, raw);
+#pragma unroll
+      for (int j = 0; j < 4; ++j) acc[j] += __uint_as_float(raw[j]);
     }
+  };
+  int i = b + slot;
+  for (; i + (U - 1) * RPP < e; i += U * RPP) {
+    u32x4 raw[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u)
+      raw[u] = *reinterpret_cast<const u32x4*>(K + (size_t)clamp_idx(perm[i + u * RPP], N) * ROWB);
+#pragma unroll
+    for (int u = 0; u < U; ++u) add(raw[u]);
   }
+  for (; i < e; i += RPP) add(*reinterpret_cast<const u32x4*>(K + (size_t)clamp_idx(perm[i], N) * ROWB));
+#pragma unroll
+  for (int j = 0; j < EPC; ++j) red[slot * D + cc * EPC + j] = acc[j];
   __syncthreads();
-  if (t >= D || n <= 0) return;
-  // group of position p0: the last g with off[g] <= p0 (runs of empty groups skipped)
-  int lo = 0, hi = G;   // invariant off[lo] <= p0 < off[hi] (off[G] = N > p0)
-  while (hi - lo > 1) {
-    const int mid = (lo + hi) >> 1;
-    if (off[mid] <= p0) lo = mid; else hi = mid;
+  if (t < D) {
+    float s = 0.f;
+    for (int k = 0; k < RPP; ++k) s += red[k * D + t];
+    kbar[((size_t)h * G + g) * D + t] = s / (float)(e - b);
   }
-  int g = lo, end = off[g + 1];
-  float acc = 0.f;
-  for (int r = 0; r < n; ++r) {
-    const int pos = p0 + r;
-    if (pos >= end) {
-      part[(size_t)(g + c) * D + t] = acc;
-      acc = 0.f;
-      do {
-        ++g;
-        end = off[g + 1];
-      } while (pos >= end);
-    }
-    acc += tile[r * PITCH + t];
-  }
-  part[(size_t)(g + c) * D + t] = acc;
-}
-
-// kbar_g = (sum of the group's tile partials, in tile order) / n_g for
-// non-empty groups; empty groups keep kbar. grid (G, H), block D.
-template <int D>
-__global__ void k_seg_final(const float* partial, const int32_t* group_off, int G, int ntile,
-                            float* kbar) {
-  const int g = blockIdx.x, h = blockIdx.y, e = threadIdx.x;
-  const int off = group_off[(size_t)h * (G + 1) + g];
-  const int end = group_off[(size_t)h * (G + 1) + g + 1];
-  if (end <= off) return;
-  const float* part = partial + (size_t)h * (G + ntile) * D;
-  float s = 0.f;
-  for (int c = off / 64; c <= (end - 1) / 64; ++c) s += part[(size_t)(g + c) * D + e];
-  kbar[((size_t)h * G + g) * D + e] = s / (float)(end - off);
 }
 
 // Random-block variant: label of key perm[i] is the run g with
@@ -704,7 +711,6 @@ static hipError_t partition_impl(const Dims& d, const void* Q, const void* K, co
   int32_t* counts = reinterpret_cast<int32_t*>(ws + L.counts);
   int32_t* totals = reinterpret_cast<int32_t*>(ws + L.totals);
   int32_t* starts = reinterpret_cast<int32_t*>(ws + L.starts);
-  float* partial = reinterpret_cast<float*>(ws + L.partial);
   unsigned long long* best = reinterpret_cast<unsigned long long*>(ws + L.best);
   const dim3 rows64((d.N + 63) / 64, d.H);
   const dim3 per_group(d.G, d.H);
@@ -713,10 +719,7 @@ static hipError_t partition_impl(const Dims& d, const void* Q, const void* K, co
     hipError_t e = launch_sort_pass_u32(d, key_label, d.gbits, nullptr, key_perm, counts, totals,
                                         starts, group_off, st);
     if (e != hipSuccess) return e;
-    k_seg_partial<BF16, D><<<dim3(d.ntile64, d.H), 256, 0, st>>>(K, key_perm, group_off, d.N, d.G,
-                                                                  d.ntile64, partial);
-    SPR_CHECK_LAUNCH();
-    k_seg_final<D><<<per_group, D, 0, st>>>(partial, group_off, d.G, d.ntile64, kbar);
+    k_group_mean<BF16, D><<<per_group, 256, 0, st>>>(K, key_perm, group_off, d.N, d.G, kbar);
     SPR_CHECK_LAUNCH();
     return hipSuccess;
   };
@@ -727,7 +730,8 @@ static hipError_t partition_impl(const Dims& d, const void* Q, const void* K, co
     k_centroid_init<BF16, D><<<per_group, D, 0, st>>>(K, init_idx, d.N, d.G, kbar);
     SPR_CHECK_LAUNCH();
     for (int it = 0; it < d.T; ++it) {
-      k_centroid_prep<D><<<per_group, D, 0, st>>>(M, kbar, d.G, P, Phl, bvec);
+      k_centroid_prep_g8<D><<<dim3((d.G + kPrepGroups - 1) / kPrepGroups, d.H), 256, 0, st>>>(
+          M, kbar, d.G, P, Phl, bvec);
       SPR_CHECK_LAUNCH();
       float* dbg_it = (it == d.T - 1) ? dbg : nullptr;
       if (BF16) {
