@@ -15,14 +15,21 @@
 namespace spr {
 
 // ---------------------------------------------------------------- metric M
-// M[h] = tau_h^2 * sum_s q_s q_s^T in fp64. grid (H, D/16), block 256.
+// M[h] = tau_h^2 * sum_s q_s q_s^T in fp64 (samples added in increasing s).
+// Chunks of 32 sampled rows are read with 16-byte loads into a double buffer
+// in LDS; the next chunk's loads are in flight while this one is summed.
+// grid (H, D/16), block 256.
 template <bool BF16, int D>
 __global__ __launch_bounds__(256) void k_metric(const void* Qv, const float* scale,
                                                 const int32_t* sample_idx, int S, int N,
                                                 double* M) {
-  using E = Elt<BF16>;
-  const typename E::T* Q = static_cast<const typename E::T*>(Qv) + (size_t)blockIdx.x * N * D;
-  __shared__ float xs[32][D];
+  using T = typename Elt<BF16>::T;
+  constexpr int ROWB = D * (int)sizeof(T);
+  constexpr int CPR = ROWB / 16;             // 16-byte chunks per row
+  constexpr int EPC = 16 / (int)sizeof(T);   // elements per chunk
+  constexpr int LPT = (32 * CPR + 255) / 256;  // loads per thread per chunk of rows
+  const char* Q = static_cast<const char*>(Qv) + (size_t)blockIdx.x * N * ROWB;
+  __shared__ float xs[2][32][D];
   const int t = threadIdx.x;
   const int i = blockIdx.y * 16 + t / 16;
   const int jl = t % 16;
@@ -30,19 +37,52 @@ __global__ __launch_bounds__(256) void k_metric(const void* Qv, const float* sca
   double acc[U];
 #pragma unroll
   for (int u = 0; u < U; ++u) acc[u] = 0.0;
+  u32x4 raw[LPT];
+  auto fetch = [&](int s0) {
+    const int ns = min(32, S - s0);
+#pragma unroll
+    for (int l = 0; l < LPT; ++l) {
+      const int e = t + 256 * l, ss = e / CPR, c = e % CPR;
+      raw[l] = u32x4{0u, 0u, 0u, 0u};
+      if (e < 32 * CPR && ss < ns)
+        raw[l] = *reinterpret_cast<const u32x4*>(Q + (size_t)clamp_idx(sample_idx[s0 + ss], N) * ROWB + c * 16);
+    }
+  };
+  auto stash = [&](int buf) {
+#pragma unroll
+    for (int l = 0; l < LPT; ++l) {
+      const int e = t + 256 * l, ss = e / CPR, c = e % CPR;
+      if (e >= 32 * CPR) continue;
+      float* dst = &xs[buf][ss][c * EPC];
+      if (BF16) {
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+          dst[2 * u] = __uint_as_float(raw[l][u] << 16);
+          dst[2 * u + 1] = __uint_as_float(raw[l][u] & 0xffff0000u);
+        }
+      } else {
+#pragma unroll
+        for (int u = 0; u < 4; ++u) dst[u] = __uint_as_float(raw[l][u]);
+      }
+    }
+  };
+  if (S > 0) {
+    fetch(0);
+    stash(0);
+  }
+  __syncthreads();
+  int buf = 0;
   for (int s0 = 0; s0 < S; s0 += 32) {
     const int ns = min(32, S - s0);
-    for (int e = t; e < 32 * D; e += 256) {
-      const int ss = e / D, c = e % D;
-      xs[ss][c] = ss < ns ? E::ld(Q, (size_t)clamp_idx(sample_idx[s0 + ss], N) * D + c) : 0.f;
-    }
-    __syncthreads();
+    if (s0 + 32 < S) fetch(s0 + 32);
     for (int ss = 0; ss < ns; ++ss) {
-      const double xi = xs[ss][i];
+      const double xi = xs[buf][ss][i];
 #pragma unroll
-      for (int u = 0; u < U; ++u) acc[u] += xi * (double)xs[ss][jl + 16 * u];
+      for (int u = 0; u < U; ++u) acc[u] += xi * (double)xs[buf][ss][jl + 16 * u];
     }
+    if (s0 + 32 < S) stash(buf ^ 1);
     __syncthreads();
+    buf ^= 1;
   }
   const double tau = scale[blockIdx.x];
   double* Mh = M + (size_t)blockIdx.x * D * D;

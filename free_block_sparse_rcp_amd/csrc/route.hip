@@ -65,18 +65,28 @@ __global__ __launch_bounds__(256) void k_route_scores(const void* Qv, const int3
       float acc[EPC];
 #pragma unroll
       for (int u = 0; u < EPC; ++u) acc[u] = 0.f;
-      for (int r = rg; r < n; r += RG) {
-        const int tok = clamp_idx(qp[p0 + r], N);
-        const u32x4 raw = *reinterpret_cast<const u32x4*>(Q + (size_t)tok * ROWB + c * 16);
-        if (BF16) {
+      // rows rg, rg + RG, ... in increasing order, eight loads in flight
+      for (int r0 = rg; r0 < n; r0 += 8 * RG) {
+        u32x4 raw[8];
 #pragma unroll
-          for (int u = 0; u < 4; ++u) {
-            acc[2 * u] += __uint_as_float(raw[u] << 16);
-            acc[2 * u + 1] += __uint_as_float(raw[u] & 0xffff0000u);
+        for (int v = 0; v < 8; ++v) {
+          const int r = r0 + v * RG;
+          const int tok = clamp_idx(qp[p0 + min(r, n - 1)], N);
+          raw[v] = *reinterpret_cast<const u32x4*>(Q + (size_t)tok * ROWB + c * 16);
+        }
+#pragma unroll
+        for (int v = 0; v < 8; ++v) {
+          if (r0 + v * RG >= n) break;
+          if (BF16) {
+#pragma unroll
+            for (int u = 0; u < 4; ++u) {
+              acc[2 * u] += __uint_as_float(raw[v][u] << 16);
+              acc[2 * u + 1] += __uint_as_float(raw[v][u] & 0xffff0000u);
+            }
+          } else {
+#pragma unroll
+            for (int u = 0; u < 4; ++u) acc[u] += __uint_as_float(raw[v][u]);
           }
-        } else {
-#pragma unroll
-          for (int u = 0; u < 4; ++u) acc[u] += __uint_as_float(raw[u]);
         }
       }
 #pragma unroll
