@@ -19,7 +19,7 @@
 
 namespace spr {
 
-constexpr int kFitThreads = 256;
+constexpr int kFitThreads = 512;
 
 __device__ __forceinline__ double wave_sum_f64(double v) {
 #pragma unroll
@@ -43,13 +43,20 @@ __device__ __forceinline__ double wg_sum1(double v, double* red2, int& slot) {
 }
 
 // Number of eigenvalues of the symmetric tridiagonal (a, b) below x.
+// 1/q from the hardware reciprocal and one Newton step (relative error near
+// the double rounding unit); only the signs of the recurrence are used.
+__device__ __forceinline__ double rcp_nr(double q) {
+  const double r = __builtin_amdgcn_rcp(q);
+  return fma(r, fma(-q, r, 1.0), r);
+}
+
 __device__ int sturm_count(const double* a, const double* b2, int n, double x, double pivmin) {
   int cnt = 0;
   double q = a[0] - x;
   if (fabs(q) < pivmin) q = -pivmin;
   cnt += q < 0.0;
   for (int i = 1; i < n; ++i) {
-    q = (a[i] - x) - b2[i - 1] / q;
+    q = (a[i] - x) - b2[i - 1] * rcp_nr(q);
     if (fabs(q) < pivmin) q = -pivmin;
     cnt += q < 0.0;
   }
@@ -184,9 +191,12 @@ __global__ __launch_bounds__(kFitThreads) void k_fit(int m, int kmax, float* U_o
   constexpr int BIG = (D + 1) * (D + 2);
   __shared__ double big[BIG];
   __shared__ double dg[D], od[D], od2[D], beta[D], vv[D], pv[D], vn[D];
-  __shared__ double lam_top[D];
+  __shared__ double lam_top[D + 1];   // eigenvalues, later 1 / L_ii of the ridge factor
   __shared__ double red2[2 * NT / 64];
   __shared__ double dots[D];
+  constexpr int NSEG = NT / D;             // segments of the Householder product
+  static_assert(NSEG >= 1 && NT % D == 0, "threads must cover whole rows");
+  __shared__ double pseg[NSEG > 1 ? NSEG - 1 : 1][D];
   const int h = blockIdx.x, t = threadIdx.x;
   float* Uh = U_out + (size_t)h * D * kmax;
   float* Th = Th_out + (size_t)h * (D + 1) * kmax;
@@ -232,13 +242,13 @@ __global__ __launch_bounds__(kFitThreads) void k_fit(int m, int kmax, float* U_o
     const double v0 = x0 - alpha;
     const double bk = 2.0 / (v0 * v0 + sig2);
     // p = beta A22 v with v_0 = v0, v_j = A[k+1+j][k]. Row i of the product is
-    // split between two waves by halves of j; every step of a partial sum reads
+    // split over NSEG waves by segments of j; every step of a partial sum reads
     // one row of A22 across the wave. v^T p comes from the partials directly.
-    const int i = t & (D - 1), half = t / D;
-    const int jm = (L + 1) / 2;
+    const int i = t & (D - 1), seg = t / D;
+    const int jm = (L + NSEG - 1) / NSEG;
     double s = 0.0;
-    if (i < L && half < 2) {
-      const int j0 = half * jm, j1 = half == 0 ? jm : L;
+    if (i < L) {
+      const int j0 = min(L, seg * jm), j1 = min(L, j0 + jm);
       // four independent partial sums keep several LDS reads in flight
       double s4[4] = {0.0, 0.0, 0.0, 0.0};
       int j = j0;
@@ -255,11 +265,14 @@ __global__ __launch_bounds__(kFitThreads) void k_fit(int m, int kmax, float* U_o
       s = (s4[0] + s4[1]) + (s4[2] + s4[3]);
     }
     const double v_i = i == 0 ? v0 : (i < L ? A[(k + 1 + i) * PA + k] : 0.0);
-    if (half == 1 && i < L) pv[i] = s;   // partial of the second half
-    const double vp = (i < L && half < 2) ? v_i * bk * s : 0.0;
+    if (seg > 0 && i < L) pseg[seg - 1][i] = s;   // partials of the later segments
+    const double vp = i < L ? v_i * bk * s : 0.0;
     const double K = 0.5 * bk * wg_sum1(vp, red2, slot);
-    if (half == 0 && i < L) {
-      const double p_i = bk * (s + pv[i]);
+    if (seg == 0 && i < L) {
+      double st = s;
+#pragma unroll
+      for (int q = 0; q < NSEG - 1; ++q) st += pseg[q][i];
+      const double p_i = bk * st;
       pv[i] = p_i - K * v_i;   // q
       vv[i] = v_i;
     }
@@ -284,8 +297,8 @@ __global__ __launch_bounds__(kFitThreads) void k_fit(int m, int kmax, float* U_o
   __syncthreads();
   for (int i = t; i < D; i += NT) od2[i] = od[i] * od[i];
   __syncthreads();
-  // ---- eigenvalues r = 0..keff-1 from the top: 8-point multisection per
-  // eigenvalue; 16 steps shrink the Gershgorin interval by 9^16 > 2^50
+  // ---- eigenvalues r = 0..keff-1 from the top by multisection of the
+  // Gershgorin interval with Sturm counts
   double glo = 1e300, ghi = -1e300, maxb2 = 0.0, tnorm = 0.0;
   for (int i = 0; i < D; ++i) {
     const double bl = i > 0 ? fabs(od[i - 1]) : 0.0;
@@ -299,17 +312,21 @@ __global__ __launch_bounds__(kFitThreads) void k_fit(int m, int kmax, float* U_o
   const double pad = 2.2e-16 * fmax(tnorm, 1e-300) + pivmin;
   glo -= pad;
   ghi += pad;
-  for (int base = 0; base < keff; base += NT / 8) {
-    const int r = base + t / 8, sub = t % 8;
+  // P-point multisection per eigenvalue, P = 32, 16 or 8 as keff allows; the
+  // interval shrinks by (P + 1)^iters > 2^50
+  const int P = keff <= NT / 32 ? 32 : (keff <= NT / 16 ? 16 : 8);
+  const int iters = P == 32 ? 10 : (P == 16 ? 13 : 16);
+  for (int base = 0; base < keff; base += NT / P) {
+    const int r = base + t / P, sub = t % P;
     const int j = D - 1 - (r < keff ? r : 0);  // ascending eigenvalue index
     double lo = glo, hi = ghi;
-    for (int iter = 0; iter < 16; ++iter) {
-      const double x = lo + (hi - lo) * (double)(sub + 1) / 9.0;
+    for (int iter = 0; iter < iters; ++iter) {
+      const double x = lo + (hi - lo) * (double)(sub + 1) / (double)(P + 1);
       const int cnt = sturm_count(dg, od2, D, x, pivmin);
       double nlo = lo, nhi = hi;
-      for (int s8 = 0; s8 < 8; ++s8) {
-        const double xs = __shfl(x, (t & ~7) + s8);
-        const int cs = __shfl(cnt, (t & ~7) + s8);
+      for (int sp = 0; sp < P; ++sp) {
+        const double xs = __shfl(x, (t & ~(P - 1)) + sp);
+        const int cs = __shfl(cnt, (t & ~(P - 1)) + sp);
         if (cs <= j) nlo = fmax(nlo, xs);
         else nhi = fmin(nhi, xs);
       }
@@ -440,22 +457,23 @@ __global__ __launch_bounds__(kFitThreads) void k_fit(int m, int kmax, float* U_o
     double nxt = 0.0;
     if (k > 0 && t < L + 1) nxt = f.hv[(size_t)(k + t) * D + (k - 1)];
     const double bk = beta[k];
-    for (int c0 = 0; c0 < keff; c0 += NT / 8) {
-      const int cc = c0 + t / 8, sub = t % 8;
+    for (int c0 = 0; c0 < keff; c0 += NT / 16) {
+      const int cc = c0 + t / 16, sub = t % 16;
       double sacc = 0.0;
       if (cc < keff && bk != 0.0) {
         double s2[2] = {0.0, 0.0};
         int i = sub;
-        for (; i + 8 < L; i += 16) {
+        for (; i + 16 < L; i += 32) {
           s2[0] += vc[i] * X[(k + 1 + i) * PXK + cc];
-          s2[1] += vc[i + 8] * X[(k + 9 + i) * PXK + cc];
+          s2[1] += vc[i + 16] * X[(k + 17 + i) * PXK + cc];
         }
-        for (; i < L; i += 8) s2[0] += vc[i] * X[(k + 1 + i) * PXK + cc];
+        for (; i < L; i += 16) s2[0] += vc[i] * X[(k + 1 + i) * PXK + cc];
         sacc = s2[0] + s2[1];
       }
       sacc += __shfl_xor(sacc, 1);
       sacc += __shfl_xor(sacc, 2);
       sacc += __shfl_xor(sacc, 4);
+      sacc += __shfl_xor(sacc, 8);
       if (cc < keff && sub == 0) dots[cc] = bk * sacc;
     }
     __syncthreads();
@@ -536,31 +554,39 @@ __global__ __launch_bounds__(kFitThreads) void k_fit(int m, int kmax, float* U_o
   }
   if (t == 0) big[(NX - 1) * NX / 2 + (NX - 1)] = sqrt(dprev);
   __syncthreads();
-  // ---- L y = b, then L^T x = y: four lanes per right-hand-side column, each
-  // column handled by one wave, so only wave-level ordering is needed
+  double* rdiag = lam_top;   // free again: 1 / L_ii for the substitutions
+  static_assert(NX <= D + 1, "reciprocal diagonal fits in lam_top");
+  for (int i = t; i < NX; i += NT) rdiag[i] = 1.0 / big[i * (i + 1) / 2 + i];
+  __syncthreads();
+  // ---- L y = b, then L^T x = y: sixteen lanes per right-hand-side column,
+  // each column handled by one wave, so only wave-level ordering is needed
   {
+    constexpr int LPC = 16;                     // lanes per column
+    constexpr int NU = (NX + LPC - 1) / LPC;    // terms per lane at most
     const int lane = t & 63, w = t >> 6;
-    const int part = lane & 3;
-    for (int cb = 0; cb < keff; cb += 64) {
-      const int cc = cb + 16 * w + (lane >> 2);
+    const int part = lane & (LPC - 1);
+    for (int cb = 0; cb < keff; cb += (64 / LPC) * (NT / 64)) {
+      const int cc = cb + (64 / LPC) * w + lane / LPC;
       const bool on = cc < keff;
       for (int i = 0; i < NX; ++i) {
         double s = 0.0;
         if (on) {
           const double* row = big + i * (i + 1) / 2;
+          // all of the lane's terms are read at once (one LDS round trip)
           double s2[2] = {0.0, 0.0};
-          int l = part;
-          for (; l + 4 < i; l += 8) {
-            s2[0] += row[l] * rhs[(size_t)l * rstride + cc];
-            s2[1] += row[l + 4] * rhs[(size_t)(l + 4) * rstride + cc];
+#pragma unroll
+          for (int u = 0; u < NU; ++u) {
+            const int l = part + u * LPC;
+            if (l < i) s2[u & 1] += row[l] * rhs[(size_t)l * rstride + cc];
           }
-          for (; l < i; l += 4) s2[0] += row[l] * rhs[(size_t)l * rstride + cc];
           s = s2[0] + s2[1];
         }
         s += __shfl_xor(s, 1);
         s += __shfl_xor(s, 2);
+        s += __shfl_xor(s, 4);
+        s += __shfl_xor(s, 8);
         if (on && part == 0)
-          rhs[(size_t)i * rstride + cc] = (rhs[(size_t)i * rstride + cc] - s) / big[i * (i + 1) / 2 + i];
+          rhs[(size_t)i * rstride + cc] = (rhs[(size_t)i * rstride + cc] - s) * rdiag[i];
         if (rhs_lds) __builtin_amdgcn_wave_barrier();
         else __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "workgroup");
       }
@@ -568,18 +594,19 @@ __global__ __launch_bounds__(kFitThreads) void k_fit(int m, int kmax, float* U_o
         double s = 0.0;
         if (on) {
           double s2[2] = {0.0, 0.0};
-          int l = i + 1 + part;
-          for (; l + 4 < NX; l += 8) {
-            s2[0] += big[l * (l + 1) / 2 + i] * rhs[(size_t)l * rstride + cc];
-            s2[1] += big[(l + 4) * (l + 5) / 2 + i] * rhs[(size_t)(l + 4) * rstride + cc];
+#pragma unroll
+          for (int u = 0; u < NU; ++u) {
+            const int l = i + 1 + part + u * LPC;
+            if (l < NX) s2[u & 1] += big[l * (l + 1) / 2 + i] * rhs[(size_t)l * rstride + cc];
           }
-          for (; l < NX; l += 4) s2[0] += big[l * (l + 1) / 2 + i] * rhs[(size_t)l * rstride + cc];
           s = s2[0] + s2[1];
         }
         s += __shfl_xor(s, 1);
         s += __shfl_xor(s, 2);
+        s += __shfl_xor(s, 4);
+        s += __shfl_xor(s, 8);
         if (on && part == 0)
-          rhs[(size_t)i * rstride + cc] = (rhs[(size_t)i * rstride + cc] - s) / big[i * (i + 1) / 2 + i];
+          rhs[(size_t)i * rstride + cc] = (rhs[(size_t)i * rstride + cc] - s) * rdiag[i];
         if (rhs_lds) __builtin_amdgcn_wave_barrier();
         else __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "workgroup");
       }
