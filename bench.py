@@ -94,6 +94,64 @@ def pmc_summary(fetch_csv, write_csv, workload, copy_mib):
     print(json.dumps(rec))
 
 
+def pmc_table(fetch_csv, write_csv, workload, copy_mib):
+    """HBM bytes and achieved bandwidth of every kernel in a FETCH_SIZE run and a
+    WRITE_SIZE run, each counter scaled by what it reports for the plain copy of
+    copy_mib MiB; durations from the FETCH run's dispatch timestamps. Writes
+    profiles/hbm_traffic_<workload>.md."""
+    import csv
+    from collections import defaultdict
+
+    def short(name):
+        name = name.replace("void ", "")
+        return name.split("(")[0][:60]
+
+    def per_kernel(path, counter):
+        acc = defaultdict(list)
+        dur = defaultdict(list)
+        copy = []
+        for r in csv.DictReader(open(path)):
+            if r["Counter_Name"] != counter:
+                continue
+            v = float(r["Counter_Value"])
+            if COPY_KERNEL in r["Kernel_Name"]:
+                copy.append(v)
+                continue
+            k = short(r["Kernel_Name"])
+            acc[k].append(v)
+            dur[k].append((int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) * 1e-9)
+        if not copy:
+            raise SystemExit(f"{path}: no {counter} rows for the copy kernel")
+        return acc, dur, sum(copy) / len(copy)
+
+    copy_kib = copy_mib * 1024.0
+    fk, fdur, fc = per_kernel(fetch_csv, "FETCH_SIZE")
+    wk, _, wc = per_kernel(write_csv, "WRITE_SIZE")
+    fs, ws = copy_kib / fc, copy_kib / wc
+    rows = []
+    for k in fk:
+        if k not in wk:
+            continue
+        f_b = sum(fk[k]) / len(fk[k]) * fs * 1024.0
+        w_b = sum(wk[k]) / len(wk[k]) * ws * 1024.0
+        t = sum(fdur[k]) / len(fdur[k])
+        rows.append((k, len(fk[k]), f_b, w_b, t))
+    rows.sort(key=lambda r: -r[4] * r[1])
+    lines = [f"| kernel | dispatches | fetch GB | write GB | avg ms | GB/s | % of 8 TB/s |",
+             "|---|---:|---:|---:|---:|---:|---:|"]
+    for k, n, f_b, w_b, t in rows:
+        bw = (f_b + w_b) / t / 1e9 if t > 0 else 0.0
+        lines.append(f"| `{k}` | {n} | {f_b / 1e9:.3f} | {w_b / 1e9:.3f} | {t * 1e3:.4f} | "
+                     f"{bw:.0f} | {100 * bw / 8000:.1f} |")
+    text = "\n".join(lines)
+    out = os.path.join(ROOT, "profiles", f"hbm_traffic_{workload}.md")
+    with open(out, "w") as f:
+        f.write(f"# HBM traffic per kernel, {workload}\n\n"
+                f"Scale factors from a {copy_mib} MiB copy: FETCH_SIZE x{fs:.3f}, WRITE_SIZE x{ws:.3f}. "
+                "Durations are the dispatch timestamps of the FETCH_SIZE run.\n\n" + text + "\n")
+    print(text)
+
+
 def cpu_baseline(wl, inp, block_stride):
     """The fp64 oracle, as it stands, on head 0 of the same workload: every
     stage in the pages' order; the block-sparse attention step runs on every
@@ -175,10 +233,18 @@ def main():
     ap.add_argument("--calibration-copy-mib", type=int, default=0,
                     help="also run one plain device copy of this many MiB (a known-size "
                          "kernel for scaling the FETCH_SIZE / WRITE_SIZE counters)")
+    ap.add_argument("--pmc-table", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
+                    help="write a per-kernel HBM traffic table from two rocprofv3 --pmc runs "
+                         "(FETCH_SIZE, WRITE_SIZE) that include the calibration copy")
     ap.add_argument("--pmc-summary", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
                     help="summarise two rocprofv3 PMC runs of this script (FETCH_SIZE, "
                          "WRITE_SIZE) into profiles/attend_traffic_<workload>.json and exit")
     args = ap.parse_args()
+    if args.pmc_table:
+        from free_block_sparse_rcp_amd import configs
+        pmc_table(args.pmc_table[0], args.pmc_table[1], configs.get(args.config).name,
+                  args.calibration_copy_mib or 1024)
+        return
     if args.pmc_summary:
         from free_block_sparse_rcp_amd import configs
         pmc_summary(args.pmc_summary[0], args.pmc_summary[1], configs.get(args.config).name,
