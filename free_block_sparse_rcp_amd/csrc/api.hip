@@ -121,7 +121,7 @@ static int32_t make_dims(const sparsepr_params* p, bool full, Dims* d) {
   d->bf16 = p->dtype == SPARSEPR_BF16;
   d->BQ = p->q_block;
   d->nb = (d->N + d->BQ - 1) / d->BQ;
-  d->nchunk = (d->N + 255) / 256;
+  d->nchunk = (d->N + kSortChunk - 1) / kSortChunk;
   d->G = 1;
   d->S = 1;
   d->T = 1;

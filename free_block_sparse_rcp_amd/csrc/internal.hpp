@@ -10,13 +10,15 @@
 namespace spr {
 
 // Sizes derived from sparsepr_params, computed once per call on the host.
+constexpr int kSortChunk = 2048;   // elements per workgroup of a counting-sort pass
+
 struct Dims {
   int H, N, D, G, S, T, BQ, nb, m, k;
   bool bf16;
   int mode;
   double rho, lam;
   int64_t kappa;
-  int nchunk;     // ceil(N / 256): chunks of the counting-sort passes
+  int nchunk;     // ceil(N / kSortChunk): chunks of the counting-sort passes
   int gbits;      // bits needed for a group index (0 when G == 1)
   int nsplit;     // probe attention: key splits
   int split_len;  // probe attention: keys per split (multiple of 64)

@@ -495,6 +495,8 @@ hipError_t launch_split_hilo(const float* src, size_t rows, int D, uint16_t* dst
 }
 
 // ------------------------------------------------ stable counting-sort pass
+// (kSortChunk, the elements per workgroup of the histogram and scatter passes,
+// is declared with the dimensions.)
 __device__ __forceinline__ uint32_t digit_of(int32_t key, int shift, uint32_t mask) {
   return (static_cast<uint32_t>(key) >> shift) & mask;
 }
@@ -502,7 +504,8 @@ __device__ __forceinline__ uint32_t digit_of(uint64_t key, int shift, uint32_t m
   return static_cast<uint32_t>(key >> shift) & mask;
 }
 
-// counts layout [H][nbuckets][nchunk]; chunks of 256 elements. grid (nchunk, H).
+// counts layout [H][nbuckets][nchunk]; chunks of kSortChunk elements, taken
+// as kSortChunk / 256 consecutive sub-chunks of 256. grid (nchunk, H).
 template <typename KeyT>
 __global__ __launch_bounds__(256) void k_digit_hist(const KeyT* keys, int N, int nchunk,
                                                     int shift, int bits, int32_t* counts) {
@@ -512,8 +515,11 @@ __global__ __launch_bounds__(256) void k_digit_hist(const KeyT* keys, int N, int
   const int h = blockIdx.y, c = blockIdx.x, t = threadIdx.x;
   for (int b = t; b < nbuckets; b += 256) hist[b] = 0;
   __syncthreads();
-  const int i = c * 256 + t;
-  if (i < N) atomicAdd(&hist[digit_of(keys[(size_t)h * N + i], shift, mask)], 1);
+#pragma unroll
+  for (int sub = 0; sub < kSortChunk / 256; ++sub) {
+    const int i = c * kSortChunk + sub * 256 + t;
+    if (i < N) atomicAdd(&hist[digit_of(keys[(size_t)h * N + i], shift, mask)], 1);
+  }
   __syncthreads();
   for (int b = t; b < nbuckets; b += 256) counts[((size_t)h * nbuckets + b) * nchunk + c] = hist[b];
 }
@@ -552,8 +558,10 @@ __global__ __launch_bounds__(1024) void k_scan_buckets(const int32_t* totals, in
   }
 }
 
-// Stable scatter: in-chunk rank from wavefront ballots over the digit bits,
-// then per-wave digit counts in LDS. grid (nchunk, H).
+// Stable scatter: the chunk's sub-chunks of 256 are taken in order; in each,
+// a key's rank comes from wavefront ballots over the digit bits and per-wave
+// digit counts in LDS, after the keys of that digit in the earlier sub-chunks
+// (running count). grid (nchunk, H).
 template <typename KeyT, bool WRITE_KEYS>
 __global__ __launch_bounds__(256) void k_digit_scatter(const KeyT* keys_in, KeyT* keys_out,
                                                        const int32_t* vals_in, int32_t* vals_out,
@@ -561,32 +569,44 @@ __global__ __launch_bounds__(256) void k_digit_scatter(const KeyT* keys_in, KeyT
                                                        const int32_t* counts,
                                                        const int32_t* starts) {
   __shared__ int wcnt[4 * 1024];
+  __shared__ int running[1024];
   const int nbuckets = 1 << bits;
   const uint32_t mask = nbuckets - 1;
   const int h = blockIdx.y, c = blockIdx.x, t = threadIdx.x, w = t >> 6;
   for (int b = t; b < 4 * nbuckets; b += 256) wcnt[b] = 0;
+  for (int b = t; b < nbuckets; b += 256) running[b] = 0;
   __syncthreads();
-  const int i = c * 256 + t;
-  const bool valid = i < N;
-  const KeyT key = valid ? keys_in[(size_t)h * N + i] : KeyT(0);
-  const uint32_t dg = digit_of(key, shift, mask);
-  uint64_t match = __ballot(valid);
-  for (int bit = 0; bit < bits; ++bit) {
-    const bool set = (dg >> bit) & 1u;
-    const uint64_t bb = __ballot(valid && set);
-    match &= set ? bb : ~bb;
-  }
   const uint64_t lt = lanemask_lt();
-  const int rank = __popcll(match & lt);
-  if (valid && (match & lt) == 0) wcnt[w * nbuckets + dg] = __popcll(match);
-  __syncthreads();
-  if (valid) {
-    int before = 0;
-    for (int ww = 0; ww < w; ++ww) before += wcnt[ww * nbuckets + dg];
-    const int pos = starts[(size_t)h * nbuckets + dg] +
-                    counts[((size_t)h * nbuckets + dg) * nchunk + c] + before + rank;
-    if (WRITE_KEYS) keys_out[(size_t)h * N + pos] = key;
-    vals_out[(size_t)h * N + pos] = vals_in ? vals_in[(size_t)h * N + i] : i;
+  for (int sub = 0; sub < kSortChunk / 256; ++sub) {
+    const int i = c * kSortChunk + sub * 256 + t;
+    if (c * kSortChunk + sub * 256 >= N) break;   // uniform: no key left in the chunk
+    const bool valid = i < N;
+    const KeyT key = valid ? keys_in[(size_t)h * N + i] : KeyT(0);
+    const uint32_t dg = digit_of(key, shift, mask);
+    uint64_t match = __ballot(valid);
+    for (int bit = 0; bit < bits; ++bit) {
+      const bool set = (dg >> bit) & 1u;
+      const uint64_t bb = __ballot(valid && set);
+      match &= set ? bb : ~bb;
+    }
+    const int rank = __popcll(match & lt);
+    const bool leader = valid && (match & lt) == 0;
+    if (leader) wcnt[w * nbuckets + dg] = __popcll(match);
+    __syncthreads();
+    if (valid) {
+      int before = running[dg];
+      for (int ww = 0; ww < w; ++ww) before += wcnt[ww * nbuckets + dg];
+      const int pos = starts[(size_t)h * nbuckets + dg] +
+                      counts[((size_t)h * nbuckets + dg) * nchunk + c] + before + rank;
+      if (WRITE_KEYS) keys_out[(size_t)h * N + pos] = key;
+      vals_out[(size_t)h * N + pos] = vals_in ? vals_in[(size_t)h * N + i] : i;
+    }
+    __syncthreads();
+    if (leader) {
+      atomicAdd(&running[dg], __popcll(match));
+      wcnt[w * nbuckets + dg] = 0;
+    }
+    __syncthreads();
   }
 }
 
