@@ -251,12 +251,23 @@ __global__ __launch_bounds__(kApplyWaves * 64) void k_apply_mfma(const float* S,
     const bool valid = pos < N;
     const float* srow = Sh + (size_t)(valid ? pos : 0) * D;
     bf16x8 shi[NKK], slo[NKK];
+    // se[kk] / so[kk]: s in the output layout for column chunks q = 2 (kk % 2) and
+    // q = 2 (kk % 2) + 1 of tile nt = kk / 2, from one lane-half swap of the loaded
+    // values (lanes l and l ^ 32 hold the two halves of a 16-column slice)
+    f32x4 se[NKK], so[NKK];
 #pragma unroll
     for (int kk = 0; kk < NKK; ++kk) {
       f32x4 x0 = {0.f, 0.f, 0.f, 0.f}, x1 = x0;
       if (valid) {
         x0 = *reinterpret_cast<const f32x4*>(srow + 16 * kk + 8 * hl);
         x1 = *reinterpret_cast<const f32x4*>(srow + 16 * kk + 8 * hl + 4);
+      }
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        float lo, hi;
+        lane_half_swap(x0[u], x1[u], lo, hi);
+        se[kk][u] = lo;
+        so[kk][u] = hi;
       }
 #pragma unroll
       for (int u = 0; u < 4; ++u) {
@@ -296,7 +307,7 @@ __global__ __launch_bounds__(kApplyWaves * 64) void k_apply_mfma(const float* S,
         if (pi >= 0) {
           v = *reinterpret_cast<const f32x4*>(O_probe + ((size_t)h * m + pi) * D + d0);
         } else {
-          v = *reinterpret_cast<const f32x4*>(srow + d0);
+          v = (q & 1) ? so[2 * nt + (q >> 1)] : se[2 * nt + (q >> 1)];
 #pragma unroll
           for (int u = 0; u < 4; ++u) v[u] += acc[4 * q + u] + wbias[d0 + u];
         }

@@ -70,6 +70,17 @@ __device__ __forceinline__ int xcd_remap(int w, int total) {
 // Workgroup barrier for LDS-only exchange: waits for this wave's LDS
 // operations, not for its outstanding global loads (which __syncthreads()'s
 // fence would drain, stalling a prefetch in flight).
+// v_permlane32_swap on two floats: lo gets a in lanes 0-31 and b of lane
+// l - 32 in lanes 32-63; hi gets a of lane l + 32 in lanes 0-31 and b in lanes
+// 32-63. Scalar arguments and results (the builtin mis-lowers when fed vector
+// elements directly).
+__device__ __forceinline__ void lane_half_swap(float a, float b, float& lo, float& hi) {
+  const auto sw = __builtin_amdgcn_permlane32_swap(__builtin_bit_cast(unsigned, a),
+                                                   __builtin_bit_cast(unsigned, b), false, false);
+  lo = __builtin_bit_cast(float, (unsigned)sw[0]);
+  hi = __builtin_bit_cast(float, (unsigned)sw[1]);
+}
+
 __device__ __forceinline__ void lds_barrier() {
   __atomic_signal_fence(__ATOMIC_SEQ_CST);
   __builtin_amdgcn_s_waitcnt(0xc07f);  // lgkmcnt(0); vmcnt and expcnt untouched
