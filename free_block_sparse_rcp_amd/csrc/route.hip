@@ -34,7 +34,8 @@ __global__ void k_copy_perm(const int32_t* perm, int N, int32_t* out) {
 // sigma[b,g] = tau * qbar_b . kbar_g over non-empty groups (-inf for empty).
 // A workgroup takes kRsBlocks consecutive blocks: their query rows are
 // gathered with 16-byte loads and summed per column (row groups combined in a
-// fixed order); the centroids are then staged in LDS kRsGroups rows at a time.
+// fixed order); the scores of the 16 blocks against kRsGroups groups at a time
+// are fp32 MFMA tiles (16 x 16 per wave), centroids read from L2.
 // grid (ceil(nb / kRsBlocks), H), block 256.
 constexpr int kRsBlocks = 16;
 constexpr int kRsGroups = 64;
@@ -49,11 +50,8 @@ __global__ __launch_bounds__(256) void k_route_scores(const void* Qv, const int3
   constexpr int CPR = ROWB / 16;             // 16-byte chunks per row
   constexpr int EPC = 16 / (int)sizeof(T);   // elements per chunk
   constexpr int RG = 256 / CPR;              // row groups
-  constexpr int KP = D + 1;
-  constexpr int BPT = kRsBlocks / 4;         // blocks per thread in the scores
   __shared__ float qb[kRsBlocks][D];
   __shared__ float part[RG][D];
-  __shared__ float kt[kRsGroups * KP];
   const int h = blockIdx.y, b0 = blockIdx.x * kRsBlocks, t = threadIdx.x;
   const char* Q = static_cast<const char*>(Qv) + (size_t)h * N * ROWB;
   const int32_t* qp = query_perm + (size_t)h * N;
@@ -102,28 +100,28 @@ __global__ __launch_bounds__(256) void k_route_scores(const void* Qv, const int3
   }
   const float tau = scale[h];
   const int32_t* off = group_off + (size_t)h * (G + 1);
-  const int gl = t % kRsGroups, bq = t / kRsGroups;
+  const int lane = t & 63, w = t >> 6, r16 = lane & 15, kq = lane >> 4;
+  static_assert(kRsBlocks == 16 && kRsGroups == 64 && D % 4 == 0, "16 x 64 score tiles on four waves");
   for (int g0 = 0; g0 < G; g0 += kRsGroups) {
-    __syncthreads();
-    for (int i = t; i < kRsGroups * D; i += 256) {
-      const int row = i / D, e = i % D, g = g0 + row;
-      kt[row * KP + e] = g < G ? kbar[((size_t)h * G + g) * D + e] : 0.f;
-    }
-    __syncthreads();
-    float acc[BPT];
+    // wave w: the 16 blocks x groups [g0 + 16 w, g0 + 16 w + 16) with
+    // v_mfma_f32_16x16x4_f32 (fp32 products and sums); lane (r16, kq) feeds
+    // block r16 (LDS) and group 16 w + r16 (read from L2) at d = k0 + kq, and
+    // receives blocks 4 kq .. 4 kq + 3 of group 16 w + r16
+    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+    const float* arow = &qb[r16][kq];
+    const float* brow = kbar + ((size_t)h * G + min(g0 + 16 * w + r16, G - 1)) * D + kq;
+    float bv[D / 4];
 #pragma unroll
-    for (int u = 0; u < BPT; ++u) acc[u] = 0.f;
-    for (int e = 0; e < D; ++e) {
-      const float kv = kt[gl * KP + e];
+    for (int u = 0; u < D / 4; ++u) bv[u] = brow[4 * u];
 #pragma unroll
-      for (int u = 0; u < BPT; ++u) acc[u] = fmaf(qb[bq + 4 * u][e], kv, acc[u]);
-    }
-    const int g = g0 + gl;
+    for (int u = 0; u < D / 4; ++u)
+      acc = __builtin_amdgcn_mfma_f32_16x16x4f32(arow[4 * u], bv[u], acc, 0, 0, 0);
+    const int g = g0 + 16 * w + r16;
     if (g < G) {
       const bool ne = off[g + 1] > off[g];
 #pragma unroll
-      for (int u = 0; u < BPT; ++u) {
-        const int j = bq + 4 * u;
+      for (int u = 0; u < 4; ++u) {
+        const int j = 4 * kq + u;
         if (j < nblk) {
           const float sc = ne ? tau * acc[u] : -__builtin_inff();
           sigma[((size_t)h * nb + b0 + j) * G + g] = sc;
