@@ -50,6 +50,8 @@ def load_traffic(workload):
 
 SPARSE_KERNEL = "k_attn_mfma<128, 128, 0>"   # sparsepr_attend's kernel (d=128, B_q=128)
 COPY_KERNEL = "neg_kernel"                    # the --calibration-copy-mib kernel
+PMC_KERNELS = ("k_attn_mfma|k_group_mean|k_gather_rows|k_apply_mfma|k_rowvec_mfma|k_route_scores|"
+               "k_metric|neg_kernel")              # the kernels the per-kernel traffic table covers
 
 
 def pmc_summary(fetch_csv, write_csv, workload, copy_mib):
@@ -146,9 +148,19 @@ def pmc_table(fetch_csv, write_csv, workload, copy_mib):
     text = "\n".join(lines)
     out = os.path.join(ROOT, "profiles", f"hbm_traffic_{workload}.md")
     with open(out, "w") as f:
+        runs = "\n".join(
+            f'timeout -s KILL 240 rocprofv3 --pmc {c} --kernel-include-regex "{PMC_KERNELS}" '
+            f"--output-format csv -d gpurun_out/pmc/{c} -o run -- python3 bench.py --steps 1 --warmup 0 "
+            f"--no-cpu-baseline --no-dense --calibration-copy-mib {copy_mib}"
+            for c in ("FETCH_SIZE", "WRITE_SIZE"))
         f.write(f"# HBM traffic per kernel, {workload}\n\n"
                 f"Scale factors from a {copy_mib} MiB copy: FETCH_SIZE x{fs:.3f}, WRITE_SIZE x{ws:.3f}. "
-                "Durations are the dispatch timestamps of the FETCH_SIZE run.\n\n" + text + "\n")
+                "Durations are the dispatch timestamps of the FETCH_SIZE run (one call; counters "
+                "serialise the dispatches). Commands (from the repository root, on one MI355X, each "
+                "counter in a run of its own):\n\n```\ncd /tmp && export TMPDIR=/tmp && cd -\n"
+                f"{runs}\npython3 bench.py --pmc-table gpurun_out/pmc/FETCH_SIZE/run_counter_collection.csv "
+                f"gpurun_out/pmc/WRITE_SIZE/run_counter_collection.csv --calibration-copy-mib {copy_mib}\n```\n\n"
+                + text + "\n")
     print(text)
 
 

@@ -268,6 +268,29 @@ __device__ __forceinline__ void attn_tile(const char* __restrict__ kb, const cha
     }
 }
 
+// Direct global->LDS loads of one tile by one wave, NJ per wave: every
+// row-table read first (a read placed after a direct load would wait for it,
+// as the load writes LDS), then the loads. words[j]: byte offset of the lane's
+// row-table entry (low 16 bits) and of its 16-byte chunk in the row (high 16
+// bits); us[j]: the 1 KB load index, or -1.
+template <int NJ>
+__device__ __forceinline__ void issue_rows(const char* base, const int* rows, const int* words,
+                                           const int* us, char* dst) {
+  uint32_t ro[NJ];
+#pragma unroll
+  for (int j = 0; j < NJ; ++j) {
+    const int x = words[j];
+    ro[j] = *reinterpret_cast<const uint32_t*>(reinterpret_cast<const char*>(rows) + (x & 0xffff)) +
+            ((uint32_t)x >> 16);
+  }
+#pragma unroll
+  for (int j = 0; j < NJ; ++j)
+    if (us[j] >= 0)
+      __builtin_amdgcn_global_load_lds((const void*)(base + ro[j]),
+                                       (__attribute__((address_space(3))) void*)(dst + us[j] * 1024),
+                                       16, 0, 0);
+}
+
 template <int D, int BQ, int MODE>
 __global__ __launch_bounds__(BQ * 2) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void k_attn_mfma(AttnArgs a) {
@@ -328,10 +351,16 @@ void k_attn_mfma(AttnArgs a) {
   const int ntiles = (total + KT - 1) / KT;
   int cursor = 0;
   // wave 0 writes the Kp/Vp row of each of a tile's 64 key positions
+  // (the sparse and probe modes keep byte offsets of rows, dense mode row indices)
+  constexpr bool kByteRows = MODE != ATTN_DENSE;
   auto fill_rows = [&](int tile) {
-    if (w == 0 && tile < ntiles) ridx[tile & 1][lane] = key_row(tile * KT + lane, total, ng, r_start, r_cum, cursor);
+    if (w == 0 && tile < ntiles) {
+      const int r = key_row(tile * KT + lane, total, ng, r_start, r_cum, cursor);
+      ridx[tile & 1][lane] = kByteRows ? (int)((uint32_t)r * ROWB) : r;
+    }
   };
-  // direct global->LDS loads: 1 KB per wave instruction, lane i -> chunk 64u + i of the tile
+  // dense mode: the row table holds row indices and each load computes its
+  // address on its own, which measures faster there than the batched form
   auto issue_tile = [&](int tile, char* kdst, char* vdst) {
     const int* rows = ridx[tile & 1];
 #pragma unroll
@@ -357,11 +386,43 @@ void k_attn_mfma(AttnArgs a) {
       }
     }
   };
+  // direct global->LDS loads: 1 KB per wave instruction, lane i -> chunk 64u + i
+  // of the tile. Each lane's part of load j is a packed word: byte offset of its
+  // row-table entry (low 16 bits) and of its 16-byte chunk in the row (high 16
+  // bits; pad chunks re-read chunk 0). Row-table entries are byte offsets of
+  // rows, so a load address is the head base plus one 32-bit sum.
+  auto lane_word = [&](int u, int ch) {
+    const int q = 64 * u + lane;
+    const int r = q / ch, cc = q - r * ch;
+    return (4 * r) | (((cc < CPR ? cc : 0) * 16) << 16);
+  };
+  int kw[KINS_W], vw[VINS_W], ku[KINS_W], vu[VINS_W];
+#pragma unroll
+  for (int j = 0; j < KINS_W; ++j) {
+    kw[j] = lane_word(w + NW * j, TG::KCH);
+    ku[j] = w + NW * j < TG::KINS ? w + NW * j : -1;
+  }
+#pragma unroll
+  for (int j = 0; j < VINS_W; ++j) {
+    vw[j] = lane_word(w + NW * j, TG::VCH);
+    vu[j] = w + NW * j < TG::VINS ? w + NW * j : -1;
+  }
+  // (a macro rather than a lambda: a lambda here is host-device, and host-side
+  // overload resolution rejects calls from it to device-only templates)
+#define ISSUE_TILE(TILE, KDST, VDST)                                                       \
+  do {                                                                                     \
+    if constexpr (kByteRows) {                                                             \
+      issue_rows<KINS_W>(Kh, ridx[(TILE) & 1], kw, ku, KDST);                              \
+      issue_rows<VINS_W>(Vh, ridx[(TILE) & 1], vw, vu, VDST);                              \
+    } else {                                                                               \
+      issue_tile(TILE, KDST, VDST);                                                        \
+    }                                                                                      \
+  } while (0)
 
   fill_rows(0);
   fill_rows(1);
   __syncthreads();
-  if (ntiles > 0) issue_tile(0, lds_k0, lds_v0);
+  if (ntiles > 0) ISSUE_TILE(0, lds_k0, lds_v0);
   __builtin_amdgcn_s_waitcnt(0);
   __syncthreads();
 
@@ -371,19 +432,20 @@ void k_attn_mfma(AttnArgs a) {
   const int voff = (4 * (grp >> 1) + (gl >> 2)) * TG::VP + (16 * (grp & 1) + 4 * (gl & 3)) * 2;
   // two tiles per trip: even tiles live in buffer 0, odd tiles in buffer 1
   for (int tile = 0; tile < ntiles; tile += 2) {
-    if (tile + 1 < ntiles) issue_tile(tile + 1, lds_k1, lds_v1);
+    if (tile + 1 < ntiles) ISSUE_TILE(tile + 1, lds_k1, lds_v1);
     fill_rows(tile + 2);
     attn_tile<D>(lds_k0 + koff, lds_v0 + voff, qreg, acc_o, m_run, l_run, c, tile * KT, total, hl);
     __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
     if (tile + 1 >= ntiles) break;
-    if (tile + 2 < ntiles) issue_tile(tile + 2, lds_k0, lds_v0);
+    if (tile + 2 < ntiles) ISSUE_TILE(tile + 2, lds_k0, lds_v0);
     fill_rows(tile + 3);
     attn_tile<D>(lds_k1 + koff, lds_v1 + voff, qreg, acc_o, m_run, l_run, c, (tile + 1) * KT, total, hl);
     __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
   }
 
+#undef ISSUE_TILE
   // ---- epilogue
   const float l_tot = l_run + __shfl_xor(l_run, 32);
   const float inv = l_tot > 0.f ? 1.0f / l_tot : 0.f;
