@@ -164,6 +164,44 @@ def pmc_table(fetch_csv, write_csv, workload, copy_mib):
     print(text)
 
 
+def semantic_comparator(args, p, Q, K, V, scale, inp, ref, rn, mask, err_sparsepr):
+    """Semantic block-sparse attention without residual correction at the same
+    executed-pair density (no probes, so the whole budget goes to the sparse
+    pass): its error on the rows SparsePR leaves unprobed, the error reduction
+    1 - e(SparsePR) / e(semantic), and its call time. Runs after the timed
+    region."""
+    import dataclasses
+    import numpy as np
+    import torch
+    from free_block_sparse_rcp_amd import binding
+
+    ps = dataclasses.replace(p, partition_mode=binding.SEMANTIC, n_probes=0, rank=0)
+    dev = Q.device
+    cop = binding.SparsePR(ps, dev)
+    cidx = cop.upload_indices(init_idx=inp.init_idx)
+    log("[bench] semantic comparator")
+    cop.run(Q, K, V, scale, cidx)
+    torch.cuda.synchronize()
+    n = max(1, min(args.steps, 3))
+    evs = [dict() for _ in range(n)]
+    for i in range(n):
+        cop.run(Q, K, V, scale, cidx, events=evs[i])
+    torch.cuda.synchronize()
+    call_ms = float(np.mean([e["start"].elapsed_time(e["apply"]) for e in evs]))
+    with torch.no_grad():
+        ec = ((cop.buffers.O.float() - ref).norm(dim=2) / rn)[mask]
+    E = int(cop.buffers.executed_pairs.sum().item())
+    out = {"rel_l2_mean_unprobed": float(ec.mean()),
+           "error_reduction": 1.0 - err_sparsepr / float(ec.mean()),
+           "realized_density": E / (p.heads * float(p.n_tokens) ** 2),
+           "call_ms": call_ms,
+           "definition": "k-means (same G, T, init rows) on raw key rows and on raw query rows, "
+                         "queries in (cluster, token) order, same routing rule and kernels, "
+                         "no probes or correction"}
+    del cop
+    return out
+
+
 def cpu_baseline(wl, inp, block_stride):
     """The fp64 oracle, as it stands, on head 0 of the same workload: every
     stage in the pages' order; the block-sparse attention step runs on every
@@ -238,6 +276,8 @@ def main():
                     help="oracle samples every n-th query block (0: chosen by workload size)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-dense", action="store_true")
+    ap.add_argument("--no-comparator", action="store_true",
+                    help="skip the semantic block-sparse comparator (error reduction)")
     ap.add_argument("--overlap", action="store_true",
                     help="attend the blocks holding probe rows first and run the probe fit on a "
                          "second stream while the other blocks are attended (default: the five "
@@ -378,6 +418,9 @@ def main():
                        "rel_l2_mean_unprobed": float(e.mean()),
                        "rel_l2_p99_unprobed": float(torch.quantile(e[:1_000_000].float(), 0.99)),
                        "hard_drop_rel_l2_mean": float(e0.mean())}
+        if not args.no_comparator:
+            quality["semantic"] = semantic_comparator(args, p, Q, K, V, scale, inp, ref, rn, mask,
+                                                      float(e.mean()))
 
     traffic = load_traffic(wl.name)
     roofline = {"bound": "mfma", "kernel": "k_attn_mfma (sparsepr_attend)",

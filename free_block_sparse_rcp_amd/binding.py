@@ -32,6 +32,7 @@ EXPORTS = ("sparsepr_abi_version", "sparsepr_status_string", "sparsepr_last_erro
            "sparsepr_attend_subset", "sparsepr_probe_fit", "sparsepr_apply",
            "sparsepr_dense_attention")
 BLOCKS_ALL, BLOCKS_WITH_PROBE, BLOCKS_WITHOUT_PROBE = 0, 1, 2
+RESPONSE_COUPLED, RANDOM_BLOCK, SEMANTIC = 0, 1, 2   # partition modes
 
 
 class CParams(ctypes.Structure):
@@ -165,6 +166,11 @@ class Buffers:
     rank_eff: torch.Tensor
     O: torch.Tensor
     workspace: torch.Tensor
+    # semantic mode only: the query partition (its key_perm is the query order)
+    query_label: Optional[torch.Tensor] = None
+    query_order: Optional[torch.Tensor] = None
+    query_group_off: Optional[torch.Tensor] = None
+    query_centroid: Optional[torch.Tensor] = None
 
 
 def alloc_buffers(p: Params, device) -> Buffers:
@@ -173,6 +179,11 @@ def alloc_buffers(p: Params, device) -> Buffers:
     dt = torch_dtype(p)
     i32 = dict(dtype=torch.int32, device=device)
     f32 = dict(dtype=torch.float32, device=device)
+    semantic = {}
+    if p.partition_mode == SEMANTIC:
+        semantic = dict(query_label=torch.empty(H, N, **i32), query_order=torch.empty(H, N, **i32),
+                        query_group_off=torch.empty(H, G + 1, **i32),
+                        query_centroid=torch.empty(H, G, D, **f32))
     return Buffers(
         key_label=torch.empty(H, N, **i32), key_perm=torch.empty(H, N, **i32),
         group_off=torch.empty(H, G + 1, **i32), key_centroid=torch.empty(H, G, D, **f32),
@@ -186,7 +197,7 @@ def alloc_buffers(p: Params, device) -> Buffers:
         U=torch.empty(H, D, max(p.rank, 1), **f32),
         Theta=torch.empty(H, D + 1, max(p.rank, 1), **f32),
         rank_eff=torch.empty(H, **i32), O=torch.empty(H, N, D, dtype=dt, device=device),
-        workspace=torch.empty(workspace_bytes(p), dtype=torch.uint8, device=device))
+        workspace=torch.empty(workspace_bytes(p), dtype=torch.uint8, device=device), **semantic)
 
 
 # ------------------------------------------------------------ stage calls
@@ -200,6 +211,19 @@ def partition(p: Params, Q, K, V, scale, sample_idx, init_idx, b: Buffers, rand_
         _ptr(rand_key_perm), _ptr(b.key_label), _ptr(b.key_perm), _ptr(b.group_off),
         _ptr(b.key_centroid), _ptr(b.Kp), _ptr(b.Vp), _ptr(dbg_assign_scores),
         _ptr(b.workspace), b.workspace.numel(), _stream(K.device)))
+
+
+def partition_queries(p: Params, Q, init_idx, b: Buffers,
+                      dbg_assign_scores: Optional[torch.Tensor] = None) -> None:
+    """Semantic mode: the partition stage run on the queries (no gather); its
+    group-contiguous order b.query_order is the query order for route."""
+    lib = load()
+    cp = c_params(p)
+    _check(lib.sparsepr_partition(
+        ctypes.byref(cp), None, _ptr(Q), None, None, None, _ptr(init_idx), None,
+        _ptr(b.query_label), _ptr(b.query_order), _ptr(b.query_group_off),
+        _ptr(b.query_centroid), None, None, _ptr(dbg_assign_scores),
+        _ptr(b.workspace), b.workspace.numel(), _stream(Q.device)))
 
 
 def route(p: Params, Q, scale, b: Buffers, rand_query_perm=None, dbg_coords=None,
@@ -277,6 +301,8 @@ class SparsePR:
         if p.partition_mode == 0:
             out["sample_idx"] = index_tensor(sample_idx, p.n_tokens, p.n_samples, "sample_idx", dev, True)
             out["init_idx"] = index_tensor(init_idx, p.n_tokens, p.n_groups, "init_idx", dev, True)
+        elif p.partition_mode == SEMANTIC:
+            out["init_idx"] = index_tensor(init_idx, p.n_tokens, p.n_groups, "init_idx", dev, True)
         else:
             out["rand_key_perm"] = index_tensor(rand_key_perm, p.n_tokens, p.n_tokens, "rand_key_perm", dev, True)
             out["rand_query_perm"] = index_tensor(rand_query_perm, p.n_tokens, p.n_tokens, "rand_query_perm", dev, True)
@@ -313,8 +339,12 @@ class SparsePR:
         mark("start")
         partition(p, Q, K, V, scale, idx.get("sample_idx"), idx.get("init_idx"), b,
                   rand_key_perm=idx.get("rand_key_perm"))
+        qorder = idx.get("rand_query_perm")
+        if p.partition_mode == SEMANTIC:
+            partition_queries(p, Q, idx["init_idx"], b)
+            qorder = b.query_order
         mark("partition")
-        route(p, Q, scale, b, rand_query_perm=idx.get("rand_query_perm"))
+        route(p, Q, scale, b, rand_query_perm=qorder)
         mark("route")
         if not overlap:
             attend(p, Q, scale, b)

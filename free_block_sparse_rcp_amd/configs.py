@@ -31,7 +31,7 @@ class Params:
     n_probes: int            # m
     rank: int                # k
     ridge_lambda: float      # lambda
-    partition_mode: int = 0  # 0 response-coupled, 1 random-block
+    partition_mode: int = 0  # 0 response-coupled, 1 random-block, 2 semantic comparator
 
     @property
     def n_blocks(self) -> int:

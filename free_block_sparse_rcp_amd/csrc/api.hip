@@ -136,13 +136,15 @@ static int32_t make_dims(const sparsepr_params* p, bool full, Dims* d) {
   d->split_len = d->N;
   if (!full) return SPARSEPR_OK;
   if (p->reserved != 0) return fail(SPARSEPR_ERR_INVALID_ARG, "reserved must be 0");
-  if (p->partition_mode != SPARSEPR_RESPONSE_COUPLED && p->partition_mode != SPARSEPR_RANDOM_BLOCK)
-    return fail(SPARSEPR_ERR_INVALID_ARG, "partition_mode must be 0 or 1 (got %d)", p->partition_mode);
+  if (p->partition_mode != SPARSEPR_RESPONSE_COUPLED && p->partition_mode != SPARSEPR_RANDOM_BLOCK &&
+      p->partition_mode != SPARSEPR_SEMANTIC)
+    return fail(SPARSEPR_ERR_INVALID_ARG, "partition_mode must be 0, 1 or 2 (got %d)", p->partition_mode);
   if (p->n_groups < 1 || p->n_groups > 1024 || p->n_groups > p->n_tokens)
     return fail(SPARSEPR_ERR_INVALID_ARG, "n_groups must be in [1, min(N, 1024)] (got %d)", p->n_groups);
-  if (p->partition_mode == SPARSEPR_RESPONSE_COUPLED) {
-    if (p->n_samples < 1 || p->n_samples > p->n_tokens)
-      return fail(SPARSEPR_ERR_INVALID_ARG, "n_samples must be in [1, N] (got %d)", p->n_samples);
+  if (p->partition_mode == SPARSEPR_RESPONSE_COUPLED &&
+      (p->n_samples < 1 || p->n_samples > p->n_tokens))
+    return fail(SPARSEPR_ERR_INVALID_ARG, "n_samples must be in [1, N] (got %d)", p->n_samples);
+  if (p->partition_mode != SPARSEPR_RANDOM_BLOCK) {
     if (p->kmeans_iters < 1)
       return fail(SPARSEPR_ERR_INVALID_ARG, "kmeans_iters must be >= 1 (got %d)", p->kmeans_iters);
   }
@@ -245,11 +247,15 @@ int32_t sparsepr_partition(const sparsepr_params* params, const void* Q, const v
   int32_t s = make_dims(params, true, &d);
   if (s != SPARSEPR_OK) return s;
   SPR_REQUIRE(K, "K");
-  SPR_REQUIRE(V, "V");
+  if ((Kp == nullptr) != (Vp == nullptr))
+    return fail(SPARSEPR_ERR_INVALID_ARG, "Kp and Vp must both be given or both be NULL");
+  if (Kp != nullptr) SPR_REQUIRE(V, "V");
   if (d.mode == SPARSEPR_RESPONSE_COUPLED) {
     SPR_REQUIRE(Q, "Q");
     SPR_REQUIRE(scale, "scale");
     SPR_REQUIRE(sample_idx, "sample_idx");
+    SPR_REQUIRE(init_idx, "init_idx");
+  } else if (d.mode == SPARSEPR_SEMANTIC) {
     SPR_REQUIRE(init_idx, "init_idx");
   } else {
     SPR_REQUIRE(rand_key_perm, "rand_key_perm");
@@ -258,8 +264,6 @@ int32_t sparsepr_partition(const sparsepr_params* params, const void* Q, const v
   SPR_REQUIRE(key_perm, "key_perm");
   SPR_REQUIRE(group_off, "group_off");
   SPR_REQUIRE(key_centroid, "key_centroid");
-  SPR_REQUIRE(Kp, "Kp");
-  SPR_REQUIRE(Vp, "Vp");
   if ((s = check_ws(d, workspace, workspace_bytes)) != SPARSEPR_OK) return s;
   return hip_status(launch_partition(d, Q, K, V, scale, sample_idx, init_idx, rand_key_perm,
                                      key_label, key_perm, group_off, key_centroid, Kp, Vp,
@@ -281,7 +285,7 @@ int32_t sparsepr_route(const sparsepr_params* params, const void* Q, const float
   SPR_REQUIRE(scale, "scale");
   SPR_REQUIRE(key_centroid, "key_centroid");
   SPR_REQUIRE(group_off, "group_off");
-  if (d.mode == SPARSEPR_RANDOM_BLOCK) SPR_REQUIRE(rand_query_perm, "rand_query_perm");
+  if (d.mode != SPARSEPR_RESPONSE_COUPLED) SPR_REQUIRE(rand_query_perm, "rand_query_perm");
   SPR_REQUIRE(query_perm, "query_perm");
   SPR_REQUIRE(block_ptr, "block_ptr");
   SPR_REQUIRE(block_groups, "block_groups");

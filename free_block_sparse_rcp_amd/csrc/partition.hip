@@ -672,6 +672,12 @@ __global__ __launch_bounds__(256) void k_group_mean(const void* Kv, const int32_
 
 // Random-block variant: label of key perm[i] is the run g with
 // floor(gN/G) <= i < floor((g+1)N/G). grid (ceil(N/256), H).
+// M = I per head (d x d, fp64). grid (ceil(d*d/256), H), block 256.
+__global__ void k_identity_f64(int D, double* M) {
+  const int i = blockIdx.x * 256 + threadIdx.x;
+  if (i < D * D) M[(size_t)blockIdx.y * D * D + i] = (i / D == i % D) ? 1.0 : 0.0;
+}
+
 __global__ void k_random_labels(const int32_t* perm, int N, int G, int32_t* labels) {
   const int i = blockIdx.x * 256 + threadIdx.x;
   if (i >= N) return;
@@ -784,8 +790,13 @@ static hipError_t partition_impl(const Dims& d, const void* Q, const void* K, co
     return hipSuccess;
   };
 
-  if (d.mode == SPARSEPR_RESPONSE_COUPLED) {
-    k_metric<BF16, D><<<dim3(d.H, D / 16), 256, 0, st>>>(Q, scale, sample_idx, d.S, d.N, M);
+  if (d.mode != SPARSEPR_RANDOM_BLOCK) {
+    if (d.mode == SPARSEPR_RESPONSE_COUPLED) {
+      k_metric<BF16, D><<<dim3(d.H, D / 16), 256, 0, st>>>(Q, scale, sample_idx, d.S, d.N, M);
+    } else {
+      // semantic mode: plain squared distances between raw rows
+      k_identity_f64<<<dim3((D * D + 255) / 256, d.H), 256, 0, st>>>(D, M);
+    }
     SPR_CHECK_LAUNCH();
     k_centroid_init<BF16, D><<<per_group, D, 0, st>>>(K, init_idx, d.N, d.G, kbar);
     SPR_CHECK_LAUNCH();
@@ -819,6 +830,7 @@ static hipError_t partition_impl(const Dims& d, const void* Q, const void* K, co
     hipError_t e = regroup();
     if (e != hipSuccess) return e;
   }
+  if (Kp == nullptr) return hipSuccess;
   constexpr int ROWB = D * (BF16 ? 2 : 4);
   const size_t nchunks = (size_t)d.N * (ROWB / 16);
   k_gather_rows<ROWB><<<dim3((unsigned)((nchunks + 255) / 256), d.H), 256, 0, st>>>(

@@ -25,9 +25,11 @@ __global__ void k_make_qkeys(const int32_t* g1, const float* v, int N, uint64_t*
   if (dbg_val) dbg_val[o] = x;
 }
 
-__global__ void k_copy_perm(const int32_t* perm, int N, int32_t* out) {
+// out[h] = perm (head stride 0: one order shared by every head) or perm[h]
+// (head stride N: an order per head).
+__global__ void k_copy_perm(const int32_t* perm, size_t head_stride, int N, int32_t* out) {
   const int i = blockIdx.x * 256 + threadIdx.x;
-  if (i < N) out[(size_t)blockIdx.y * N + i] = clamp_idx(perm[i], N);
+  if (i < N) out[(size_t)blockIdx.y * N + i] = clamp_idx(perm[blockIdx.y * head_stride + i], N);
 }
 
 // Mean query of each block and its scores against every group:
@@ -334,7 +336,8 @@ hipError_t launch_route(const Dims& d, const void* Q, const float* scale, const 
       kout = tk;
     }
   } else {
-    k_copy_perm<<<rows256, 256, 0, st>>>(rand_query_perm, d.N, query_perm);
+    const size_t stride = d.mode == SPARSEPR_SEMANTIC ? (size_t)d.N : 0;
+    k_copy_perm<<<rows256, 256, 0, st>>>(rand_query_perm, stride, d.N, query_perm);
     SPR_CHECK_LAUNCH();
   }
   const dim3 blocks(d.nb, d.H);

@@ -73,6 +73,7 @@ extern "C" {
 /* partition modes */
 #define SPARSEPR_RESPONSE_COUPLED 0
 #define SPARSEPR_RANDOM_BLOCK 1     /* ablation without response-coupled partitioning */
+#define SPARSEPR_SEMANTIC 2         /* comparator: k-means on raw key (and query) features */
 
 /*
  * Parameters of one call. The executed-pair budget follows the pages' rule
@@ -94,7 +95,7 @@ typedef struct sparsepr_params {
   int32_t n_probes;       /* m, 0 <= m <= N: exact probe rows per head */
   int32_t rank;           /* k, 0 <= k <= d: residual subspace rank */
   double ridge_lambda;    /* lambda > 0: ridge penalty (bias unpenalised) */
-  int32_t partition_mode; /* SPARSEPR_RESPONSE_COUPLED or SPARSEPR_RANDOM_BLOCK */
+  int32_t partition_mode; /* SPARSEPR_RESPONSE_COUPLED, SPARSEPR_RANDOM_BLOCK or SPARSEPR_SEMANTIC */
   int32_t reserved;       /* must be 0 */
 } sparsepr_params;
 
@@ -127,6 +128,12 @@ int32_t sparsepr_workspace_bytes(const sparsepr_params* params, size_t* bytes);
  * Random-block mode: the permutation rand_key_perm is cut into G runs,
  * run g = positions floor(gN/G) .. floor((g+1)N/G)-1; sample_idx, init_idx
  * are ignored.
+ * Semantic mode, the comparator the pages measure against (arxivdaily
+ * 2608.18484, English abstract: semantic block-sparse attention without
+ * residual correction): the same Lloyd k-means on the raw key rows, i.e.
+ * metric M = I and centroid g starting at K[init_idx[g]]; Q, scale and
+ * sample_idx are ignored. Run with K := Q it clusters the queries, and its
+ * key_perm is then the semantic query order for sparsepr_route.
  *
  * Inputs : Q, K, V [H,N,d] dtype; scale [H] fp32 (tau per head);
  *          sample_idx [S] int32 and init_idx [G] int32 (response mode;
@@ -139,7 +146,8 @@ int32_t sparsepr_workspace_bytes(const sparsepr_params* params, size_t* bytes);
  *            group_off[g+1]-1]; empty groups have equal offsets;
  *          key_centroid [H,G,d] fp32 mean key of each group (for an empty
  *            group: its last centroid; it is excluded downstream);
- *          Kp, Vp [H,N,d] dtype: K and V rows gathered in key_perm order;
+ *          Kp, Vp [H,N,d] dtype: K and V rows gathered in key_perm order
+ *            (both NULL: no gather; V is then not read and may be NULL);
  *          dbg_assign_scores [H,N,G] fp32 or NULL: the scores the final
  *            assignment took its argmin over, score(j,g) = ||r_j - c_g||^2
  *            - ||r_j||^2 (argmin over g of these is key_label).
@@ -160,7 +168,10 @@ int32_t sparsepr_partition(const sparsepr_params* params, const void* Q, const v
  * C[q,g] = tau * q . kbar_g over non-empty groups. Response mode: each
  * query's dominant group g1 = argmax_g C (lowest g on ties) and value
  * v = C[q,g1]; queries are ordered by (g1 ascending, v descending, token
- * ascending). Random-block mode: the order is rand_query_perm. The order is
+ * ascending). Random-block mode: the order is rand_query_perm. Semantic
+ * mode: the order is given per head in rand_query_perm [H,N] (the key_perm
+ * of sparsepr_partition run in semantic mode on the queries: queries sorted
+ * by (query cluster, token)). The order is
  * cut into blocks of B_q (the last may be shorter). Each block b scores
  * groups by sigma[b,g] = tau * qbar_b . kbar_g (qbar_b = the block's mean
  * query, equal to the block mean of C), ranks non-empty groups by (sigma
@@ -168,7 +179,8 @@ int32_t sparsepr_partition(const sparsepr_params* params, const void* Q, const v
  * key count is <= kappa (at least one group).
  *
  * Inputs : Q [H,N,d]; scale [H]; key_centroid [H,G,d]; group_off [H,G+1];
- *          rand_query_perm [N] int32 (random-block mode, else may be NULL).
+ *          rand_query_perm [N] int32 (random-block mode) or [H,N] int32
+ *          (semantic mode), else may be NULL.
  * Outputs: query_perm [H,N] int32 position -> query token;
  *          block_ptr [H,nb+1] int32 and block_groups [H, nb*G] int32: CSR of
  *            the selected groups of each block, ascending; head h's offsets

@@ -155,6 +155,23 @@ def random_block_labels(rand_key_perm, n_groups):
     return lab
 
 
+def semantic_order(X, init_idx, iters, n_groups):
+    """Semantic block-sparse comparator ([AD]: the error reduction is measured
+    against semantic block-sparse attention without residual correction).
+
+    Reading: the pages name the comparator but do not define it. Its
+    partition here is the same Lloyd k-means as ``kmeans`` (T steps, initial
+    centroids = the rows at ``init_idx``, lowest-index ties, empty groups
+    keep their centroid) on the raw feature rows X instead of on response
+    profiles, and the rows are ordered by (cluster, token). Applied to K it
+    gives the key groups; applied to Q, the query order.
+    Returns (labels, order).
+    """
+    km = kmeans(X, init_idx, iters)
+    order, _, _ = group_members(km.labels, n_groups)
+    return km.labels, order
+
+
 # ---------------------------------------------------------------------------
 # Query coordinates, grouping and shared routing  ([AD], [PC], [SK])
 # ---------------------------------------------------------------------------
@@ -415,9 +432,11 @@ def sparsepr_head(Q, K, V, scale, *, q_block, n_groups, kmeans_iters, density, n
     """The whole operator for one head, in the pages' order ([AD]).
 
     1. keys: response profiles under the sampled queries, k-means, paired K/V
-       groups (random-block variant: a seeded permutation cut into G runs);
+       groups (random-block variant: a seeded permutation cut into G runs;
+       semantic comparator, partition_mode 2: k-means on the raw key rows);
     2. queries: coordinates against the key-group centroids, grouped into
-       blocks of B_q (random-block variant: a seeded permutation);
+       blocks of B_q (random-block variant: a seeded permutation; semantic
+       comparator: k-means on the raw query rows, ordered by cluster);
     3. route each block to its best groups within the key budget;
     4. block-sparse attention; exact attention on the probe rows;
     5. weighted ridge fit of the probe residuals inside their subspace;
@@ -433,6 +452,9 @@ def sparsepr_head(Q, K, V, scale, *, q_block, n_groups, kmeans_iters, density, n
         R = key_responses(Q, K, scale, sample_idx)
         km = kmeans(R, init_idx, kmeans_iters, keep_scores=keep_scores)
         labels = km.labels
+    elif partition_mode == 2:
+        km = kmeans(K, init_idx, kmeans_iters, keep_scores=keep_scores)
+        labels = km.labels
     else:
         labels = random_block_labels(rand_key_perm, n_groups)
     key_perm, group_off, sizes = group_members(labels, n_groups)
@@ -441,6 +463,8 @@ def sparsepr_head(Q, K, V, scale, *, q_block, n_groups, kmeans_iters, density, n
     g1, v = dominant_groups(C, sizes)
     if partition_mode == 0:
         qperm = query_order(g1, v)
+    elif partition_mode == 2:
+        _, qperm = semantic_order(Q, init_idx, kmeans_iters, n_groups)
     else:
         qperm = np.asarray(rand_query_perm, np.int64)
     blocks = query_blocks(qperm, q_block)

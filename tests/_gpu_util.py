@@ -76,8 +76,14 @@ def run_pipeline(wl: Workload, heads=None, dbg: bool = True, dbg_heads_ok: bool 
         d["sigma"] = torch.full((H, nb, G), float("nan"), **f32)
     binding.partition(p, Q, K, V, scale, idx.get("sample_idx"), idx.get("init_idx"), b,
                       rand_key_perm=idx.get("rand_key_perm"),
-                      dbg_assign_scores=d.get("assign") if p.partition_mode == 0 else None)
-    binding.route(p, Q, scale, b, rand_query_perm=idx.get("rand_query_perm"),
+                      dbg_assign_scores=d.get("assign") if p.partition_mode != 1 else None)
+    qorder = idx.get("rand_query_perm")
+    if p.partition_mode == binding.SEMANTIC:
+        if dbg:
+            d["qassign"] = torch.full((H, N, G), float("nan"), dtype=torch.float32, device=dev)
+        binding.partition_queries(p, Q, idx["init_idx"], b, dbg_assign_scores=d.get("qassign"))
+        qorder = b.query_order
+    binding.route(p, Q, scale, b, rand_query_perm=qorder,
                   dbg_coords=d.get("coords"), dbg_dominant=d.get("dom"),
                   dbg_dominant_val=d.get("domval"), dbg_block_score=d.get("sigma"))
     binding.attend(p, Q, scale, b)

@@ -106,6 +106,18 @@ def test_null_pointers_and_small_workspace_are_rejected(lib):
     st = lib.sparsepr_route(ctypes.byref(p), fake, fake, fake, fake, None, fake, fake, fake, fake,
                             None, None, None, None, fake, 1 << 40, None)
     assert st == 1 and "rand_query_perm" in lib.sparsepr_last_error().decode()
+    # semantic comparator mode: init_idx is required, Kp/Vp come as a pair,
+    # and route needs the per-head query order
+    p.partition_mode = 2
+    st = lib.sparsepr_partition(ctypes.byref(p), None, fake, fake, None, None, None, None, fake,
+                                fake, fake, fake, fake, fake, None, fake, 1 << 40, None)
+    assert st == 1 and "init_idx" in lib.sparsepr_last_error().decode()
+    st = lib.sparsepr_partition(ctypes.byref(p), None, fake, fake, None, None, fake, None, fake,
+                                fake, fake, fake, fake, None, None, fake, 1 << 40, None)
+    assert st == 1 and "Kp and Vp" in lib.sparsepr_last_error().decode()
+    st = lib.sparsepr_route(ctypes.byref(p), fake, fake, fake, fake, None, fake, fake, fake, fake,
+                            None, None, None, None, fake, 1 << 40, None)
+    assert st == 1 and "rand_query_perm" in lib.sparsepr_last_error().decode()
     # attend with no lse
     p.partition_mode = 0
     st = lib.sparsepr_attend(ctypes.byref(p), fake, fake, fake, fake, fake, fake, fake, fake, fake,

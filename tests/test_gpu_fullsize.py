@@ -52,6 +52,10 @@ CASES = {
     "sweep": configs.SWEEP,
     "sweep_rho15_m32_random": _sweep_point(0.15, 32, 1, "sweep_rho15_m32_random"),
     "sweep_rho30_m256": _sweep_point(0.30, 256, 0, "sweep_rho30_m256"),
+    # the semantic comparator the bench runs beside the hunyuan call
+    "hunyuan_semantic": replace(configs.HUNYUAN, name="hunyuan_semantic",
+                                params=replace(configs.HUNYUAN.params, partition_mode=2,
+                                               n_probes=0, rank=0)),
 }
 
 
@@ -69,12 +73,14 @@ class FullRun:
         self.bench = run_pipeline(wl, dbg=False, inp=self.inp)
         print(f"[gpu-full] {name}: debug run", flush=True)
         self.dbg = run_pipeline(wl, dbg=True, inp=self.inp)
-        self.prev = None
-        if self.p.partition_mode == 0 and self.p.kmeans_iters > 1:
+        self.prev = self.prev_q = None
+        if self.p.partition_mode != 1 and self.p.kmeans_iters > 1:
             print(f"[gpu-full] {name}: run with T-1 k-means iterations", flush=True)
             pp = replace(self.p, kmeans_iters=self.p.kmeans_iters - 1)
             r = run_pipeline(wl, dbg=False, inp=self.inp, p=pp)
             self.prev = r.b.key_centroid.detach().cpu().numpy()
+            if r.b.query_centroid is not None:
+                self.prev_q = r.b.query_centroid.detach().cpu().numpy()
             del r
         torch.cuda.synchronize()
         H = self.p.heads
@@ -110,8 +116,13 @@ def test_debug_run_matches_bench_run(fr):
     name = fr.wl.name
     a, b = fr.bench.b, fr.dbg.b
     for n in ("key_label", "key_perm", "group_off", "key_centroid", "Kp", "Vp", "query_perm",
-              "block_ptr", "executed_pairs", "S", "lse", "O_probe", "U", "Theta", "rank_eff", "O"):
+              "block_ptr", "executed_pairs", "S", "lse", "rank_eff", "O"):
         assert torch.equal(getattr(a, n), getattr(b, n)), n
+    # written extents only (buffers keep one slot when m or k is 0)
+    m, k = fr.p.n_probes, fr.p.rank
+    assert torch.equal(a.O_probe[:, :m], b.O_probe[:, :m])
+    assert torch.equal(a.U[:, :, :k], b.U[:, :, :k])
+    assert torch.equal(a.Theta[:, :, :k], b.Theta[:, :, :k])
     ptr = a.block_ptr.cpu().numpy()
     ga, gb = a.block_groups.cpu().numpy(), b.block_groups.cpu().numpy()
     for h in range(fr.p.heads):
@@ -125,7 +136,7 @@ def test_partition_full(fr):
     for h in fr.heads:
         print(f"[gpu-full] {name} partition head {h}", flush=True)
         lab = fr.get("key_label", h)
-        if p.partition_mode == 0:
+        if p.partition_mode != 1:
             scores = fr.get("assign", h)
             assert np.array_equal(orc.argmin_lowest(scores), lab)
         else:
@@ -144,10 +155,14 @@ def test_partition_full(fr):
         if fr.prev is not None:
             # dumped scores of the last iteration against fp64 from the previous centroids
             keys = np.sort(rng.choice(p.n_tokens, 4096, replace=False))
-            tau = float(fr.inp.scale[h])
-            Qs = fr.inp.Q[h][fr.inp.sample_idx].astype(np.float64)
-            R = tau * K[keys] @ Qs.T
-            C = tau * fr.prev[h].astype(np.float64) @ Qs.T
+            if p.partition_mode == 0:
+                tau = float(fr.inp.scale[h])
+                Qs = fr.inp.Q[h][fr.inp.sample_idx].astype(np.float64)
+                R = tau * K[keys] @ Qs.T
+                C = tau * fr.prev[h].astype(np.float64) @ Qs.T
+            else:
+                # semantic comparator: raw key rows, metric I
+                R, C = K[keys], fr.prev[h].astype(np.float64)
             ref = orc.squared_distances(R, C) - (R * R).sum(1)[:, None]
             scale_ref = (C * C).sum(1)[None, :] + 2 * np.abs(R @ C.T)
             assert np.all(np.abs(scores[keys] - ref) <= SCORE_TOL * scale_ref + 1e-6)
@@ -178,6 +193,22 @@ def test_route_full(fr):
             C = orc.query_coordinates(Q[rows], kb, tau)
             assert rel_l2(coords[rows][:, ne], C[:, ne]) < SCORE_TOL
             assert np.all(np.isneginf(coords[rows][:, ~ne]))
+        elif p.partition_mode == 2:
+            # semantic comparator: query labels from the dumped query-side scores,
+            # queries in (cluster, token) order
+            qlab = fr.get("query_label", h)
+            qsc = fr.get("qassign", h)
+            assert np.array_equal(orc.argmin_lowest(qsc), qlab)
+            assert np.array_equal(orc.group_members(qlab, p.n_groups)[0], qperm)
+            Q = fr.inp.Q[h].astype(np.float64)
+            rows = np.sort(rng.choice(p.n_tokens, 4096, replace=False))
+            C = fr.prev_q[h].astype(np.float64)
+            ref = orc.squared_distances(Q[rows], C) - (Q[rows] ** 2).sum(1)[:, None]
+            bound = (C * C).sum(1)[None, :] + 2 * np.abs(Q[rows] @ C.T)
+            assert np.all(np.abs(qsc[rows] - ref) <= SCORE_TOL * bound + 1e-6)
+            tau = float(fr.inp.scale[h])
+            kb = fr.get("key_centroid", h).astype(np.float64)
+            ne = sizes > 0
         else:
             assert np.array_equal(qperm, fr.inp.rand_query_perm)
             Q = fr.inp.Q[h].astype(np.float64)
@@ -238,6 +269,13 @@ def test_probes_fit_apply_full(fr):
     for h in fr.heads:
         print(f"[gpu-full] {name} probes/fit/apply head {h}", flush=True)
         qperm = fr.get("query_perm", h)
+        if p.n_probes == 0:
+            # no probes: no correction, the output is the sparse output in token order
+            assert int(fr.get("rank_eff", h)) == 0
+            O = fr.get("O", h)
+            rows_q = np.sort(rng.choice(N, 4096, replace=False))
+            assert np.array_equal(O[qperm[rows_q]], bf16_round(fr.get("S", h)[rows_q]))
+            continue
         Q, K, V = (x[h] for x in (fr.inp.Q, fr.inp.K, fr.inp.V))
         tau = float(fr.inp.scale[h])
         pos = orc.probe_positions(N, p.n_probes)
@@ -279,6 +317,10 @@ def test_overlapped_call_matches(fr):
     b = fr.bench
     op.run(b.Q, b.K, b.V, b.scale, b.idx, overlap=True)
     torch.cuda.synchronize()
-    for n in ("O", "S", "lse", "U", "Theta", "O_probe", "query_perm", "key_perm"):
+    for n in ("O", "S", "lse", "query_perm", "key_perm"):
         assert torch.equal(getattr(op.buffers, n), getattr(b.b, n)), n
+    m, k = fr.p.n_probes, fr.p.rank
+    assert torch.equal(op.buffers.O_probe[:, :m], b.b.O_probe[:, :m])
+    assert torch.equal(op.buffers.U[:, :, :k], b.b.U[:, :, :k])
+    assert torch.equal(op.buffers.Theta[:, :, :k], b.b.Theta[:, :, :k])
     del op

@@ -337,6 +337,64 @@ def test_random_block_variant():
         assert rel_l2(g["O"], o["O"]) < TOL["bf16"]
 
 
+SEMANTIC_WORKLOADS = {
+    "bf16": small_bf16(name="semantic", mode=2, m=0, k=0, seed=21),
+    "f32": replace(configs.TINY, params=replace(configs.TINY.params, partition_mode=2, n_probes=0,
+                                                 rank=0)),
+}
+
+
+@pytest.mark.parametrize("name", list(SEMANTIC_WORKLOADS))
+def test_semantic_comparator(name):
+    """Semantic comparator: k-means on raw key rows and on raw query rows
+    (metric I), queries in (cluster, token) order, shared routing, no
+    correction. Index stages bit-exact from the dumped scores; every
+    k-means iteration's scores against fp64 on the previous GPU centroids;
+    the output against the oracle on the GPU's indices."""
+    wl = SEMANTIC_WORKLOADS[name]
+    inp = wl.make_inputs()
+    p = wl.params
+    tol = TOL[p.dtype]
+    prev_k = [inp.K[h][inp.init_idx].astype(np.float64) for h in range(p.heads)]
+    prev_q = [inp.Q[h][inp.init_idx].astype(np.float64) for h in range(p.heads)]
+    for T in range(1, p.kmeans_iters + 1):
+        print(f"[gpu] semantic {name} T={T}", flush=True)
+        r = run_pipeline(wl, p=replace(p, kmeans_iters=T), inp=inp)
+        for h in range(p.heads):
+            g = head_arrays(r, h)
+            qlab = r.np("query_label")[h]
+            for X, sc, lab, prev in ((r.inp.K[h], g["assign"], g["key_label"], prev_k),
+                                     (r.inp.Q[h], r.np("qassign")[h], qlab, prev_q)):
+                assert np.array_equal(orc.argmin_lowest(sc), lab)
+                X = X.astype(np.float64)
+                C = prev[h]
+                ref = orc.squared_distances(X, C) - (X * X).sum(1)[:, None]
+                bound = (C * C).sum(1)[None, :] + 2 * np.abs(X @ C.T)
+                assert np.all(np.abs(sc - ref) <= 1e-5 * bound + 1e-6)
+            prev_k[h] = g["key_centroid"].astype(np.float64)
+            prev_q[h] = r.np("query_centroid")[h].astype(np.float64)
+            if T < p.kmeans_iters:
+                continue
+            kp, goff, sizes = orc.group_members(g["key_label"], p.n_groups)
+            assert np.array_equal(kp, g["key_perm"]) and np.array_equal(goff, g["group_off"])
+            assert np.array_equal(g["Kp"], r.inp.K[h][kp])
+            qorder, _, _ = orc.group_members(qlab, p.n_groups)
+            assert np.array_equal(qorder, r.np("query_order")[h])
+            assert np.array_equal(qorder, g["query_perm"])
+            ptr, grp = orc.route(g["sigma"], sizes, p.key_budget)
+            assert np.array_equal(ptr, g["block_ptr"])
+            assert np.array_equal(grp, g["block_groups"][:ptr[-1]])
+            Q, K, V = (x[h].astype(np.float64) for x in (r.inp.Q, r.inp.K, r.inp.V))
+            o = oracle_on_gpu_indices(Q, K, V, float(r.inp.scale[h]), p, g)
+            assert int(g["executed_pairs"]) == o["E"]
+            assert int(g["rank_eff"]) == 0
+            out = to_token_order(g["S"], g["query_perm"])
+            assert rel_l2(out, o["S"]) < tol
+            if p.dtype == "bf16":
+                out = bf16_round(out)
+            assert np.array_equal(g["O"], out)
+
+
 def test_full_density_equals_dense():
     wl = small_bf16(name="full", rho=1.0, m=0, k=0, G=16, seed=15)
     r = run_pipeline(wl)

@@ -130,6 +130,56 @@ def brute_kmeans(Q, K, scale, sample_idx, init_idx, iters):
     return np.array(labels), np.array(cents)
 
 
+def brute_kmeans_rows(X, init_idx, iters):
+    """Lloyd k-means of raw rows by plain loops (semantic comparator)."""
+    n = len(X)
+    cents = [list(X[i]) for i in init_idx]
+    labels = [0] * n
+    for _ in range(iters):
+        for j in range(n):
+            best, bestg = None, -1
+            for g, c in enumerate(cents):
+                dist = sum((X[j][t] - c[t]) ** 2 for t in range(len(c)))
+                if best is None or dist < best:
+                    best, bestg = dist, g
+            labels[j] = bestg
+        for g in range(len(cents)):
+            mem = [j for j in range(n) if labels[j] == g]
+            if mem:
+                cents[g] = [sum(X[j][t] for j in mem) / len(mem) for t in range(len(cents[g]))]
+    return labels
+
+
+def brute_route_attend(Q, K, V, scale, labels, order, q_block, n_groups, kappa):
+    """Routing and block-sparse attention by enumeration, from key labels and
+    a query order: (S [n, d], executed sparse pairs counted from the mask)."""
+    n, G = len(Q), n_groups
+    members = [[j for j in range(n) if labels[j] == g] for g in range(G)]
+    kbar = [np.mean(K[m], axis=0) if m else None for m in members]
+    coords = [[scale * float(np.dot(Q[q], kbar[g])) if members[g] else -np.inf for g in range(G)]
+              for q in range(n)]
+    mask = np.zeros((n, n), bool)
+    S = np.zeros((n, V.shape[1]))
+    for b0 in range(0, n, q_block):
+        blk = order[b0:b0 + q_block]
+        sig = [np.mean([coords[q][g] for q in blk]) if members[g] else None for g in range(G)]
+        ranked = sorted([g for g in range(G) if members[g]], key=lambda g: (-sig[g], g))
+        chosen, tot = [], 0
+        for g in ranked:
+            if tot + len(members[g]) > kappa:
+                break
+            chosen.append(g)
+            tot += len(members[g])
+        if not chosen:
+            chosen = ranked[:1]
+        keys = [j for g in sorted(chosen) for j in members[g]]
+        for q in blk:
+            mask[q, keys] = True
+        bo, _ = brute_attention(Q[blk].tolist(), K[keys].tolist(), V[keys].tolist(), scale)
+        S[blk] = bo
+    return S, int(mask.sum())
+
+
 def test_p5_brute_attention():
     Q, K, V = tiny_case(n=20, d=5, seed=3)
     out, lse = orc.softmax_attention(Q[:7], K, V, 0.9)
@@ -194,6 +244,46 @@ def test_p5_brute_full_head():
     E = int(mask.sum()) + 4 * n
     assert res.executed_pairs == E
     np.testing.assert_allclose(res.S, S, rtol=0, atol=1e-13)
+
+
+def test_p5_brute_semantic_head():
+    """Semantic comparator by enumeration: raw-row k-means of keys and of
+    queries, queries in (cluster, token) order, then the shared routing rule
+    and block-sparse attention; no probes, so the output is the sparse one."""
+    Q, K, V = tiny_case(n=40, d=5, seed=17)
+    scale, G, T, B = 0.6, 5, 3, 8
+    iidx = np.random.default_rng(4).choice(40, G, replace=False)
+    res = orc.sparsepr_head(Q, K, V, scale, q_block=B, n_groups=G, kmeans_iters=T, density=0.4,
+                            n_probes=0, rank=2, ridge_lambda=1e-3, init_idx=iidx,
+                            partition_mode=2)
+    klab = brute_kmeans_rows(K.tolist(), iidx, T)
+    qlab = brute_kmeans_rows(Q.tolist(), iidx, T)
+    assert res.labels.tolist() == klab
+    order = sorted(range(40), key=lambda q: (qlab[q], q))
+    assert res.query_perm.tolist() == order
+    kappa = math.floor(0.4 * 40)
+    S, E = brute_route_attend(Q, K, V, scale, klab, order, B, G, kappa)
+    assert res.executed_pairs == E
+    np.testing.assert_allclose(res.S, S, rtol=0, atol=1e-13)
+    np.testing.assert_array_equal(res.O, res.S)
+
+
+def test_p6_semantic_kmeans_equals_sklearn_lloyd():
+    """The semantic partition is scikit-learn's Lloyd k-means started from the
+    same rows, on separated clusters where it converges within T steps and
+    no group empties (scikit-learn would relocate an empty one)."""
+    from sklearn.cluster import KMeans
+    rng = np.random.default_rng(8)
+    G, n, d = 6, 240, 7
+    mu = rng.standard_normal((G, d)) * 4.0
+    lab = np.repeat(np.arange(G), n // G)
+    X = mu[lab] + 0.5 * rng.standard_normal((n, d))
+    iidx = np.array([np.nonzero(lab == g)[0][3] for g in range(G)])[::-1]
+    labels, order = orc.semantic_order(X, iidx, 25, G)
+    ref = KMeans(n_clusters=G, init=X[iidx], n_init=1, max_iter=25, tol=0.0,
+                 algorithm="lloyd").fit(X)
+    assert labels.tolist() == ref.labels_.tolist()
+    assert order.tolist() == np.argsort(ref.labels_, kind="stable").tolist()
 
 
 # ---------------------------------------------- P6 library reductions
