@@ -164,6 +164,30 @@ def pmc_table(fetch_csv, write_csv, workload, copy_mib):
     print(text)
 
 
+SUPPORT_MASS = 0.9   # target mass of the support diagnostics
+
+
+def support_summary(p, b, Q, K, scale, blocks):
+    """Support and mass diagnostics of sampled blocks of head 0 for one
+    partition's routing (sparsepr_support_stats), summarised."""
+    import numpy as np
+    from free_block_sparse_rcp_amd import binding
+
+    st = binding.support_stats(p, 0, Q, K, scale, b, blocks, SUPPORT_MASS)
+    v = st.valid
+    s = st.support.astype(np.float64)
+    mean_s = np.array([s[i][v[i]].mean() for i in range(len(blocks))])
+    N = p.n_tokens
+    return {"routed_mass_mean": float(st.routed_mass[v].mean()),
+            "routed_mass_p10": float(np.quantile(st.routed_mass[v], 0.1)),
+            "support_frac_mean": float(s[v].mean() / N),
+            "support_on_route_mean": float((st.support_routed[v] / s[v]).mean()),
+            "pooled_frac_mean": float(st.pooled.mean() / N),
+            "pooled_over_mean_support": float((st.pooled / mean_s).mean()),
+            "pooled_on_route_mean": float((st.pooled_routed / st.pooled).mean()),
+            "route_frac": float(p.key_budget / N)}
+
+
 def semantic_comparator(args, p, Q, K, V, scale, inp, ref, rn, mask, err_sparsepr):
     """Semantic block-sparse attention without residual correction at the same
     executed-pair density (no probes, so the whole budget goes to the sparse
@@ -191,14 +215,39 @@ def semantic_comparator(args, p, Q, K, V, scale, inp, ref, rn, mask, err_sparsep
     with torch.no_grad():
         ec = ((cop.buffers.O.float() - ref).norm(dim=2) / rn)[mask]
     E = int(cop.buffers.executed_pairs.sum().item())
+    support = support_summary(ps, cop.buffers, Q, K, scale, support_blocks(p))
     out = {"rel_l2_mean_unprobed": float(ec.mean()),
            "error_reduction": 1.0 - err_sparsepr / float(ec.mean()),
            "realized_density": E / (p.heads * float(p.n_tokens) ** 2),
            "call_ms": call_ms,
            "definition": "k-means (same G, T, init rows) on raw key rows and on raw query rows, "
                          "queries in (cluster, token) order, same routing rule and kernels, "
-                         "no probes or correction"}
+                         "no probes or correction",
+           "support": support}
     del cop
+    return out
+
+
+def support_blocks(p):
+    """Eight query blocks spread over head 0, the first and the ragged last included."""
+    import numpy as np
+    return sorted(set(np.linspace(0, p.n_blocks - 1, 8).round().astype(int).tolist()))
+
+
+def random_block_support(p, Q, K, V, scale, inp):
+    """The random-block partition (no probes, same density) on the same inputs:
+    its support diagnostics."""
+    import dataclasses
+    import torch
+    from free_block_sparse_rcp_amd import binding
+
+    pr = dataclasses.replace(p, partition_mode=binding.RANDOM_BLOCK, n_probes=0, rank=0)
+    op = binding.SparsePR(pr, Q.device)
+    idx = op.upload_indices(rand_key_perm=inp.rand_key_perm, rand_query_perm=inp.rand_query_perm)
+    op.run(Q, K, V, scale, idx)
+    torch.cuda.synchronize()
+    out = support_summary(pr, op.buffers, Q, K, scale, support_blocks(p))
+    del op
     return out
 
 
@@ -421,6 +470,12 @@ def main():
         if not args.no_comparator:
             quality["semantic"] = semantic_comparator(args, p, Q, K, V, scale, inp, ref, rn, mask,
                                                       float(e.mean()))
+            log("[bench] support diagnostics")
+            quality["support"] = {
+                "mass": SUPPORT_MASS, "head": 0, "blocks": support_blocks(p),
+                "response_coupled": support_summary(p, b, Q, K, scale, support_blocks(p)),
+                "semantic": quality["semantic"].pop("support"),
+                "random_block": random_block_support(p, Q, K, V, scale, inp)}
 
     traffic = load_traffic(wl.name)
     roofline = {"bound": "mfma", "kernel": "k_attn_mfma (sparsepr_attend)",

@@ -30,7 +30,7 @@ STATUS = {0: "SPARSEPR_OK", 1: "SPARSEPR_ERR_INVALID_ARG", 2: "SPARSEPR_ERR_UNSU
 EXPORTS = ("sparsepr_abi_version", "sparsepr_status_string", "sparsepr_last_error",
            "sparsepr_workspace_bytes", "sparsepr_partition", "sparsepr_route", "sparsepr_attend",
            "sparsepr_attend_subset", "sparsepr_probe_fit", "sparsepr_apply",
-           "sparsepr_dense_attention")
+           "sparsepr_dense_attention", "sparsepr_support_stats")
 BLOCKS_ALL, BLOCKS_WITH_PROBE, BLOCKS_WITHOUT_PROBE = 0, 1, 2
 RESPONSE_COUPLED, RANDOM_BLOCK, SEMANTIC = 0, 1, 2   # partition modes
 
@@ -76,6 +76,8 @@ def load(path: Optional[str] = None) -> ctypes.CDLL:
     lib.sparsepr_probe_fit.argtypes = [pp] + [_c_p] * 10 + [_c_p, _c_sz, _c_p]
     lib.sparsepr_apply.argtypes = [pp] + [_c_p] * 7 + [_c_p, _c_sz, _c_p]
     lib.sparsepr_dense_attention.argtypes = [pp] + [_c_p] * 6 + [_c_p]
+    lib.sparsepr_support_stats.argtypes = ([pp, _c_i32] + [_c_p] * 8 + [_c_i32, ctypes.c_double] +
+                                           [_c_p] * 7 + [_c_sz, _c_p])
     for name in ("sparsepr_partition", "sparsepr_route", "sparsepr_attend", "sparsepr_attend_subset",
                  "sparsepr_probe_fit", "sparsepr_apply", "sparsepr_dense_attention"):
         getattr(lib, name).restype = _c_i32
@@ -278,6 +280,49 @@ def dense_attention(p: Params, Q, K, V, scale, O=None, lse=None):
     _check(lib.sparsepr_dense_attention(ctypes.byref(cp), _ptr(Q), _ptr(K), _ptr(V), _ptr(scale),
                                         _ptr(O), _ptr(lse), _stream(Q.device)))
     return O, lse
+
+
+@dataclass
+class SupportStats:
+    """Per-row and per-block support and mass diagnostics (host arrays)."""
+
+    lse: np.ndarray             # [n_blocks, B_q] full-row log-sum-exp
+    routed_mass: np.ndarray     # [n_blocks, B_q] softmax mass on the block's routed keys
+    support: np.ndarray         # [n_blocks, B_q] keys holding the target mass
+    support_routed: np.ndarray  # [n_blocks, B_q] of those, keys routed to the block
+    pooled: np.ndarray          # [n_blocks] union of the rows' supports
+    pooled_routed: np.ndarray   # [n_blocks] its part on routed keys
+    valid: np.ndarray           # [n_blocks, B_q] row lies inside N
+
+
+def support_stats(p: Params, head: int, Q, K, scale, b: Buffers, blocks, mass: float = 0.9,
+                  workspace: Optional[torch.Tensor] = None) -> SupportStats:
+    """Diagnostics of sampled blocks of one head (K in token order), after route."""
+    lib = load()
+    cp = c_params(p)
+    dev = Q.device
+    blk = index_tensor(blocks, p.n_blocks, len(blocks), "blocks", dev)
+    nbk, BQ = len(blocks), p.q_block
+    f32 = dict(dtype=torch.float32, device=dev)
+    i32 = dict(dtype=torch.int32, device=dev)
+    lse, rm = torch.empty(nbk * BQ, **f32), torch.empty(nbk * BQ, **f32)
+    sup, supr = torch.empty(nbk * BQ, **i32), torch.empty(nbk * BQ, **i32)
+    pool, poolr = torch.empty(nbk, **i32), torch.empty(nbk, **i32)
+    need = 4 * nbk * BQ * (p.n_tokens + 1)
+    if workspace is None or workspace.numel() < need:
+        workspace = torch.empty(need, dtype=torch.uint8, device=dev)
+    _check(lib.sparsepr_support_stats(
+        ctypes.byref(cp), int(head), _ptr(Q), _ptr(K), _ptr(scale), _ptr(b.key_label),
+        _ptr(b.query_perm), _ptr(b.block_ptr), _ptr(b.block_groups), _ptr(blk), nbk, float(mass),
+        _ptr(lse), _ptr(rm), _ptr(sup), _ptr(supr), _ptr(pool), _ptr(poolr), _ptr(workspace),
+        workspace.numel(), _stream(dev)))
+    torch.cuda.synchronize(dev)
+    pos = np.asarray(blocks, np.int64)[:, None] * BQ + np.arange(BQ)[None, :]
+    return SupportStats(lse=lse.view(nbk, BQ).cpu().numpy(), routed_mass=rm.view(nbk, BQ).cpu().numpy(),
+                        support=sup.view(nbk, BQ).cpu().numpy(),
+                        support_routed=supr.view(nbk, BQ).cpu().numpy(),
+                        pooled=pool.cpu().numpy(), pooled_routed=poolr.cpu().numpy(),
+                        valid=pos < p.n_tokens)
 
 
 class SparsePR:

@@ -18,7 +18,8 @@ LIBDIR = os.path.join(PKG, "lib")
 LIBNAME = "libsparsepr.so"
 BUILD = os.path.join(ROOT, "_build")
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
-SOURCES = ["api.hip", "partition.hip", "route.hip", "attention.hip", "fit.hip", "apply.hip"]
+SOURCES = ["api.hip", "partition.hip", "route.hip", "attention.hip", "fit.hip", "apply.hip",
+           "support.hip"]
 FLAGS = [
     "--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC", "-Wall", "-Wno-unused-function",
     # packed fp32 instructions are kept out of every kernel

@@ -349,6 +349,70 @@ int32_t sparsepr_attend(const sparsepr_params* params, const void* Q, const void
                                 block_groups, S_out, lse, SPARSEPR_BLOCKS_ALL, stream);
 }
 
+int32_t sparsepr_support_stats(const sparsepr_params* params, int32_t head, const void* Q,
+                               const void* K, const float* scale, const int32_t* key_label,
+                               const int32_t* query_perm, const int32_t* block_ptr,
+                               const int32_t* block_groups, const int32_t* blocks,
+                               int32_t n_blocks, double mass, float* lse, float* routed_mass,
+                               int32_t* support, int32_t* support_routed, int32_t* pooled,
+                               int32_t* pooled_routed, void* workspace, size_t workspace_bytes,
+                               void* stream) {
+  Dims d;
+  int32_t s = make_dims(params, true, &d);
+  if (s != SPARSEPR_OK) return s;
+  if (head < 0 || head >= d.H)
+    return fail(SPARSEPR_ERR_INVALID_ARG, "head must be in [0, H) (got %d)", head);
+  if (n_blocks < 1 || n_blocks > d.nb)
+    return fail(SPARSEPR_ERR_INVALID_ARG, "n_blocks must be in [1, nb] (got %d)", n_blocks);
+  if (!(mass > 0.0 && mass <= 1.0))
+    return fail(SPARSEPR_ERR_INVALID_ARG, "mass must be in (0, 1] (got %g)", mass);
+  SPR_REQUIRE(Q, "Q");
+  SPR_REQUIRE(K, "K");
+  SPR_REQUIRE(scale, "scale");
+  SPR_REQUIRE(key_label, "key_label");
+  SPR_REQUIRE(query_perm, "query_perm");
+  SPR_REQUIRE(block_ptr, "block_ptr");
+  SPR_REQUIRE(block_groups, "block_groups");
+  SPR_REQUIRE(blocks, "blocks");
+  SPR_REQUIRE(lse, "lse");
+  SPR_REQUIRE(routed_mass, "routed_mass");
+  SPR_REQUIRE(support, "support");
+  SPR_REQUIRE(support_routed, "support_routed");
+  SPR_REQUIRE(pooled, "pooled");
+  SPR_REQUIRE(pooled_routed, "pooled_routed");
+  const size_t rows = (size_t)n_blocks * d.BQ;
+  const size_t need = rows * ((size_t)d.N + 1) * sizeof(float);
+  if (workspace == nullptr || workspace_bytes < need)
+    return fail(SPARSEPR_ERR_WORKSPACE, "workspace of %zu bytes needed (got %zu%s)", need,
+                workspace_bytes, workspace == nullptr ? ", NULL" : "");
+  SupportArgs a{};
+  a.Q = Q;
+  a.K = K;
+  a.scale = scale;
+  a.key_label = key_label;
+  a.query_perm = query_perm;
+  a.block_ptr = block_ptr;
+  a.block_groups = block_groups;
+  a.blocks = blocks;
+  a.n_blocks = n_blocks;
+  a.head = head;
+  a.N = d.N;
+  a.nb = d.nb;
+  a.G = d.G;
+  a.BQ = d.BQ;
+  a.mu = mass;
+  a.xs = static_cast<float*>(workspace);
+  a.thr = a.xs + rows * (size_t)d.N;
+  a.lse = lse;
+  a.mass = routed_mass;
+  a.support = support;
+  a.support_routed = support_routed;
+  a.pooled = pooled;
+  a.pooled_routed = pooled_routed;
+  return hip_status(launch_support(d, a, static_cast<hipStream_t>(stream)),
+                    "sparsepr_support_stats");
+}
+
 int32_t sparsepr_probe_fit(const sparsepr_params* params, const void* Q, const void* K,
                            const void* V, const float* scale, const int32_t* query_perm,
                            const float* S_out, float* O_probe, float* U, float* Theta,

@@ -103,6 +103,29 @@ hipError_t launch_attention(const Dims& d, AttnMode mode, const AttnArgs& a, hip
 hipError_t launch_probe_merge(const Dims& d, const float* opart, const float* lsepart,
                               float* O_probe, hipStream_t st);
 
+// ---- support.hip
+struct SupportArgs {
+  const void* Q;
+  const void* K;               // token order
+  const float* scale;
+  const int32_t* key_label;
+  const int32_t* query_perm;
+  const int32_t* block_ptr;
+  const int32_t* block_groups;
+  const int32_t* blocks;       // [n_blocks] sampled block indices
+  int n_blocks, head, N, nb, G, BQ;
+  double mu;                   // target mass
+  float* xs;                   // workspace: [n_blocks * B_q, N] logits
+  float* thr;                  // workspace: [n_blocks * B_q] support thresholds
+  float* lse;                  // [n_blocks * B_q]
+  float* mass;                 // [n_blocks * B_q]
+  int32_t* support;            // [n_blocks * B_q]
+  int32_t* support_routed;     // [n_blocks * B_q]
+  int32_t* pooled;             // [n_blocks]
+  int32_t* pooled_routed;      // [n_blocks]
+};
+hipError_t launch_support(const Dims& d, const SupportArgs& a, hipStream_t st);
+
 // ---- fit.hip
 hipError_t launch_fit(const Dims& d, const float* S_out, const float* O_probe, float* U,
                       float* Theta, int32_t* rank_eff, char* fit_ws, hipStream_t st);

@@ -288,6 +288,47 @@ int32_t sparsepr_apply(const sparsepr_params* params, const float* S_out,
                        size_t workspace_bytes, void* stream);
 
 /*
+ * Support and mass diagnostics of sampled query blocks of one head (skillfed
+ * article, the two problem paragraphs: queries that share a block route may
+ * prefer different keys, and keeping most attention mass need not keep the
+ * output; arxivdaily 2608.18484, English abstract: the partition decides how
+ * much the grouped queries' preferred supports overlap). Not a stage of the
+ * call: it measures one, after sparsepr_route.
+ *
+ * For row r of sampled block blocks[i] (query position p = blocks[i] B_q + r,
+ * token q = query_perm[p]), with logits x_j = tau q . k_j over ALL N keys
+ * (fp32) and probabilities p_j = softmax_j(x):
+ *   lse[i B_q + r]            = log sum_j exp(x_j)
+ *   routed_mass[i B_q + r]    = sum of p_j over the block's routed keys K(b)
+ *                               (keys whose key_label is a routed group)
+ *   theta                     = the largest logit t with sum_{x_j >= t} p_j >= mass
+ *   support[i B_q + r]        = #{j : x_j >= theta}: the fewest keys that hold
+ *                               the given mass (keys tied at theta all count)
+ *   support_routed[i B_q + r] = #{j in K(b) : x_j >= theta}
+ *   pooled[i]                 = |union over the block's rows of {j : x_j >= theta}|
+ *   pooled_routed[i]          = the part of that union inside K(b).
+ * Rows past N (ragged last block) give lse = -inf and zeros. Sums over keys
+ * are accumulated in fp64.
+ *
+ * Inputs : head in [0, H); Q, K [H,N,d] dtype in TOKEN order; scale [H];
+ *          key_label [H,N] (stage 1); query_perm, block_ptr, block_groups
+ *          (stage 2); blocks [n_blocks] int32 device array of block indices
+ *          (1 <= n_blocks <= nb); mass in (0, 1].
+ * Outputs: lse, routed_mass [n_blocks B_q] fp32; support, support_routed
+ *          [n_blocks B_q] int32; pooled, pooled_routed [n_blocks] int32.
+ * Workspace: at least 4 n_blocks B_q (N + 1) bytes (the rows' logits and
+ *          thresholds); its own, not the stages' workspace size.
+ */
+int32_t sparsepr_support_stats(const sparsepr_params* params, int32_t head, const void* Q,
+                               const void* K, const float* scale, const int32_t* key_label,
+                               const int32_t* query_perm, const int32_t* block_ptr,
+                               const int32_t* block_groups, const int32_t* blocks,
+                               int32_t n_blocks, double mass, float* lse, float* routed_mass,
+                               int32_t* support, int32_t* support_routed, int32_t* pooled,
+                               int32_t* pooled_routed, void* workspace, size_t workspace_bytes,
+                               void* stream);
+
+/*
  * Exact softmax attention over all keys, the operator SparsePR replaces
  * (arxivdaily 2608.18484, English abstract: speedups are over dense
  * attention). O[q] = softmax(tau q K^T) V, lse[q] = log sum exp(tau q K^T),

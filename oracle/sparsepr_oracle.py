@@ -499,6 +499,65 @@ def sparsepr_head(Q, K, V, scale, *, q_block, n_groups, kmeans_iters, density, n
 
 
 # ---------------------------------------------------------------------------
+# Support and mass diagnostics  ([SK] the two problem paragraphs; [AD] the
+# partition decides how far grouped queries' preferred supports overlap)
+# ---------------------------------------------------------------------------
+
+def support_threshold(x, mass):
+    """For one query's logits x over all keys: the largest logit t whose
+    upper set {j : x_j >= t} holds at least `mass` of the softmax, and that
+    set. Reading: "the keys a query prefers" is the smallest upper set of its
+    logits that holds the target mass; keys tied at the threshold all count.
+    Returns (t, boolean mask of the set)."""
+    x = np.asarray(x, F64)
+    xs = np.sort(x)[::-1]                           # logits, descending
+    cum = np.cumsum(np.exp(xs - xs[0]))
+    # an upper set {x >= t} ends where a run of equal logits ends
+    ends = np.nonzero(np.append(xs[1:] != xs[:-1], True))[0]
+    reach = cum[ends] >= mass * cum[-1]
+    t = xs[ends[int(np.argmax(reach))]]
+    return t, x >= t
+
+
+def support_stats(Q, K, scale, labels, query_perm, block_ptr, block_groups, q_block, blocks,
+                  mass):
+    """Per sampled block b and row q (all N keys): full-row lse, the softmax
+    mass on the block's routed keys, the size of q's preferred support at the
+    target mass and its part on routed keys; per block the pooled support
+    (union over the block's rows) and its routed part. Rows past N are
+    skipped (NaN / 0)."""
+    Q = np.asarray(Q, F64)
+    K = np.asarray(K, F64)
+    n = Q.shape[0]
+    labels = np.asarray(labels)
+    nbk = len(blocks)
+    out = {"lse": np.full((nbk, q_block), -np.inf), "routed_mass": np.zeros((nbk, q_block)),
+           "support": np.zeros((nbk, q_block), np.int64),
+           "support_routed": np.zeros((nbk, q_block), np.int64),
+           "pooled": np.zeros(nbk, np.int64), "pooled_routed": np.zeros(nbk, np.int64)}
+    for i, b in enumerate(blocks):
+        groups = np.asarray(block_groups[block_ptr[b]:block_ptr[b + 1]], np.int64)
+        sel = np.isin(labels, groups)                # key j routed to block b
+        union = np.zeros(n, bool)
+        for r in range(q_block):
+            p = b * q_block + r
+            if p >= n:
+                break
+            x = scale * (K @ Q[query_perm[p]])
+            mx = x.max()
+            z = np.exp(x - mx).sum()
+            out["lse"][i, r] = mx + np.log(z)
+            out["routed_mass"][i, r] = np.exp(x[sel] - mx).sum() / z
+            _, S = support_threshold(x, mass)
+            out["support"][i, r] = int(S.sum())
+            out["support_routed"][i, r] = int((S & sel).sum())
+            union |= S
+        out["pooled"][i] = int(union.sum())
+        out["pooled_routed"][i] = int((union & sel).sum())
+    return out
+
+
+# ---------------------------------------------------------------------------
 # Evaluation  ([AD] error definition; [SK] ablation paragraph for p99)
 # ---------------------------------------------------------------------------
 

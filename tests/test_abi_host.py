@@ -118,6 +118,22 @@ def test_null_pointers_and_small_workspace_are_rejected(lib):
     st = lib.sparsepr_route(ctypes.byref(p), fake, fake, fake, fake, None, fake, fake, fake, fake,
                             None, None, None, None, fake, 1 << 40, None)
     assert st == 1 and "rand_query_perm" in lib.sparsepr_last_error().decode()
+    # support diagnostics: head, block count, mass and workspace are validated
+    p.partition_mode = 0
+    args = [fake] * 8
+    outs = [fake] * 6
+    st = lib.sparsepr_support_stats(ctypes.byref(p), 1, *args, 1, 0.9, *outs, fake, 1 << 40, None)
+    assert st == 1 and "head" in lib.sparsepr_last_error().decode()
+    st = lib.sparsepr_support_stats(ctypes.byref(p), 0, *args, 0, 0.9, *outs, fake, 1 << 40, None)
+    assert st == 1 and "n_blocks" in lib.sparsepr_last_error().decode()
+    st = lib.sparsepr_support_stats(ctypes.byref(p), 0, *args, 1, 1.5, *outs, fake, 1 << 40, None)
+    assert st == 1 and "mass" in lib.sparsepr_last_error().decode()
+    st = lib.sparsepr_support_stats(ctypes.byref(p), 0, *args, 1, 0.9, *outs[:5], None, fake,
+                                    1 << 40, None)
+    assert st == 1 and "pooled_routed" in lib.sparsepr_last_error().decode()
+    st = lib.sparsepr_support_stats(ctypes.byref(p), 0, *args, 2, 0.9, *outs, fake,
+                                    4 * 2 * 64 * 2049 - 1, None)
+    assert st == 3
     # attend with no lse
     p.partition_mode = 0
     st = lib.sparsepr_attend(ctypes.byref(p), fake, fake, fake, fake, fake, fake, fake, fake, fake,

@@ -549,6 +549,77 @@ def test_random_block_head_runs_and_is_valid():
     assert np.all(np.isfinite(res.O))
 
 
+# ------------------------------------------------ support and mass diagnostics
+
+def test_support_is_the_smallest_subset_holding_the_mass():
+    """Brute force over all 2^10 key subsets: the support size is the fewest
+    keys whose softmax mass reaches the target, and the set is the top keys."""
+    import itertools
+    rng = np.random.default_rng(31)
+    for trial in range(4):
+        x = rng.standard_normal(10) * 1.7
+        p = np.exp(x - x.max())
+        p /= p.sum()
+        for mu in (0.3, 0.6, 0.9, 0.99):
+            best = None
+            for k in range(1, 11):
+                if any(p[list(c)].sum() >= mu for c in itertools.combinations(range(10), k)):
+                    best = k
+                    break
+            _, S = orc.support_threshold(x, mu)
+            assert S.sum() == best
+            assert set(np.nonzero(S)[0]) == set(np.argsort(-x)[:best].tolist())
+
+
+def test_support_closed_forms():
+    x = -np.arange(12) * math.log(2.0)      # p_j proportional to 2^-j
+    for mu, k in ((0.5, 1), (0.75, 2), (0.875, 3), (1.0, 12)):
+        assert orc.support_threshold(x, mu)[1].sum() == k
+    assert orc.support_threshold(np.zeros(9), 0.2)[1].sum() == 9   # ties all count
+
+
+def _support_case(density):
+    Q, K, V = tiny_case(n=48, d=6, seed=33)
+    res, _, _ = run_head(Q, K, V, 0.7, q_block=8, n_groups=6, kmeans_iters=4, density=density,
+                         n_probes=0, rank=0)
+    blocks = [0, 2, 5]
+    st = orc.support_stats(Q, K, 0.7, res.labels, res.query_perm, res.block_ptr,
+                           res.block_groups, 8, blocks, 0.9)
+    return Q, K, V, res, blocks, st
+
+
+def test_routed_mass_is_the_lse_difference():
+    """Mass on the routed keys = exp(lse over K(b) - lse over all keys)."""
+    Q, K, V, res, blocks, st = _support_case(0.4)
+    _, lse_d = orc.dense_attention(Q, K, V, 0.7)
+    for i, b in enumerate(blocks):
+        for r in range(8):
+            q = res.query_perm[b * 8 + r]
+            np.testing.assert_allclose(st["lse"][i, r], lse_d[q], rtol=0, atol=1e-12)
+            np.testing.assert_allclose(st["routed_mass"][i, r], math.exp(res.lse[q] - lse_d[q]),
+                                       rtol=0, atol=1e-12)
+
+
+def test_support_full_density_and_pooled_by_loops():
+    Q, K, V, res, blocks, st = _support_case(1.0)
+    np.testing.assert_allclose(st["routed_mass"], 1.0, rtol=0, atol=1e-12)
+    assert np.array_equal(st["support_routed"], st["support"])
+    assert np.array_equal(st["pooled_routed"], st["pooled"])
+    Q, K, V, res, blocks, st = _support_case(0.4)
+    for i, b in enumerate(blocks):
+        union, routed = set(), set()
+        keys = set(int(k) for k in res.key_sets[b])
+        for r in range(8):
+            x = 0.7 * (K @ Q[res.query_perm[b * 8 + r]])
+            order = np.argsort(-x)
+            k = int(st["support"][i, r])
+            top = set(order[:k].tolist())
+            assert len(top & keys) == st["support_routed"][i, r]
+            union |= top
+        assert len(union) == st["pooled"][i]
+        assert len(union & keys) == st["pooled_routed"][i]
+
+
 # ----------------------------------------------- P14 direction (report only)
 
 def test_p14_reconstruction_direction_report(capsys):
