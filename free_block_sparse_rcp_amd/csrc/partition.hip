@@ -276,7 +276,10 @@ __global__ __launch_bounds__(256) void k_rowvec_argsel(const void* Xv, const flo
 // multiplied by the exact bf16 rows with fp32 accumulation. The product is
 // formed transposed (groups x keys) so that each lane holds one key and 16
 // groups. Each workgroup covers 256 groups (8 waves x 32, operands held in
-// registers) for a chunk of 512 keys streamed through padded LDS tiles; the
+// registers) for a chunk of kRvKeys keys streamed through padded LDS tiles.
+// The kernel fits 128 VGPRs, so two workgroups share a CU: the tile's two
+// 32-key halves are scored one after the other, the group biases are read
+// from LDS, and tile loads use 32-bit offsets from the head's base. The
 // per-key winner over its groups is merged into best[h][key] with a 64-bit
 // atomicMin on (orderable score << 32 | g), which is order independent, so
 // results are deterministic and ties go to the lowest g.
@@ -287,7 +290,7 @@ constexpr int kRvKeys = 2048;
 constexpr int kRvTile = 64;
 
 template <int D, int MODE>
-__global__ __launch_bounds__(kRvWaves * 64) void k_rowvec_mfma(
+__global__ __launch_bounds__(kRvWaves * 64) __attribute__((amdgpu_waves_per_eu(4, 4))) void k_rowvec_mfma(
     const uint16_t* X, const uint16_t* Phl, const float* bvec, const float* scale,
     const int32_t* group_off, int N, int G, int nkc, unsigned long long* best, float* dbg) {
   constexpr int NKK = D / 16;
@@ -298,6 +301,7 @@ __global__ __launch_bounds__(kRvWaves * 64) void k_rowvec_mfma(
   __shared__ __attribute__((aligned(1024))) char kt0[NINS * 1024];
   __shared__ __attribute__((aligned(1024))) char kt1[NINS * 1024];
   __shared__ unsigned long long red[2][kRvWaves][kRvTile];
+  __shared__ __attribute__((aligned(16))) float bsh[32 * kRvWaves];
   const int h = blockIdx.y;
   const int kc = blockIdx.x % nkc, gt = blockIdx.x / nkc;
   const int t = threadIdx.x, lane = t & 63, hl = lane >> 5, ql = lane & 31;
@@ -323,18 +327,21 @@ __global__ __launch_bounds__(kRvWaves * 64) void k_rowvec_mfma(
   // Scores are minimised in the form  sgn * acc + bias  (MODE 0: -2 k.P_g + b_g;
   // MODE 1: -tau q.kbar_g); slots that must never win get bias = +inf.
   const int gbase = gt * (32 * kRvWaves) + 32 * w + 4 * hl;
-  float bias[16];
-#pragma unroll
-  for (int r = 0; r < 16; ++r) {
-    const int g = gbase + 8 * (r >> 2) + (r & 3);
+  // per-group bias of this workgroup's groups, in LDS (read back 4 at a time in
+  // the epilogue, so that it holds no registers across the tile loop)
+  for (int i = t; i < 32 * kRvWaves; i += kRvWaves * 64) {
+    const int g = gt * (32 * kRvWaves) + i;
     bool ok = g < G;
+    float v;
     if (MODE == 0) {
-      bias[r] = ok ? bvec[(size_t)h * G + g] : __builtin_inff();
+      v = ok ? bvec[(size_t)h * G + g] : __builtin_inff();
     } else {
       if (ok) ok = group_off[(size_t)h * (G + 1) + g + 1] > group_off[(size_t)h * (G + 1) + g];
-      bias[r] = ok ? 0.f : __builtin_inff();
+      v = ok ? 0.f : __builtin_inff();
     }
+    bsh[i] = v;
   }
+  const float* brow = bsh + 32 * w + 4 * hl;   // slot r: brow[8 (r / 4) + r % 4]
   const float sgn = MODE == 0 ? -2.0f : -scale[h];
   const int k0 = kc * kRvKeys, k1 = min(N, k0 + kRvKeys);
   const int ntile = (k1 - k0 + kRvTile - 1) / kRvTile;
@@ -346,49 +353,55 @@ __global__ __launch_bounds__(kRvWaves * 64) void k_rowvec_mfma(
       const int q = 64 * u + lane;
       if (u < NINS && q * 16 < TILEB) {
         const int r = q / KCH, cc = q - r * KCH;
-        const int key = min(k0 + tile * kRvTile + r, N - 1);
-        const uint16_t* src = Xh + (size_t)key * D + (cc < D / 8 ? cc : 0) * 8;
-        __builtin_amdgcn_global_load_lds(src, (__attribute__((address_space(3))) void*)(dst + u * 1024),
+        // uniform head base + 32-bit lane offset (N d < 2^31 keeps it in range)
+        const uint32_t key = (uint32_t)min(k0 + tile * kRvTile + r, N - 1);
+        const uint32_t off = key * (uint32_t)(2 * D) + (uint32_t)((cc < D / 8 ? cc : 0) * 16);
+        __builtin_amdgcn_global_load_lds((const void*)(reinterpret_cast<const char*>(Xh) + off),
+                                         (__attribute__((address_space(3))) void*)(dst + u * 1024),
                                          16, 0, 0);
       }
     }
   };
-  // scores of one tile; the per-key winner of this wave goes to red[tile & 1][w]
+  // scores of one tile, one 32-key half at a time; the per-key winner of this
+  // wave goes to red[tile & 1][w]
   auto compute = [&](int tile, const char* __restrict__ buf) {
-    f32x16 acc[2];
-#pragma unroll
-    for (int hk = 0; hk < 2; ++hk)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) acc[hk][r] = 0.f;
     const char* kb = buf + ql * KP + hl * 16;
 #pragma unroll
-    for (int kk = 0; kk < NKK; ++kk) {
-#pragma unroll
-      for (int hk = 0; hk < 2; ++hk) {
-        const bf16x8 kop = *reinterpret_cast<const bf16x8*>(kb + 32 * hk * KP + 32 * kk);
-        acc[hk] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(phi[kk], kop, acc[hk], 0, 0, 0);
-        acc[hk] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(plo[kk], kop, acc[hk], 0, 0, 0);
-      }
-    }
-#pragma unroll
     for (int hk = 0; hk < 2; ++hk) {
+      f32x16 acc;
+#pragma unroll
+      for (int r = 0; r < 16; ++r) acc[r] = 0.f;
+#pragma unroll
+      for (int kk = 0; kk < NKK; ++kk) {
+        const bf16x8 kop = *reinterpret_cast<const bf16x8*>(kb + 32 * hk * KP + 32 * kk);
+        acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(phi[kk], kop, acc, 0, 0, 0);
+        acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(plo[kk], kop, acc, 0, 0, 0);
+      }
       const int key = k0 + tile * kRvTile + 32 * hk + ql;
       float bs = __builtin_inff();
       int br = -1;
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const float sc = fmaf(sgn, acc[hk][r], bias[r]);
-        if (sc < bs) {
-          bs = sc;
-          br = r;
+      for (int j = 0; j < 4; ++j) {
+        const f32x4 b4 = *reinterpret_cast<const f32x4*>(brow + 8 * j);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const float sc = fmaf(sgn, acc[4 * j + i], b4[i]);
+          if (sc < bs) {
+            bs = sc;
+            br = 4 * j + i;
+          }
         }
       }
       if (dbg != nullptr && key < k1) {
 #pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const int g = gbase + 8 * (r >> 2) + (r & 3);
-          const float sc = fmaf(sgn, acc[hk][r], bias[r]);
-          if (g < G) dbg[((size_t)h * N + key) * G + g] = MODE == 0 ? sc : -sc;
+        for (int j = 0; j < 4; ++j) {
+          const f32x4 b4 = *reinterpret_cast<const f32x4*>(brow + 8 * j);
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            const int g = gbase + 8 * j + i;
+            const float sc = fmaf(sgn, acc[4 * j + i], b4[i]);
+            if (g < G) dbg[((size_t)h * N + key) * G + g] = MODE == 0 ? sc : -sc;
+          }
         }
       }
       unsigned long long bk = ~0ull;
