@@ -151,7 +151,7 @@ def pmc_table(fetch_csv, write_csv, workload, copy_mib):
         runs = "\n".join(
             f'timeout -s KILL 240 rocprofv3 --pmc {c} --kernel-include-regex "{PMC_KERNELS}" '
             f"--output-format csv -d gpurun_out/pmc/{c} -o run -- python3 bench.py --steps 1 --warmup 0 "
-            f"--no-cpu-baseline --no-dense --calibration-copy-mib {copy_mib}"
+            f"--no-cpu-baseline --no-dense --no-comparator --calibration-copy-mib {copy_mib}"
             for c in ("FETCH_SIZE", "WRITE_SIZE"))
         f.write(f"# HBM traffic per kernel, {workload}\n\n"
                 f"Scale factors from a {copy_mib} MiB copy: FETCH_SIZE x{fs:.3f}, WRITE_SIZE x{ws:.3f}. "
