@@ -148,9 +148,12 @@ def pmc_table(fetch_csv, write_csv, workload, copy_mib):
     text = "\n".join(lines)
     out = os.path.join(ROOT, "profiles", f"hbm_traffic_{workload}.md")
     with open(out, "w") as f:
+        # the commands as run: output directories are those of the two CSV files
+        outdir = {c: os.path.dirname(path) for c, path in (("FETCH_SIZE", fetch_csv),
+                                                           ("WRITE_SIZE", write_csv))}
         runs = "\n".join(
             f'timeout -s KILL 240 rocprofv3 --pmc {c} --kernel-include-regex "{PMC_KERNELS}" '
-            f"--output-format csv -d gpurun_out/pmc/{c} -o run -- python3 bench.py --steps 1 --warmup 0 "
+            f"--output-format csv -d {outdir[c]} -o run -- python3 bench.py --steps 1 --warmup 0 "
             f"--no-cpu-baseline --no-dense --no-comparator --calibration-copy-mib {copy_mib}"
             for c in ("FETCH_SIZE", "WRITE_SIZE"))
         f.write(f"# HBM traffic per kernel, {workload}\n\n"
@@ -158,8 +161,8 @@ def pmc_table(fetch_csv, write_csv, workload, copy_mib):
                 "Durations are the dispatch timestamps of the FETCH_SIZE run (one call; counters "
                 "serialise the dispatches). Commands (from the repository root, on one MI355X, each "
                 "counter in a run of its own):\n\n```\ncd /tmp && export TMPDIR=/tmp && cd -\n"
-                f"{runs}\npython3 bench.py --pmc-table gpurun_out/pmc/FETCH_SIZE/run_counter_collection.csv "
-                f"gpurun_out/pmc/WRITE_SIZE/run_counter_collection.csv --calibration-copy-mib {copy_mib}\n```\n\n"
+                f"{runs}\npython3 bench.py --pmc-table {fetch_csv} {write_csv} "
+                f"--calibration-copy-mib {copy_mib}\n```\n\n"
                 + text + "\n")
     print(text)
 
