@@ -454,6 +454,68 @@ def test_support_stats(name):
     assert ambiguous <= max(2, checked // 10)
 
 
+def _degenerate(name, grid, d, dtype, BQ, G, S, rho, m, k, gen="g1"):
+    n = grid[0] * grid[1] * grid[2]
+    p = configs.Params(heads=1, n_tokens=n, head_dim=d, dtype=dtype, q_block=BQ, n_groups=G,
+                       n_samples=S, kmeans_iters=4, density=rho, n_probes=m, rank=k,
+                       ridge_lambda=1e-3)
+    return configs.Workload(name=name, grid=grid, params=p, scales=[d ** -0.5], generator=gen,
+                            seed=31)
+
+
+DEGENERATE = {
+    # one token: one group, one block of one row, softmax over one key
+    "n1_f32": _degenerate("n1_f32", (1, 1, 1), 64, "f32", 64, 1, 1, 1.0, 0, 0),
+    "n2_bf16": _degenerate("n2_bf16", (1, 1, 2), 128, "bf16", 128, 1, 2, 1.0, 0, 0, gen="g2"),
+    # a single ragged block; every key is its own group
+    "n37_every_key_a_group": _degenerate("n37", (1, 1, 37), 64, "f32", 64, 37, 5, 0.5, 2, 2),
+    # one group larger than the budget: the at-least-one-group rule routes it
+    "single_group": _degenerate("g1_only", (2, 10, 10), 128, "bf16", 128, 1, 16, 0.3, 4, 4,
+                                gen="g2"),
+    # a budget of one key: every block keeps only its best group
+    "budget_one_key": _degenerate("kappa1", (3, 10, 10), 128, "bf16", 128, 16, 32, 1.5 / 300,
+                                  0, 0, gen="g2"),
+    # every row but one is a probe
+    "probes_all_but_one": _degenerate("m63", (1, 4, 16), 64, "f32", 64, 4, 8, 1.0, 63, 16),
+    # full-rank correction (k = d) with more probes than d
+    "full_rank": _degenerate("k_eq_d", (2, 8, 16), 64, "bf16", 64, 8, 32, 0.5, 96, 64,
+                             gen="g2"),
+}
+
+
+@pytest.mark.parametrize("name", list(DEGENERATE))
+def test_degenerate_calls(name):
+    """Edge shapes of the method, each through all five stages: index stages
+    exactly from the dumped scores, values against the oracle on the GPU's
+    own indices."""
+    wl = DEGENERATE[name]
+    r = run_pipeline(wl)
+    p = r.p
+    tol = TOL[p.dtype]
+    g = head_arrays(r, 0)
+    assert np.array_equal(orc.argmin_lowest(g["assign"]), g["key_label"])
+    kp, goff, sizes = orc.group_members(g["key_label"], p.n_groups)
+    assert np.array_equal(kp, g["key_perm"]) and np.array_equal(goff, g["group_off"])
+    g1, v = orc.dominant_groups(g["coords"], sizes)
+    assert np.array_equal(g1, g["dom"])
+    assert np.array_equal(orc.query_order(g["dom"], g["domval"]), g["query_perm"])
+    ptr, grp = orc.route(g["sigma"], sizes, p.key_budget)
+    assert np.array_equal(ptr, g["block_ptr"])
+    assert np.array_equal(grp, g["block_groups"][:ptr[-1]])
+    if p.key_budget < sizes.max():
+        # the smallest budgets route exactly one group per block
+        assert np.all(np.diff(ptr) >= 1)
+    Q, K, V = (x[0].astype(np.float64) for x in (r.inp.Q, r.inp.K, r.inp.V))
+    o = oracle_on_gpu_indices(Q, K, V, float(r.inp.scale[0]), p, g)
+    assert int(g["executed_pairs"]) == o["E"]
+    assert rel_l2(to_token_order(g["S"], g["query_perm"]), o["S"]) < tol
+    # k_eff = min(k, m, d), or 0 when the residuals vanish (one group: sparse == dense)
+    assert int(g["rank_eff"]) == o["U"].shape[1]
+    assert rel_l2(g["O"], o["O"]) < tol
+    if p.n_tokens == 1:
+        np.testing.assert_allclose(g["O"][0], r.inp.V[0][0], rtol=1e-2 if p.dtype == "bf16" else 1e-6)
+
+
 def test_full_density_equals_dense():
     wl = small_bf16(name="full", rho=1.0, m=0, k=0, G=16, seed=15)
     r = run_pipeline(wl)
