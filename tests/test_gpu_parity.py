@@ -480,6 +480,14 @@ DEGENERATE = {
     # full-rank correction (k = d) with more probes than d
     "full_rank": _degenerate("k_eq_d", (2, 8, 16), 64, "bf16", 64, 8, 32, 0.5, 96, 64,
                              gen="g2"),
+    # the largest group count (G = 1024) with a wide budget
+    "max_groups": _degenerate("g1024", (2, 64, 64), 128, "bf16", 128, 1024, 64, 0.5, 8, 4,
+                              gen="g2"),
+    # kernel shapes the other workloads do not reach
+    "bf16_d64_bq128": _degenerate("d64_bq128", (3, 16, 25), 64, "bf16", 128, 24, 64, 0.25, 32,
+                                  8, gen="g2"),
+    "f32_d128": _degenerate("f32_d128", (3, 16, 25), 128, "f32", 128, 24, 64, 0.25, 32, 8,
+                            gen="g2"),
 }
 
 
