@@ -569,6 +569,40 @@ def test_determinism():
         assert np.array_equal(a.np("block_groups")[h][:ptr[h][-1]], b.np("block_groups")[h][:ptr[h][-1]])
 
 
+def test_concurrent_calls_on_two_streams():
+    """Calls on different streams with disjoint buffers may overlap: two
+    operators (different inputs, each with its own buffers and workspace),
+    enqueued on two streams of default priority without synchronising in
+    between, give exactly what each gives alone."""
+    wl_a = WORKLOADS["bf16_d128"]
+    wl_b = small_bf16(name="concurrent_b", seed=19, m=64, k=16)
+    dev = torch.device("cuda")
+    ops, args, alone = [], [], []
+    for wl in (wl_a, wl_b):
+        inp = wl.make_inputs()
+        op = binding.SparsePR(wl.params, dev)
+        dt = binding.torch_dtype(wl.params)
+        Q, K, V = (torch.from_numpy(x).to(dev, dt) for x in (inp.Q, inp.K, inp.V))
+        scale = torch.from_numpy(inp.scale).to(dev)
+        idx = op.upload_indices(inp.sample_idx, inp.init_idx)
+        op.run(Q, K, V, scale, idx)
+        torch.cuda.synchronize()
+        alone.append(op.buffers.O.clone())
+        ops.append(op)
+        args.append((Q, K, V, scale, idx))
+    streams = [torch.cuda.Stream(device=dev), torch.cuda.Stream(device=dev)]
+    for rep in range(3):
+        for op in ops:
+            op.buffers.O.zero_()
+        torch.cuda.synchronize()
+        for op, a, st in zip(ops, args, streams):
+            with torch.cuda.stream(st):
+                op.run(*a)
+        torch.cuda.synchronize()
+        for op, ref in zip(ops, alone):
+            assert torch.equal(op.buffers.O, ref), f"repeat {rep}"
+
+
 def test_attend_block_subsets_compose():
     """Blocks holding probe rows, then the others, write exactly the full attention."""
     r = run_pipeline(small_bf16(name="subsets", m=8, k=4, seed=17))   # 8 of 24 blocks hold probes
