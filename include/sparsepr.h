@@ -38,7 +38,9 @@
  *   refers to token query_perm[h, i].
  * - `stream` is a hipStream_t (NULL = legacy default stream). Work is only
  *   enqueued; results are valid after the stream is synchronised. Calls on
- *   different streams with disjoint buffers may run concurrently.
+ *   different streams with disjoint buffers may run concurrently. No entry
+ *   point allocates, copies, clears memory with a memset or synchronises, so
+ *   a sequence of calls can be captured in a HIP graph and replayed.
  * - Errors: validation is done on the host before anything is enqueued. A
  *   non-zero status means nothing was launched, except SPARSEPR_ERR_HIP,
  *   which reports that a launch failed (earlier launches of the same call
