@@ -268,6 +268,23 @@ def test_p5_brute_semantic_head():
     np.testing.assert_array_equal(res.O, res.S)
 
 
+def test_kmeans_empty_group_keeps_its_centroid():
+    """Hand-derived: two initial centroids on a duplicated point; the
+    lowest-index tie rule empties group 1 in the first step, and its kept
+    centroid (3, 3) attracts rows 0-2 in the second step. A centroid reset to
+    the origin would take row 3 instead."""
+    X = np.array([[3, 3], [3, 3], [3.2, 3], [0, 0], [8, 8], [8.1, 8]], dtype=float)
+    init = np.array([0, 1, 4])
+    km1 = orc.kmeans(X, init, 1)
+    assert km1.labels.tolist() == [0, 0, 0, 0, 2, 2]
+    np.testing.assert_array_equal(km1.centroids[1], [3.0, 3.0])
+    np.testing.assert_allclose(km1.centroids[0], [2.3, 2.25], rtol=0, atol=1e-15)
+    km2 = orc.kmeans(X, init, 2)
+    assert km2.labels.tolist() == [1, 1, 1, 0, 2, 2]
+    assert orc.semantic_order(X, init, 2, 3)[0].tolist() == [1, 1, 1, 0, 2, 2]
+    assert brute_kmeans_rows(X.tolist(), init, 2) == [1, 1, 1, 0, 2, 2]
+
+
 def test_p6_semantic_kmeans_equals_sklearn_lloyd():
     """The semantic partition is scikit-learn's Lloyd k-means started from the
     same rows, on separated clusters where it converges within T steps and
