@@ -285,6 +285,51 @@ def test_kmeans_empty_group_keeps_its_centroid():
     assert brute_kmeans_rows(X.tolist(), init, 2) == [1, 1, 1, 0, 2, 2]
 
 
+def test_dominant_group_skips_empty_groups_lowest_index_on_ties():
+    """Hand-derived: group 1 is empty, so its large responses never win; an
+    exact tie between groups 0 and 2 goes to group 0."""
+    C = np.array([[5.0, 9.0, 5.0], [1.0, 1.0, 0.0], [2.0, 7.0, 7.0]])
+    g1, v = orc.dominant_groups(C, np.array([3, 0, 2]))
+    assert g1.tolist() == [0, 0, 2]
+    assert v.tolist() == [5.0, 1.0, 7.0]
+
+
+def test_query_order_ties_by_token():
+    """Hand-derived: group 0 first (tokens 1, 3 tie on v, ascending token),
+    then group 1 by v descending (token 4, then tokens 0, 2 tied)."""
+    g1 = np.array([1, 0, 1, 0, 1])
+    v = np.array([2.0, 3.0, 2.0, 3.0, 5.0])
+    assert orc.query_order(g1, v).tolist() == [1, 3, 4, 0, 2]
+
+
+def test_subspace_rank_at_most_the_probe_count():
+    """m residual rows span at most m directions, so k_eff = min(k, m, d);
+    an all-zero residual leaves no subspace."""
+    R = np.random.default_rng(5).standard_normal((3, 6))
+    U, _ = orc.residual_subspace(R, np.full(3, 1 / 3), 5)
+    assert U.shape == (6, 3)
+    np.testing.assert_allclose(U.T @ U, np.eye(3), rtol=0, atol=1e-12)
+    U0, _ = orc.residual_subspace(np.zeros((4, 6)), np.full(4, 0.25), 2)
+    assert U0.shape == (6, 0)
+
+
+def test_error_summary_is_mean_and_99th_percentile():
+    """Closed form: errors 0, 0.01, ..., 1.00 have mean 0.5 and 99th
+    percentile 0.99."""
+    s = orc.error_summary(np.arange(101) / 100.0)
+    assert s["mean"] == pytest.approx(0.5, abs=1e-15)
+    assert s["p99"] == pytest.approx(0.99, abs=1e-15)
+
+
+def test_sampled_metric_closed_form():
+    """One-dimensional keys: M = tau^2 (2^2 + 3^2) for sampled queries 2 and 3,
+    so two keys 1 apart are sqrt(M) apart in response space."""
+    Q = np.array([[7.0], [2.0], [3.0]])
+    M = orc.sampled_metric(Q, 0.5, np.array([1, 2]))
+    assert M.shape == (1, 1)
+    assert M[0, 0] == pytest.approx(0.25 * 13.0, abs=1e-15)
+
+
 def test_p6_semantic_kmeans_equals_sklearn_lloyd():
     """The semantic partition is scikit-learn's Lloyd k-means started from the
     same rows, on separated clusters where it converges within T steps and
