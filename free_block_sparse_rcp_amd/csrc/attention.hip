@@ -5,12 +5,14 @@
 //
 // bf16 path (gfx950 MFMA, v_mfma_f32_32x32x16_bf16). One workgroup owns one
 // query block of BQ rows; each wavefront owns 32 query rows. Keys stream in
-// tiles of 64 through double-buffered LDS. The product is formed transposed,
-// S^T = K Q^T, so each lane holds the logits of ONE query (lane % 32) for 16
-// keys of each 32-key half: the online-softmax statistics are per-lane
-// scalars, and the probabilities are already in the B-operand layout of
-// O^T = V^T P^T. V stays row-major in LDS (chunks XOR-swizzled) and is read
-// transposed with ds_read_b64_tr_b16. The key list of a block is the
+// tiles of KT through double-buffered LDS: 32 in the sparse and probe modes,
+// where the smaller buffers let three workgroups share a CU, and 64 in dense
+// mode, where the longer tile between barriers pays more. The product is
+// formed transposed, S^T = K Q^T, so each lane holds the logits of ONE query
+// (lane % 32) for 16 keys of each 32-key part of the tile: the online-softmax
+// statistics are per-lane scalars, and the probabilities are already in the
+// B-operand layout of O^T = V^T P^T. V stays row-major in LDS (rows padded)
+// and is read transposed with ds_read_b64_tr_b16. The key list of a block is the
 // concatenation of its routed groups' ranges in the group-contiguous Kp/Vp;
 // tiles run across group boundaries, so only the block's last tile is ragged.
 #include "common.hpp"
@@ -28,19 +30,25 @@ constexpr int kMaxGroups = 1024;
 // bytes (the transposing ds_read_b64_tr_b16 reads 4 rows x 64 bytes per 32
 // lanes, and the pitch puts those rows on disjoint banks). Both keep every
 // LDS read address affine in the loop indices.
-template <int D>
+// LDS geometry of one KT-key tile. A buffer is rounded up to whole 1 KB
+// loads; load lanes past the tile's data re-read chunk 0 of the tile's first
+// row into that padding.
+template <int D, int KT>
 struct TileGeom {
+  static_assert(KT == 32 || KT == 64, "tiles of 32 or 64 keys");
   static constexpr int ROWB = 2 * D;
   static constexpr int KP = ROWB + 16;
   static constexpr int VP = ROWB + 64;
   static constexpr int KCH = KP / 16;          // 16-byte chunks per padded K row
   static constexpr int VCH = VP / 16;
-  static constexpr int KBYTES = 64 * KP;
-  static constexpr int VBYTES = 64 * VP;
+  static constexpr int KBYTES = (KT * KP + 1023) / 1024 * 1024;
+  static constexpr int VBYTES = (KT * VP + 1023) / 1024 * 1024;
   static constexpr int KINS = KBYTES / 1024;   // 1 KB direct loads per tile
   static constexpr int VINS = VBYTES / 1024;
-  static_assert(KBYTES % 1024 == 0 && VBYTES % 1024 == 0, "tiles must be whole 1 KB loads");
 };
+
+template <int MODE>
+constexpr int tile_keys() { return MODE == ATTN_DENSE ? 64 : 32; }
 
 // Decoded work item of one workgroup.
 struct Item {
@@ -173,20 +181,20 @@ __device__ __forceinline__ int key_row(int p, int total, int ng, const int* r_st
   return r_start[cur] + (p - r_cum[cur]);
 }
 
-// One 64-key tile of the flash loop: S^T = K Q^T, online softmax, O^T += V^T P^T.
+// One KT-key tile of the flash loop: S^T = K Q^T, online softmax, O^T += V^T P^T.
 // Ktile / Vtile point at distinct __shared__ buffers, so the compiler can see
 // that these reads do not alias the direct loads filling the other buffer.
-template <int D>
+template <int D, int KT>
 __device__ __forceinline__ void attn_tile(const char* __restrict__ kb, const char* __restrict__ vb,
                                           const bf16x8* qreg, f32x16* acc_o, float& m_run,
                                           float& l_run, float c, int kbase, int total, int hl) {
-  using TG = TileGeom<D>;
-  constexpr int KT = 64;
+  using TG = TileGeom<D, KT>;
+  constexpr int NKT = KT / 32;   // 32-key parts of the tile
   constexpr int NDT = D / 32;
   constexpr int NKK = D / 16;
-  f32x16 s[2];
+  f32x16 s[NKT];
 #pragma unroll
-  for (int kt = 0; kt < 2; ++kt) {
+  for (int kt = 0; kt < NKT; ++kt) {
 #pragma unroll
     for (int r = 0; r < 16; ++r) s[kt][r] = 0.f;
 #pragma unroll
@@ -198,7 +206,7 @@ __device__ __forceinline__ void attn_tile(const char* __restrict__ kb, const cha
   // online softmax in log2 units; the max is only re-based when it grows by > 8
   if (kbase + KT > total) {
 #pragma unroll
-    for (int kt = 0; kt < 2; ++kt)
+    for (int kt = 0; kt < NKT; ++kt)
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
         const int kp = kbase + 32 * kt + 8 * (r >> 2) + 4 * hl + (r & 3);
@@ -207,7 +215,7 @@ __device__ __forceinline__ void attn_tile(const char* __restrict__ kb, const cha
   }
   float mx = -__builtin_inff();
 #pragma unroll
-  for (int kt = 0; kt < 2; ++kt)
+  for (int kt = 0; kt < NKT; ++kt)
 #pragma unroll
     for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[kt][r]);
   {
@@ -228,9 +236,9 @@ __device__ __forceinline__ void attn_tile(const char* __restrict__ kb, const cha
     if (need) m_run = m_new;
   }
   const float neg_m = -m_run;
-  bf16x8 pk[2][2];
+  bf16x8 pk[NKT][2];
 #pragma unroll
-  for (int kt = 0; kt < 2; ++kt)
+  for (int kt = 0; kt < NKT; ++kt)
 #pragma unroll
     for (int hf = 0; hf < 2; ++hf) {
       float pv[8];
@@ -249,7 +257,7 @@ __device__ __forceinline__ void attn_tile(const char* __restrict__ kb, const cha
     }
   // V^T operand via transposing LDS reads
 #pragma unroll
-  for (int kt = 0; kt < 2; ++kt)
+  for (int kt = 0; kt < NKT; ++kt)
 #pragma unroll
     for (int hf = 0; hf < 2; ++hf) {
       const int chunk = 32 * kt + 16 * hf;
@@ -292,12 +300,13 @@ __device__ __forceinline__ void issue_rows(const char* base, const int* rows, co
 }
 
 template <int D, int BQ, int MODE>
-__global__ __launch_bounds__(BQ * 2) __attribute__((amdgpu_waves_per_eu(2, 2)))
+__global__ __launch_bounds__(BQ * 2)
+__attribute__((amdgpu_waves_per_eu(tile_keys<MODE>() == 32 ? 3 : 2, tile_keys<MODE>() == 32 ? 3 : 2)))
 void k_attn_mfma(AttnArgs a) {
-  using TG = TileGeom<D>;
+  constexpr int KT = tile_keys<MODE>();
+  using TG = TileGeom<D, KT>;
   constexpr int NT = BQ * 2;
   constexpr int NW = BQ / 32;
-  constexpr int KT = 64;
   constexpr int ROWB = TG::ROWB;
   constexpr int CPR = ROWB / 16;             // data chunks per row
   constexpr int NDT = D / 32;                // 32-wide output d tiles
@@ -354,7 +363,7 @@ void k_attn_mfma(AttnArgs a) {
   // (the sparse and probe modes keep byte offsets of rows, dense mode row indices)
   constexpr bool kByteRows = MODE != ATTN_DENSE;
   auto fill_rows = [&](int tile) {
-    if (w == 0 && tile < ntiles) {
+    if (w == 0 && tile < ntiles && lane < KT) {
       const int r = key_row(tile * KT + lane, total, ng, r_start, r_cum, cursor);
       ridx[tile & 1][lane] = kByteRows ? (int)((uint32_t)r * ROWB) : r;
     }
@@ -367,7 +376,7 @@ void k_attn_mfma(AttnArgs a) {
     for (int j = 0; j < KINS_W; ++j) {
       const int u = w + NW * j;
       if (u < TG::KINS) {
-        const int q = 64 * u + lane;
+        const int q0 = 64 * u + lane, q = q0 < KT * TG::KCH ? q0 : 0;
         const int r = q / TG::KCH, cc = q - r * TG::KCH;
         const char* src = Kh + (size_t)rows[r] * ROWB + (cc < CPR ? cc : 0) * 16;
         __builtin_amdgcn_global_load_lds(
@@ -378,7 +387,7 @@ void k_attn_mfma(AttnArgs a) {
     for (int j = 0; j < VINS_W; ++j) {
       const int u = w + NW * j;
       if (u < TG::VINS) {
-        const int q = 64 * u + lane;
+        const int q0 = 64 * u + lane, q = q0 < KT * TG::VCH ? q0 : 0;
         const int r = q / TG::VCH, cc = q - r * TG::VCH;
         const char* src = Vh + (size_t)rows[r] * ROWB + (cc < CPR ? cc : 0) * 16;
         __builtin_amdgcn_global_load_lds(
@@ -392,7 +401,7 @@ void k_attn_mfma(AttnArgs a) {
   // bits; pad chunks re-read chunk 0). Row-table entries are byte offsets of
   // rows, so a load address is the head base plus one 32-bit sum.
   auto lane_word = [&](int u, int ch) {
-    const int q = 64 * u + lane;
+    const int q0 = 64 * u + lane, q = q0 < KT * ch ? q0 : 0;   // past the tile: padding
     const int r = q / ch, cc = q - r * ch;
     return (4 * r) | (((cc < CPR ? cc : 0) * 16) << 16);
   };
@@ -434,13 +443,13 @@ void k_attn_mfma(AttnArgs a) {
   for (int tile = 0; tile < ntiles; tile += 2) {
     if (tile + 1 < ntiles) ISSUE_TILE(tile + 1, lds_k1, lds_v1);
     fill_rows(tile + 2);
-    attn_tile<D>(lds_k0 + koff, lds_v0 + voff, qreg, acc_o, m_run, l_run, c, tile * KT, total, hl);
+    attn_tile<D, KT>(lds_k0 + koff, lds_v0 + voff, qreg, acc_o, m_run, l_run, c, tile * KT, total, hl);
     __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
     if (tile + 1 >= ntiles) break;
     if (tile + 2 < ntiles) ISSUE_TILE(tile + 2, lds_k0, lds_v0);
     fill_rows(tile + 3);
-    attn_tile<D>(lds_k1 + koff, lds_v1 + voff, qreg, acc_o, m_run, l_run, c, (tile + 1) * KT, total, hl);
+    attn_tile<D, KT>(lds_k1 + koff, lds_v1 + voff, qreg, acc_o, m_run, l_run, c, (tile + 1) * KT, total, hl);
     __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
   }
