@@ -254,6 +254,64 @@ def random_block_support(p, Q, K, V, scale, inp):
     return out
 
 
+def unprobed_mask(p, b):
+    """[H, N] token mask of the rows that are not probe rows of this call."""
+    import torch
+    H, N = p.heads, p.n_tokens
+    mask = torch.ones(H, N, dtype=torch.bool, device=b.S.device)
+    if p.n_probes:
+        pos = torch.tensor([((2 * i + 1) * N) // (2 * p.n_probes) for i in range(p.n_probes)],
+                           dtype=torch.long, device=b.S.device)
+        mask.scatter_(1, b.query_perm.long().gather(1, pos[None].expand(H, -1)), False)
+    return mask
+
+
+def residual_r2(p, b, ref, mask):
+    """How affine-predictable the dense-minus-sparse residual is under one
+    call's partition: R^2 of the fitted map r = U Theta^T [s; 1] on the rows the
+    fit did not see (every unprobed row), against R = O_dense - S. Pooled over
+    heads; each head's R is centred on its own mean over those rows."""
+    import torch
+    D = p.head_dim
+    with torch.no_grad():
+        S_tok = torch.empty_like(b.S)
+        S_tok.scatter_(1, b.query_perm.long()[:, :, None].expand(-1, -1, D), b.S)
+        num = den = 0.0
+        for h in range(p.heads):
+            m = mask[h]
+            s = S_tok[h][m].double()
+            R = ref[h][m].double() - s
+            k = int(b.rank_eff[h].item())
+            if k > 0:
+                xa = torch.cat([s, torch.ones_like(s[:, :1])], dim=1)
+                R_hat = (xa @ b.Theta[h][:, :k].double()) @ b.U[h][:, :k].double().T
+            else:
+                R_hat = torch.zeros_like(R)
+            num += float(((R - R_hat) ** 2).sum())
+            den += float(((R - R.mean(dim=0)) ** 2).sum())
+    return 1.0 - num / den if den > 0 else float("nan")
+
+
+def comparator_r2(p, mode, Q, K, V, scale, inp, ref):
+    """Residual R^2 under another partition (random-block or semantic), with the
+    same probe count, rank and ridge as the response-coupled call."""
+    import dataclasses
+    import torch
+    from free_block_sparse_rcp_amd import binding
+
+    pc = dataclasses.replace(p, partition_mode=mode)
+    op = binding.SparsePR(pc, Q.device)
+    if mode == binding.RANDOM_BLOCK:
+        idx = op.upload_indices(rand_key_perm=inp.rand_key_perm, rand_query_perm=inp.rand_query_perm)
+    else:
+        idx = op.upload_indices(init_idx=inp.init_idx)
+    op.run(Q, K, V, scale, idx)
+    torch.cuda.synchronize()
+    out = residual_r2(pc, op.buffers, ref, unprobed_mask(pc, op.buffers))
+    del op
+    return out
+
+
 def cpu_baseline(wl, inp, block_stride):
     """The fp64 oracle, as it stands, on head 0 of the same workload: every
     stage in the pages' order; the block-sparse attention step runs on every
@@ -458,11 +516,7 @@ def main():
             ref = O_dense.float()
             S_tok = torch.empty_like(b.S)
             S_tok.scatter_(1, b.query_perm.long()[:, :, None].expand(-1, -1, D), b.S)
-            mask = torch.ones(H, N, dtype=torch.bool, device=dev)
-            pos = torch.tensor([((2 * i + 1) * N) // (2 * p.n_probes) for i in range(p.n_probes)],
-                               dtype=torch.long, device=dev)
-            if p.n_probes:
-                mask.scatter_(1, b.query_perm.long().gather(1, pos[None].expand(H, -1)), False)
+            mask = unprobed_mask(p, b)
             rn = ref.norm(dim=2)
             e = ((b.O.float() - ref).norm(dim=2) / rn)[mask]
             e0 = ((S_tok - ref).norm(dim=2) / rn)[mask]
@@ -479,6 +533,14 @@ def main():
                 "response_coupled": support_summary(p, b, Q, K, scale, support_blocks(p)),
                 "semantic": quality["semantic"].pop("support"),
                 "random_block": random_block_support(p, Q, K, V, scale, inp)}
+            if p.n_probes and p.rank:
+                log("[bench] residual R^2 per partition")
+                quality["residual_r2"] = {
+                    "response_coupled": residual_r2(p, b, ref, mask),
+                    "random_block": comparator_r2(p, binding.RANDOM_BLOCK, Q, K, V, scale, inp, ref),
+                    "semantic": comparator_r2(p, binding.SEMANTIC, Q, K, V, scale, inp, ref),
+                    "definition": "1 - sum |R - U Theta^T [s;1]|^2 / sum |R - mean R|^2 over unprobed "
+                                  "rows, R = dense - sparse output; same m, k, lambda per partition"}
 
     traffic = load_traffic(wl.name)
     roofline = {"bound": "mfma", "kernel": "k_attn_mfma (sparsepr_attend)",
