@@ -395,6 +395,52 @@ def test_semantic_comparator(name):
             assert np.array_equal(g["O"], out)
 
 
+def test_semantic_partition_with_probe_correction():
+    """The semantic partition with probes, the residual fit and its application
+    (the combination the residual-predictability diagnostic runs): query order
+    bit-exact, executed pairs exact, sparse and probe rows against the oracle on
+    the GPU's indices, and the output against the fp64 fit and apply on the
+    GPU's own S and probe rows. The end-to-end output is printed, not bounded:
+    with m <= d+1 and a small gap below the k-th eigenvalue (5.9e-4 on head 1
+    here), the bf16 path's 1e-3 differences in S turn the subspace's last
+    directions and move the output by a few percent."""
+    wl = small_bf16(name="semantic_probes", mode=2, seed=22)
+    r = run_pipeline(wl)
+    p = r.p
+    assert p.n_probes > 0 and p.rank > 0
+    for h in range(p.heads):
+        g = head_arrays(r, h)
+        qorder, _, _ = orc.group_members(r.np("query_label")[h], p.n_groups)
+        assert np.array_equal(qorder, g["query_perm"])
+        Q, K, V = (x[h].astype(np.float64) for x in (r.inp.Q, r.inp.K, r.inp.V))
+        o = oracle_on_gpu_indices(Q, K, V, float(r.inp.scale[h]), p, g)
+        assert int(g["executed_pairs"]) == o["E"]
+        assert int(g["rank_eff"]) == o["U"].shape[1]
+        e_s = rel_l2(to_token_order(g["S"], g["query_perm"]), o["S"])
+        e_p = rel_l2(g["O_probe"], o["Op"])
+        e_o = rel_l2(g["O"], o["O"])
+        # the fit from the GPU's own S and probe rows, applied in fp64
+        pos = orc.probe_positions(p.n_tokens, p.n_probes)
+        Sp = g["S"][pos].astype(np.float64)
+        Op = g["O_probe"].astype(np.float64)
+        w = orc.probe_weights(Op)
+        U, ev = orc.residual_subspace(Op - Sp, w, p.rank)
+        Th = orc.ridge_fit(Sp, (Op - Sp) @ U, w, p.ridge_lambda)
+        S_q = g["S"].astype(np.float64)
+        O_fit = S_q + orc.predicted_residual(S_q, U, Th)
+        O_fit[pos] = Op                                   # probe rows are exact rows
+        O_fit = to_token_order(O_fit, g["query_perm"])
+        e_f = rel_l2(g["O"], O_fit)
+        keff = U.shape[1]
+        gap = (ev[keff - 1] - ev[keff]) / max(ev[0], 1e-300) if keff < len(ev) else 1.0
+        print(f"[gpu] semantic+probes head {h}: S {e_s:.2e} probes {e_p:.2e} O {e_o:.2e} "
+              f"O vs fit on GPU inputs {e_f:.2e} gap {gap:.1e} |Theta| {np.linalg.norm(Th):.1f}",
+              flush=True)
+        assert e_s < TOL["bf16"] and e_p < TOL["bf16"]
+        if gap > 1e-4:
+            assert e_f < 5e-3      # O is stored in bf16: relative rounding up to 2^-9 per element
+
+
 @pytest.mark.parametrize("name", ["tiny", "bf16_d128", "bf16_d64_bq64"])
 def test_support_stats(name):
     """Support and mass diagnostics against fp64 on the GPU's own labels and
