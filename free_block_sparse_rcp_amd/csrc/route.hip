@@ -60,20 +60,29 @@ __global__ __launch_bounds__(256) void k_route_scores(const void* Qv, const int3
   const int nblk = min(kRsBlocks, nb - b0);
   {
     const int c = t % CPR, rg = t / CPR;
+    // one round of eight row chunks of block j starting at row r0 (rows past
+    // the block's end re-read its last row and are not added)
+    auto load_round = [&](int j, int r0, u32x4* raw) {
+      const int p0 = (b0 + j) * BQ, n = min(N, p0 + BQ) - p0;
+#pragma unroll
+      for (int v = 0; v < 8; ++v) {
+        const int r = r0 + v * RG;
+        const int tok = clamp_idx(qp[p0 + min(r, n - 1)], N);
+        raw[v] = *reinterpret_cast<const u32x4*>(Q + (size_t)tok * ROWB + c * 16);
+      }
+    };
+    // the next block's first round is issued as soon as this block's first
+    // round has been added, so it is in flight during the reduction below
+    u32x4 raw[8];
+    if (nblk > 0) load_round(0, rg, raw);
     for (int j = 0; j < nblk; ++j) {
       const int p0 = (b0 + j) * BQ, n = min(N, p0 + BQ) - p0;
       float acc[EPC];
 #pragma unroll
       for (int u = 0; u < EPC; ++u) acc[u] = 0.f;
       // rows rg, rg + RG, ... in increasing order, eight loads in flight
-      for (int r0 = rg; r0 < n; r0 += 8 * RG) {
-        u32x4 raw[8];
-#pragma unroll
-        for (int v = 0; v < 8; ++v) {
-          const int r = r0 + v * RG;
-          const int tok = clamp_idx(qp[p0 + min(r, n - 1)], N);
-          raw[v] = *reinterpret_cast<const u32x4*>(Q + (size_t)tok * ROWB + c * 16);
-        }
+      for (int r0 = rg;; r0 += 8 * RG) {
+        if (r0 != rg) load_round(j, r0, raw);
 #pragma unroll
         for (int v = 0; v < 8; ++v) {
           if (r0 + v * RG >= n) break;
@@ -87,6 +96,10 @@ __global__ __launch_bounds__(256) void k_route_scores(const void* Qv, const int3
 #pragma unroll
             for (int u = 0; u < 4; ++u) acc[u] += __uint_as_float(raw[v][u]);
           }
+        }
+        if (r0 + 8 * RG >= n) {
+          if (j + 1 < nblk) load_round(j + 1, rg, raw);
+          break;
         }
       }
 #pragma unroll
