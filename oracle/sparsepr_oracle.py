@@ -354,37 +354,108 @@ def residual_subspace(R_probe, w, rank):
     return evecs[:, :k_eff].copy(), evals
 
 
-def ridge_fit(S_probe, Y, w, lam):
-    """Weighted ridge regression of Y on [s, 1] with an unpenalised bias.
+def map_inputs(S_rows, U):
+    """Inputs of the fitted map: each sparse output's coordinates in the
+    residual subspace, z = U^T s.
 
-    Solves (X^T W X + lam * I~) Theta = X^T W Y with X = [S_probe, 1],
-    W = diag(w), I~ = diag(1, ..., 1, 0). Returns Theta [d+1, k].
+    Reading: the pages describe the correction as a small linear map from the
+    sparse output that reaches the residual subspace ([SK], paragraph on
+    partition geometry) and as an affine correction from the sparse output
+    within the output subspace seen in the probe residuals ([PC]). The map
+    therefore reads s through the same k_eff directions it writes: it has
+    k_eff + 1 inputs (with the bias), not d + 1.
     """
-    S_probe = np.asarray(S_probe, F64)
-    m, d = S_probe.shape
-    X = np.hstack([S_probe, np.ones((m, 1))])
-    W = np.asarray(w, F64)[:, None]
-    A = X.T @ (W * X)
-    A[np.arange(d), np.arange(d)] += lam
-    B = X.T @ (W * np.asarray(Y, F64))
+    return np.asarray(S_rows, F64) @ np.asarray(U, F64)
+
+
+def ridge_penalty(Z, w, lam):
+    """Penalty on the slopes: lam times the mean, over the k input
+    coordinates, of their weighted variance about their weighted mean.
+
+    Reading: the pages say only "weighted ridge regression" ([AD]). The
+    penalty is taken relative to the spread of the map's inputs, so that
+    scaling V (hence s, o and r) by c scales the correction by c and the same
+    lam means the same amount of shrinkage on every head.
+    """
+    Z = np.asarray(Z, F64)
+    w = np.asarray(w, F64)
+    k = Z.shape[1]
+    tw = w.sum()
+    if k == 0 or tw <= 0:
+        return 0.0
+    zbar = (w[:, None] * Z).sum(axis=0) / tw
+    var = (w[:, None] * (Z - zbar) ** 2).sum(axis=0) / tw
+    var[np.all(Z == Z[:1], axis=0)] = 0.0     # a constant input has no spread
+    return float(lam * var.mean())
+
+
+def ridge_fit(Z, Y, w, lam):
+    """Weighted ridge regression of Y on [z, 1] with an unpenalised bias.
+
+    Solves (X^T W X + lam_eff I~) Theta = X^T W Y with X = [Z, 1],
+    W = diag(w), I~ = diag(1, ..., 1, 0) and lam_eff = ridge_penalty(Z, w,
+    lam). Returns Theta [k+1, q]: rows 0..k-1 are the slopes, row k the bias.
+    When lam > 0 but the inputs do not vary, the slopes are 0 (any positive
+    penalty forces them there) and the bias is the weighted mean of Y.
+    """
+    Z = np.asarray(Z, F64)
+    Y = np.asarray(Y, F64)
+    w = np.asarray(w, F64)
+    m, k = Z.shape
+    X = np.hstack([Z, np.ones((m, 1))])
+    A = X.T @ (w[:, None] * X)
+    B = X.T @ (w[:, None] * Y)
+    lam_eff = ridge_penalty(Z, w, lam)
+    if lam > 0 and lam_eff == 0.0:
+        Th = np.zeros((k + 1, Y.shape[1]))
+        Th[k] = B[k] / A[k, k]
+        return Th
+    A[np.arange(k), np.arange(k)] += lam_eff
     return np.linalg.solve(A, B)
 
 
-def normal_equation_residual(S_probe, Y, w, lam, Theta):
-    """||(X^T W X + lam I~) Theta - X^T W Y|| / ||X^T W Y||."""
-    S_probe = np.asarray(S_probe, F64)
-    m, d = S_probe.shape
-    X = np.hstack([S_probe, np.ones((m, 1))])
+def normal_equation_residual(Z, Y, w, lam, Theta):
+    """||(X^T W X + lam_eff I~) Theta - X^T W Y|| / ||X^T W Y||, X = [Z, 1]."""
+    Z = np.asarray(Z, F64)
+    m, k = Z.shape
+    X = np.hstack([Z, np.ones((m, 1))])
     W = np.asarray(w, F64)[:, None]
     A = X.T @ (W * X)
-    A[np.arange(d), np.arange(d)] += lam
+    A[np.arange(k), np.arange(k)] += ridge_penalty(Z, w, lam)
     B = X.T @ (W * np.asarray(Y, F64))
     nb = np.linalg.norm(B)
     return float(np.linalg.norm(A @ Theta - B) / nb) if nb > 0 else float(np.linalg.norm(A @ Theta))
 
 
+def lift_map(U, Theta_z):
+    """The fitted map written on [s; 1]: Theta = [U Theta_z[:k]; Theta_z[k]]
+    ([d+1, k]), so that Theta^T [s; 1] = Theta_z^T [U^T s; 1]."""
+    U = np.asarray(U, F64)
+    Theta_z = np.asarray(Theta_z, F64)
+    k = U.shape[1]
+    return np.vstack([U @ Theta_z[:k], Theta_z[k:k + 1]])
+
+
+def fit_probe_map(S_probe, O_probe, rank, lam):
+    """The reconstruction fit from the probe rows' sparse and exact outputs:
+    weights, residual subspace, then the ridge map on the subspace
+    coordinates. Returns (w, U [d, k_eff], eigenvalues, Theta [d+1, k_eff])."""
+    S_probe = np.asarray(S_probe, F64)
+    O_probe = np.asarray(O_probe, F64)
+    m, d = S_probe.shape
+    w = probe_weights(O_probe)
+    if m == 0:
+        return w, np.zeros((d, 0)), np.zeros(d), np.zeros((d + 1, 0))
+    Rp = O_probe - S_probe
+    U, evals = residual_subspace(Rp, w, rank)
+    if U.shape[1] == 0:
+        return w, U, evals, np.zeros((d + 1, 0))
+    Theta_z = ridge_fit(map_inputs(S_probe, U), Rp @ U, w, lam)
+    return w, U, evals, lift_map(U, Theta_z)
+
+
 def predicted_residual(S_rows, U, Theta):
-    """U Theta^T [s; 1] for each row s."""
+    """U Theta^T [s; 1] for each row s (Theta on [s; 1], [d+1, k])."""
     S_rows = np.asarray(S_rows, F64)
     if U.shape[1] == 0:
         return np.zeros_like(S_rows)
@@ -419,7 +490,7 @@ class HeadResult:
     w: np.ndarray
     U: np.ndarray
     evals: np.ndarray
-    Theta: np.ndarray
+    Theta: np.ndarray        # fitted map on [s; 1], [d+1, k_eff]
     O: np.ndarray            # final output, token order
     executed_pairs: int
     density: float
@@ -439,7 +510,8 @@ def sparsepr_head(Q, K, V, scale, *, q_block, n_groups, kmeans_iters, density, n
        comparator: k-means on the raw query rows, ordered by cluster);
     3. route each block to its best groups within the key budget;
     4. block-sparse attention; exact attention on the probe rows;
-    5. weighted ridge fit of the probe residuals inside their subspace;
+    5. weighted ridge fit of the probe residuals' subspace coordinates on the
+       sparse outputs' subspace coordinates (and a bias);
     6. add the predicted residual to unprobed rows; probes keep their exact
        output.
     """
@@ -481,13 +553,7 @@ def sparsepr_head(Q, K, V, scale, *, q_block, n_groups, kmeans_iters, density, n
         O_p, _ = dense_attention(Q, K, V, scale, rows=ptok)
     else:
         O_p = np.zeros((0, d), F64)
-    w = probe_weights(O_p)
-    Rp = O_p - S[ptok]
-    U, evals = residual_subspace(Rp, w, rank) if n_probes > 0 else (np.zeros((d, 0)), np.zeros(d))
-    if U.shape[1] > 0:
-        Theta = ridge_fit(S[ptok], Rp @ U, w, ridge_lambda)
-    else:
-        Theta = np.zeros((d + 1, 0))
+    w, U, evals, Theta = fit_probe_map(S[ptok], O_p, rank, ridge_lambda)
     O = S + predicted_residual(S, U, Theta)
     O[ptok] = O_p
     E = executed_pairs(blocks, ksets, n_probes, n)

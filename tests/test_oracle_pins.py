@@ -436,9 +436,15 @@ def test_p2_zero_probes_or_rank_gives_sparse_output():
 def test_p3_normal_equations():
     Q, K, V = tiny_case(n=64, d=6, seed=17)
     res, _, _ = run_head(Q, K, V, 0.8, n_probes=10, rank=4)
-    Rp = res.O_probe - res.S[res.probe_tokens]
-    Y = Rp @ res.U
-    r = orc.normal_equation_residual(res.S[res.probe_tokens], Y, res.w, 1e-3, res.Theta)
+    k = res.U.shape[1]
+    assert k == 4
+    Sp = res.S[res.probe_tokens]
+    Y = (res.O_probe - Sp) @ res.U
+    # the map written on [s; 1] reads s only through U^T s
+    slopes = res.Theta[:-1]
+    np.testing.assert_allclose(slopes - res.U @ (res.U.T @ slopes), 0.0, rtol=0, atol=1e-12)
+    Theta_z = np.vstack([res.U.T @ slopes, res.Theta[-1:]])
+    r = orc.normal_equation_residual(orc.map_inputs(Sp, res.U), Y, res.w, 1e-3, Theta_z)
     assert r <= 1e-12
 
 
@@ -486,33 +492,144 @@ def test_p7_block_score_identity():
 # ----------------------------------------------- P8 / P9 closed forms
 
 def test_p8_planted_affine_residual():
+    """r = U0 (A0 U0^T s + c0): the subspace is U0 and the fit recovers A0, c0."""
     rng = np.random.default_rng(31)
     m, d, k = 80, 10, 3
     U0, _ = np.linalg.qr(rng.standard_normal((d, k)))
-    A0 = rng.standard_normal((k, d))
+    A0 = rng.standard_normal((k, k))
     c0 = rng.standard_normal(k)
     S = rng.standard_normal((m, d))
-    R = (S @ A0.T + c0) @ U0.T
+    R = (S @ U0 @ A0.T + c0) @ U0.T
     w = rng.random(m)
     w /= w.sum()
-    U, _ = orc.residual_subspace(R, w, k)
+    O_p = S + R
+    w2, U, _, Th = orc.fit_probe_map(S, O_p, k, 1e-12)
+    np.testing.assert_allclose(w2, orc.probe_weights(O_p), rtol=0, atol=0)
     np.testing.assert_allclose(U @ U.T, U0 @ U0.T, rtol=0, atol=1e-8)
-    Th = orc.ridge_fit(S, R @ U, w, 1e-12)
     Snew = rng.standard_normal((7, d))
     pred = orc.predicted_residual(Snew, U, Th)
-    np.testing.assert_allclose(pred, (Snew @ A0.T + c0) @ U0.T, rtol=0, atol=1e-8)
+    np.testing.assert_allclose(pred, (Snew @ U0 @ A0.T + c0) @ U0.T, rtol=0, atol=1e-8)
 
 
 def test_p9_interpolation_small_probe_count():
+    """m <= k_eff + 1 and lambda -> 0: the map reproduces every probe's residual."""
     rng = np.random.default_rng(37)
-    m, d = 7, 8                         # m <= d + 1
+    m, d = 7, 8
     S = rng.standard_normal((m, d))
     R = rng.standard_normal((m, d))
     w = rng.random(m)
     w /= w.sum()
-    U, _ = orc.residual_subspace(R, w, d)   # k_eff = m >= rank(R)
-    Th = orc.ridge_fit(S, R @ U, w, 1e-13)
+    U, _ = orc.residual_subspace(R, w, d)   # k_eff = m, the span of the residuals
+    assert U.shape[1] == m
+    Th = orc.lift_map(U, orc.ridge_fit(orc.map_inputs(S, U), R @ U, w, 1e-13))
     np.testing.assert_allclose(orc.predicted_residual(S, U, Th), R, rtol=0, atol=1e-8)
+
+
+def test_golden_ridge_one_input():
+    """Hand-derived slope and bias of a one-input weighted ridge."""
+    for case in GOLD["ridge_one_input"]:
+        z = np.array(case["z"])[:, None]
+        y = np.array(case["y"])[:, None]
+        Th = orc.ridge_fit(z, y, np.array(case["w"]), case["lam"])
+        a, b = case["expected_slope"], case["expected_bias"]
+        np.testing.assert_allclose(Th[0, 0], a[0] / a[1], rtol=0, atol=1e-14)
+        np.testing.assert_allclose(Th[1, 0], b[0] / b[1], rtol=0, atol=1e-14)
+
+
+def test_p6_ridge_equals_sklearn_weighted_ridge():
+    """Library pin: scikit-learn's Ridge with sample weights and a fitted
+    intercept minimises sum_i w_i ||y_i - B z_i - c||^2 + alpha ||B||^2 with an
+    unpenalised intercept; alpha is lam times the mean weighted variance of
+    the inputs, computed here with numpy's weighted covariance."""
+    from sklearn.linear_model import Ridge
+    rng = np.random.default_rng(41)
+    for m, k, q, lam in ((30, 4, 3, 1e-3), (12, 5, 2, 0.7), (6, 5, 5, 1e-2)):
+        Z = rng.standard_normal((m, k)) * rng.uniform(0.2, 3.0, k) + rng.standard_normal(k)
+        Y = rng.standard_normal((m, q))
+        w = rng.random(m)
+        w /= w.sum()
+        cov = np.atleast_2d(np.cov(Z.T, aweights=w, bias=True))
+        alpha = lam * np.trace(cov) / k
+        ref = Ridge(alpha=alpha, fit_intercept=True, solver="cholesky", tol=1e-14).fit(
+            Z, Y, sample_weight=w)
+        Th = orc.ridge_fit(Z, Y, w, lam)
+        np.testing.assert_allclose(Th[:k], ref.coef_.T, rtol=0, atol=1e-9)
+        np.testing.assert_allclose(Th[k], ref.intercept_, rtol=0, atol=1e-9)
+
+
+def test_ridge_large_penalty_limit():
+    """As lambda grows the slopes vanish and the bias tends to the weighted
+    mean of the targets (an unpenalised bias); constant inputs give that
+    limit exactly."""
+    rng = np.random.default_rng(43)
+    Z = rng.standard_normal((9, 3))
+    Y = rng.standard_normal((9, 2)) + 5.0
+    w = rng.random(9)
+    w /= w.sum()
+    Th = orc.ridge_fit(Z, Y, w, 1e12)
+    np.testing.assert_allclose(Th[:3], 0.0, rtol=0, atol=1e-10)
+    np.testing.assert_allclose(Th[3], w @ Y, rtol=0, atol=1e-10)
+    Th0 = orc.ridge_fit(np.ones((9, 3)), Y, w, 1e-3)
+    assert np.array_equal(Th0[:3], np.zeros((3, 2)))
+    np.testing.assert_allclose(Th0[3], w @ Y, rtol=0, atol=1e-14)
+
+
+def test_map_reads_only_subspace_coordinates():
+    """The correction depends on s only through U^T s: moving every sparse
+    output orthogonally to the subspace leaves the predicted residual as is."""
+    Q, K, V = tiny_case(n=64, d=6, seed=45)
+    res, _, _ = run_head(Q, K, V, 0.8, n_probes=10, rank=3)
+    U = res.U
+    assert U.shape[1] == 3
+    rng = np.random.default_rng(46)
+    X = rng.standard_normal(res.S.shape)
+    Xperp = X - (X @ U) @ U.T
+    np.testing.assert_allclose(orc.predicted_residual(res.S + Xperp, U, res.Theta),
+                               orc.predicted_residual(res.S, U, res.Theta), rtol=0, atol=1e-12)
+
+
+def test_value_scale_equivariance():
+    """Attention is linear in V; so are the sparse output, the probe rows and
+    their residuals. With the penalty relative to the inputs' spread, the
+    corrected output scales with V as well."""
+    Q, K, V = tiny_case(n=64, d=6, seed=47)
+    res, _, _ = run_head(Q, K, V, 0.8, n_probes=10, rank=4, ridge_lambda=0.05)
+    res2, _, _ = run_head(Q, K, 37.0 * V, 0.8, n_probes=10, rank=4, ridge_lambda=0.05)
+    unp = np.setdiff1d(np.arange(64), res.probe_tokens)
+    assert np.abs(res.O[unp] - res.S[unp]).max() > 1e-3       # a non-zero correction
+    np.testing.assert_allclose(res2.O, 37.0 * res.O, rtol=1e-6, atol=1e-9)
+
+
+def test_step14_duplicate_of_a_probe_gets_its_exact_row():
+    """Unprobed rows get s + U Theta^T [s; 1]; probe rows their exact output.
+    With m <= k_eff + 1 and a vanishing penalty the map interpolates the probe
+    residuals, so an unprobed query identical to a probe query (same block,
+    same s) must come out as that probe's exact dense row. A sign error in
+    the correction gives s - r instead."""
+    rng = np.random.default_rng(49)
+    found = 0
+    for trial in range(40):
+        Q, K, V = tiny_case(n=48, d=6, seed=200 + trial)
+        a, b = rng.choice(48, 2, replace=False)
+        Q[b] = Q[a]
+        res, _, _ = run_head(Q, K, V, 0.8, density=0.35, n_probes=5, rank=6,
+                             ridge_lambda=1e-12)
+        assert res.U.shape[1] == 5
+        probes = set(res.probe_tokens.tolist())
+        if (a in probes) == (b in probes):
+            continue
+        p, u = (a, b) if a in probes else (b, a)
+        pos = np.argsort(res.query_perm)
+        if pos[p] // 8 != pos[u] // 8:
+            continue
+        np.testing.assert_allclose(res.S[u], res.S[p], rtol=0, atol=1e-14)
+        dense, _ = orc.dense_attention(Q, K, V, 0.8, rows=[u])
+        if np.linalg.norm(dense[0] - res.S[u]) < 1e-2:
+            continue                                  # look for a clearly non-zero residual
+        np.testing.assert_allclose(res.O[u], dense[0], rtol=0, atol=1e-7)
+        np.testing.assert_allclose(res.O[p], dense[0], rtol=0, atol=1e-13)
+        found += 1
+    assert found >= 2
 
 
 # ----------------------------------------------- P10 Lloyd, P11 CSR
