@@ -359,10 +359,7 @@ def cpu_baseline(wl, inp, block_stride):
     t0 = time.perf_counter()
     ptok = qperm[orc.probe_positions(N, p.n_probes)]
     Op, _ = orc.dense_attention(Q, K, V, tau, rows=ptok)
-    w = orc.probe_weights(Op)
-    Rp = Op - S[ptok]
-    U, _ = orc.residual_subspace(Rp, w, p.rank)
-    Th = orc.ridge_fit(S[ptok], Rp @ U, w, p.ridge_lambda)
+    _, U, _, Th = orc.fit_probe_map(S[ptok], Op, p.rank, p.ridge_lambda)
     O = S + orc.predicted_residual(S, U, Th)
     O[ptok] = Op
     t["probe_fit_apply"] = time.perf_counter() - t0

@@ -1,19 +1,27 @@
 // Probe-fitted residual reconstruction: the fit (arxivdaily 2608.18484,
 // English abstract: weighted ridge regression of the dense-minus-sparse
 // differences of the probe rows on the sparse output; skillfed article and
-// peercurrent abstract: an affine map, call-specific, restricted to the output
-// subspace seen in the probe residuals).
+// peercurrent abstract: an affine map, call-specific, a small linear map from
+// the sparse output within the output subspace seen in the probe residuals).
 //
-// All in fp64, with X = [s, 1] and r_i = o_i - s_i for the m probe rows:
+// All in fp64, for the m probe rows with s_i the sparse output and
+// r_i = o_i - s_i:
 //   k_fit_prep (many workgroups per head): w_i = ||o_i||^-2 / sum ||o||^-2,
-//     Sigma = sum w_i r_i r_i^T, the ridge Gram X^T W X + lambda I~ (bias row
-//     unpenalised) and X^T W R, a block of 8 rows per workgroup;
+//     Sigma = sum w_i r_i r_i^T, the Gram G = sum w_i [s_i;1][s_i;1]^T and
+//     sum w_i [s_i;1] r_i^T, a block of 8 rows per workgroup;
 //   k_fit (one workgroup per head): top-k_eff eigenvectors U of Sigma by
 //     Householder tridiagonalisation in LDS, Sturm-count multisection,
 //     inverse iteration on the tridiagonal, classical Gram-Schmidt twice and
-//     the back-transform through the reflectors; then the right-hand side
-//     X^T W (R U) = (X^T W R) U and Theta by a packed Cholesky factorisation
-//     in LDS with forward and backward substitution.
+//     the back-transform through the reflectors. The map's inputs are the
+//     subspace coordinates z = U^T s, so its normal equations are those of
+//     [z;1] on the targets U^T r: G_z = T^T G T and T^T (sum w [s;1] r^T) U
+//     with T = diag(U, 1). The bias is eliminated (its row of the normal
+//     equations is exact), leaving (C + lambda_eff I) B = rhs with the
+//     weighted covariance C of z and lambda_eff = lambda tr(C) / (k sum w),
+//     i.e. lambda times the mean weighted variance of the inputs; B comes
+//     from a packed Cholesky factorisation in LDS with forward and backward
+//     substitution, the bias from the eliminated row. The map is returned on
+//     [s; 1]: Theta = [U B; bias].
 #include "common.hpp"
 #include "internal.hpp"
 
@@ -99,13 +107,12 @@ __device__ __forceinline__ double row_inv_norm2(const float* row, int D) {
 }
 
 // ---------------------------------------------------------------- prep
-// grid (H, ceil((d+1)/8)), block 256. Workgroup b accumulates rows [8b, 8b+8)
-// of Sigma (rows < d), of X^T W R and of the Gram (rows < d+1) over chunks of
-// 256 probe rows staged in LDS.
+// grid (H, ceil((d+1)/8)), block 512. Workgroup b accumulates rows [8b, 8b+8)
+// of Sigma (rows < d), of sum w [s;1] r^T and of the Gram (rows < d+1) over
+// chunks of 256 probe rows staged in LDS.
 template <int D>
 __global__ __launch_bounds__(kFitThreads) void k_fit_prep(const float* S_out, const float* O_probe,
-                                                          int N, int m, int kmax, double lambda,
-                                                          double* scratch) {
+                                                          int N, int m, int kmax, double* scratch) {
   constexpr int NT = kFitThreads;
   constexpr int NX = D + 1;
   constexpr int RB = 8;
@@ -172,9 +179,7 @@ __global__ __launch_bounds__(kFitThreads) void k_fit_prep(const float* S_out, co
         else if (kind == 1) dst = a < NX ? f.xtwr + (size_t)a * D + c : nullptr;
         else dst = a < NX ? f.gram + (size_t)a * NX + c : nullptr;
         if (dst == nullptr) continue;
-        double v = (i0 == 0 ? 0.0 : *dst) + acc[u];
-        if (kind == 2 && i0 + mi == m && a == c && a < D) v += lambda;
-        *dst = v;
+        *dst = (i0 == 0 ? 0.0 : *dst) + acc[u];
       }
     }
   }
@@ -182,12 +187,12 @@ __global__ __launch_bounds__(kFitThreads) void k_fit_prep(const float* S_out, co
 
 // ---------------------------------------------------------------- fit
 template <int D>
-__global__ __launch_bounds__(kFitThreads) void k_fit(int m, int kmax, float* U_out, float* Th_out,
-                                                     int32_t* rank_eff, double* scratch) {
+__global__ __launch_bounds__(kFitThreads) void k_fit(int m, int kmax, double lambda, float* U_out,
+                                                     float* Th_out, int32_t* rank_eff,
+                                                     double* scratch) {
   constexpr int NT = kFitThreads;
   constexpr int PA = D + 1;                // pitch of the eigen matrix
-  constexpr int NX = D + 1;                // ridge unknowns (d weights + bias)
-  constexpr int NP = NX * (NX + 1) / 2;    // packed lower triangle of the ridge matrix
+  constexpr int NX = D + 1;                // rows of the Gram on [s; 1]
   constexpr int BIG = (D + 1) * (D + 2);
   __shared__ double big[BIG];
   __shared__ double dg[D], od[D], od2[D], beta[D], vv[D], pv[D], vn[D];
@@ -490,12 +495,19 @@ __global__ __launch_bounds__(kFitThreads) void k_fit(int m, int kmax, float* U_o
     const int e = idx / keff, cc = idx % keff;
     Uh[(size_t)e * kmax + cc] = (float)X[e * PXK + cc];
   }
-  // ---- right-hand side (X^T W R) U in 4 x 4 register tiles, into the
-  // workspace (it is copied behind the packed ridge matrix when it fits)
+  // U in fp64 to the workspace (pitch keff): the reflectors are no longer needed
+  for (int idx = t; idx < D * keff; idx += NT) f.hv[idx] = X[(idx / keff) * PXK + idx % keff];
+  // ---- products with U in 4 x 4 register tiles: rows [0, D] of
+  // F = (sum w [s;1] r^T) U into rhs (pitch kmax), and rows [0, D) of
+  // H = G[:, 0:D] U into sig (pitch keff); row D of H is the bias column g
   {
     const int ntr = (NX + 3) / 4, ntc = (keff + 3) / 4;
-    for (int tile = t; tile < ntr * ntc; tile += NT) {
-      const int r0 = 4 * (tile / ntc), c0 = 4 * (tile % ntc);
+    for (int tile = t; tile < 2 * ntr * ntc; tile += NT) {
+      const bool isF = tile < ntr * ntc;
+      const int tt = isF ? tile : tile - ntr * ntc;
+      const int r0 = 4 * (tt / ntc), c0 = 4 * (tt % ntc);
+      const double* src = isF ? f.xtwr : f.gram;
+      const int pitch = isF ? D : NX;
       double acc[4][4];
 #pragma unroll
       for (int u = 0; u < 4; ++u)
@@ -504,7 +516,7 @@ __global__ __launch_bounds__(kFitThreads) void k_fit(int m, int kmax, float* U_o
       for (int e = 0; e < D; ++e) {
         double xr[4], uc[4];
 #pragma unroll
-        for (int u = 0; u < 4; ++u) xr[u] = r0 + u < NX ? f.xtwr[(size_t)(r0 + u) * D + e] : 0.0;
+        for (int u = 0; u < 4; ++u) xr[u] = r0 + u < NX ? src[(size_t)(r0 + u) * pitch + e] : 0.0;
 #pragma unroll
         for (int v = 0; v < 4; ++v) uc[v] = c0 + v < keff ? X[e * PXK + c0 + v] : 0.0;
 #pragma unroll
@@ -515,61 +527,105 @@ __global__ __launch_bounds__(kFitThreads) void k_fit(int m, int kmax, float* U_o
 #pragma unroll
       for (int u = 0; u < 4; ++u)
 #pragma unroll
-        for (int v = 0; v < 4; ++v)
-          if (r0 + u < NX && c0 + v < keff) f.rhs[(size_t)(r0 + u) * kmax + c0 + v] = acc[u][v];
+        for (int v = 0; v < 4; ++v) {
+          const int r = r0 + u, c = c0 + v;
+          if (r >= NX || c >= keff) continue;
+          if (isF) f.rhs[(size_t)r * kmax + c] = acc[u][v];
+          else if (r < D) f.sig[(size_t)r * keff + c] = acc[u][v];
+          else dots[c] = acc[u][v];     // g_c = sum_i G[D][i] U[i][c]
+        }
     }
   }
   __syncthreads();
-  const bool rhs_lds = NP + NX * keff <= BIG;
-  double* rhs = rhs_lds ? big + NP : f.rhs;
-  const int rstride = rhs_lds ? keff : kmax;
-  // ---- packed ridge matrix P(i, j) = i (i + 1) / 2 + j, j <= i
-  for (int idx = t; idx < NX * NX; idx += NT) {
-    const int i = idx / NX, j = idx % NX;
-    if (j <= i) big[i * (i + 1) / 2 + j] = f.gram[idx];
+  // ---- the bias-eliminated system in LDS (X is dead from here on):
+  //   C   = U^T H - g g^T / G_DD          packed lower triangle, keff rows
+  //   rhs = U^T F[0:D] - g F[D] / G_DD    keff x keff (in LDS when it fits)
+  const int NPZ = keff * (keff + 1) / 2;
+  const bool rhs_lds = NPZ + keff * keff <= BIG;
+  double* rz = rhs_lds ? big + NPZ : f.xtwr;   // sum w [s;1] r^T is no longer read
+  const double gdd = f.gram[(size_t)D * NX + D];   // sum of the weights
+  const double igdd = gdd > 0.0 ? 1.0 / gdd : 0.0;
+  for (int job = t; job < NPZ + keff * keff; job += NT) {
+    int a, b;
+    const bool isC = job < NPZ;
+    if (isC) {
+      a = (int)((sqrt(8.0 * job + 1.0) - 1.0) * 0.5);
+      while (a * (a + 1) / 2 > job) --a;
+      while ((a + 1) * (a + 2) / 2 <= job) ++a;
+      b = job - a * (a + 1) / 2;
+    } else {
+      a = (job - NPZ) / keff;
+      b = (job - NPZ) % keff;
+    }
+    const double* col = isC ? f.sig : f.rhs;
+    const int pitch = isC ? keff : kmax;
+    double s2[2] = {0.0, 0.0};
+    for (int e = 0; e < D; e += 2) {
+      s2[0] += f.hv[(size_t)e * keff + a] * col[(size_t)e * pitch + b];
+      s2[1] += f.hv[(size_t)(e + 1) * keff + a] * col[(size_t)(e + 1) * pitch + b];
+    }
+    const double tail = isC ? dots[b] : f.rhs[(size_t)D * kmax + b];
+    const double v = (s2[0] + s2[1]) - dots[a] * tail * igdd;
+    if (isC) big[job] = v;
+    else rz[(size_t)a * keff + b] = v;
   }
-  if (rhs_lds)
-    for (int idx = t; idx < NX * keff; idx += NT) rhs[idx] = f.rhs[(size_t)(idx / keff) * kmax + idx % keff];
   __syncthreads();
-  // ---- Cholesky, right-looking, one barrier per column: the trailing update
-  // uses the unscaled column j and 1/d_j; column j is scaled in the next step,
-  // when it is no longer read.
-  double dprev = 1.0;
-  for (int j = 0; j < NX; ++j) {
-    double dj = big[j * (j + 1) / 2 + j];
-    dj = dj > 0.0 ? dj : 1e-300;
-    const double rd = 1.0 / dj;
-    if (j > 0) {
-      const double sc = 1.0 / sqrt(dprev);
-      for (int i = j + t; i < NX; i += NT) big[i * (i + 1) / 2 + (j - 1)] *= sc;
-      if (t == 0) big[(j - 1) * j / 2 + (j - 1)] = sqrt(dprev);
+  // ---- penalty: lambda times the mean weighted variance of the inputs. An
+  // input set without spread (trace of C at the rounding level of the
+  // uncentred Gram) leaves the slopes at 0 and the bias at the weighted mean.
+  double trc_part = 0.0, trg_part = 0.0;
+  for (int a = t; a < keff; a += NT) {
+    trc_part += big[a * (a + 1) / 2 + a];
+    trg_part += big[a * (a + 1) / 2 + a] + dots[a] * dots[a] * igdd;
+  }
+  const double trc = wg_sum1(trc_part, red2, slot);
+  const double trg = wg_sum1(trg_part, red2, slot);
+  const bool spread = trc > 64.0 * 2.220446049250313e-16 * trg && gdd > 0.0;
+  if (spread) {
+    const double lam_eff = lambda * trc * igdd / (double)keff;
+    for (int a = t; a < keff; a += NT) big[a * (a + 1) / 2 + a] += lam_eff;
+  } else {
+    for (int idx = t; idx < keff * keff; idx += NT) rz[idx] = 0.0;
+  }
+  __syncthreads();
+  if (spread) {
+    // ---- Cholesky, right-looking, one barrier per column: the trailing
+    // update uses the unscaled column j and 1/d_j; column j is scaled in the
+    // next step, when it is no longer read.
+    double dprev = 1.0;
+    for (int j = 0; j < keff; ++j) {
+      double dj = big[j * (j + 1) / 2 + j];
+      dj = dj > 0.0 ? dj : 1e-300;
+      const double rd = 1.0 / dj;
+      if (j > 0) {
+        const double sc = 1.0 / sqrt(dprev);
+        for (int i = j + t; i < keff; i += NT) big[i * (i + 1) / 2 + (j - 1)] *= sc;
+        if (t == 0) big[(j - 1) * j / 2 + (j - 1)] = sqrt(dprev);
+      }
+      for (int i = j + 1 + (t >> 5); i < keff; i += NT / 32) {
+        double* row = big + i * (i + 1) / 2;
+        const double lij = row[j] * rd;
+        for (int l = j + 1 + (t & 31); l <= i; l += 32) row[l] -= lij * big[l * (l + 1) / 2 + j];
+      }
+      dprev = dj;
+      __syncthreads();
     }
-    for (int i = j + 1 + (t >> 5); i < NX; i += NT / 32) {
-      double* row = big + i * (i + 1) / 2;
-      const double lij = row[j] * rd;
-      for (int l = j + 1 + (t & 31); l <= i; l += 32) row[l] -= lij * big[l * (l + 1) / 2 + j];
-    }
-    dprev = dj;
+    if (t == 0) big[(keff - 1) * keff / 2 + (keff - 1)] = sqrt(dprev);
     __syncthreads();
-  }
-  if (t == 0) big[(NX - 1) * NX / 2 + (NX - 1)] = sqrt(dprev);
-  __syncthreads();
-  double* rdiag = lam_top;   // free again: 1 / L_ii for the substitutions
-  static_assert(NX <= D + 1, "reciprocal diagonal fits in lam_top");
-  for (int i = t; i < NX; i += NT) rdiag[i] = 1.0 / big[i * (i + 1) / 2 + i];
-  __syncthreads();
-  // ---- L y = b, then L^T x = y: sixteen lanes per right-hand-side column,
-  // each column handled by one wave, so only wave-level ordering is needed
-  {
-    constexpr int LPC = 16;                     // lanes per column
-    constexpr int NU = (NX + LPC - 1) / LPC;    // terms per lane at most
-    const int lane = t & 63, w = t >> 6;
+    double* rdiag = lam_top;   // free again: 1 / L_ii for the substitutions
+    for (int i = t; i < keff; i += NT) rdiag[i] = 1.0 / big[i * (i + 1) / 2 + i];
+    __syncthreads();
+    // ---- L y = b, then L^T x = y: sixteen lanes per right-hand-side column,
+    // each column handled by one wave, so only wave-level ordering is needed
+    constexpr int LPC = 16;                    // lanes per column
+    constexpr int NU = (D + LPC - 1) / LPC;    // terms per lane at most
+    const int lane = t & 63, wv = t >> 6;
     const int part = lane & (LPC - 1);
     for (int cb = 0; cb < keff; cb += (64 / LPC) * (NT / 64)) {
-      const int cc = cb + (64 / LPC) * w + lane / LPC;
+      const int cc = cb + (64 / LPC) * wv + lane / LPC;
       const bool on = cc < keff;
-      for (int i = 0; i < NX; ++i) {
-        double s = 0.0;
+      for (int i = 0; i < keff; ++i) {
+        double sacc = 0.0;
         if (on) {
           const double* row = big + i * (i + 1) / 2;
           // all of the lane's terms are read at once (one LDS round trip)
@@ -577,45 +633,52 @@ __global__ __launch_bounds__(kFitThreads) void k_fit(int m, int kmax, float* U_o
 #pragma unroll
           for (int u = 0; u < NU; ++u) {
             const int l = part + u * LPC;
-            if (l < i) s2[u & 1] += row[l] * rhs[(size_t)l * rstride + cc];
+            if (l < i) s2[u & 1] += row[l] * rz[(size_t)l * keff + cc];
           }
-          s = s2[0] + s2[1];
+          sacc = s2[0] + s2[1];
         }
-        s += __shfl_xor(s, 1);
-        s += __shfl_xor(s, 2);
-        s += __shfl_xor(s, 4);
-        s += __shfl_xor(s, 8);
-        if (on && part == 0)
-          rhs[(size_t)i * rstride + cc] = (rhs[(size_t)i * rstride + cc] - s) * rdiag[i];
+        sacc += __shfl_xor(sacc, 1);
+        sacc += __shfl_xor(sacc, 2);
+        sacc += __shfl_xor(sacc, 4);
+        sacc += __shfl_xor(sacc, 8);
+        if (on && part == 0) rz[(size_t)i * keff + cc] = (rz[(size_t)i * keff + cc] - sacc) * rdiag[i];
         if (rhs_lds) __builtin_amdgcn_wave_barrier();
         else __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "workgroup");
       }
-      for (int i = NX - 1; i >= 0; --i) {
-        double s = 0.0;
+      for (int i = keff - 1; i >= 0; --i) {
+        double sacc = 0.0;
         if (on) {
           double s2[2] = {0.0, 0.0};
 #pragma unroll
           for (int u = 0; u < NU; ++u) {
             const int l = i + 1 + part + u * LPC;
-            if (l < NX) s2[u & 1] += big[l * (l + 1) / 2 + i] * rhs[(size_t)l * rstride + cc];
+            if (l < keff) s2[u & 1] += big[l * (l + 1) / 2 + i] * rz[(size_t)l * keff + cc];
           }
-          s = s2[0] + s2[1];
+          sacc = s2[0] + s2[1];
         }
-        s += __shfl_xor(s, 1);
-        s += __shfl_xor(s, 2);
-        s += __shfl_xor(s, 4);
-        s += __shfl_xor(s, 8);
-        if (on && part == 0)
-          rhs[(size_t)i * rstride + cc] = (rhs[(size_t)i * rstride + cc] - s) * rdiag[i];
+        sacc += __shfl_xor(sacc, 1);
+        sacc += __shfl_xor(sacc, 2);
+        sacc += __shfl_xor(sacc, 4);
+        sacc += __shfl_xor(sacc, 8);
+        if (on && part == 0) rz[(size_t)i * keff + cc] = (rz[(size_t)i * keff + cc] - sacc) * rdiag[i];
         if (rhs_lds) __builtin_amdgcn_wave_barrier();
         else __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "workgroup");
       }
     }
+    __syncthreads();
   }
-  __syncthreads();
+  // ---- the map on [s; 1]: slopes U B (rows < D), bias (F[D] - g^T B) / G_DD
   for (int idx = t; idx < NX * keff; idx += NT) {
-    const int ra = idx / keff, cc = idx % keff;
-    Th[(size_t)ra * kmax + cc] = (float)rhs[(size_t)ra * rstride + cc];
+    const int r = idx / keff, cc = idx % keff;
+    double v = 0.0;
+    if (r < D) {
+      for (int a = 0; a < keff; ++a) v += f.hv[(size_t)r * keff + a] * rz[(size_t)a * keff + cc];
+    } else {
+      double gb = 0.0;
+      for (int a = 0; a < keff; ++a) gb += dots[a] * rz[(size_t)a * keff + cc];
+      v = (f.rhs[(size_t)D * kmax + cc] - gb) * igdd;
+    }
+    Th[(size_t)r * kmax + cc] = (float)v;
   }
   if (t == 0) rank_eff[h] = keff;
 }
@@ -630,9 +693,8 @@ hipError_t launch_fit(const Dims& d, const float* S_out, const float* O_probe, f
   const dim3 pgrid(d.H, (d.D + 1 + 7) / 8);
 #define SPR_FIT(DD)                                                                         \
   do {                                                                                      \
-    k_fit_prep<DD><<<pgrid, kFitThreads, 0, st>>>(S_out, O_probe, d.N, d.m, d.k, d.lam,     \
-                                                   scratch);                                \
-    k_fit<DD><<<d.H, kFitThreads, 0, st>>>(d.m, d.k, U, Theta, rank_eff, scratch);          \
+    k_fit_prep<DD><<<pgrid, kFitThreads, 0, st>>>(S_out, O_probe, d.N, d.m, d.k, scratch); \
+    k_fit<DD><<<d.H, kFitThreads, 0, st>>>(d.m, d.k, d.lam, U, Theta, rank_eff, scratch);   \
   } while (0)
   if (d.D == 128) SPR_FIT(128);
   else SPR_FIT(64);

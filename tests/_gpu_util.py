@@ -93,6 +93,18 @@ def run_pipeline(wl: Workload, heads=None, dbg: bool = True, dbg_heads_ok: bool 
     return GpuRun(p=p, inp=inp, Q=Q, K=K, V=V, scale=scale, idx=idx, b=b, dbg=d)
 
 
+def map_in_subspace(U, Theta):
+    """The map on [s; 1] (Theta [d+1, k]) written on the subspace coordinates
+    [U^T s; 1]: rows U^T Theta[:d] and the bias row. Also returns how far the
+    slopes stray from span(U) (0 for a map that reads only U^T s)."""
+    U = np.asarray(U, np.float64)
+    Th = np.asarray(Theta, np.float64)
+    slopes = Th[:-1]
+    inside = U.T @ slopes
+    stray = float(np.abs(slopes - U @ inside).max()) if slopes.size else 0.0
+    return np.vstack([inside, Th[-1:]]), stray
+
+
 def rel_l2(a, b):
     a = np.asarray(a, np.float64)
     b = np.asarray(b, np.float64)

@@ -20,7 +20,7 @@ import torch
 from oracle import sparsepr_oracle as orc
 from free_block_sparse_rcp_amd import binding, configs
 
-from _gpu_util import bf16_round, csr_lists, rel_l2, run_pipeline, small_bf16
+from _gpu_util import bf16_round, csr_lists, map_in_subspace, rel_l2, run_pipeline, small_bf16
 
 pytestmark = pytest.mark.gpu
 
@@ -82,13 +82,7 @@ def oracle_on_gpu_indices(Q, K, V, tau, p, g):
         Op, _ = orc.dense_attention(Q, K, V, tau, rows=ptok)
     else:
         Op = np.zeros((0, p.head_dim))
-    w = orc.probe_weights(Op)
-    Rp = Op - S[ptok]
-    if p.n_probes:
-        U, ev = orc.residual_subspace(Rp, w, p.rank)
-    else:
-        U, ev = np.zeros((p.head_dim, 0)), np.zeros(p.head_dim)
-    Th = orc.ridge_fit(S[ptok], Rp @ U, w, p.ridge_lambda) if U.shape[1] else np.zeros((p.head_dim + 1, 0))
+    w, U, ev, Th = orc.fit_probe_map(S[ptok], Op, p.rank, p.ridge_lambda)
     O = S + orc.predicted_residual(S, U, Th)
     O[ptok] = Op
     E = orc.executed_pairs(blocks, ksets, p.n_probes, N)
@@ -223,25 +217,45 @@ def test_fit_matches_oracle_on_gpu_inputs(name):
         assert keff == U.shape[1]
         Ug = g["U"][:, :keff].astype(np.float64)
         Thg = g["Theta"][:, :keff].astype(np.float64)
-        # orthonormal basis of the same subspace
+        # orthonormal basis of the same subspace. Both sides form Sigma in fp64
+        # from the same fp32 inputs, so they differ by rounding only (~1e-15
+        # relative) and the subspace is pinned unless the k-th and (k+1)-th
+        # eigenvalues coincide to ~1e-9 (Davis-Kahan: sin angle <= |dSigma| / gap)
         assert np.max(np.abs(Ug.T @ Ug - np.eye(keff))) < 1e-5
         gap = (ev[keff - 1] - ev[keff]) / max(ev[0], 1e-300) if keff < len(ev) else 1.0
-        if gap > 1e-4:
+        if gap > 1e-9:
             assert np.max(np.abs(Ug @ Ug.T - U @ U.T)) < 1e-3
-        # normal equations satisfied by the GPU's Theta in its own basis
-        res = orc.normal_equation_residual(Sp, Rp @ Ug, w, p.ridge_lambda, Thg)
+        else:
+            print(f"[{name} h{h}] eigenvalues {keff} and {keff + 1} coincide (gap {gap:.1e}): "
+                  f"projector and prediction not compared", flush=True)
+        # the GPU's map reads s only through U^T s, and its Theta satisfies the
+        # normal equations in the GPU's own basis
+        Thz, stray = map_in_subspace(Ug, Thg)
+        assert stray <= 1e-5 * max(1.0, np.abs(Thg).max())
+        res = orc.normal_equation_residual(orc.map_inputs(Sp, Ug), Rp @ Ug, w, p.ridge_lambda, Thz)
         assert res < 1e-4
-        Th = orc.ridge_fit(Sp, Rp @ U, w, p.ridge_lambda)
+        _, _, _, Th = orc.fit_probe_map(Sp, Op, p.rank, p.ridge_lambda)
         S_all = g["S"].astype(np.float64)
-        if gap > 1e-4:
+        if gap > 1e-9:
             assert rel_l2(orc.predicted_residual(S_all, Ug, Thg),
                           orc.predicted_residual(S_all, U, Th)) < 1e-3
 
 
 # ------------------------------------------------------------ (iii) per-query error
 
+ROW_TOL_BF16 = 2e-2   # the bf16 output bound, applied to each row
+
+
 @pytest.mark.parametrize("name", list(WORKLOADS))
 def test_per_query_error_agreement(name):
+    """Per-query relative error against dense, GPU vs oracle (its output
+    rounded to the output dtype). The pages' metric, the mean over unprobed
+    queries, must agree within 1e-3. Per row: within 1e-3 on the fp32 path;
+    on the bf16 path each row's output must lie within the bf16 output bound
+    (relative L2 2e-2) of the oracle's row, which bounds its error difference
+    by 2e-2 (1 + e). A per-row 1e-3 is out of reach there: bf16 probabilities
+    in P V alone move single rows' errors by more than that
+    (test_bf16_probabilities_move_single_rows in test_oracle_pins.py)."""
     r = get_run(name)
     p = r.p
     rng = np.random.default_rng(5)
@@ -259,15 +273,20 @@ def test_per_query_error_agreement(name):
         e_gpu = orc.relative_l2_rows(g["O"][rows], dense)
         e_or = orc.relative_l2_rows(O_or, dense)
         dd = np.abs(e_gpu - e_or)
+        row_rel = orc.relative_l2_rows(g["O"][rows], O_or)
         e_hd = orc.relative_l2_rows(to_token_order(g["S"], g["query_perm"])[rows], dense)
         print(f"[{name} h{h}] mean err {e_gpu.mean():.4g} (oracle {e_or.mean():.4g}); "
               f"hard-drop {e_hd.mean():.4g}; |de| mean {dd.mean():.2e} p99 "
-              f"{np.percentile(dd, 99):.2e} max {dd.max():.2e}; "
-              f"density {int(g['executed_pairs']) / p.n_tokens**2:.4f}")
+              f"{np.percentile(dd, 99):.2e} max {dd.max():.2e}; |de|/(1+e) max "
+              f"{(dd / (1 + e_or)).max():.2e}; row output diff p99 {np.percentile(row_rel, 99):.2e} "
+              f"max {row_rel.max():.2e}; density {int(g['executed_pairs']) / p.n_tokens**2:.4f}")
         # the pages' metric: mean relative error over unprobed queries
         assert abs(e_gpu.mean() - e_or.mean()) <= 1e-3
         if p.dtype == "f32":
             assert dd.max() <= 1e-3
+        else:
+            assert row_rel.max() <= ROW_TOL_BF16
+            assert np.all(dd <= ROW_TOL_BF16 * (1.0 + e_or))
 
 
 # ------------------------------------------------------------ (iv) independent
@@ -399,15 +418,19 @@ def test_semantic_partition_with_probe_correction():
     """The semantic partition with probes, the residual fit and its application
     (the combination the residual-predictability diagnostic runs): query order
     bit-exact, executed pairs exact, sparse and probe rows against the oracle on
-    the GPU's indices, and the output against the fp64 fit and apply on the
-    GPU's own S and probe rows. The end-to-end output is printed, not bounded:
-    with m <= d+1 and a small gap below the k-th eigenvalue (5.9e-4 on head 1
-    here), the bf16 path's 1e-3 differences in S turn the subspace's last
-    directions and move the output by a few percent."""
+    the GPU's indices, the output against the fp64 fit and apply on the GPU's
+    own S and probe rows, and the end-to-end output against the oracle within
+    the bf16 bound 2e-2 wherever the rank-k subspace is determined by the
+    data: by Davis-Kahan the subspace turns by at most |Sigma_gpu - Sigma| /
+    gap, which must stay below 0.1 (about 6 degrees). Where the k-th and
+    (k+1)-th eigenvalues nearly coincide the GPU's ~1e-3 differences in S and
+    the probe rows can turn the last directions, and the output is compared
+    with the fit on the GPU's own inputs only."""
     wl = small_bf16(name="semantic_probes", mode=2, seed=22)
     r = run_pipeline(wl)
     p = r.p
     assert p.n_probes > 0 and p.rank > 0
+    bounded = 0
     for h in range(p.heads):
         g = head_arrays(r, h)
         qorder, _, _ = orc.group_members(r.np("query_label")[h], p.n_groups)
@@ -423,22 +446,29 @@ def test_semantic_partition_with_probe_correction():
         pos = orc.probe_positions(p.n_tokens, p.n_probes)
         Sp = g["S"][pos].astype(np.float64)
         Op = g["O_probe"].astype(np.float64)
-        w = orc.probe_weights(Op)
-        U, ev = orc.residual_subspace(Op - Sp, w, p.rank)
-        Th = orc.ridge_fit(Sp, (Op - Sp) @ U, w, p.ridge_lambda)
+        w, U, ev, Th = orc.fit_probe_map(Sp, Op, p.rank, p.ridge_lambda)
         S_q = g["S"].astype(np.float64)
         O_fit = S_q + orc.predicted_residual(S_q, U, Th)
         O_fit[pos] = Op                                   # probe rows are exact rows
         O_fit = to_token_order(O_fit, g["query_perm"])
         e_f = rel_l2(g["O"], O_fit)
         keff = U.shape[1]
-        gap = (ev[keff - 1] - ev[keff]) / max(ev[0], 1e-300) if keff < len(ev) else 1.0
+        # Davis-Kahan: how far the GPU's inputs can turn the oracle's subspace
+        w_or = orc.probe_weights(o["Op"])
+        R_or = o["Op"] - o["S"][o["ptok"]]
+        Sig_or = (R_or * w_or[:, None]).T @ R_or
+        Sig_g = ((Op - Sp) * w[:, None]).T @ (Op - Sp)
+        ev_or = np.linalg.eigvalsh(Sig_or)[::-1]
+        gap_abs = ev_or[keff - 1] - ev_or[keff] if keff < len(ev_or) else np.inf
+        turn = np.linalg.norm(Sig_g - Sig_or, 2) / gap_abs
         print(f"[gpu] semantic+probes head {h}: S {e_s:.2e} probes {e_p:.2e} O {e_o:.2e} "
-              f"O vs fit on GPU inputs {e_f:.2e} gap {gap:.1e} |Theta| {np.linalg.norm(Th):.1f}",
-              flush=True)
+              f"O vs fit on GPU inputs {e_f:.2e} Davis-Kahan bound {turn:.2e}", flush=True)
         assert e_s < TOL["bf16"] and e_p < TOL["bf16"]
-        if gap > 1e-4:
-            assert e_f < 5e-3      # O is stored in bf16: relative rounding up to 2^-9 per element
+        assert e_f < 5e-3          # O is stored in bf16: relative rounding up to 2^-9 per element
+        if turn < 0.1:
+            assert e_o < TOL["bf16"]
+            bounded += 1
+    print(f"[gpu] semantic+probes: end-to-end output bounded on {bounded} of {p.heads} heads")
 
 
 @pytest.mark.parametrize("name", ["tiny", "bf16_d128", "bf16_d64_bq64"])
