@@ -266,6 +266,26 @@ def unprobed_mask(p, b):
     return mask
 
 
+def error_summary(p, b, ref, rn, mask):
+    """Per-query relative L2 error against the dense output over all unprobed
+    rows of every head (mean and 99th percentile, linear interpolation), for
+    the corrected output and for the sparse output alone (hard drop)."""
+    import numpy as np
+    import torch
+    D = p.head_dim
+    with torch.no_grad():
+        S_tok = torch.empty_like(b.S)
+        S_tok.scatter_(1, b.query_perm.long()[:, :, None].expand(-1, -1, D), b.S.float())
+        e = ((b.O.float() - ref).norm(dim=2) / rn)[mask].double().cpu().numpy()
+        e0 = ((S_tok - ref).norm(dim=2) / rn)[mask].double().cpu().numpy()
+    return {"rel_l2_mean_unprobed": float(e.mean()),
+            "rel_l2_p99_unprobed": float(np.percentile(e, 99)),
+            "hard_drop_rel_l2_mean": float(e0.mean()),
+            "hard_drop_rel_l2_p99": float(np.percentile(e0, 99)),
+            "correction_minus_hard_drop": float(e.mean() - e0.mean()),
+            "rows": int(e.size)}
+
+
 def residual_r2(p, b, ref, mask):
     """How affine-predictable the dense-minus-sparse residual is under one
     call's partition: R^2 of the fitted map r = U Theta^T [s; 1] on the rows the
@@ -313,9 +333,12 @@ def comparator_r2(p, mode, Q, K, V, scale, inp, ref):
 
 
 def cpu_baseline(wl, inp, block_stride):
-    """The fp64 oracle, as it stands, on head 0 of the same workload: every
-    stage in the pages' order; the block-sparse attention step runs on every
-    `block_stride`-th query block and its time is scaled by executed pairs."""
+    """The fp64 oracle, as it stands, on the heads held by `inp` (the bench
+    passes heads 0, H/2 and H-1 of the same workload): every stage in the
+    pages' order; the block-sparse attention step runs on every
+    `block_stride`-th query block and its time is scaled by executed pairs.
+    Throughput is executed-pair flops over the scaled time, summed over the
+    timed heads."""
     import numpy as np
     from oracle import sparsepr_oracle as orc
     try:
@@ -324,53 +347,133 @@ def cpu_baseline(wl, inp, block_stride):
     except Exception:  # pragma: no cover
         cores = os.cpu_count() or 1
     p = wl.params
-    Q, K, V = (x[0].astype(np.float64) for x in (inp.Q, inp.K, inp.V))
-    tau = float(inp.scale[0])
     N = p.n_tokens
-    t = {}
-    t0 = time.perf_counter()
-    if p.partition_mode == 0:
-        R = orc.key_responses(Q, K, tau, inp.sample_idx)
-        labels = orc.kmeans(R, inp.init_idx, p.kmeans_iters).labels
-        del R
-    else:
-        labels = orc.random_block_labels(inp.rand_key_perm, p.n_groups)
-    key_perm, group_off, sizes = orc.group_members(labels, p.n_groups)
-    kbar, _ = orc.key_centroids(K, labels, p.n_groups)
-    t["partition"] = time.perf_counter() - t0
-    t0 = time.perf_counter()
-    C = orc.query_coordinates(Q, kbar, tau)
-    g1, v = orc.dominant_groups(C, sizes)
-    qperm = orc.query_order(g1, v) if p.partition_mode == 0 else np.asarray(inp.rand_query_perm)
-    blocks = orc.query_blocks(qperm, p.q_block)
-    sigma = orc.block_scores(C, blocks)
-    del C
-    bptr, bgrp = orc.route(sigma, sizes, orc.key_budget(N, p.density, p.n_probes))
-    ksets = orc.block_key_sets(bptr, bgrp, key_perm, group_off)
-    t["route"] = time.perf_counter() - t0
-    E = orc.executed_pairs(blocks, ksets, p.n_probes, N)
-    sp_all = E - p.n_probes * N
-    sel = list(range(0, len(blocks), block_stride))
-    sp_sample = sum(len(blocks[b]) * len(ksets[b]) for b in sel)
-    t0 = time.perf_counter()
-    S, _ = orc.sparse_attention(Q, K, V, tau, [blocks[b] for b in sel], [ksets[b] for b in sel])
-    t["attend_sampled"] = time.perf_counter() - t0
-    t["attend_scaled"] = t["attend_sampled"] * sp_all / max(sp_sample, 1)
-    t0 = time.perf_counter()
-    ptok = qperm[orc.probe_positions(N, p.n_probes)]
-    Op, _ = orc.dense_attention(Q, K, V, tau, rows=ptok)
-    _, U, _, Th = orc.fit_probe_map(S[ptok], Op, p.rank, p.ridge_lambda)
-    O = S + orc.predicted_residual(S, U, Th)
-    O[ptok] = Op
-    t["probe_fit_apply"] = time.perf_counter() - t0
+    t = {"partition": 0.0, "route": 0.0, "attend_sampled": 0.0, "attend_scaled": 0.0,
+         "probe_fit_apply": 0.0}
+    flops = 0.0
+    n_sel = n_blocks = 0
+    for i, h in enumerate(inp.heads):
+        Q, K, V = (x[i].astype(np.float64) for x in (inp.Q, inp.K, inp.V))
+        tau = float(inp.scale[i])
+        t0 = time.perf_counter()
+        if p.partition_mode == 0:
+            R = orc.key_responses(Q, K, tau, inp.sample_idx)
+            labels = orc.kmeans(R, inp.init_idx, p.kmeans_iters).labels
+            del R
+        else:
+            labels = orc.random_block_labels(inp.rand_key_perm, p.n_groups)
+        key_perm, group_off, sizes = orc.group_members(labels, p.n_groups)
+        kbar, _ = orc.key_centroids(K, labels, p.n_groups)
+        t["partition"] += time.perf_counter() - t0
+        t0 = time.perf_counter()
+        C = orc.query_coordinates(Q, kbar, tau)
+        g1, v = orc.dominant_groups(C, sizes)
+        qperm = orc.query_order(g1, v) if p.partition_mode == 0 else np.asarray(inp.rand_query_perm)
+        blocks = orc.query_blocks(qperm, p.q_block)
+        sigma = orc.block_scores(C, blocks)
+        del C
+        bptr, bgrp = orc.route(sigma, sizes, orc.key_budget(N, p.density, p.n_probes))
+        ksets = orc.block_key_sets(bptr, bgrp, key_perm, group_off)
+        t["route"] += time.perf_counter() - t0
+        E = orc.executed_pairs(blocks, ksets, p.n_probes, N)
+        flops += 4.0 * p.head_dim * E
+        sp_all = E - p.n_probes * N
+        sel = list(range(i % block_stride, len(blocks), block_stride))
+        n_sel += len(sel)
+        n_blocks += len(blocks)
+        sp_sample = sum(len(blocks[b]) * len(ksets[b]) for b in sel)
+        t0 = time.perf_counter()
+        S, _ = orc.sparse_attention(Q, K, V, tau, [blocks[b] for b in sel], [ksets[b] for b in sel])
+        dt = time.perf_counter() - t0
+        t["attend_sampled"] += dt
+        t["attend_scaled"] += dt * sp_all / max(sp_sample, 1)
+        t0 = time.perf_counter()
+        ptok = qperm[orc.probe_positions(N, p.n_probes)]
+        Op, _ = orc.dense_attention(Q, K, V, tau, rows=ptok)
+        _, U, _, Th = orc.fit_probe_map(S[ptok], Op, p.rank, p.ridge_lambda)
+        O = S + orc.predicted_residual(S, U, Th)
+        O[ptok] = Op
+        t["probe_fit_apply"] += time.perf_counter() - t0
     total = t["partition"] + t["route"] + t["attend_scaled"] + t["probe_fit_apply"]
-    tflops = 4.0 * p.head_dim * E / total / 1e12
     spent = t["partition"] + t["route"] + t["attend_sampled"] + t["probe_fit_apply"]
-    return {"value": tflops, "unit": "TFLOP/s", "cores": int(cores), "kind": "oracle",
-            "sample": f"head 0 of {p.heads}: every oracle stage in order; sparse attention on "
-                      f"{len(sel)} of {len(blocks)} query blocks (every {block_stride}th), time "
-                      f"scaled by executed pairs; {spent:.1f} s of CPU time",
-            "stage_seconds": t, "call_ms_scaled_all_heads": total * 1e3 * p.heads}
+    nh = len(inp.heads)
+    return {"value": flops / total / 1e12, "unit": "TFLOP/s", "cores": int(cores), "kind": "oracle",
+            "sample": f"heads {list(inp.heads)} of {p.heads}: every oracle stage in order; sparse "
+                      f"attention on {n_sel} of {n_blocks} query blocks (every {block_stride}th "
+                      f"per head), time scaled by executed pairs; {spent:.1f} s of CPU time",
+            "stage_seconds": t, "call_ms_scaled_all_heads": total * 1e3 * p.heads / nh}
+
+
+def run_sweep(args):
+    """Sensitivity sweep on the sweep workload (32 heads, N = 65536: heads 0-15
+    concentrated, 16-31 broad): probes per head x executed-pair density x
+    partition (response-coupled or random-block), one JSON line per point.
+    Each point: call ms (HIP events, mean of the timed calls), realized
+    density, and against this build's dense output the per-query relative
+    error of the corrected and of the uncorrected (hard-drop) output over all
+    unprobed rows, overall and per head half, with the residual R^2 of the
+    fitted map. The inputs and the dense output are made once."""
+    import dataclasses
+    import numpy as np
+    import torch
+    from free_block_sparse_rcp_amd import binding, configs
+
+    binding.load()
+    wl = configs.get(args.config)
+    dev = torch.device("cuda:0")
+    log(f"[sweep] generating {wl.name}")
+    inp = wl.make_inputs()
+    p0 = wl.params
+    dt = binding.torch_dtype(p0)
+    Q, K, V = (torch.from_numpy(x).to(dev, dt) for x in (inp.Q, inp.K, inp.V))
+    scale = torch.from_numpy(inp.scale).to(dev)
+    O_dense = torch.empty_like(Q)
+    binding.dense_attention(p0, Q, K, V, scale, O_dense)
+    torch.cuda.synchronize()
+    ref = O_dense.float()
+    rn = ref.norm(dim=2)
+    del O_dense
+    H = p0.heads
+    halves = {"concentrated": [h for h in range(H) if inp.scale[h] > inp.scale.min()],
+              "broad": [h for h in range(H) if inp.scale[h] == inp.scale.min()]}
+    modes = ((0, "response_coupled"), (1, "random_block"))
+    n_timed = max(1, args.steps)
+    for mode, mode_name in modes:
+        for rho in configs.SWEEP_DENSITIES:
+            for m in configs.SWEEP_PROBES:
+                p = dataclasses.replace(p0, density=rho, n_probes=m, partition_mode=mode)
+                log(f"[sweep] {mode_name} rho={rho} m={m}")
+                op = binding.SparsePR(p, dev)
+                idx = op.upload_indices(inp.sample_idx, inp.init_idx, inp.rand_key_perm,
+                                        inp.rand_query_perm)
+                for _ in range(max(1, args.warmup)):
+                    op.run(Q, K, V, scale, idx)
+                evs = [dict() for _ in range(n_timed)]
+                for e in evs:
+                    op.run(Q, K, V, scale, idx, events=e)
+                torch.cuda.synchronize()
+                call_ms = float(np.mean([e["start"].elapsed_time(e["apply"]) for e in evs]))
+                b = op.buffers
+                E = int(b.executed_pairs.sum().item())
+                mask = unprobed_mask(p, b)
+                err = error_summary(p, b, ref, rn, mask)
+                per_half = {}
+                for name, hs in halves.items():
+                    hm = torch.zeros_like(mask)
+                    hm[hs] = mask[hs]
+                    per_half[name] = {k: v for k, v in error_summary(p, b, ref, rn, hm).items()
+                                      if k != "rows"}
+                line = {"sweep_point": {"partition": mode_name, "density_target": rho,
+                                        "n_probes": m, "rank": p.rank},
+                        "workload": wl.name, "call_ms": call_ms, "timed_calls": n_timed,
+                        "executed_pairs": E,
+                        "realized_density": E / (H * float(p.n_tokens) ** 2),
+                        "key_budget": p.key_budget, **err, "by_head_type": per_half,
+                        "residual_r2": residual_r2(p, b, ref, mask),
+                        "reference": "this build's dense kernel (bf16 output)"}
+                print(json.dumps(line), flush=True)
+                del op, b
+                torch.cuda.empty_cache()
 
 
 def main():
@@ -378,7 +481,11 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=10)
     ap.add_argument("--warmup", type=int, default=3)
-    ap.add_argument("--config", default="hunyuan")
+    ap.add_argument("--config", default=None,
+                    help="workload (default hunyuan; the sweep runs on the sweep workload)")
+    ap.add_argument("--sweep", action="store_true",
+                    help="probes x density x partition sensitivity sweep on the sweep workload, "
+                         "one JSON line per point")
     ap.add_argument("--cpu-block-stride", type=int, default=0,
                     help="oracle samples every n-th query block (0: chosen by workload size)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -399,6 +506,7 @@ def main():
                     help="summarise two rocprofv3 PMC runs of this script (FETCH_SIZE, "
                          "WRITE_SIZE) into profiles/attend_traffic_<workload>.json and exit")
     args = ap.parse_args()
+    args.config = args.config or ("sweep" if args.sweep else "hunyuan")
     if args.pmc_table:
         from free_block_sparse_rcp_amd import configs
         pmc_table(args.pmc_table[0], args.pmc_table[1], configs.get(args.config).name,
@@ -413,6 +521,9 @@ def main():
         print(f"bench.py runs on one GPU only: the operator is per call and per head, and this "
               f"build has no multi-GPU path (asked for --gpus {args.gpus}).", file=sys.stderr)
         sys.exit(2)
+    if args.sweep:
+        run_sweep(args)
+        return
 
     import numpy as np
     import torch
@@ -511,19 +622,14 @@ def main():
     if not args.no_dense:
         with torch.no_grad():
             ref = O_dense.float()
-            S_tok = torch.empty_like(b.S)
-            S_tok.scatter_(1, b.query_perm.long()[:, :, None].expand(-1, -1, D), b.S)
             mask = unprobed_mask(p, b)
             rn = ref.norm(dim=2)
-            e = ((b.O.float() - ref).norm(dim=2) / rn)[mask]
-            e0 = ((S_tok - ref).norm(dim=2) / rn)[mask]
-            quality = {"reference": "this build's dense kernel (bf16 output)",
-                       "rel_l2_mean_unprobed": float(e.mean()),
-                       "rel_l2_p99_unprobed": float(torch.quantile(e[:1_000_000].float(), 0.99)),
-                       "hard_drop_rel_l2_mean": float(e0.mean())}
+        quality = {"reference": "this build's dense kernel (bf16 output)",
+                   **error_summary(p, b, ref, rn, mask)}
+        e_mean = quality["rel_l2_mean_unprobed"]
         if not args.no_comparator:
             quality["semantic"] = semantic_comparator(args, p, Q, K, V, scale, inp, ref, rn, mask,
-                                                      float(e.mean()))
+                                                      e_mean)
             log("[bench] support diagnostics")
             quality["support"] = {
                 "mass": SUPPORT_MASS, "head": 0, "blocks": support_blocks(p),
@@ -549,9 +655,10 @@ def main():
 
     cpu = None
     if not args.no_cpu_baseline:
-        stride = args.cpu_block_stride or max(1, int(round(4.0 * N / 118800)))
-        log(f"[bench] cpu baseline (oracle), head 0, block stride {stride}")
-        sub = inp if H == 1 else wl.make_inputs([0])
+        stride = args.cpu_block_stride or max(1, int(round(8.0 * N / 118800)))
+        heads = sorted({0, H // 2, H - 1})
+        log(f"[bench] cpu baseline (oracle), heads {heads}, block stride {stride}")
+        sub = inp if H == 1 else wl.make_inputs(heads)
         cpu = cpu_baseline(wl, sub, stride)
 
     out = {
@@ -567,6 +674,7 @@ def main():
         "speedup_vs_dense": (dense_ms / call_ms) if dense_ms else None,
         "attend_speedup_vs_dense": (dense_ms / stage_ms["attend"]) if dense_ms else None,
         "stage_ms": stage_ms, "wall_ms_per_step": wall * 1e3 / args.steps,
+        "reconstruction_share": (stage_ms["probe_fit"] + stage_ms["apply"]) / call_ms,
         "pipeline": ("probe blocks attended first; probe fit on a second stream overlaps the "
                      "attention of the other blocks" if overlap else "stages back to back"),
         "executed_pairs": E, "realized_density": density,

@@ -254,8 +254,14 @@ int32_t sparsepr_attend_subset(const sparsepr_params* params, const void* Q, con
  *   r_i = o_i - s_i;  w_i = ||o_i||^-2 / sum ||o||^-2 (0 where o_i = 0);
  *   Sigma = sum_i w_i r_i r_i^T;  U = eigenvectors of Sigma's k_eff largest
  *   eigenvalues, k_eff = min(k, m, d), or 0 when trace(Sigma) = 0;
- *   Theta solves (X^T W X + lambda I~) Theta = X^T W (R U), X = [s_i, 1],
- *   I~ = diag(1,..,1,0) (unpenalised bias).
+ *   the map reads the subspace coordinates z_i = U^T s_i (skillfed article:
+ *   a small linear map from the sparse output; peercurrent abstract: within
+ *   the output subspace of the probe residuals): B solves
+ *   (Z^T W Z + lambda_eff I~) B = Z^T W (R U) with Z = [z_i, 1],
+ *   I~ = diag(1,..,1,0) (unpenalised bias) and lambda_eff = lambda times the
+ *   mean weighted variance of the k_eff input coordinates (so the correction
+ *   scales with V). Theta = [U B[0:k_eff]; B[k_eff]] is the same map written
+ *   on [s; 1]: Theta^T [s; 1] = B^T [U^T s; 1].
  *
  * Inputs : Q [H,N,d]; K, V [H,N,d] (any key order); scale [H];
  *          query_perm [H,N]; S_out [H,N,d] fp32 (query order, from stage 3).

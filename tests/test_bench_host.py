@@ -59,3 +59,27 @@ def test_unprobed_mask_removes_the_probe_tokens():
     for h in range(p.heads):
         probe_tokens = set(b.query_perm[h, pos].tolist())
         assert set(np.nonzero(~mask[h].numpy())[0].tolist()) == probe_tokens
+
+
+def test_error_summary_over_all_unprobed_rows():
+    """Mean and 99th percentile of ||o - ref|| / ||ref|| over every unprobed
+    row, for the output and for the sparse output in token order."""
+    p, b, S_tok, R_fit = _call(H=3, N=50, seed=5)
+    g = torch.Generator().manual_seed(9)
+    ref = torch.randn(3, 50, 6, generator=g)
+    b.O = S_tok + R_fit
+    mask = bench.unprobed_mask(p, b)
+    rn = ref.norm(dim=2)
+    got = bench.error_summary(p, b, ref, rn, mask)
+    e, e0 = [], []
+    for h in range(3):
+        for t in range(50):
+            if mask[h, t]:
+                r = ref[h, t].double().numpy()
+                e.append(np.linalg.norm(b.O[h, t].double().numpy() - r) / np.linalg.norm(r))
+                e0.append(np.linalg.norm(S_tok[h, t].double().numpy() - r) / np.linalg.norm(r))
+    assert got["rows"] == len(e) == 3 * (50 - p.n_probes)
+    assert abs(got["rel_l2_mean_unprobed"] - np.mean(e)) < 1e-6
+    assert abs(got["rel_l2_p99_unprobed"] - np.percentile(e, 99)) < 1e-6
+    assert abs(got["hard_drop_rel_l2_mean"] - np.mean(e0)) < 1e-6
+    assert abs(got["hard_drop_rel_l2_p99"] - np.percentile(e0, 99)) < 1e-6

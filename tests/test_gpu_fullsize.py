@@ -52,6 +52,9 @@ CASES = {
     "sweep": configs.SWEEP,
     "sweep_rho15_m32_random": _sweep_point(0.15, 32, 1, "sweep_rho15_m32_random"),
     "sweep_rho30_m256": _sweep_point(0.30, 256, 0, "sweep_rho30_m256"),
+    # the remaining corners of the probes x density grid
+    "sweep_rho30_m32": _sweep_point(0.30, 32, 0, "sweep_rho30_m32"),
+    "sweep_rho15_m256_random": _sweep_point(0.15, 256, 1, "sweep_rho15_m256_random"),
     # the semantic comparator the bench runs beside the hunyuan call
     "hunyuan_semantic": replace(configs.HUNYUAN, name="hunyuan_semantic",
                                 params=replace(configs.HUNYUAN.params, partition_mode=2,
