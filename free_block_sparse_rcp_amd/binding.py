@@ -30,7 +30,7 @@ STATUS = {0: "SPARSEPR_OK", 1: "SPARSEPR_ERR_INVALID_ARG", 2: "SPARSEPR_ERR_UNSU
 EXPORTS = ("sparsepr_abi_version", "sparsepr_status_string", "sparsepr_last_error",
            "sparsepr_workspace_bytes", "sparsepr_partition", "sparsepr_route", "sparsepr_attend",
            "sparsepr_attend_subset", "sparsepr_probe_fit", "sparsepr_apply",
-           "sparsepr_dense_attention", "sparsepr_support_stats")
+           "sparsepr_apply_noalloc", "sparsepr_dense_attention", "sparsepr_support_stats")
 BLOCKS_ALL, BLOCKS_WITH_PROBE, BLOCKS_WITHOUT_PROBE = 0, 1, 2
 RESPONSE_COUPLED, RANDOM_BLOCK, SEMANTIC = 0, 1, 2   # partition modes
 
@@ -75,11 +75,13 @@ def load(path: Optional[str] = None) -> ctypes.CDLL:
     lib.sparsepr_attend_subset.argtypes = [pp] + [_c_p] * 10 + [_c_i32, _c_p]
     lib.sparsepr_probe_fit.argtypes = [pp] + [_c_p] * 10 + [_c_p, _c_sz, _c_p]
     lib.sparsepr_apply.argtypes = [pp] + [_c_p] * 7 + [_c_p, _c_sz, _c_p]
+    lib.sparsepr_apply_noalloc.argtypes = [pp] + [_c_p] * 7 + [_c_p]
     lib.sparsepr_dense_attention.argtypes = [pp] + [_c_p] * 6 + [_c_p]
     lib.sparsepr_support_stats.argtypes = ([pp, _c_i32] + [_c_p] * 8 + [_c_i32, ctypes.c_double] +
                                            [_c_p] * 7 + [_c_sz, _c_p])
     for name in ("sparsepr_partition", "sparsepr_route", "sparsepr_attend", "sparsepr_attend_subset",
-                 "sparsepr_probe_fit", "sparsepr_apply", "sparsepr_dense_attention"):
+                 "sparsepr_probe_fit", "sparsepr_apply", "sparsepr_apply_noalloc",
+                 "sparsepr_dense_attention"):
         getattr(lib, name).restype = _c_i32
     if lib.sparsepr_abi_version() != 1:
         raise RuntimeError("libsparsepr ABI version mismatch")
@@ -268,6 +270,18 @@ def apply(p: Params, b: Buffers) -> None:
         ctypes.byref(cp), _ptr(b.S), _ptr(b.query_perm), _ptr(b.O_probe), _ptr(b.U),
         _ptr(b.Theta), _ptr(b.rank_eff), _ptr(b.O), _ptr(b.workspace), b.workspace.numel(),
         _stream(b.S.device)))
+
+
+def apply_noalloc(p: Params, b: Buffers, O=None) -> torch.Tensor:
+    """Stage 5 through the entry point that uses the library's fixed scratch
+    instead of the workspace; writes O (default: b.O)."""
+    lib = load()
+    cp = c_params(p)
+    O = b.O if O is None else O
+    _check(lib.sparsepr_apply_noalloc(
+        ctypes.byref(cp), _ptr(b.S), _ptr(b.query_perm), _ptr(b.O_probe), _ptr(b.U),
+        _ptr(b.Theta), _ptr(b.rank_eff), _ptr(O), _stream(b.S.device)))
+    return O
 
 
 def dense_attention(p: Params, Q, K, V, scale, O=None, lse=None):

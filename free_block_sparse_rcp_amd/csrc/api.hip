@@ -5,6 +5,7 @@
 #include <cstdarg>
 #include <cstdio>
 #include <cstring>
+#include <mutex>
 
 #include "internal.hpp"
 
@@ -205,6 +206,38 @@ static int32_t hip_status(hipError_t e, const char* stage) {
     return SPARSEPR_OK;
   }
   return fail(SPARSEPR_ERR_HIP, "%s: %s", stage, hipGetErrorString(e));
+}
+
+// ---- fixed scratch of sparsepr_apply_noalloc: the per-head matrix Theta U^T
+// (bf16 hi/lo parts) and bias that sparsepr_apply keeps in the workspace live
+// here instead. Each device holds its own copy for the life of the process.
+// In host code `scratch` is only a stand-in for the symbol: kernels receive
+// the device address looked up below, never the array's name.
+static __device__ __align__(256) char scratch[SPARSEPR_APPLY_SCRATCH_BYTES];
+
+constexpr int kMaxDevices = 64;
+static std::mutex g_scratch_mu;
+static char* g_scratch_ptr[kMaxDevices] = {};
+
+// Device address of `scratch` on the current device, looked up once per device
+// (with that device current) and kept.
+static int32_t scratch_address(char** out) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return fail(SPARSEPR_ERR_HIP, "hipGetDevice: %s", hipGetErrorString(e));
+  if (dev < 0 || dev >= kMaxDevices)
+    return fail(SPARSEPR_ERR_UNSUPPORTED, "device index %d beyond %d", dev, kMaxDevices);
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (g_scratch_ptr[dev] == nullptr) {
+    void* ptr = nullptr;
+    e = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+    if (e != hipSuccess || ptr == nullptr)
+      return fail(SPARSEPR_ERR_HIP, "hipGetSymbolAddress(scratch) on device %d: %s", dev,
+                  hipGetErrorString(e));
+    g_scratch_ptr[dev] = static_cast<char*>(ptr);
+  }
+  *out = g_scratch_ptr[dev];
+  return SPARSEPR_OK;
 }
 
 }  // namespace spr
@@ -492,6 +525,35 @@ int32_t sparsepr_apply(const sparsepr_params* params, const float* S_out,
   return hip_status(launch_apply(d, S_out, query_perm, O_probe, U, Theta, rank_eff, O,
                                  static_cast<char*>(workspace), static_cast<hipStream_t>(stream)),
                     "sparsepr_apply");
+}
+
+int32_t sparsepr_apply_noalloc(const sparsepr_params* params, const float* S_out,
+                               const int32_t* query_perm, const float* O_probe, const float* U,
+                               const float* Theta, const int32_t* rank_eff, void* O,
+                               void* stream) {
+  Dims d;
+  int32_t s = make_dims(params, true, &d);
+  if (s != SPARSEPR_OK) return s;
+  SPR_REQUIRE(S_out, "S_out");
+  SPR_REQUIRE(query_perm, "query_perm");
+  SPR_REQUIRE(rank_eff, "rank_eff");
+  SPR_REQUIRE(O, "O");
+  if (d.m > 0) SPR_REQUIRE(O_probe, "O_probe");
+  if (d.k > 0) {
+    SPR_REQUIRE(U, "U");
+    SPR_REQUIRE(Theta, "Theta");
+  }
+  const size_t need = d.bf16 ? apply_ws(d).end : 0;
+  if (need > SPARSEPR_APPLY_SCRATCH_BYTES)
+    return fail(SPARSEPR_ERR_WORKSPACE,
+                "sparsepr_apply_noalloc needs %zu bytes of scratch for %d heads of dimension %d; "
+                "its fixed scratch holds %zu (use sparsepr_apply with a workspace)",
+                need, d.H, d.D, (size_t)SPARSEPR_APPLY_SCRATCH_BYTES);
+  char* ws = nullptr;
+  if ((s = scratch_address(&ws)) != SPARSEPR_OK) return s;
+  return hip_status(launch_apply(d, S_out, query_perm, O_probe, U, Theta, rank_eff, O, ws,
+                                 static_cast<hipStream_t>(stream)),
+                    "sparsepr_apply_noalloc");
 }
 
 int32_t sparsepr_dense_attention(const sparsepr_params* params, const void* Q, const void* K,

@@ -26,7 +26,9 @@
  * - Every pointer argument except `params` and `workspace_bytes`-style host
  *   outputs is a DEVICE pointer on the current HIP device. The library
  *   allocates nothing and keeps no state between calls; the caller owns all
- *   buffers, including the workspace.
+ *   buffers, including the workspace. (One exception by design:
+ *   sparsepr_apply_noalloc keeps its scratch in a fixed device array of the
+ *   library, see there.)
  * - Tensors are contiguous, head-major: [H, N, d] means element
  *   (h, i, e) at ((h * N) + i) * d + e. Per-head index arrays are [H, N] etc.
  * - `dtype` selects the element type of Q, K, V, Kp, Vp and O:
@@ -294,6 +296,28 @@ int32_t sparsepr_apply(const sparsepr_params* params, const float* S_out,
                        const int32_t* query_perm, const float* O_probe, const float* U,
                        const float* Theta, const int32_t* rank_eff, void* O, void* workspace,
                        size_t workspace_bytes, void* stream);
+
+/*
+ * Stage 5 without a workspace, for callers that cannot allocate device memory
+ * (code under HIP graph capture, tight serving loops, harnesses that forbid
+ * allocation). Computes exactly what sparsepr_apply computes, with the same
+ * kernels, arguments and errors, except that the per-head matrix Theta U^T
+ * and bias live in a fixed device array inside the library instead of the
+ * caller's workspace. That array holds SPARSEPR_APPLY_SCRATCH_BYTES on each
+ * device the library runs on, until the process ends; its address is looked
+ * up on a device's first call. The bf16 path needs H * (4 d^2 + 4 d) bytes
+ * (256-byte aligned parts): up to 127 heads at d = 128, 503 at d = 64; the
+ * fp32 path needs none. Larger calls are rejected with
+ * SPARSEPR_ERR_WORKSPACE before anything is launched. Nothing is allocated,
+ * freed or cleared. All calls on one device share the array and leave their
+ * contents there: calls that may overlap on one device (other streams,
+ * other threads) race and must be serialised by the caller.
+ */
+#define SPARSEPR_APPLY_SCRATCH_BYTES ((size_t)8 << 20)
+int32_t sparsepr_apply_noalloc(const sparsepr_params* params, const float* S_out,
+                               const int32_t* query_perm, const float* O_probe, const float* U,
+                               const float* Theta, const int32_t* rank_eff, void* O,
+                               void* stream);
 
 /*
  * Support and mass diagnostics of sampled query blocks of one head (skillfed

@@ -150,6 +150,16 @@ def test_null_pointers_and_small_workspace_are_rejected(lib):
     st = lib.sparsepr_apply(ctypes.byref(p), fake, fake, fake, fake, fake, fake, fake, fake, 16,
                             None)
     assert st == 3
+    # apply without a workspace: NULL output, then more heads than the fixed
+    # scratch holds (bf16, d = 128: 66048 bytes per head, 8 MiB in all)
+    st = lib.sparsepr_apply_noalloc(ctypes.byref(p), fake, fake, fake, fake, fake, fake, None,
+                                    None)
+    assert st == 1 and "O is NULL" in lib.sparsepr_last_error().decode()
+    big = binding.c_params(configs.HUNYUAN.params)
+    big.heads = 128
+    st = lib.sparsepr_apply_noalloc(ctypes.byref(big), fake, fake, fake, fake, fake, fake, fake,
+                                    None)
+    assert st == 3 and "fixed scratch" in lib.sparsepr_last_error().decode()
     # dense attention validates only the shape fields
     q = binding.c_params(configs.TINY.params)
     q.head_dim = 80
