@@ -276,32 +276,10 @@ __device__ __forceinline__ void attn_tile(const char* __restrict__ kb, const cha
     }
 }
 
-// Direct global->LDS loads of one tile by one wave, NJ per wave: every
-// row-table read first (a read placed after a direct load would wait for it,
-// as the load writes LDS), then the loads. words[j]: byte offset of the lane's
-// row-table entry (low 16 bits) and of its 16-byte chunk in the row (high 16
-// bits); us[j]: the 1 KB load index, or -1.
-template <int NJ>
-__device__ __forceinline__ void issue_rows(const char* base, const int* rows, const int* words,
-                                           const int* us, char* dst) {
-  uint32_t ro[NJ];
-#pragma unroll
-  for (int j = 0; j < NJ; ++j) {
-    const int x = words[j];
-    ro[j] = *reinterpret_cast<const uint32_t*>(reinterpret_cast<const char*>(rows) + (x & 0xffff)) +
-            ((uint32_t)x >> 16);
-  }
-#pragma unroll
-  for (int j = 0; j < NJ; ++j)
-    if (us[j] >= 0)
-      __builtin_amdgcn_global_load_lds((const void*)(base + ro[j]),
-                                       (__attribute__((address_space(3))) void*)(dst + us[j] * 1024),
-                                       16, 0, 0);
-}
-
 template <int D, int BQ, int MODE>
 __global__ __launch_bounds__(BQ * 2)
-__attribute__((amdgpu_waves_per_eu(tile_keys<MODE>() == 32 ? 3 : 2, tile_keys<MODE>() == 32 ? 3 : 2)))
+__attribute__((amdgpu_waves_per_eu(BQ == 128 ? (tile_keys<MODE>() == 32 ? 3 : 2) : 1,
+                                   BQ == 128 ? (tile_keys<MODE>() == 32 ? 3 : 2) : 1)))
 void k_attn_mfma(AttnArgs a) {
   constexpr int KT = tile_keys<MODE>();
   using TG = TileGeom<D, KT>;
@@ -311,16 +289,26 @@ void k_attn_mfma(AttnArgs a) {
   constexpr int CPR = ROWB / 16;             // data chunks per row
   constexpr int NDT = D / 32;                // 32-wide output d tiles
   constexpr int NKK = D / 16;                // k-steps of the QK^T product
-  constexpr int KINS_W = (TG::KINS + NW - 1) / NW;
-  constexpr int VINS_W = (TG::VINS + NW - 1) / NW;
-  __shared__ __attribute__((aligned(1024))) char lds_k0[TG::KBYTES];
-  __shared__ __attribute__((aligned(1024))) char lds_k1[TG::KBYTES];
-  __shared__ __attribute__((aligned(1024))) char lds_v0[TG::VBYTES];
-  __shared__ __attribute__((aligned(1024))) char lds_v1[TG::VBYTES];
-  __shared__ int ridx[2][KT];
+  // one stage = a tile's K rows (KBYTES) followed by its V rows (VBYTES);
+  // two stages in distinct arrays, so the compiler sees that the compute reads
+  // of one never alias the direct loads filling the other
+  constexpr int NLOAD = TG::KINS + TG::VINS;   // 1 KB direct loads per tile
+  constexpr int SLOTS = (NLOAD + NW - 1) / NW; // the same number for every wave
+  constexpr int CHT = 16;                      // tiles per row-table chunk
+  constexpr bool kTable = MODE == ATTN_SPARSE; // dense and probe keys are one contiguous range
+  __shared__ __attribute__((aligned(1024))) char lds_s0[NLOAD * 1024];
+  __shared__ __attribute__((aligned(1024))) char lds_s1[NLOAD * 1024];
+  __shared__ int ridx[2][kTable ? CHT * KT : 1];
   __shared__ int r_start[kMaxRanges + 1];
   __shared__ int r_cum[kMaxRanges + 2];
-  __shared__ int tmp[NT];
+  // scan scratch of the range builder; during the tile loop it absorbs the
+  // loads of the slots past NLOAD (never read)
+  __shared__ __attribute__((aligned(1024))) int tmp[NT > 256 ? NT : 256];
+  char* const lds_pad = reinterpret_cast<char*>(tmp);
+  char* const lds_k0 = lds_s0;
+  char* const lds_v0 = lds_s0 + TG::KBYTES;
+  char* const lds_k1 = lds_s1;
+  char* const lds_v1 = lds_s1 + TG::KBYTES;
 
   const int nqb = MODE == ATTN_PROBE ? (a.m + BQ - 1) / BQ : a.nb;
   const Item it = decode_item<MODE>(a, nqb);
@@ -328,7 +316,8 @@ void k_attn_mfma(AttnArgs a) {
   if (MODE == ATTN_SPARSE && a.subset != 0 && block_has_probe(it.b, a.N, a.m, BQ) != (a.subset == 1))
     return;
   const int t = threadIdx.x;
-  const int lane = t & 63, w = t >> 6;
+  const int lane = t & 63;
+  const int w = __builtin_amdgcn_readfirstlane(t >> 6);   // uniform across the wave
   const int hl = lane >> 5;       // which half of the wave
   const int ql = lane & 31;       // query within the wave
   const size_t hoff = (size_t)it.h * a.N * D;
@@ -359,79 +348,76 @@ void k_attn_mfma(AttnArgs a) {
 
   const int ntiles = (total + KT - 1) / KT;
   int cursor = 0;
-  // wave 0 writes the Kp/Vp row of each of a tile's 64 key positions
-  // (the sparse and probe modes keep byte offsets of rows, dense mode row indices)
-  constexpr bool kByteRows = MODE != ATTN_DENSE;
-  auto fill_rows = [&](int tile) {
-    if (w == 0 && tile < ntiles && lane < KT) {
-      const int r = key_row(tile * KT + lane, total, ng, r_start, r_cum, cursor);
-      ridx[tile & 1][lane] = kByteRows ? (int)((uint32_t)r * ROWB) : r;
-    }
-  };
-  // dense mode: the row table holds row indices and each load computes its
-  // address on its own, which measures faster there than the batched form
-  auto issue_tile = [&](int tile, char* kdst, char* vdst) {
-    const int* rows = ridx[tile & 1];
+  // Sparse mode: the row table holds the byte offset in Kp/Vp of each key
+  // position, CHT tiles per chunk, two chunks; all threads fill a chunk at
+  // once (each thread's positions increase, so its range cursor only moves
+  // forward). Dense and probe modes read one contiguous key range from row0.
+  const int row0 = r_start[0];
+  auto fill_chunk = [&](int chunk) {
+    int* dst = ridx[chunk & 1];
 #pragma unroll
-    for (int j = 0; j < KINS_W; ++j) {
-      const int u = w + NW * j;
-      if (u < TG::KINS) {
-        const int q0 = 64 * u + lane, q = q0 < KT * TG::KCH ? q0 : 0;
-        const int r = q / TG::KCH, cc = q - r * TG::KCH;
-        const char* src = Kh + (size_t)rows[r] * ROWB + (cc < CPR ? cc : 0) * 16;
-        __builtin_amdgcn_global_load_lds(
-            src, (__attribute__((address_space(3))) void*)(kdst + u * 1024), 16, 0, 0);
-      }
-    }
-#pragma unroll
-    for (int j = 0; j < VINS_W; ++j) {
-      const int u = w + NW * j;
-      if (u < TG::VINS) {
-        const int q0 = 64 * u + lane, q = q0 < KT * TG::VCH ? q0 : 0;
-        const int r = q / TG::VCH, cc = q - r * TG::VCH;
-        const char* src = Vh + (size_t)rows[r] * ROWB + (cc < CPR ? cc : 0) * 16;
-        __builtin_amdgcn_global_load_lds(
-            src, (__attribute__((address_space(3))) void*)(vdst + u * 1024), 16, 0, 0);
+    for (int e0 = 0; e0 < CHT * KT; e0 += NT) {
+      const int e = e0 + t;
+      if (e < CHT * KT) {
+        const int r = key_row(chunk * CHT * KT + e, total, ng, r_start, r_cum, cursor);
+        dst[e] = (int)((uint32_t)r * ROWB);
       }
     }
   };
-  // direct global->LDS loads: 1 KB per wave instruction, lane i -> chunk 64u + i
-  // of the tile. Each lane's part of load j is a packed word: byte offset of its
-  // row-table entry (low 16 bits) and of its 16-byte chunk in the row (high 16
-  // bits; pad chunks re-read chunk 0). Row-table entries are byte offsets of
-  // rows, so a load address is the head base plus one 32-bit sum.
-  auto lane_word = [&](int u, int ch) {
-    const int q0 = 64 * u + lane, q = q0 < KT * ch ? q0 : 0;   // past the tile: padding
+  // A tile is NLOAD direct global->LDS loads of 1 KB (K rows, then V rows),
+  // dealt out SLOTS per wave so that every wave runs the same branch-free
+  // sequence; a slot past NLOAD re-reads chunk 0 of the tile's first row into
+  // a buffer nobody reads. Lane i of load u moves chunk 64 (u mod tile part)
+  // + i; its word packs 4x its row in the tile (low 16 bits) and the byte
+  // offset of its 16-byte chunk in the row (high 16 bits; chunks past a row's
+  // data re-read chunk 0). Keys past the list's end re-read a valid row.
+  int sw[SLOTS];
+  const char* sbase[SLOTS];
+  int sdst[SLOTS];
+#pragma unroll
+  for (int j = 0; j < SLOTS; ++j) {
+    const int u = w * SLOTS + j;
+    const bool isk = u < TG::KINS;
+    const int ul = isk ? u : u - TG::KINS;
+    const int ch = isk ? TG::KCH : TG::VCH;
+    const int q0 = 64 * ul + lane;
+    const int q = (u < NLOAD && q0 < KT * ch) ? q0 : 0;
     const int r = q / ch, cc = q - r * ch;
-    return (4 * r) | (((cc < CPR ? cc : 0) * 16) << 16);
+    sw[j] = (4 * r) | (((cc < CPR ? cc : 0) * 16) << 16);
+    sbase[j] = isk ? Kh : Vh;
+    sdst[j] = u < NLOAD ? u * 1024 : -1;
+  }
+  auto issue_slots = [&](int tile, char* stage) {
+    uint32_t ro[SLOTS];
+    if constexpr (kTable) {
+      const char* tab = reinterpret_cast<const char*>(ridx[(tile / CHT) & 1]) + (tile % CHT) * KT * 4;
+#pragma unroll
+      for (int j = 0; j < SLOTS; ++j)
+        ro[j] = *reinterpret_cast<const uint32_t*>(tab + (sw[j] & 0xffff)) + ((uint32_t)sw[j] >> 16);
+    } else {
+#pragma unroll
+      for (int j = 0; j < SLOTS; ++j) {
+        const int pk = min(tile * KT + ((sw[j] & 0xffff) >> 2), total - 1);
+        ro[j] = (uint32_t)(row0 + pk) * (uint32_t)ROWB + ((uint32_t)sw[j] >> 16);
+      }
+    }
+#pragma unroll
+    for (int j = 0; j < SLOTS; ++j) {
+      char* dst = sdst[j] >= 0 ? stage + sdst[j] : lds_pad;
+      __builtin_amdgcn_global_load_lds((const void*)(sbase[j] + ro[j]),
+                                       (__attribute__((address_space(3))) void*)dst, 16, 0, 0);
+    }
   };
-  int kw[KINS_W], vw[VINS_W], ku[KINS_W], vu[VINS_W];
-#pragma unroll
-  for (int j = 0; j < KINS_W; ++j) {
-    kw[j] = lane_word(w + NW * j, TG::KCH);
-    ku[j] = w + NW * j < TG::KINS ? w + NW * j : -1;
-  }
-#pragma unroll
-  for (int j = 0; j < VINS_W; ++j) {
-    vw[j] = lane_word(w + NW * j, TG::VCH);
-    vu[j] = w + NW * j < TG::VINS ? w + NW * j : -1;
-  }
-  // (a macro rather than a lambda: a lambda here is host-device, and host-side
-  // overload resolution rejects calls from it to device-only templates)
-#define ISSUE_TILE(TILE, KDST, VDST)                                                       \
+#define NEXT_ROWS(TILE)                                                                    \
   do {                                                                                     \
-    if constexpr (kByteRows) {                                                             \
-      issue_rows<KINS_W>(Kh, ridx[(TILE) & 1], kw, ku, KDST);                              \
-      issue_rows<VINS_W>(Vh, ridx[(TILE) & 1], vw, vu, VDST);                              \
-    } else {                                                                               \
-      issue_tile(TILE, KDST, VDST);                                                        \
+    if constexpr (kTable) {                                                                \
+      if ((TILE) % CHT == 0) fill_chunk((TILE) / CHT + 1);                                 \
     }                                                                                      \
   } while (0)
 
-  fill_rows(0);
-  fill_rows(1);
+  if constexpr (kTable) fill_chunk(0);
   __syncthreads();
-  if (ntiles > 0) ISSUE_TILE(0, lds_k0, lds_v0);
+  if (ntiles > 0) issue_slots(0, lds_s0);
   __builtin_amdgcn_s_waitcnt(0);
   __syncthreads();
 
@@ -439,22 +425,22 @@ void k_attn_mfma(AttnArgs a) {
   // per-lane LDS byte offsets (the tile loop adds only compile-time constants)
   const int koff = ql * TG::KP + hl * 16;
   const int voff = (4 * (grp >> 1) + (gl >> 2)) * TG::VP + (16 * (grp & 1) + 4 * (gl & 3)) * 2;
-  // two tiles per trip: even tiles live in buffer 0, odd tiles in buffer 1
+  // two tiles per trip: even tiles live in stage 0, odd tiles in stage 1
   for (int tile = 0; tile < ntiles; tile += 2) {
-    if (tile + 1 < ntiles) ISSUE_TILE(tile + 1, lds_k1, lds_v1);
-    fill_rows(tile + 2);
+    if (tile + 1 < ntiles) issue_slots(tile + 1, lds_s1);
+    NEXT_ROWS(tile);
     attn_tile<D, KT>(lds_k0 + koff, lds_v0 + voff, qreg, acc_o, m_run, l_run, c, tile * KT, total, hl);
     __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
     if (tile + 1 >= ntiles) break;
-    if (tile + 2 < ntiles) ISSUE_TILE(tile + 2, lds_k0, lds_v0);
-    fill_rows(tile + 3);
+    if (tile + 2 < ntiles) issue_slots(tile + 2, lds_s0);
+    NEXT_ROWS(tile + 1);
     attn_tile<D, KT>(lds_k1 + koff, lds_v1 + voff, qreg, acc_o, m_run, l_run, c, (tile + 1) * KT, total, hl);
     __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
   }
 
-#undef ISSUE_TILE
+#undef NEXT_ROWS
   // ---- epilogue
   const float l_tot = l_run + __shfl_xor(l_run, 32);
   const float inv = l_tot > 0.f ? 1.0f / l_tot : 0.f;
