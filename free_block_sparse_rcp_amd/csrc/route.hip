@@ -71,7 +71,7 @@ __global__ __launch_bounds__(256) void k_route_scores(const void* Qv, const int3
         raw[v] = *reinterpret_cast<const u32x4*>(Q + (size_t)tok * ROWB + c * 16);
       }
     };
-    // the next block's first round is issued as soon as this block's first
+    // the next block's first round is issued as soon as this block's last
     // round has been added, so it is in flight during the reduction below
     u32x4 raw[8];
     if (nblk > 0) load_round(0, rg, raw);
