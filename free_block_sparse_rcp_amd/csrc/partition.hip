@@ -378,20 +378,31 @@ __global__ __launch_bounds__(kRvWaves * 64) __attribute__((amdgpu_waves_per_eu(4
         acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(plo[kk], kop, acc, 0, 0, 0);
       }
       const int key = k0 + tile * kRvTile + 32 * hk + ql;
-      float bs = __builtin_inff();
-      int br = -1;
+      // lowest-slot minimum of the 16 scores by a pairwise tree (the left
+      // operand holds the lower slots and keeps ties), so that the compares of
+      // one level are independent; slots whose bias is +inf never win
+      float sv[16];
+      int si[16];
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
         const f32x4 b4 = *reinterpret_cast<const f32x4*>(brow + 8 * j);
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-          const float sc = fmaf(sgn, acc[4 * j + i], b4[i]);
-          if (sc < bs) {
-            bs = sc;
-            br = 4 * j + i;
-          }
+          sv[4 * j + i] = fmaf(sgn, acc[4 * j + i], b4[i]);
+          si[4 * j + i] = 4 * j + i;
         }
       }
+#pragma unroll
+      for (int width = 8; width >= 1; width >>= 1) {
+#pragma unroll
+        for (int p = 0; p < width; ++p) {
+          const bool right = sv[2 * p + 1] < sv[2 * p];
+          sv[p] = right ? sv[2 * p + 1] : sv[2 * p];
+          si[p] = right ? si[2 * p + 1] : si[2 * p];
+        }
+      }
+      const float bs = sv[0];
+      const int br = bs < __builtin_inff() ? si[0] : -1;
       if (dbg != nullptr && key < k1) {
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
