@@ -184,7 +184,12 @@ __device__ __forceinline__ int key_row(int p, int total, int ng, const int* r_st
 // One KT-key tile of the flash loop: S^T = K Q^T, online softmax, O^T += V^T P^T.
 // Ktile / Vtile point at distinct __shared__ buffers, so the compiler can see
 // that these reads do not alias the direct loads filling the other buffer.
-template <int D, int KT>
+// RSUM (sparse and probe modes): the row sum adds the bf16-rounded
+// probabilities that P V uses, two per v_dot2_f32_bf16, so each output row is
+// a convex combination of its V rows with exactly those weights; the
+// log-sum-exp then differs from the exact one by at most log(1 + 2^-9). The
+// dense mode sums the fp32 probabilities.
+template <int D, int KT, bool RSUM>
 __device__ __forceinline__ void attn_tile(const char* __restrict__ kb, const char* __restrict__ vb,
                                           const bf16x8* qreg, f32x16* acc_o, float& m_run,
                                           float& l_run, float c, int kbase, int total, int hl) {
@@ -245,7 +250,7 @@ __device__ __forceinline__ void attn_tile(const char* __restrict__ kb, const cha
 #pragma unroll
       for (int q = 0; q < 8; ++q) {
         pv[q] = __builtin_amdgcn_exp2f(fmaf(s[kt][8 * hf + q], c, neg_m));
-        l_run += pv[q];
+        if (!RSUM) l_run += pv[q];
       }
 #pragma unroll
       for (int q = 0; q < 8; q += 2) {
@@ -253,6 +258,10 @@ __device__ __forceinline__ void attn_tile(const char* __restrict__ kb, const cha
         const bf16x2 bb = __builtin_convertvector(f, bf16x2);
         pk[kt][hf][q] = bb[0];
         pk[kt][hf][q + 1] = bb[1];
+        if (RSUM) {
+          const bf16x2 one = {(__bf16)1.0f, (__bf16)1.0f};
+          l_run = __builtin_amdgcn_fdot2_f32_bf16(bb, one, l_run, false);
+        }
       }
     }
   // V^T operand via transposing LDS reads
@@ -429,13 +438,13 @@ void k_attn_mfma(AttnArgs a) {
   for (int tile = 0; tile < ntiles; tile += 2) {
     if (tile + 1 < ntiles) issue_slots(tile + 1, lds_s1);
     NEXT_ROWS(tile);
-    attn_tile<D, KT>(lds_k0 + koff, lds_v0 + voff, qreg, acc_o, m_run, l_run, c, tile * KT, total, hl);
+    attn_tile<D, KT, MODE != ATTN_DENSE>(lds_k0 + koff, lds_v0 + voff, qreg, acc_o, m_run, l_run, c, tile * KT, total, hl);
     __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
     if (tile + 1 >= ntiles) break;
     if (tile + 2 < ntiles) issue_slots(tile + 2, lds_s0);
     NEXT_ROWS(tile + 1);
-    attn_tile<D, KT>(lds_k1 + koff, lds_v1 + voff, qreg, acc_o, m_run, l_run, c, (tile + 1) * KT, total, hl);
+    attn_tile<D, KT, MODE != ATTN_DENSE>(lds_k1 + koff, lds_v1 + voff, qreg, acc_o, m_run, l_run, c, (tile + 1) * KT, total, hl);
     __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
   }

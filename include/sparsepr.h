@@ -211,7 +211,10 @@ int32_t sparsepr_route(const sparsepr_params* params, const void* Q, const float
  *   S_out[i] = sum_{j in K(b)} softmax_{K(b)}(tau q . k_j) v_j,
  *   lse[i]   = log sum_{j in K(b)} exp(tau q . k_j),
  * where K(b) = the keys of the block's selected groups, read from the
- * group-contiguous Kp/Vp. Needs no workspace.
+ * group-contiguous Kp/Vp. Needs no workspace. On the bf16 path the
+ * probabilities are rounded to bf16 for the product with V, and both the
+ * normalisation and lse use the sum of those rounded values, so lse is within
+ * log(1 + 2^-9) < 2e-3 of the exact value.
  *
  * Inputs : Q [H,N,d]; Kp, Vp [H,N,d] (from stage 1); scale [H];
  *          group_off [H,G+1]; query_perm [H,N]; block_ptr, block_groups.
