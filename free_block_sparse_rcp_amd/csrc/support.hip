@@ -83,9 +83,9 @@ __global__ __launch_bounds__(256) void k_support_logits(SupportArgs a) {
     }
 #pragma unroll
     for (int r = 0; r < kSupRows; ++r) {
-      if (r0 + r >= a.BQ) break;
       const int p = b * a.BQ + r0 + r;
-      a.xs[((size_t)i * a.BQ + r0 + r) * a.N + j] = p < a.N ? tau * acc[r] : -__builtin_inff();
+      if (r0 + r < a.BQ)
+        a.xs[((size_t)i * a.BQ + r0 + r) * a.N + j] = p < a.N ? tau * acc[r] : -__builtin_inff();
     }
   }
 }
