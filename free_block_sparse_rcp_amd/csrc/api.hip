@@ -100,6 +100,8 @@ ApplyWs apply_ws(const Dims& d) {
   return L;
 }
 
+constexpr int kProbeSlots = 768;   // resident probe-attention workgroups: 3 per CU x 256 CUs
+
 // Validation of the parameters; `full` also checks the fields that only the
 // sparse stages use.
 static int32_t make_dims(const sparsepr_params* p, bool full, Dims* d) {
@@ -172,9 +174,11 @@ static int32_t make_dims(const sparsepr_params* p, bool full, Dims* d) {
   d->kappa = (int64_t)kap;
   d->gbits = bits_for(d->G);
   if (d->m > 0) {
+    // key splits of the exact probe rows: as many workgroups as fit on the chip
+    // at once (three per CU on 256 CUs), so that the pass runs in one round
     const int nqb = (d->m + d->BQ - 1) / d->BQ;
     const int items = d->H * nqb;
-    int nsplit = (1024 + items - 1) / items;
+    int nsplit = kProbeSlots / items;
     nsplit = std::max(1, std::min(nsplit, (d->N + 255) / 256));
     int len = (d->N + nsplit - 1) / nsplit;
     len = (len + 63) / 64 * 64;
