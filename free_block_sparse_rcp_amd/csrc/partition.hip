@@ -650,8 +650,10 @@ __global__ __launch_bounds__(256) void k_group_mean(const void* Kv, const int32_
   constexpr int CPR = ROWB / 16;              // threads per row
   constexpr int EPC = 16 / (int)sizeof(T);    // elements per chunk
   constexpr int RPP = 256 / CPR;              // rows per pass
-  constexpr int U = 4;                        // row loads in flight per thread
+  constexpr int U = 8;                        // row loads in flight per thread
+  constexpr int PCH = 64 * RPP;               // key indices staged per chunk (a multiple of RPP)
   __shared__ float red[RPP * D];
+  __shared__ int pidx[PCH];
   const int g = blockIdx.x, h = blockIdx.y, t = threadIdx.x;
   const int32_t* off = group_off + (size_t)h * (G + 1);
   const int b = off[g], e = off[g + 1];
@@ -674,16 +676,26 @@ __global__ __launch_bounds__(256) void k_group_mean(const void* Kv, const int32_
       for (int j = 0; j < 4; ++j) acc[j] += __uint_as_float(raw[j]);
     }
   };
-  int i = b + slot;
-  for (; i + (U - 1) * RPP < e; i += U * RPP) {
-    u32x4 raw[U];
+  // The group's key indices are staged in LDS a chunk at a time, so the row
+  // loads do not wait behind dependent index loads. Thread (slot, cc) adds
+  // rows b + slot, b + slot + RPP, ... in that order whatever the chunking
+  // (PCH is a multiple of RPP), so the sum is the same as a plain loop.
+  for (int c0 = b; c0 < e; c0 += PCH) {
+    const int n = min(PCH, e - c0);
+    __syncthreads();
+    for (int j = t; j < n; j += 256) pidx[j] = clamp_idx(perm[c0 + j], N);
+    __syncthreads();
+    int i = slot;
+    for (; i + (U - 1) * RPP < n; i += U * RPP) {
+      u32x4 raw[U];
 #pragma unroll
-    for (int u = 0; u < U; ++u)
-      raw[u] = *reinterpret_cast<const u32x4*>(K + (size_t)clamp_idx(perm[i + u * RPP], N) * ROWB);
+      for (int u = 0; u < U; ++u)
+        raw[u] = *reinterpret_cast<const u32x4*>(K + (size_t)pidx[i + u * RPP] * ROWB);
 #pragma unroll
-    for (int u = 0; u < U; ++u) add(raw[u]);
+      for (int u = 0; u < U; ++u) add(raw[u]);
+    }
+    for (; i < n; i += RPP) add(*reinterpret_cast<const u32x4*>(K + (size_t)pidx[i] * ROWB));
   }
-  for (; i < e; i += RPP) add(*reinterpret_cast<const u32x4*>(K + (size_t)clamp_idx(perm[i], N) * ROWB));
 #pragma unroll
   for (int j = 0; j < EPC; ++j) red[slot * D + cc * EPC + j] = acc[j];
   __syncthreads();
