@@ -224,10 +224,12 @@ __device__ __forceinline__ void attn_tile(const char* __restrict__ kb, const cha
 #pragma unroll
     for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[kt][r]);
   {
-    // lanes l and l ^ 32 hold the two halves of one query row
-    const auto sw = __builtin_amdgcn_permlane32_swap(__builtin_bit_cast(unsigned, mx),
-                                                     __builtin_bit_cast(unsigned, mx), false, false);
-    mx = fmaxf(__builtin_bit_cast(float, sw[0]), __builtin_bit_cast(float, sw[1])) * c;
+    // lanes l and l ^ 32 hold the two halves of one query row (the helper
+    // reads both swap results through integer casts: a bit_cast of a vector
+    // element straight from the builtin's result reads element 0 twice)
+    float lo, hi;
+    lane_half_swap(mx, mx, lo, hi);
+    mx = (lo > hi ? lo : hi) * c;
   }
   const float m_new = fmaxf(m_run, mx);
   const bool need = m_new > m_run + 8.0f;
@@ -346,7 +348,20 @@ void k_attn_mfma(AttnArgs a) {
   for (int kk = 0; kk < NKK; ++kk)
     qreg[kk] = *reinterpret_cast<const bf16x8*>(Qh + (size_t)qtok * D + 16 * kk + 8 * hl);
 
-  const float c = a.scale[it.h] * kLog2e;
+  // The online softmax scales each tile's largest raw logit by c, which is the
+  // largest scaled logit only when c >= 0. For a negative scale the Q operand
+  // is negated (an exact sign flip of every bf16 element), so that the kernel
+  // runs with |c| on the same scaled logits.
+  float c = a.scale[it.h] * kLog2e;
+  if (c < 0.f) {
+#pragma unroll
+    for (int kk = 0; kk < NKK; ++kk) {
+      u32x4 bits = __builtin_bit_cast(u32x4, qreg[kk]);
+      bits ^= 0x80008000u;
+      qreg[kk] = __builtin_bit_cast(bf16x8, bits);
+    }
+    c = -c;
+  }
   float m_run = -__builtin_inff();   // running max of the scaled logits (log2 units)
   float l_run = 0.f;
   f32x16 acc_o[NDT];

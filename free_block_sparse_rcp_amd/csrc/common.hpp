@@ -72,8 +72,10 @@ __device__ __forceinline__ int xcd_remap(int w, int total) {
 // fence would drain, stalling a prefetch in flight).
 // v_permlane32_swap on two floats: lo gets a in lanes 0-31 and b of lane
 // l - 32 in lanes 32-63; hi gets a of lane l + 32 in lanes 0-31 and b in lanes
-// 32-63. Scalar arguments and results (the builtin mis-lowers when fed vector
-// elements directly).
+// 32-63. Scalar arguments and results: the builtin mis-lowers when fed vector
+// elements directly, and a __builtin_bit_cast of an element of its result
+// reads element 0 whichever element is named, so each result goes through an
+// integer cast first.
 __device__ __forceinline__ void lane_half_swap(float a, float b, float& lo, float& hi) {
   const auto sw = __builtin_amdgcn_permlane32_swap(__builtin_bit_cast(unsigned, a),
                                                    __builtin_bit_cast(unsigned, b), false, false);

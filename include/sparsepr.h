@@ -50,6 +50,9 @@
  *   calling thread's last failure. Index arrays living on the device are not
  *   validated on the host: out-of-range entries are clamped into [0, N) by
  *   the kernels (never read out of bounds) and give meaningless results.
+ * - The softmax scale `scale[h]` (tau, fp32 on the device) may be any finite
+ *   value, negative or zero included; the attention kernels keep their
+ *   exponentials in range for any span of the scaled logits.
  */
 #ifndef SPARSEPR_H
 #define SPARSEPR_H

@@ -41,6 +41,9 @@ WORKLOADS = {
     "bf16_mixed_temp": small_bf16(name="bf16_mixed", heads=2, seed=13,
                                   scales=[2.0 / math.sqrt(128), 0.3 / math.sqrt(128)],
                                   smoothing=True, m=96, k=24),
+    # a negative softmax scale on head 0: the definitions hold for any real tau
+    "bf16_signed_scale": small_bf16(name="bf16_signed_scale", heads=2, seed=15,
+                                    scales=[-1.0 / math.sqrt(128), 1.5 / math.sqrt(128)]),
 }
 
 _RUNS = {}
@@ -313,14 +316,14 @@ def test_independent_oracle_run_report(name):
 @pytest.mark.parametrize("dtype,d,bq,n", [("f32", 64, 64, 1000), ("f32", 128, 128, 777),
                                           ("bf16", 128, 128, 3045), ("bf16", 64, 64, 1500),
                                           ("bf16", 128, 64, 200)])
-def test_dense_attention(dtype, d, bq, n):
+def test_dense_attention(dtype, d, bq, n, scales=(1.3, 0.4)):
     rng = np.random.default_rng(n + d)
     H = 2
     from free_block_sparse_rcp_amd.inputs import round_to_dtype
     Q = round_to_dtype(rng.standard_normal((H, n, d)), dtype)
     K = round_to_dtype(rng.standard_normal((H, n, d)), dtype)
     V = round_to_dtype(rng.standard_normal((H, n, d)), dtype)
-    sc = np.array([1.3 / math.sqrt(d), 0.4 / math.sqrt(d)], np.float32)
+    sc = np.array([scales[0] / math.sqrt(d), scales[1] / math.sqrt(d)], np.float32)
     p = configs.Params(heads=H, n_tokens=n, head_dim=d, dtype=dtype, q_block=bq, n_groups=1,
                        n_samples=1, kmeans_iters=1, density=1.0, n_probes=0, rank=0,
                        ridge_lambda=1.0)
@@ -335,6 +338,15 @@ def test_dense_attention(dtype, d, bq, n):
         # bf16: output storage (~1.7e-3) plus bf16 probabilities in P V
         assert rel_l2(O[h], ref) < (5e-3 if dtype == "bf16" else TOL[dtype])
         assert np.max(np.abs(lse[h] - rl)) < 1e-4
+
+
+@pytest.mark.parametrize("dtype,d,bq,n", [("f32", 64, 64, 1000), ("bf16", 128, 128, 1000),
+                                         ("bf16", 64, 64, 700)])
+def test_dense_attention_negative_scale(dtype, d, bq, n):
+    """A large negative scale on head 0: scaled logits span about +-170 in log2
+    units, so a running maximum taken on the wrong side overflows exp2 (the MFMA
+    kernel runs a negative scale with the Q operand negated and |scale|)."""
+    test_dense_attention(dtype, d, bq, n, scales=(-40.0, 0.4))
 
 
 # ------------------------------------------------------------ variants and edges
