@@ -362,6 +362,10 @@ void k_attn_mfma(AttnArgs a) {
     }
     c = -c;
   }
+  // Masked keys carry a raw logit of -inf, which a zero scale would turn into
+  // NaN. The smallest normal scale gives the same result as zero: every scaled
+  // logit is then below 2^-100 in magnitude, so each exponential rounds to 1.
+  if (c == 0.f) c = __FLT_MIN__;
   float m_run = -__builtin_inff();   // running max of the scaled logits (log2 units)
   float l_run = 0.f;
   f32x16 acc_o[NDT];

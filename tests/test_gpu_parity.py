@@ -44,6 +44,9 @@ WORKLOADS = {
     # a negative softmax scale on head 0: the definitions hold for any real tau
     "bf16_signed_scale": small_bf16(name="bf16_signed_scale", heads=2, seed=15,
                                     scales=[-1.0 / math.sqrt(128), 1.5 / math.sqrt(128)]),
+    # sharp softmax: scaled logits span hundreds (log2 units) in every row
+    "bf16_sharp": small_bf16(name="bf16_sharp", heads=2, seed=16,
+                             scales=[40.0 / math.sqrt(128), -25.0 / math.sqrt(128)]),
 }
 
 _RUNS = {}
@@ -347,6 +350,12 @@ def test_dense_attention_negative_scale(dtype, d, bq, n):
     units, so a running maximum taken on the wrong side overflows exp2 (the MFMA
     kernel runs a negative scale with the Q operand negated and |scale|)."""
     test_dense_attention(dtype, d, bq, n, scales=(-40.0, 0.4))
+
+
+@pytest.mark.parametrize("dtype,d,bq,n", [("f32", 64, 64, 300), ("bf16", 128, 128, 300)])
+def test_dense_attention_zero_scale(dtype, d, bq, n):
+    """tau = 0 on head 0: every logit is 0, each output row is the mean of V."""
+    test_dense_attention(dtype, d, bq, n, scales=(0.0, -0.4))
 
 
 # ------------------------------------------------------------ variants and edges
