@@ -551,13 +551,13 @@ def test_support_stats(name):
     assert ambiguous <= max(2, checked // 10)
 
 
-def _degenerate(name, grid, d, dtype, BQ, G, S, rho, m, k, gen="g1"):
+def _degenerate(name, grid, d, dtype, BQ, G, S, rho, m, k, gen="g1", scale=None):
     n = grid[0] * grid[1] * grid[2]
     p = configs.Params(heads=1, n_tokens=n, head_dim=d, dtype=dtype, q_block=BQ, n_groups=G,
                        n_samples=S, kmeans_iters=4, density=rho, n_probes=m, rank=k,
                        ridge_lambda=1e-3)
-    return configs.Workload(name=name, grid=grid, params=p, scales=[d ** -0.5], generator=gen,
-                            seed=31)
+    sc = d ** -0.5 if scale is None else scale
+    return configs.Workload(name=name, grid=grid, params=p, scales=[sc], generator=gen, seed=31)
 
 
 DEGENERATE = {
@@ -585,6 +585,12 @@ DEGENERATE = {
                                   8, gen="g2"),
     "f32_d128": _degenerate("f32_d128", (3, 16, 25), 128, "f32", 128, 24, 64, 0.25, 32, 8,
                             gen="g2"),
+    # tau = 0: every response and coordinate is 0, so every tie goes to the
+    # lowest index, one group takes all keys and attention is uniform
+    "zero_scale_bf16": _degenerate("tau0_bf16", (2, 10, 10), 128, "bf16", 128, 16, 32, 0.3, 8, 4,
+                                   gen="g2", scale=0.0),
+    "zero_scale_f32": _degenerate("tau0_f32", (2, 10, 10), 64, "f32", 64, 16, 32, 0.3, 8, 4,
+                                  scale=0.0),
 }
 
 
