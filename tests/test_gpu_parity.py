@@ -627,6 +627,30 @@ def test_degenerate_calls(name):
         np.testing.assert_allclose(g["O"][0], r.inp.V[0][0], rtol=1e-2 if p.dtype == "bf16" else 1e-6)
 
 
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+def test_zero_values_head(dtype):
+    """V = 0 on head 0: every output is 0, the probes' ridge weights (1/||o||^2,
+    0 where o = 0) all vanish and no correction is fitted; head 1 is ordinary."""
+    wl = small_bf16(name="zero_v", heads=2, seed=17)
+    if dtype == "f32":
+        wl = replace(wl, params=replace(wl.params, dtype="f32", head_dim=64, q_block=64))
+    inp = wl.make_inputs()
+    inp.V[0] = 0
+    r = run_pipeline(wl, inp=inp)
+    p = r.p
+    for h in range(p.heads):
+        g = head_arrays(r, h)
+        Q, K, V = (x[h].astype(np.float64) for x in (r.inp.Q, r.inp.K, r.inp.V))
+        o = oracle_on_gpu_indices(Q, K, V, float(r.inp.scale[h]), p, g)
+        assert int(g["rank_eff"]) == o["U"].shape[1]
+        assert np.all(np.isfinite(g["O"])) and np.all(np.isfinite(g["Theta"]))
+        if h == 0:
+            assert int(g["rank_eff"]) == 0
+            assert np.all(g["O"] == 0) and np.all(g["O_probe"] == 0)
+        else:
+            assert rel_l2(g["O"], o["O"]) < TOL[p.dtype]
+
+
 def test_full_density_equals_dense():
     wl = small_bf16(name="full", rho=1.0, m=0, k=0, G=16, seed=15)
     r = run_pipeline(wl)
