@@ -585,6 +585,8 @@ DEGENERATE = {
                                   8, gen="g2"),
     "f32_d128": _degenerate("f32_d128", (3, 16, 25), 128, "f32", 128, 24, 64, 0.25, 32, 8,
                             gen="g2"),
+    "bf16_d128_bq64": _degenerate("d128_bq64", (3, 16, 25), 128, "bf16", 64, 24, 64, 0.25, 32,
+                                  8, gen="g2"),
     # tau = 0: every response and coordinate is 0, so every tie goes to the
     # lowest index, one group takes all keys and attention is uniform
     "zero_scale_bf16": _degenerate("tau0_bf16", (2, 10, 10), 128, "bf16", 128, 16, 32, 0.3, 8, 4,
