@@ -7,6 +7,8 @@
 // rank is processed in chunks of 32 columns so LDS stays small for any k;
 // threads are register-blocked (4 rows x 2 columns, then 4 rows x d/16
 // contiguous outputs) and write whole 8/16-byte pieces of each output row.
+#include <algorithm>
+
 #include "common.hpp"
 #include "internal.hpp"
 
@@ -155,7 +157,7 @@ __global__ __launch_bounds__(256) void k_apply(const float* S, const int32_t* qu
 // correction keeps near-fp32 accuracy. Each wave takes 32 query positions at a
 // time; s is re-read in the output layout for the final sum, and the output
 // tile is staged in LDS so that every row (token order) is written whole.
-constexpr int kApplyTilesPerWg = 128;  // 32-row tiles per workgroup
+constexpr int kApplyTilesPerWg = 128;  // most 32-row tiles per workgroup
 constexpr int kApplyWaves = 8;
 
 // grid (H), block 256. wt: [H][2][d][d] bf16 (hi, lo) of W^T; bias: [H][d].
@@ -242,14 +244,42 @@ __global__ __launch_bounds__(kApplyWaves * 64) void k_apply_mfma(const float* S,
   __syncthreads();
 
   const int ntile = (N + 31) / 32;
-  const int t0 = part * kApplyTilesPerWg, t1 = min(ntile, t0 + kApplyTilesPerWg);
+  const int per = (ntile + wg_per_head - 1) / wg_per_head;
+  const int t0 = part * per, t1 = min(ntile, t0 + per);
   const float* Sh = S + (size_t)h * N * D;
   uint16_t* Oh = O + (size_t)h * N * D;
   uint16_t* stg = ostage[w];
+  // Raw s of the wave's next tile: lane (ql, hl) holds columns 16 kk + 8 hl ..
+  // + 7 of its row. The loads of tile t + 8 are issued while tile t is
+  // computed: the first half once tile t's values are converted, the second
+  // once half of tile t's output slices no longer need their s.
+  f32x4 xr[2 * NKK];
+  // half 0: columns of k-steps [0, NKK/2), half 1: the rest
+  auto load_tile = [&](int tile, int half) {
+    const int pos = tile * 32 + ql;
+    const bool ok = pos < N;
+    const float* srow = Sh + (size_t)(ok ? pos : 0) * D;
+#pragma unroll
+    for (int kk = half * NKK / 2; kk < (half + 1) * NKK / 2; ++kk) {
+      f32x4 x0 = {0.f, 0.f, 0.f, 0.f}, x1 = x0;
+      if (ok) {
+        x0 = *reinterpret_cast<const f32x4*>(srow + 16 * kk + 8 * hl);
+        x1 = *reinterpret_cast<const f32x4*>(srow + 16 * kk + 8 * hl + 4);
+      }
+      xr[2 * kk] = x0;
+      xr[2 * kk + 1] = x1;
+    }
+  };
+  if (t0 + w < t1) {
+    load_tile(t0 + w, 0);
+    load_tile(t0 + w, 1);
+  }
   for (int tile = t0 + w; tile < t1; tile += kApplyWaves) {
     const int pos = tile * 32 + ql;
     const bool valid = pos < N;
-    const float* srow = Sh + (size_t)(valid ? pos : 0) * D;
+    // token of this lane's row, read early; the store loop takes each row's
+    // token from the lane that owns the row
+    const int tok = valid ? clamp_idx(query_perm[(size_t)h * N + pos], N) : 0;
     bf16x8 shi[NKK], slo[NKK];
     // se[kk] / so[kk]: s in the output layout for column chunks q = 2 (kk % 2) and
     // q = 2 (kk % 2) + 1 of tile nt = kk / 2, from one lane-half swap of the loaded
@@ -257,11 +287,7 @@ __global__ __launch_bounds__(kApplyWaves * 64) void k_apply_mfma(const float* S,
     f32x4 se[NKK], so[NKK];
 #pragma unroll
     for (int kk = 0; kk < NKK; ++kk) {
-      f32x4 x0 = {0.f, 0.f, 0.f, 0.f}, x1 = x0;
-      if (valid) {
-        x0 = *reinterpret_cast<const f32x4*>(srow + 16 * kk + 8 * hl);
-        x1 = *reinterpret_cast<const f32x4*>(srow + 16 * kk + 8 * hl + 4);
-      }
+      const f32x4 x0 = xr[2 * kk], x1 = xr[2 * kk + 1];
 #pragma unroll
       for (int u = 0; u < 4; ++u) {
         float lo, hi;
@@ -279,6 +305,8 @@ __global__ __launch_bounds__(kApplyWaves * 64) void k_apply_mfma(const float* S,
         slo[kk][4 + u] = static_cast<__bf16>(x1[u] - static_cast<float>(h1));
       }
     }
+    const bool has_next = tile + kApplyWaves < t1;
+    if (has_next) load_tile(tile + kApplyWaves, 0);
     const int pi = valid ? probe_index(pos, N, m) : -1;
     // W fragments are re-read from LDS every tile: kept opaque so that the
     // compiler does not hoist all of them into registers (occupancy)
@@ -299,6 +327,8 @@ __global__ __launch_bounds__(kApplyWaves * 64) void k_apply_mfma(const float* S,
         acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(alo, shi[kk], acc, 0, 0, 0);
         acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ahi, slo[kk], acc, 0, 0, 0);
       }
+      // the second half of the next tile, once the first output slices' s are used
+      if (nt == NDT / 2 && has_next) load_tile(tile + kApplyWaves, 1);
       if (!valid) continue;
 #pragma unroll
       for (int q = 0; q < 4; ++q) {
@@ -327,8 +357,8 @@ __global__ __launch_bounds__(kApplyWaves * 64) void k_apply_mfma(const float* S,
     for (int r0 = 0; r0 < 32; r0 += RPI) {
       const int r = r0 + lane / LPR, c = lane % LPR;
       const int rpos = tile * 32 + r;
+      const int rtok = __shfl(tok, r);
       if (rpos < N) {
-        const int rtok = clamp_idx(query_perm[(size_t)h * N + rpos], N);
         const u32x4 v = *reinterpret_cast<const u32x4*>(stg + r * OP + 8 * c);
         *reinterpret_cast<u32x4*>(Oh + (size_t)rtok * D + 8 * c) = v;
       }
@@ -344,7 +374,15 @@ hipError_t launch_apply(const Dims& d, const float* S_out, const int32_t* query_
     const ApplyWs L = apply_ws(d);
     uint16_t* wt = reinterpret_cast<uint16_t*>(ws + L.wt);
     float* bias = reinterpret_cast<float*>(ws + L.bias);
-    const int wgph = ((d.N + 31) / 32 + kApplyTilesPerWg - 1) / kApplyTilesPerWg;
+    // workgroups per head: at most kApplyTilesPerWg tiles each, and the grid
+    // filled up to whole rounds of resident workgroups (W and the output
+    // staging allow one per CU at d = 128, two at d = 64; 256 CUs)
+    const int ntile = (d.N + 31) / 32;
+    const int base = (ntile + kApplyTilesPerWg - 1) / kApplyTilesPerWg;
+    const int slots = 256 * (d.D == 128 ? 1 : 2);
+    const int rounds = (d.H * base + slots - 1) / slots;
+    int wgph = std::max(base, rounds * slots / d.H);
+    wgph = std::min(wgph, std::max(base, (ntile + kApplyWaves - 1) / kApplyWaves));  // a tile per wave at least
     uint16_t* Ob = static_cast<uint16_t*>(O);
     if (d.D == 128) {
       k_apply_weights<128><<<d.H, 256, 0, st>>>(U, Theta, rank_eff, d.k, wt, bias);
