@@ -155,8 +155,9 @@ __global__ __launch_bounds__(256) void k_apply(const float* S, const int32_t* qu
 // O^T = W^T S^T as v_mfma_f32_32x32x16_bf16 with S split into hi + lo too
 // (hi*hi + lo*hi + hi*lo; the dropped lo*lo term is ~2^-16 relative), so the
 // correction keeps near-fp32 accuracy. Each wave takes 32 query positions at a
-// time; s is re-read in the output layout for the final sum, and the output
-// tile is staged in LDS so that every row (token order) is written whole.
+// time; the copy of s in the output layout for the final sum comes from a
+// lane-half swap of the loaded values, and the output tile is staged in LDS so
+// that every row (token order) is written whole.
 constexpr int kApplyTilesPerWg = 128;  // most 32-row tiles per workgroup
 constexpr int kApplyWaves = 8;
 
