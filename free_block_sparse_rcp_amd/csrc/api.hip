@@ -107,6 +107,8 @@ constexpr int kProbeSlots = 768;   // resident probe-attention workgroups: 3 per
 static int32_t make_dims(const sparsepr_params* p, bool full, Dims* d) {
   if (p == nullptr) return fail(SPARSEPR_ERR_INVALID_ARG, "params is NULL");
   if (p->heads < 1) return fail(SPARSEPR_ERR_INVALID_ARG, "heads must be >= 1 (got %d)", p->heads);
+  // heads are the second grid dimension of several launches
+  if (p->heads > 65535) return fail(SPARSEPR_ERR_UNSUPPORTED, "heads must be <= 65535 (got %d)", p->heads);
   if (p->n_tokens < 1) return fail(SPARSEPR_ERR_INVALID_ARG, "n_tokens must be >= 1 (got %d)", p->n_tokens);
   if (p->head_dim != 64 && p->head_dim != 128)
     return fail(SPARSEPR_ERR_UNSUPPORTED, "head_dim must be 64 or 128 (got %d)", p->head_dim);

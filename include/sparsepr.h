@@ -90,7 +90,7 @@ extern "C" {
  * double precision; kappa must be >= 1.
  */
 typedef struct sparsepr_params {
-  int32_t heads;          /* H >= 1 */
+  int32_t heads;          /* 1 <= H <= 65535 */
   int32_t n_tokens;       /* N >= 1 */
   int32_t head_dim;       /* d in {64, 128} */
   int32_t dtype;          /* SPARSEPR_F32 or SPARSEPR_BF16 */

@@ -67,7 +67,8 @@ def test_workspace_bytes_for_every_workload(lib, name):
 
 
 BAD = [
-    ("heads", 0, 1), ("n_tokens", 0, 1), ("head_dim", 96, 2), ("dtype", 7, 1), ("q_block", 32, 2),
+    ("heads", 0, 1), ("heads", 65536, 2), ("n_tokens", 0, 1), ("head_dim", 96, 2), ("dtype", 7, 1),
+    ("q_block", 32, 2),
     ("n_groups", 0, 1), ("n_groups", 2000, 1), ("n_samples", 0, 1), ("kmeans_iters", 0, 1),
     ("density", 0.0, 1), ("density", 1.5, 1), ("n_probes", -1, 1), ("rank", 200, 1),
     ("ridge_lambda", 0.0, 1), ("partition_mode", 3, 1), ("reserved", 1, 1),
