@@ -405,6 +405,9 @@ int32_t sparsepr_support_stats(const sparsepr_params* params, int32_t head, cons
     return fail(SPARSEPR_ERR_INVALID_ARG, "n_blocks must be in [1, nb] (got %d)", n_blocks);
   if (!(mass > 0.0 && mass <= 1.0))
     return fail(SPARSEPR_ERR_INVALID_ARG, "mass must be in (0, 1] (got %g)", mass);
+  // the pooled-support pass puts 256-key slices of a row on the grid's second dimension
+  if ((d.N + 255) / 256 > 65535)
+    return fail(SPARSEPR_ERR_UNSUPPORTED, "support statistics need N <= 16776960 (got %d)", d.N);
   SPR_REQUIRE(Q, "Q");
   SPR_REQUIRE(K, "K");
   SPR_REQUIRE(scale, "scale");

@@ -351,7 +351,8 @@ int32_t sparsepr_apply_noalloc(const sparsepr_params* params, const float* S_out
  * Inputs : head in [0, H); Q, K [H,N,d] dtype in TOKEN order; scale [H];
  *          key_label [H,N] (stage 1); query_perm, block_ptr, block_groups
  *          (stage 2); blocks [n_blocks] int32 device array of block indices
- *          (1 <= n_blocks <= nb); mass in (0, 1].
+ *          (1 <= n_blocks <= nb); mass in (0, 1]; N <= 16776960 (else
+ *          SPARSEPR_ERR_UNSUPPORTED).
  * Outputs: lse, routed_mass [n_blocks B_q] fp32; support, support_routed
  *          [n_blocks B_q] int32; pooled, pooled_routed [n_blocks] int32.
  * Workspace: at least 4 n_blocks B_q (N + 1) bytes (the rows' logits and
