@@ -29,35 +29,98 @@ namespace spr {
 
 constexpr int kFitThreads = 512;
 
-__device__ __forceinline__ double wave_sum_f64(double v) {
-#pragma unroll
-  for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o);
+// Cross-lane moves of a double, 32 bits at a time (the builtins' results go
+// through integer casts, as in lane_half_swap): a DPP pattern within rows of
+// 16 lanes.
+template <int CTRL>
+__device__ __forceinline__ double dpp_f64(double v) {
+  const uint64_t b = __builtin_bit_cast(uint64_t, v);
+  const unsigned lo = (unsigned)__builtin_amdgcn_update_dpp(0, (int)(unsigned)b, CTRL, 0xF, 0xF, false);
+  const unsigned hi = (unsigned)__builtin_amdgcn_update_dpp(0, (int)(unsigned)(b >> 32), CTRL, 0xF, 0xF, false);
+  return __builtin_bit_cast(double, ((uint64_t)hi << 32) | lo);
+}
+// v(l & ~B) + v(l | B) in every lane l, B = 16 or 32: the two results of
+// v_permlane16_swap / v_permlane32_swap with both operands v are exactly these
+// two values, so both lanes of a pair get the same bits.
+__device__ __forceinline__ double u64_to_f64(unsigned lo, unsigned hi) {
+  return __builtin_bit_cast(double, ((uint64_t)hi << 32) | lo);
+}
+__device__ __forceinline__ double pair_sum16_f64(double v) {
+  const uint64_t b = __builtin_bit_cast(uint64_t, v);
+  const unsigned l0 = (unsigned)b, h0 = (unsigned)(b >> 32);
+  const auto sl = __builtin_amdgcn_permlane16_swap(l0, l0, false, false);
+  const auto sh = __builtin_amdgcn_permlane16_swap(h0, h0, false, false);
+  const unsigned la = (unsigned)sl[0], lb = (unsigned)sl[1];
+  const unsigned ha = (unsigned)sh[0], hb = (unsigned)sh[1];
+  return u64_to_f64(la, ha) + u64_to_f64(lb, hb);
+}
+__device__ __forceinline__ double pair_sum32_f64(double v) {
+  const uint64_t b = __builtin_bit_cast(uint64_t, v);
+  const unsigned l0 = (unsigned)b, h0 = (unsigned)(b >> 32);
+  const auto sl = __builtin_amdgcn_permlane32_swap(l0, l0, false, false);
+  const auto sh = __builtin_amdgcn_permlane32_swap(h0, h0, false, false);
+  const unsigned la = (unsigned)sl[0], lb = (unsigned)sl[1];
+  const unsigned ha = (unsigned)sh[0], hb = (unsigned)sh[1];
+  return u64_to_f64(la, ha) + u64_to_f64(lb, hb);
+}
+
+// Sum over each aligned group of 16 lanes; every lane of the group gets the
+// same bits (pairwise exchanges within quads, then the half-row and row
+// mirrors, which pair lanes whose partial sums already agree).
+__device__ __forceinline__ double sum16_f64(double v) {
+  v += dpp_f64<0xB1>(v);    // quad_perm [1, 0, 3, 2]
+  v += dpp_f64<0x4E>(v);    // quad_perm [2, 3, 0, 1]
+  v += dpp_f64<0x141>(v);   // row_half_mirror
+  v += dpp_f64<0x140>(v);   // row_mirror
   return v;
+}
+
+// Sum over the wave, identical in every lane: rows of 16, then rows r and
+// r + 2 (lanes l and l ^ 32), then the two results read from lanes 0 and 16.
+__device__ __forceinline__ double wave_sum_f64(double v) {
+  v = sum16_f64(v);
+  v = pair_sum32_f64(v);
+  const uint64_t b = __builtin_bit_cast(uint64_t, v);
+  const unsigned a0 = (unsigned)__builtin_amdgcn_readlane((int)(unsigned)b, 0);
+  const unsigned a1 = (unsigned)__builtin_amdgcn_readlane((int)(unsigned)(b >> 32), 0);
+  const unsigned c0 = (unsigned)__builtin_amdgcn_readlane((int)(unsigned)b, 16);
+  const unsigned c1 = (unsigned)__builtin_amdgcn_readlane((int)(unsigned)(b >> 32), 16);
+  return __builtin_bit_cast(double, ((uint64_t)a1 << 32) | a0) +
+         __builtin_bit_cast(double, ((uint64_t)c1 << 32) | c0);
 }
 
 // Workgroup sum with one barrier. The wave partials go to one of two slots
 // that alternate between calls: a slot is rewritten only two calls later,
 // behind a barrier that every thread reaches after reading it.
+constexpr int kFitWaves = kFitThreads / 64;
 __device__ __forceinline__ double wg_sum1(double v, double* red2, int& slot) {
   v = wave_sum_f64(v);
-  double* red = red2 + slot * (kFitThreads / 64);
+  double* red = red2 + slot * kFitWaves;
   if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = v;
   __syncthreads();
   double s = 0.0;
 #pragma unroll
-  for (int i = 0; i < kFitThreads / 64; ++i) s += red[i];
+  for (int i = 0; i < kFitWaves; ++i) s += red[i];
   slot ^= 1;
   return s;
 }
-
-// Number of eigenvalues of the symmetric tridiagonal (a, b) below x.
-// 1/q from the hardware reciprocal and one Newton step (relative error near
-// the double rounding unit); only the signs of the recurrence are used.
+// 1/q from the hardware reciprocal refined by one Newton step: enough for the
+// Sturm counts, which use only the signs of their recurrence.
 __device__ __forceinline__ double rcp_nr(double q) {
   const double r = __builtin_amdgcn_rcp(q);
   return fma(r, fma(-q, r, 1.0), r);
 }
 
+// A second Newton step (the error squares again), for the multipliers and
+// pivots of the inverse iteration.
+__device__ __forceinline__ double rcp_nr2(double q) {
+  const double r = rcp_nr(q);
+  return fma(r, fma(-q, r, 1.0), r);
+}
+
+// Number of eigenvalues of the symmetric tridiagonal (a, b) below x, counted
+// as the negative pivots of the LDL^T factorisation of T - x I (tiny pivots
+// replaced by -pivmin).
 __device__ int sturm_count(const double* a, const double* b2, int n, double x, double pivmin) {
   int cnt = 0;
   double q = a[0] - x;
@@ -195,7 +258,7 @@ __global__ __launch_bounds__(kFitThreads) void k_fit(int m, int kmax, double lam
   constexpr int NX = D + 1;                // rows of the Gram on [s; 1]
   constexpr int BIG = (D + 1) * (D + 2);
   __shared__ double big[BIG];
-  __shared__ double dg[D], od[D], od2[D], beta[D], vv[D], pv[D], vn[D];
+  __shared__ double dg[D], od[D], od2[D], beta[D], vv[D], pv[D];
   __shared__ double lam_top[D + 1];   // eigenvalues, later 1 / L_ii of the ridge factor
   __shared__ double red2[2 * NT / 64];
   __shared__ double dots[D];
@@ -225,32 +288,46 @@ __global__ __launch_bounds__(kFitThreads) void k_fit(int m, int kmax, double lam
     if (t == 0) rank_eff[h] = 0;
     return;
   }
-  // ---- Householder tridiagonalisation; reflector k stored in column k below
-  // the diagonal. Four barriers per step: two sums, q ready, update done.
-  for (int k = 0; k < D - 2; ++k) {
-    const int L = D - k - 1;
+  // ---- Householder tridiagonalisation on the lower triangle of A (the upper
+  // triangle is not read after the copy); reflector k is stored in column k
+  // below the diagonal. Three barriers per step: the sum v^T p, q ready, and
+  // the end of the update, whose sum carries the next column's squared norm.
+  constexpr int NC = D / 32;   // update columns per thread (registers)
+  double sig2;
+  {
     double part = 0.0;
-    for (int i = 1 + t; i < L; i += NT) {
-      const double x = A[(k + 1 + i) * PA + k];
+    for (int i = 2 + t; i < D; i += NT) {
+      const double x = A[i * PA];
       part += x * x;
     }
-    const double sig2 = wg_sum1(part, red2, slot);
+    sig2 = wg_sum1(part, red2, slot);
+  }
+  for (int k = 0; k < D - 2; ++k) {
+    const int L = D - k - 1;
     const double x0 = A[(k + 1) * PA + k];
     if (sig2 == 0.0) {
       if (t == 0) {
         beta[k] = 0.0;
         od[k] = x0;
       }
-      continue;   // nothing is updated in this step
+      // nothing is updated in this step; the next column's norm is read directly
+      double part = 0.0;
+      for (int i = k + 3 + t; i < D; i += NT) {
+        const double x = A[i * PA + k + 1];
+        part += x * x;
+      }
+      sig2 = wg_sum1(part, red2, slot);
+      continue;
     }
     const double alpha = -copysign(sqrt(x0 * x0 + sig2), x0);
     const double v0 = x0 - alpha;
     const double bk = 2.0 / (v0 * v0 + sig2);
-    // p = beta A22 v with v_0 = v0, v_j = A[k+1+j][k]. Row i of the product is
-    // split over NSEG waves by segments of j; every step of a partial sum reads
-    // one row of A22 across the wave. v^T p comes from the partials directly.
+    // p = beta A22 v with v_0 = v0, v_j = A[k+1+j][k]; entry (i, j) of A22 is
+    // read from row max(i, j), column min(i, j). Row i of the product is split
+    // over NSEG waves by segments of j; v^T p comes from the partials directly.
     const int i = t & (D - 1), seg = t / D;
     const int jm = (L + NSEG - 1) / NSEG;
+    double* A22 = A + (k + 1) * PA + (k + 1);
     double s = 0.0;
     if (i < L) {
       const int j0 = min(L, seg * jm), j1 = min(L, j0 + jm);
@@ -258,15 +335,21 @@ __global__ __launch_bounds__(kFitThreads) void k_fit(int m, int kmax, double lam
       double s4[4] = {0.0, 0.0, 0.0, 0.0};
       int j = j0;
       if (j == 0) {
-        s4[0] = A[(k + 1) * PA + (k + 1 + i)] * v0;
+        s4[0] = A22[i * PA] * v0;
         j = 1;
       }
       for (; j + 3 < j1; j += 4) {
 #pragma unroll
-        for (int u = 0; u < 4; ++u)
-          s4[u] += A[(k + 1 + j + u) * PA + (k + 1 + i)] * A[(k + 1 + j + u) * PA + k];
+        for (int u = 0; u < 4; ++u) {
+          const int jj = j + u;
+          const int r = max(i, jj), c = min(i, jj);
+          s4[u] += A22[r * PA + c] * A[(k + 1 + jj) * PA + k];
+        }
       }
-      for (; j < j1; ++j) s4[0] += A[(k + 1 + j) * PA + (k + 1 + i)] * A[(k + 1 + j) * PA + k];
+      for (; j < j1; ++j) {
+        const int r = max(i, j), c = min(i, j);
+        s4[0] += A22[r * PA + c] * A[(k + 1 + j) * PA + k];
+      }
       s = (s4[0] + s4[1]) + (s4[2] + s4[3]);
     }
     const double v_i = i == 0 ? v0 : (i < L ? A[(k + 1 + i) * PA + k] : 0.0);
@@ -287,12 +370,48 @@ __global__ __launch_bounds__(kFitThreads) void k_fit(int m, int kmax, double lam
       A[(k + 1) * PA + k] = v0;   // x0 and the column are no longer read in this step
     }
     __syncthreads();
-    for (int i2 = t >> 5; i2 < L; i2 += NT / 32) {
-      const double vi2 = vv[i2], qi2 = pv[i2];
-      double* row = A + (k + 1 + i2) * PA + (k + 1);
-      for (int j2 = t & 31; j2 < L; j2 += 32) row[j2] -= vi2 * pv[j2] + qi2 * vv[j2];
+    // A22 -= v q^T + q v^T on the lower triangle: a thread keeps v and q of its
+    // columns jc + 32 c and of its rows t / 32 + 16 r in registers, and reads
+    // all of its old values before writing any. Column 0 of A22 (rows 2..) is
+    // the next step's column; its squared norm is summed here.
+    {
+      constexpr int RM = D / 16;   // rows per thread at most
+      static_assert(NT / 32 == 16, "16 row groups");
+      const int jc = t & 31, i20 = t >> 5;
+      double vcol[NC], qcol[NC], vrow[RM], qrow[RM], old[RM][NC];
+#pragma unroll
+      for (int c = 0; c < NC; ++c) {
+        const int j2 = jc + 32 * c;
+        vcol[c] = j2 < L ? vv[j2] : 0.0;
+        qcol[c] = j2 < L ? pv[j2] : 0.0;
+      }
+#pragma unroll
+      for (int r = 0; r < RM; ++r) {
+        const int i2 = i20 + 16 * r;
+        vrow[r] = i2 < L ? vv[i2] : 0.0;
+        qrow[r] = i2 < L ? pv[i2] : 0.0;
+#pragma unroll
+        for (int c = 0; c < NC; ++c) {
+          const int j2 = jc + 32 * c;
+          old[r][c] = (i2 < L && j2 <= i2) ? A22[i2 * PA + j2] : 0.0;
+        }
+      }
+      double part = 0.0;
+#pragma unroll
+      for (int r = 0; r < RM; ++r) {
+        const int i2 = i20 + 16 * r;
+#pragma unroll
+        for (int c = 0; c < NC; ++c) {
+          const int j2 = jc + 32 * c;
+          if (i2 < L && j2 <= i2) {
+            const double nv = old[r][c] - (vrow[r] * qcol[c] + qrow[r] * vcol[c]);
+            A22[i2 * PA + j2] = nv;
+            if (c == 0 && jc == 0 && i2 >= 2) part += nv * nv;
+          }
+        }
+      }
+      sig2 = wg_sum1(part, red2, slot);
     }
-    __syncthreads();
   }
   for (int i = t; i < D; i += NT) dg[i] = A[i * PA + i];
   if (t == 0) {
@@ -317,34 +436,42 @@ __global__ __launch_bounds__(kFitThreads) void k_fit(int m, int kmax, double lam
   const double pad = 2.2e-16 * fmax(tnorm, 1e-300) + pivmin;
   glo -= pad;
   ghi += pad;
-  // P-point multisection per eigenvalue, P = 32, 16 or 8 as keff allows; the
-  // interval shrinks by (P + 1)^iters > 2^50
-  const int P = keff <= NT / 32 ? 32 : (keff <= NT / 16 ? 16 : 8);
-  const int iters = P == 32 ? 10 : (P == 16 ? 13 : 16);
-  for (int base = 0; base < keff; base += NT / P) {
-    const int r = base + t / P, sub = t % P;
+  // P-point multisection per eigenvalue, one point per thread: P the largest
+  // power of two with P keff <= NT (at most 32), so one pass covers every
+  // eigenvalue. The interval shrinks by (P + 1)^iters > 2^40 (the eigenvalues
+  // serve only as inverse-iteration shifts); the new bracket comes from a
+  // ballot of the points' sides of the eigenvalue.
+  int P = 32;
+  while (P * keff > NT) P >>= 1;
+  const int iters = P == 32 ? 8 : (P == 16 ? 10 : (P == 8 ? 13 : 18));
+  {
+    const int r = t / P, sub = t % P;
     const int j = D - 1 - (r < keff ? r : 0);  // ascending eigenvalue index
+    const int gl = (t & 63) & ~(P - 1);        // the group's first lane in the wave
+    const uint64_t pmask = P == 32 ? 0xffffffffull : ((1ull << P) - 1);
+    const double dp = (double)(P + 1);
     double lo = glo, hi = ghi;
     for (int iter = 0; iter < iters; ++iter) {
-      const double x = lo + (hi - lo) * (double)(sub + 1) / (double)(P + 1);
+      const double w = hi - lo;
+      const double x = lo + w * (double)(sub + 1) / dp;
       const int cnt = sturm_count(dg, od2, D, x, pivmin);
+      // bit s: point s (x = lo + w (s + 1) / (P + 1)) lies left of the eigenvalue
+      const uint64_t left = (__ballot(cnt <= j) >> gl) & pmask;
+      const uint64_t right = ~left & pmask;
       double nlo = lo, nhi = hi;
-      for (int sp = 0; sp < P; ++sp) {
-        const double xs = __shfl(x, (t & ~(P - 1)) + sp);
-        const int cs = __shfl(cnt, (t & ~(P - 1)) + sp);
-        if (cs <= j) nlo = fmax(nlo, xs);
-        else nhi = fmin(nhi, xs);
-      }
+      if (left) nlo = fmax(nlo, lo + w * (double)(64 - __clzll((long long)left)) / dp);
+      if (right) nhi = fmin(nhi, lo + w * (double)__ffsll((long long)right) / dp);
       lo = nlo;
       hi = nhi;
     }
     if (r < keff && sub == 0) lam_top[r] = 0.5 * (lo + hi);
   }
   __syncthreads();
-  // ---- reflectors to the workspace; the LDS block is reused from here on
-  for (int idx = t; idx < D * D; idx += NT) {
-    const int i = idx / D, k = idx % D;
-    if (i > k && k < D - 2) f.hv[(size_t)i * D + k] = A[i * PA + k];
+  // ---- reflectors to the workspace, one per row (reflector k at [k][e], zero
+  // for e <= k); the LDS block is reused from here on
+  for (int idx = t; idx < (D - 2) * D; idx += NT) {
+    const int k = idx / D, e = idx % D;
+    f.hv[idx] = e > k ? A[e * PA + k] : 0.0;
   }
   __syncthreads();
   // ---- inverse iteration on the tridiagonal, one thread per eigenvector,
@@ -367,22 +494,31 @@ __global__ __launch_bounds__(kFitThreads) void k_fit(int m, int kmax, double lam
         const uint32_t hsh = (uint32_t)(i * 2654435761u) ^ (uint32_t)(r * 40503u + 12345u);
         Z[i * KB + t] = 0.5 + (double)(hsh % 1000u) / 1000.0;
       }
+      // three passes; a pass's normalisation is applied as the next pass (or
+      // the copy out) reads the vector
+      double inv = 1.0;
       for (int pass = 0; pass < 3; ++pass) {
-        double cd = dg[0] - lam, cu = od[0], cu2 = 0.0, cr = Z[t];
+        // LU with partial pivoting of T - lam I; U1 keeps the reciprocal pivots.
+        // The next right-hand-side entry is read one step ahead.
+        double cd = dg[0] - lam, cu = od[0], cu2 = 0.0, cr = Z[t] * inv;
+        double znext = Z[KB + t];
         for (int i = 0; i < D - 1; ++i) {
           const double nl = od[i], nd = dg[i + 1] - lam, nu = (i + 1 < D - 1) ? od[i + 1] : 0.0;
-          const double nr = Z[(i + 1) * KB + t];
-          if (fabs(cd) >= fabs(nl)) {
-            if (cd == 0.0) cd = pe;
-            const double mlt = nl / cd;
-            U1[i * KB + t] = cd; U2[i * KB + t] = cu; U3[i * KB + t] = cu2; Z[i * KB + t] = cr;
+          const double nr = znext * inv;
+          if (i + 2 < D) znext = Z[(i + 2) * KB + t];
+          const bool keep = fabs(cd) >= fabs(nl);   // no row swap
+          if (keep && cd == 0.0) cd = pe;
+          const double rp = rcp_nr2(keep ? cd : nl);
+          if (keep) {
+            const double mlt = nl * rp;
+            U1[i * KB + t] = rp; U2[i * KB + t] = cu; U3[i * KB + t] = cu2; Z[i * KB + t] = cr;
             cd = nd - mlt * cu;
             cu = nu - mlt * cu2;
             cu2 = 0.0;
             cr = nr - mlt * cr;
           } else {
-            const double mlt = cd / nl;
-            U1[i * KB + t] = nl; U2[i * KB + t] = nd; U3[i * KB + t] = nu; Z[i * KB + t] = nr;
+            const double mlt = cd * rp;
+            U1[i * KB + t] = rp; U2[i * KB + t] = nd; U3[i * KB + t] = nu; Z[i * KB + t] = nr;
             const double ncd = cu - mlt * nd;
             const double ncu = cu2 - mlt * nu;
             cr = cr - mlt * nr;
@@ -392,24 +528,34 @@ __global__ __launch_bounds__(kFitThreads) void k_fit(int m, int kmax, double lam
           }
         }
         if (fabs(cd) < pe) cd = cd < 0.0 ? -pe : pe;
-        double y1 = cr / cd, y2 = 0.0;
+        double y1 = cr * rcp_nr2(cd), y2 = 0.0;
         double nrm = y1 * y1;
         Z[(D - 1) * KB + t] = y1;
+        // back substitution, the factors of the next row read one step ahead
+        double zn = Z[(D - 2) * KB + t], u1n = U1[(D - 2) * KB + t];
+        double u2n = U2[(D - 2) * KB + t], u3n = U3[(D - 2) * KB + t];
         for (int i = D - 2; i >= 0; --i) {
-          const double y = (Z[i * KB + t] - U2[i * KB + t] * y1 - U3[i * KB + t] * y2) / U1[i * KB + t];
+          const double zi = zn, u1 = u1n, u2 = u2n, u3 = u3n;
+          if (i > 0) {
+            zn = Z[(i - 1) * KB + t];
+            u1n = U1[(i - 1) * KB + t];
+            u2n = U2[(i - 1) * KB + t];
+            u3n = U3[(i - 1) * KB + t];
+          }
+          const double y = (zi - u2 * y1 - u3 * y2) * u1;
           Z[i * KB + t] = y;
           nrm += y * y;
           y2 = y1;
           y1 = y;
         }
-        const double inv = 1.0 / sqrt(nrm);
-        for (int i = 0; i < D; ++i) Z[i * KB + t] *= inv;
+        inv = 1.0 / sqrt(nrm);
       }
+      dots[t] = inv;   // the last pass's normalisation, applied on the copy out
     }
     __syncthreads();
     for (int idx = t; idx < D * nbt; idx += NT) {
       const int i = idx / nbt, r = idx % nbt;
-      Xg[(size_t)i * kmax + b0 + r] = Z[i * KB + r];
+      Xg[(size_t)i * kmax + b0 + r] = Z[i * KB + r] * dots[r];
     }
     __syncthreads();
   }
@@ -421,74 +567,114 @@ __global__ __launch_bounds__(kFitThreads) void k_fit(int m, int kmax, double lam
     X[e * PXK + r] = Xg[(size_t)e * kmax + r];
   }
   __syncthreads();
-  // ---- classical Gram-Schmidt, twice, in eigenvalue order
-  for (int j = 1; j < keff; ++j) {
-    for (int pass = 0; pass < 2; ++pass) {
-      for (int i0 = 0; i0 < j; i0 += NT / 8) {
-        const int i = i0 + t / 8, sub = t % 8;
-        double sacc = 0.0;
-        if (i < j)
-          for (int e = sub; e < D; e += 8) sacc += X[e * PXK + i] * X[e * PXK + j];
-        sacc += __shfl_xor(sacc, 1);
-        sacc += __shfl_xor(sacc, 2);
-        sacc += __shfl_xor(sacc, 4);
-        if (i < j && sub == 0) dots[i] = sacc;
-      }
-      __syncthreads();
-      for (int e = t; e < D; e += NT) {
-        double x = X[e * PXK + j];
-        for (int i = 0; i < j; ++i) x -= dots[i] * X[e * PXK + i];
-        X[e * PXK + j] = x;
-      }
-      __syncthreads();
-    }
-    double part = 0.0;
-    for (int e = t; e < D; e += NT) {
-      const double x = X[e * PXK + j];
-      part += x * x;
-    }
-    const double nrm = sqrt(wg_sum1(part, red2, slot));
-    for (int e = t; e < D; e += NT) X[e * PXK + j] /= nrm;
-    __syncthreads();
-  }
-  // ---- back-transform through the reflectors: X <- H_0 H_1 ... H_{D-3} X.
-  // The next reflector is fetched from the workspace while this one is applied.
-  for (int i = t; i < 2; i += NT) vv[i] = f.hv[(size_t)(D - 2 + i) * D + (D - 3)];
-  __syncthreads();
-  for (int k = D - 3; k >= 0; --k) {
-    const int L = D - k - 1;
-    double* vc = ((D - 3 - k) & 1) ? vn : vv;
-    double* vnx = ((D - 3 - k) & 1) ? vv : vn;
-    double nxt = 0.0;
-    if (k > 0 && t < L + 1) nxt = f.hv[(size_t)(k + t) * D + (k - 1)];
-    const double bk = beta[k];
-    for (int c0 = 0; c0 < keff; c0 += NT / 16) {
-      const int cc = c0 + t / 16, sub = t % 16;
-      double sacc = 0.0;
-      if (cc < keff && bk != 0.0) {
-        double s2[2] = {0.0, 0.0};
-        int i = sub;
-        for (; i + 16 < L; i += 32) {
-          s2[0] += vc[i] * X[(k + 1 + i) * PXK + cc];
-          s2[1] += vc[i + 16] * X[(k + 17 + i) * PXK + cc];
+  // ---- classical Gram-Schmidt, twice, in eigenvalue order, by wave 0 alone
+  // (wave-ordered LDS, no workgroup barriers): 16 lanes per column, rows
+  // part + 16 u; every lane group holds the column being orthogonalised and
+  // the four groups take the earlier columns in turn.
+  constexpr int NR = D / 16;
+  if (t < 64) {
+    const int g = t >> 4, part = t & 15;
+    for (int j = 1; j < keff; ++j) {
+      double xj[NR];
+#pragma unroll
+      for (int u = 0; u < NR; ++u) xj[u] = X[(part + 16 * u) * PXK + j];
+      for (int pass = 0; pass < 2; ++pass) {
+        double acc[NR];
+#pragma unroll
+        for (int u = 0; u < NR; ++u) acc[u] = 0.0;
+        // four earlier columns per lane group at a time: 16 per round
+        for (int i0 = 0; i0 < j; i0 += 16) {
+          double xc[4][NR], sc[4];
+          // unconditional loads (a valid column in place of a missing one),
+          // then the missing columns zeroed
+#pragma unroll
+          for (int q = 0; q < 4; ++q) {
+            const int ic = i0 + 4 * q + g;
+            const int icl = ic < j ? ic : 0;
+#pragma unroll
+            for (int u = 0; u < NR; ++u) {
+              const double x = X[(part + 16 * u) * PXK + icl];
+              xc[q][u] = ic < j ? x : 0.0;
+            }
+          }
+#pragma unroll
+          for (int q = 0; q < 4; ++q) {
+            sc[q] = 0.0;
+#pragma unroll
+            for (int u = 0; u < NR; ++u) sc[q] += xc[q][u] * xj[u];
+          }
+#pragma unroll
+          for (int q = 0; q < 4; ++q) sc[q] = sum16_f64(sc[q]);
+#pragma unroll
+          for (int u = 0; u < NR; ++u)
+#pragma unroll
+            for (int q = 0; q < 4; ++q) acc[u] += sc[q] * xc[q][u];
         }
-        for (; i < L; i += 16) s2[0] += vc[i] * X[(k + 1 + i) * PXK + cc];
-        sacc = s2[0] + s2[1];
+#pragma unroll
+        for (int u = 0; u < NR; ++u) {
+          acc[u] = pair_sum32_f64(pair_sum16_f64(acc[u]));
+          xj[u] -= acc[u];
+        }
       }
-      sacc += __shfl_xor(sacc, 1);
-      sacc += __shfl_xor(sacc, 2);
-      sacc += __shfl_xor(sacc, 4);
-      sacc += __shfl_xor(sacc, 8);
-      if (cc < keff && sub == 0) dots[cc] = bk * sacc;
+      double n2 = 0.0;
+#pragma unroll
+      for (int u = 0; u < NR; ++u) n2 += xj[u] * xj[u];
+      const double nrm = sqrt(sum16_f64(n2));
+      if (g == 0) {
+#pragma unroll
+        for (int u = 0; u < NR; ++u) X[(part + 16 * u) * PXK + j] = xj[u] / nrm;
+      }
+      // the next column reads this one: keep the LDS accesses in program order
+      __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
+    }
+  }
+  __syncthreads();
+  // ---- back-transform through the reflectors: X <- H_0 H_1 ... H_{D-3} X.
+  // Each wave applies every reflector to its own columns (16 lanes per column,
+  // rows part + 16 u, in registers); the reflectors are read from LDS, so the
+  // loop has no workgroup barriers.
+  {
+    constexpr int NPM = D / 32;   // column slots per lane (keff <= D)
+    const int lane = t & 63, wv = t >> 6, g = lane >> 4, part = lane & 15;
+    const int npass = (keff + 31) / 32;
+    double xr[NPM][NR];
+#pragma unroll
+    for (int pp = 0; pp < NPM; ++pp) {
+      const int c = 32 * pp + 4 * wv + g;
+#pragma unroll
+      for (int u = 0; u < NR; ++u) xr[pp][u] = c < keff ? X[(part + 16 * u) * PXK + c] : 0.0;
     }
     __syncthreads();
-    if (bk != 0.0) {
-      for (int cc = t & 31; cc < keff; cc += 32) {
-        const double dc = dots[cc];
-        for (int i = t >> 5; i < L; i += NT / 32) X[(k + 1 + i) * PXK + cc] -= dc * vc[i];
+    double* HV = big;   // reflector k at HV[k * D + e]
+    for (int idx = t; idx < (D - 2) * D; idx += NT) HV[idx] = f.hv[idx];
+    __syncthreads();
+    for (int k = D - 3; k >= 0; --k) {
+      const double bk = beta[k];
+      if (bk == 0.0) continue;
+      double vr[NR];
+#pragma unroll
+      for (int u = 0; u < NR; ++u) vr[u] = HV[k * D + part + 16 * u];
+#pragma unroll
+      for (int pp = 0; pp < NPM; ++pp) {
+        if (pp < npass) {
+          double s = 0.0;
+#pragma unroll
+          for (int u = 0; u < NR; ++u) s += vr[u] * xr[pp][u];
+          const double dc = bk * sum16_f64(s);
+#pragma unroll
+          for (int u = 0; u < NR; ++u) xr[pp][u] -= dc * vr[u];
+        }
       }
     }
-    if (k > 0 && t < L + 1) vnx[t] = nxt;
+    __syncthreads();
+#pragma unroll
+    for (int pp = 0; pp < NPM; ++pp) {
+      const int c = 32 * pp + 4 * wv + g;
+      if (c < keff) {
+#pragma unroll
+        for (int u = 0; u < NR; ++u) X[(part + 16 * u) * PXK + c] = xr[pp][u];
+      }
+    }
     __syncthreads();
   }
   for (int idx = t; idx < D * keff; idx += NT) {
@@ -513,6 +699,8 @@ __global__ __launch_bounds__(kFitThreads) void k_fit(int m, int kmax, double lam
       for (int u = 0; u < 4; ++u)
 #pragma unroll
         for (int v = 0; v < 4; ++v) acc[u][v] = 0.0;
+      // unrolled so that many workspace loads are in flight at once
+#pragma unroll 8
       for (int e = 0; e < D; ++e) {
         double xr[4], uc[4];
 #pragma unroll
@@ -560,6 +748,7 @@ __global__ __launch_bounds__(kFitThreads) void k_fit(int m, int kmax, double lam
     const double* col = isC ? f.sig : f.rhs;
     const int pitch = isC ? keff : kmax;
     double s2[2] = {0.0, 0.0};
+#pragma unroll 4
     for (int e = 0; e < D; e += 2) {
       s2[0] += f.hv[(size_t)e * keff + a] * col[(size_t)e * pitch + b];
       s2[1] += f.hv[(size_t)(e + 1) * keff + a] * col[(size_t)(e + 1) * pitch + b];
@@ -637,10 +826,7 @@ __global__ __launch_bounds__(kFitThreads) void k_fit(int m, int kmax, double lam
           }
           sacc = s2[0] + s2[1];
         }
-        sacc += __shfl_xor(sacc, 1);
-        sacc += __shfl_xor(sacc, 2);
-        sacc += __shfl_xor(sacc, 4);
-        sacc += __shfl_xor(sacc, 8);
+        sacc = sum16_f64(sacc);
         if (on && part == 0) rz[(size_t)i * keff + cc] = (rz[(size_t)i * keff + cc] - sacc) * rdiag[i];
         if (rhs_lds) __builtin_amdgcn_wave_barrier();
         else __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "workgroup");
@@ -656,10 +842,7 @@ __global__ __launch_bounds__(kFitThreads) void k_fit(int m, int kmax, double lam
           }
           sacc = s2[0] + s2[1];
         }
-        sacc += __shfl_xor(sacc, 1);
-        sacc += __shfl_xor(sacc, 2);
-        sacc += __shfl_xor(sacc, 4);
-        sacc += __shfl_xor(sacc, 8);
+        sacc = sum16_f64(sacc);
         if (on && part == 0) rz[(size_t)i * keff + cc] = (rz[(size_t)i * keff + cc] - sacc) * rdiag[i];
         if (rhs_lds) __builtin_amdgcn_wave_barrier();
         else __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "workgroup");
@@ -672,6 +855,7 @@ __global__ __launch_bounds__(kFitThreads) void k_fit(int m, int kmax, double lam
     const int r = idx / keff, cc = idx % keff;
     double v = 0.0;
     if (r < D) {
+#pragma unroll 8
       for (int a = 0; a < keff; ++a) v += f.hv[(size_t)r * keff + a] * rz[(size_t)a * keff + cc];
     } else {
       double gb = 0.0;
