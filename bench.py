@@ -274,7 +274,7 @@ def error_summary(p, b, ref, rn, mask):
     import torch
     D = p.head_dim
     with torch.no_grad():
-        S_tok = torch.empty_like(b.S)
+        S_tok = torch.empty_like(b.S, dtype=torch.float32)
         S_tok.scatter_(1, b.query_perm.long()[:, :, None].expand(-1, -1, D), b.S.float())
         e = ((b.O.float() - ref).norm(dim=2) / rn)[mask].double().cpu().numpy()
         e0 = ((S_tok - ref).norm(dim=2) / rn)[mask].double().cpu().numpy()
@@ -294,8 +294,8 @@ def residual_r2(p, b, ref, mask):
     import torch
     D = p.head_dim
     with torch.no_grad():
-        S_tok = torch.empty_like(b.S)
-        S_tok.scatter_(1, b.query_perm.long()[:, :, None].expand(-1, -1, D), b.S)
+        S_tok = torch.empty_like(b.S, dtype=torch.float32)
+        S_tok.scatter_(1, b.query_perm.long()[:, :, None].expand(-1, -1, D), b.S.float())
         num = den = 0.0
         for h in range(p.heads):
             m = mask[h]

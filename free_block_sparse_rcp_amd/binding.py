@@ -71,8 +71,8 @@ def load(path: Optional[str] = None) -> ctypes.CDLL:
     pp = ctypes.POINTER(CParams)
     lib.sparsepr_partition.argtypes = [pp] + [_c_p] * 14 + [_c_p, _c_sz, _c_p]
     lib.sparsepr_route.argtypes = [pp] + [_c_p] * 13 + [_c_p, _c_sz, _c_p]
-    lib.sparsepr_attend.argtypes = [pp] + [_c_p] * 10 + [_c_p]
-    lib.sparsepr_attend_subset.argtypes = [pp] + [_c_p] * 10 + [_c_i32, _c_p]
+    lib.sparsepr_attend.argtypes = [pp] + [_c_p] * 11 + [_c_p]
+    lib.sparsepr_attend_subset.argtypes = [pp] + [_c_p] * 11 + [_c_i32, _c_p]
     lib.sparsepr_probe_fit.argtypes = [pp] + [_c_p] * 10 + [_c_p, _c_sz, _c_p]
     lib.sparsepr_apply.argtypes = [pp] + [_c_p] * 7 + [_c_p, _c_sz, _c_p]
     lib.sparsepr_apply_noalloc.argtypes = [pp] + [_c_p] * 7 + [_c_p]
@@ -83,7 +83,7 @@ def load(path: Optional[str] = None) -> ctypes.CDLL:
                  "sparsepr_probe_fit", "sparsepr_apply", "sparsepr_apply_noalloc",
                  "sparsepr_dense_attention"):
         getattr(lib, name).restype = _c_i32
-    if lib.sparsepr_abi_version() != 1:
+    if lib.sparsepr_abi_version() != 2:
         raise RuntimeError("libsparsepr ABI version mismatch")
     _LIB = lib
     return lib
@@ -163,6 +163,7 @@ class Buffers:
     block_groups: torch.Tensor
     executed_pairs: torch.Tensor
     S: torch.Tensor
+    S_probe: torch.Tensor
     lse: torch.Tensor
     O_probe: torch.Tensor
     U: torch.Tensor
@@ -196,7 +197,8 @@ def alloc_buffers(p: Params, device) -> Buffers:
         query_perm=torch.empty(H, N, **i32), block_ptr=torch.empty(H, nb + 1, **i32),
         block_groups=torch.empty(H, nb * G, **i32),
         executed_pairs=torch.empty(H, dtype=torch.int64, device=device),
-        S=torch.empty(H, N, D, **f32), lse=torch.empty(H, N, **f32),
+        S=torch.empty(H, N, D, dtype=dt, device=device),
+        S_probe=torch.empty(H, max(p.n_probes, 1), D, **f32), lse=torch.empty(H, N, **f32),
         O_probe=torch.empty(H, max(p.n_probes, 1), D, **f32),
         U=torch.empty(H, D, max(p.rank, 1), **f32),
         Theta=torch.empty(H, D + 1, max(p.rank, 1), **f32),
@@ -245,7 +247,8 @@ def attend(p: Params, Q, scale, b: Buffers, subset: int = BLOCKS_ALL) -> None:
     lib = load()
     cp = c_params(p)
     args = (ctypes.byref(cp), _ptr(Q), _ptr(b.Kp), _ptr(b.Vp), _ptr(scale), _ptr(b.group_off),
-            _ptr(b.query_perm), _ptr(b.block_ptr), _ptr(b.block_groups), _ptr(b.S), _ptr(b.lse))
+            _ptr(b.query_perm), _ptr(b.block_ptr), _ptr(b.block_groups), _ptr(b.S),
+            _ptr(b.S_probe), _ptr(b.lse))
     if subset == BLOCKS_ALL:
         _check(lib.sparsepr_attend(*args, _stream(Q.device)))
     else:
@@ -258,8 +261,8 @@ def probe_fit(p: Params, Q, scale, b: Buffers, K=None, V=None) -> None:
     K = b.Kp if K is None else K
     V = b.Vp if V is None else V
     _check(lib.sparsepr_probe_fit(
-        ctypes.byref(cp), _ptr(Q), _ptr(K), _ptr(V), _ptr(scale), _ptr(b.query_perm), _ptr(b.S),
-        _ptr(b.O_probe), _ptr(b.U), _ptr(b.Theta), _ptr(b.rank_eff), _ptr(b.workspace),
+        ctypes.byref(cp), _ptr(Q), _ptr(K), _ptr(V), _ptr(scale), _ptr(b.query_perm),
+        _ptr(b.S_probe), _ptr(b.O_probe), _ptr(b.U), _ptr(b.Theta), _ptr(b.rank_eff), _ptr(b.workspace),
         b.workspace.numel(), _stream(Q.device)))
 
 

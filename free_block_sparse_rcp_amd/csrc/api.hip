@@ -340,8 +340,8 @@ int32_t sparsepr_route(const sparsepr_params* params, const void* Q, const float
 int32_t sparsepr_attend_subset(const sparsepr_params* params, const void* Q, const void* Kp,
                                const void* Vp, const float* scale, const int32_t* group_off,
                                const int32_t* query_perm, const int32_t* block_ptr,
-                               const int32_t* block_groups, float* S_out, float* lse,
-                               int32_t subset, void* stream) {
+                               const int32_t* block_groups, void* S_out, float* S_probe,
+                               float* lse, int32_t subset, void* stream) {
   Dims d;
   int32_t s = make_dims(params, true, &d);
   if (s != SPARSEPR_OK) return s;
@@ -356,6 +356,7 @@ int32_t sparsepr_attend_subset(const sparsepr_params* params, const void* Q, con
   SPR_REQUIRE(block_ptr, "block_ptr");
   SPR_REQUIRE(block_groups, "block_groups");
   SPR_REQUIRE(S_out, "S_out");
+  if (d.m > 0) SPR_REQUIRE(S_probe, "S_probe");
   SPR_REQUIRE(lse, "lse");
   AttnArgs a{};
   a.Q = Q;
@@ -374,6 +375,7 @@ int32_t sparsepr_attend_subset(const sparsepr_params* params, const void* Q, con
   a.block_groups = block_groups;
   a.group_off = group_off;
   a.out = S_out;
+  a.sprobe = d.m > 0 ? S_probe : nullptr;
   a.lse = lse;
   a.subset = subset;
   return hip_status(launch_attention(d, ATTN_SPARSE, a, static_cast<hipStream_t>(stream)),
@@ -383,9 +385,10 @@ int32_t sparsepr_attend_subset(const sparsepr_params* params, const void* Q, con
 int32_t sparsepr_attend(const sparsepr_params* params, const void* Q, const void* Kp,
                         const void* Vp, const float* scale, const int32_t* group_off,
                         const int32_t* query_perm, const int32_t* block_ptr,
-                        const int32_t* block_groups, float* S_out, float* lse, void* stream) {
+                        const int32_t* block_groups, void* S_out, float* S_probe, float* lse,
+                        void* stream) {
   return sparsepr_attend_subset(params, Q, Kp, Vp, scale, group_off, query_perm, block_ptr,
-                                block_groups, S_out, lse, SPARSEPR_BLOCKS_ALL, stream);
+                                block_groups, S_out, S_probe, lse, SPARSEPR_BLOCKS_ALL, stream);
 }
 
 int32_t sparsepr_support_stats(const sparsepr_params* params, int32_t head, const void* Q,
@@ -457,7 +460,7 @@ int32_t sparsepr_support_stats(const sparsepr_params* params, int32_t head, cons
 
 int32_t sparsepr_probe_fit(const sparsepr_params* params, const void* Q, const void* K,
                            const void* V, const float* scale, const int32_t* query_perm,
-                           const float* S_out, float* O_probe, float* U, float* Theta,
+                           const float* S_probe, float* O_probe, float* U, float* Theta,
                            int32_t* rank_eff, void* workspace, size_t workspace_bytes,
                            void* stream) {
   Dims d;
@@ -470,7 +473,7 @@ int32_t sparsepr_probe_fit(const sparsepr_params* params, const void* Q, const v
     SPR_REQUIRE(V, "V");
     SPR_REQUIRE(scale, "scale");
     SPR_REQUIRE(query_perm, "query_perm");
-    SPR_REQUIRE(S_out, "S_out");
+    SPR_REQUIRE(S_probe, "S_probe");
     SPR_REQUIRE(O_probe, "O_probe");
   }
   if (d.k > 0) {
@@ -503,7 +506,7 @@ int32_t sparsepr_probe_fit(const sparsepr_params* params, const void* Q, const v
   }
   if (e == hipSuccess) {
     if (d.m > 0 && d.k > 0) {
-      e = launch_fit(d, S_out, O_probe, U, Theta, rank_eff, ws + L.fit, st);
+      e = launch_fit(d, S_probe, O_probe, U, Theta, rank_eff, ws + L.fit, st);
     } else {
       e = launch_fill_i32(rank_eff, (size_t)d.H, 0, st);
       if (e == hipSuccess && d.k > 0) e = launch_fill_f32(U, (size_t)d.H * d.D * d.k, 0.f, st);
@@ -514,7 +517,7 @@ int32_t sparsepr_probe_fit(const sparsepr_params* params, const void* Q, const v
   return hip_status(e, "sparsepr_probe_fit");
 }
 
-int32_t sparsepr_apply(const sparsepr_params* params, const float* S_out,
+int32_t sparsepr_apply(const sparsepr_params* params, const void* S_out,
                        const int32_t* query_perm, const float* O_probe, const float* U,
                        const float* Theta, const int32_t* rank_eff, void* O, void* workspace,
                        size_t workspace_bytes, void* stream) {
@@ -536,7 +539,7 @@ int32_t sparsepr_apply(const sparsepr_params* params, const float* S_out,
                     "sparsepr_apply");
 }
 
-int32_t sparsepr_apply_noalloc(const sparsepr_params* params, const float* S_out,
+int32_t sparsepr_apply_noalloc(const sparsepr_params* params, const void* S_out,
                                const int32_t* query_perm, const float* O_probe, const float* U,
                                const float* Theta, const int32_t* rank_eff, void* O,
                                void* stream) {

@@ -17,16 +17,6 @@ namespace spr {
 constexpr int kApplyRows = 64;
 constexpr int kApplyChunk = 32;
 
-__device__ __forceinline__ int probe_index(int pos, int N, int m) {
-  if (m <= 0) return -1;
-  const int64_t c = ((int64_t)pos * m) / N;
-  for (int64_t i = c - 1; i <= c + 1; ++i) {
-    if (i < 0 || i >= m) continue;
-    if ((int)(((2 * i + 1) * N) / (2LL * m)) == pos) return (int)i;
-  }
-  return -1;
-}
-
 template <bool BF16, int D>
 __global__ __launch_bounds__(256) void k_apply(const float* S, const int32_t* query_perm,
                                                const float* O_probe, const float* U,
@@ -152,12 +142,12 @@ __global__ __launch_bounds__(256) void k_apply(const float* S, const int32_t* qu
 // one matrix per head, W = Theta U^T ((d+1) x d): o = s + s W[:d] + W[d].
 // k_apply_weights forms W^T once per head (fp32, stored as bf16 hi + lo parts)
 // and the bias W[d]; k_apply_mfma copies them into LDS and runs the product
-// O^T = W^T S^T as v_mfma_f32_32x32x16_bf16 with S split into hi + lo too
-// (hi*hi + lo*hi + hi*lo; the dropped lo*lo term is ~2^-16 relative), so the
-// correction keeps near-fp32 accuracy. Each wave takes 32 query positions at a
-// time; the copy of s in the output layout for the final sum comes from a
-// lane-half swap of the loaded values, and the output tile is staged in LDS so
-// that every row (token order) is written whole.
+// O^T = W^T S^T as v_mfma_f32_32x32x16_bf16 on the bf16 sparse output
+// (hi*s + lo*s: the correction keeps near-fp32 accuracy). Each wave takes 32
+// query positions at a time, with the rows of its next two tiles in flight;
+// the copy of s in the output layout for the final sum comes from lane-half
+// swaps of the loaded rows, and the output tile is staged in LDS so that every
+// row (token order) is written whole.
 constexpr int kApplyTilesPerWg = 128;  // most 32-row tiles per workgroup
 constexpr int kApplyWaves = 8;
 
@@ -217,7 +207,7 @@ __global__ __launch_bounds__(256) void k_apply_weights(const float* U, const flo
 }
 
 template <int D>
-__global__ __launch_bounds__(kApplyWaves * 64) void k_apply_mfma(const float* S, const int32_t* query_perm,
+__global__ __launch_bounds__(kApplyWaves * 64) void k_apply_mfma(const uint16_t* S, const int32_t* query_perm,
                                                     const float* O_probe, const uint16_t* wt,
                                                     const float* bias, int N, int m,
                                                     int wg_per_head, uint16_t* O) {
@@ -225,16 +215,17 @@ __global__ __launch_bounds__(kApplyWaves * 64) void k_apply_mfma(const float* S,
   constexpr int NKK = D / 16, NDT = D / 32;
   constexpr int CPR = D / 8;           // 16-byte chunks per row
   constexpr int OP = D + 8;            // bf16 elements per staged output row
+  constexpr int NW = kApplyWaves;
   __shared__ __attribute__((aligned(16))) uint16_t wt_hi[D * WP];
   __shared__ __attribute__((aligned(16))) uint16_t wt_lo[D * WP];
   __shared__ float wbias[D];
-  __shared__ __attribute__((aligned(16))) uint16_t ostage[kApplyWaves][32 * OP];
+  __shared__ __attribute__((aligned(16))) uint16_t ostage[NW][32 * OP];
   const int h = blockIdx.x / wg_per_head, part = blockIdx.x % wg_per_head;
   const int t = threadIdx.x, lane = t & 63, hl = lane >> 5, ql = lane & 31;
   const int w = __builtin_amdgcn_readfirstlane(t >> 6);
   {
     const uint16_t* src = wt + (size_t)h * 2 * D * D;
-    for (int i = t; i < 2 * D * CPR; i += kApplyWaves * 64) {
+    for (int i = t; i < 2 * D * CPR; i += NW * 64) {
       const int arr = i / (D * CPR), rem = i % (D * CPR);
       const int r = rem / CPR, c = rem % CPR;
       const u32x4 v = *reinterpret_cast<const u32x4*>(src + (size_t)arr * D * D + r * D + 8 * c);
@@ -247,67 +238,29 @@ __global__ __launch_bounds__(kApplyWaves * 64) void k_apply_mfma(const float* S,
   const int ntile = (N + 31) / 32;
   const int per = (ntile + wg_per_head - 1) / wg_per_head;
   const int t0 = part * per, t1 = min(ntile, t0 + per);
-  const float* Sh = S + (size_t)h * N * D;
+  const uint16_t* Sh = S + (size_t)h * N * D;
   uint16_t* Oh = O + (size_t)h * N * D;
   uint16_t* stg = ostage[w];
-  // Raw s of the wave's next tile: lane (ql, hl) holds columns 16 kk + 8 hl ..
-  // + 7 of its row. The loads of tile t + 8 are issued while tile t is
-  // computed: the first half once tile t's values are converted, the second
-  // once half of tile t's output slices no longer need their s.
-  f32x4 xr[2 * NKK];
-  // half 0: columns of k-steps [0, NKK/2), half 1: the rest
-  auto load_tile = [&](int tile, int half) {
+  // A tile's s, as the MFMA operand: lane (ql, hl) holds columns 16 kk + 8 hl
+  // .. + 7 of its row, one 16-byte load per k-step.
+  auto load_tile = [&](u32x4 (&buf)[NKK], int tile) {
     const int pos = tile * 32 + ql;
     const bool ok = pos < N;
-    const float* srow = Sh + (size_t)(ok ? pos : 0) * D;
+    const uint16_t* srow = Sh + (size_t)(ok ? pos : 0) * D;
 #pragma unroll
-    for (int kk = half * NKK / 2; kk < (half + 1) * NKK / 2; ++kk) {
-      f32x4 x0 = {0.f, 0.f, 0.f, 0.f}, x1 = x0;
-      if (ok) {
-        x0 = *reinterpret_cast<const f32x4*>(srow + 16 * kk + 8 * hl);
-        x1 = *reinterpret_cast<const f32x4*>(srow + 16 * kk + 8 * hl + 4);
-      }
-      xr[2 * kk] = x0;
-      xr[2 * kk + 1] = x1;
+    for (int kk = 0; kk < NKK; ++kk) {
+      u32x4 v = {0u, 0u, 0u, 0u};
+      if (ok) v = *reinterpret_cast<const u32x4*>(srow + 16 * kk + 8 * hl);
+      buf[kk] = v;
     }
   };
-  if (t0 + w < t1) {
-    load_tile(t0 + w, 0);
-    load_tile(t0 + w, 1);
-  }
-  for (int tile = t0 + w; tile < t1; tile += kApplyWaves) {
+  // One tile from buf; then buf takes the tile three rounds ahead.
+  auto run_tile = [&](u32x4 (&buf)[NKK], int tile) {
     const int pos = tile * 32 + ql;
     const bool valid = pos < N;
     // token of this lane's row, read early; the store loop takes each row's
     // token from the lane that owns the row
     const int tok = valid ? clamp_idx(query_perm[(size_t)h * N + pos], N) : 0;
-    bf16x8 shi[NKK], slo[NKK];
-    // se[kk] / so[kk]: s in the output layout for column chunks q = 2 (kk % 2) and
-    // q = 2 (kk % 2) + 1 of tile nt = kk / 2, from one lane-half swap of the loaded
-    // values (lanes l and l ^ 32 hold the two halves of a 16-column slice)
-    f32x4 se[NKK], so[NKK];
-#pragma unroll
-    for (int kk = 0; kk < NKK; ++kk) {
-      const f32x4 x0 = xr[2 * kk], x1 = xr[2 * kk + 1];
-#pragma unroll
-      for (int u = 0; u < 4; ++u) {
-        float lo, hi;
-        lane_half_swap(x0[u], x1[u], lo, hi);
-        se[kk][u] = lo;
-        so[kk][u] = hi;
-      }
-#pragma unroll
-      for (int u = 0; u < 4; ++u) {
-        const __bf16 h0 = static_cast<__bf16>(x0[u]);
-        const __bf16 h1 = static_cast<__bf16>(x1[u]);
-        shi[kk][u] = h0;
-        shi[kk][4 + u] = h1;
-        slo[kk][u] = static_cast<__bf16>(x0[u] - static_cast<float>(h0));
-        slo[kk][4 + u] = static_cast<__bf16>(x1[u] - static_cast<float>(h1));
-      }
-    }
-    const bool has_next = tile + kApplyWaves < t1;
-    if (has_next) load_tile(tile + kApplyWaves, 0);
     const int pi = valid ? probe_index(pos, N, m) : -1;
     // W fragments are re-read from LDS every tile: kept opaque so that the
     // compiler does not hoist all of them into registers (occupancy)
@@ -324,32 +277,50 @@ __global__ __launch_bounds__(kApplyWaves * 64) void k_apply_mfma(const float* S,
       for (int kk = 0; kk < NKK; ++kk) {
         const bf16x8 ahi = *reinterpret_cast<const bf16x8*>(whr + 16 * kk);
         const bf16x8 alo = *reinterpret_cast<const bf16x8*>(wlr + 16 * kk);
-        acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ahi, shi[kk], acc, 0, 0, 0);
-        acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(alo, shi[kk], acc, 0, 0, 0);
-        acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ahi, slo[kk], acc, 0, 0, 0);
+        const bf16x8 sv = __builtin_bit_cast(bf16x8, buf[kk]);
+        acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ahi, sv, acc, 0, 0, 0);
+        acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(alo, sv, acc, 0, 0, 0);
       }
-      // the second half of the next tile, once the first output slices' s are used
-      if (nt == NDT / 2 && has_next) load_tile(tile + kApplyWaves, 1);
       if (!valid) continue;
 #pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        const int d0 = 32 * nt + 8 * q + 4 * hl;
-        f32x4 v;
-        if (pi >= 0) {
-          v = *reinterpret_cast<const f32x4*>(O_probe + ((size_t)h * m + pi) * D + d0);
-        } else {
-          v = (q & 1) ? so[2 * nt + (q >> 1)] : se[2 * nt + (q >> 1)];
+      for (int a = 0; a < 2; ++a) {
+        // s of output rows 8 q + 4 hl + u, q = 2 a + b, from k-step 2 nt + a:
+        // lane hl keeps or receives the dwords that hold them (b = 0: lo)
+        // (scalar copies first: a __builtin_bit_cast of a vector element
+        // names element 0 whichever element is written)
+        const u32x4 x = buf[2 * nt + a];
+        const uint32_t x0 = x[0], x1 = x[1], x2 = x[2], x3 = x[3];
+        float lo0, hi0, lo1, hi1;
+        lane_half_swap(__builtin_bit_cast(float, x0), __builtin_bit_cast(float, x2), lo0, hi0);
+        lane_half_swap(__builtin_bit_cast(float, x1), __builtin_bit_cast(float, x3), lo1, hi1);
 #pragma unroll
-          for (int u = 0; u < 4; ++u) v[u] += acc[4 * q + u] + wbias[d0 + u];
+        for (int b = 0; b < 2; ++b) {
+          const int q = 2 * a + b;
+          const int d0 = 32 * nt + 8 * q + 4 * hl;
+          f32x4 v;
+          if (pi >= 0) {
+            v = *reinterpret_cast<const f32x4*>(O_probe + ((size_t)h * m + pi) * D + d0);
+          } else {
+            const uint32_t p0 = __builtin_bit_cast(uint32_t, b ? hi0 : lo0);
+            const uint32_t p1 = __builtin_bit_cast(uint32_t, b ? hi1 : lo1);
+            const float sv4[4] = {__builtin_bit_cast(float, p0 << 16),
+                                  __builtin_bit_cast(float, p0 & 0xffff0000u),
+                                  __builtin_bit_cast(float, p1 << 16),
+                                  __builtin_bit_cast(float, p1 & 0xffff0000u)};
+#pragma unroll
+            for (int u = 0; u < 4; ++u) v[u] = sv4[u] + acc[4 * q + u] + wbias[d0 + u];
+          }
+          const f32x2 f0 = {v[0], v[1]};
+          const f32x2 f1 = {v[2], v[3]};
+          const bf16x2 b0 = __builtin_convertvector(f0, bf16x2);
+          const bf16x2 b1 = __builtin_convertvector(f1, bf16x2);
+          const bf16x4 bv = {b0[0], b0[1], b1[0], b1[1]};
+          *reinterpret_cast<bf16x4*>(stg + ql * OP + d0) = bv;
         }
-        const f32x2 f0 = {v[0], v[1]};
-        const f32x2 f1 = {v[2], v[3]};
-        const bf16x2 b0 = __builtin_convertvector(f0, bf16x2);
-        const bf16x2 b1 = __builtin_convertvector(f1, bf16x2);
-        const bf16x4 bv = {b0[0], b0[1], b1[0], b1[1]};
-        *reinterpret_cast<bf16x4*>(stg + ql * OP + d0) = bv;
       }
     }
+    // every use of buf is issued: it takes the tile three rounds ahead
+    if (tile + 3 * NW < t1) load_tile(buf, tile + 3 * NW);
     // whole output rows from the wave's staged tile: 16-byte pieces, one row per D/8 lanes
     __builtin_amdgcn_wave_barrier();
     constexpr int LPR = D / 8;          // lanes per row
@@ -365,10 +336,22 @@ __global__ __launch_bounds__(kApplyWaves * 64) void k_apply_mfma(const float* S,
       }
     }
     __builtin_amdgcn_wave_barrier();
+  };
+  // three register buffers in rotation: tiles w, w + 8 and w + 16 of this
+  // workgroup's range are in flight before the first is used
+  u32x4 b0[NKK], b1[NKK], b2[NKK];
+  const int tw = t0 + w;
+  if (tw < t1) load_tile(b0, tw);
+  if (tw + NW < t1) load_tile(b1, tw + NW);
+  if (tw + 2 * NW < t1) load_tile(b2, tw + 2 * NW);
+  for (int tile = tw; tile < t1; tile += 3 * NW) {
+    run_tile(b0, tile);
+    if (tile + NW < t1) run_tile(b1, tile + NW);
+    if (tile + 2 * NW < t1) run_tile(b2, tile + 2 * NW);
   }
 }
 
-hipError_t launch_apply(const Dims& d, const float* S_out, const int32_t* query_perm,
+hipError_t launch_apply(const Dims& d, const void* S_out, const int32_t* query_perm,
                         const float* O_probe, const float* U, const float* Theta,
                         const int32_t* rank_eff, void* O, char* ws, hipStream_t st) {
   if (d.bf16) {
@@ -385,20 +368,22 @@ hipError_t launch_apply(const Dims& d, const float* S_out, const int32_t* query_
     int wgph = std::max(base, rounds * slots / d.H);
     wgph = std::min(wgph, std::max(base, (ntile + kApplyWaves - 1) / kApplyWaves));  // a tile per wave at least
     uint16_t* Ob = static_cast<uint16_t*>(O);
+    const uint16_t* Sb = static_cast<const uint16_t*>(S_out);
     if (d.D == 128) {
       k_apply_weights<128><<<d.H, 256, 0, st>>>(U, Theta, rank_eff, d.k, wt, bias);
-      k_apply_mfma<128><<<d.H * wgph, kApplyWaves * 64, 0, st>>>(S_out, query_perm, O_probe, wt, bias, d.N,
+      k_apply_mfma<128><<<d.H * wgph, kApplyWaves * 64, 0, st>>>(Sb, query_perm, O_probe, wt, bias, d.N,
                                                     d.m, wgph, Ob);
     } else {
       k_apply_weights<64><<<d.H, 256, 0, st>>>(U, Theta, rank_eff, d.k, wt, bias);
-      k_apply_mfma<64><<<d.H * wgph, kApplyWaves * 64, 0, st>>>(S_out, query_perm, O_probe, wt, bias, d.N,
+      k_apply_mfma<64><<<d.H * wgph, kApplyWaves * 64, 0, st>>>(Sb, query_perm, O_probe, wt, bias, d.N,
                                                    d.m, wgph, Ob);
     }
     return hipGetLastError();
   }
   const dim3 grid((d.N + kApplyRows - 1) / kApplyRows, d.H);
 #define SPR_APPLY(B, DD)                                                                   \
-  k_apply<B, DD><<<grid, 256, 0, st>>>(S_out, query_perm, O_probe, U, Theta, rank_eff, d.N, \
+  k_apply<B, DD><<<grid, 256, 0, st>>>(static_cast<const float*>(S_out), query_perm, O_probe, \
+                                        U, Theta, rank_eff, d.N, \
                                         d.m, d.k, O)
   if (d.D == 128) SPR_APPLY(false, 128); else SPR_APPLY(false, 64);
 #undef SPR_APPLY

@@ -486,18 +486,8 @@ void k_attn_mfma(AttnArgs a) {
         *reinterpret_cast<f32x4*>(op + d0) = v;
       }
     if (hl == 0) a.lsepart[((size_t)it.h * a.nsplit + it.sp) * a.m + qpos] = lse;
-  } else if (MODE == ATTN_SPARSE) {
-    float* out = static_cast<float*>(a.out) + hoff + (size_t)qpos * D;
-#pragma unroll
-    for (int dt = 0; dt < NDT; ++dt)
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const int d0 = 32 * dt + 8 * j + 4 * hl;
-        const f32x4 v = {acc_o[dt][4 * j] * inv, acc_o[dt][4 * j + 1] * inv,
-                         acc_o[dt][4 * j + 2] * inv, acc_o[dt][4 * j + 3] * inv};
-        *reinterpret_cast<f32x4*>(out + d0) = v;
-      }
   } else {
+    // bf16 rows: S_out at the query position (sparse), O at the token (dense)
     uint16_t* out = static_cast<uint16_t*>(a.out) + hoff + (size_t)qpos * D;
 #pragma unroll
     for (int dt = 0; dt < NDT; ++dt)
@@ -511,6 +501,20 @@ void k_attn_mfma(AttnArgs a) {
         const bf16x4 bv = {b0[0], b0[1], b1[0], b1[1]};
         *reinterpret_cast<bf16x4*>(out + d0) = bv;
       }
+    // a probe position's row also goes out unrounded, for the fit
+    const int pi = MODE == ATTN_SPARSE && a.sprobe != nullptr ? probe_index(qpos, a.N, a.m) : -1;
+    if (pi >= 0) {
+      float* sp = a.sprobe + ((size_t)it.h * a.m + pi) * D;
+#pragma unroll
+      for (int dt = 0; dt < NDT; ++dt)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          const int d0 = 32 * dt + 8 * j + 4 * hl;
+          const f32x4 v = {acc_o[dt][4 * j] * inv, acc_o[dt][4 * j + 1] * inv,
+                           acc_o[dt][4 * j + 2] * inv, acc_o[dt][4 * j + 3] * inv};
+          *reinterpret_cast<f32x4*>(sp + d0) = v;
+        }
+    }
   }
   if (MODE != ATTN_PROBE) {
     if (hl == 0 && a.lse != nullptr) a.lse[(size_t)it.h * a.N + qpos] = lse;
@@ -631,6 +635,13 @@ __global__ __launch_bounds__(256) void k_attn_valu(AttnArgs a, int BQ) {
 #pragma unroll
     for (int u = 0; u < DU; ++u) out[4 * u + qq] = o[u] * inv;
     if (qq == 0 && a.lse != nullptr) a.lse[(size_t)it.h * a.N + qpos] = lse;
+    // a probe position's row also goes to the fit's copy
+    const int pi = MODE == ATTN_SPARSE && a.sprobe != nullptr ? probe_index(qpos, a.N, a.m) : -1;
+    if (pi >= 0) {
+      float* sp = a.sprobe + ((size_t)it.h * a.m + pi) * D;
+#pragma unroll
+      for (int u = 0; u < DU; ++u) sp[4 * u + qq] = o[u] * inv;
+    }
   }
 }
 

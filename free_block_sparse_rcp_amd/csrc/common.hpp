@@ -58,6 +58,18 @@ __device__ __forceinline__ uint32_t float_order_bits(float f) {
 // Key that sorts floats in DESCENDING order when sorted ascending.
 __device__ __forceinline__ uint32_t float_desc_bits(float f) { return ~float_order_bits(f); }
 
+// Index i of the probe at query position pos (probe i sits at
+// floor((2 i + 1) N / (2 m))), or -1 when pos holds no probe.
+__device__ __forceinline__ int probe_index(int pos, int N, int m) {
+  if (m <= 0) return -1;
+  const int64_t c = ((int64_t)pos * m) / N;
+  for (int64_t i = c - 1; i <= c + 1; ++i) {
+    if (i < 0 || i >= m) continue;
+    if ((int)(((2 * i + 1) * N) / (2LL * m)) == pos) return (int)i;
+  }
+  return -1;
+}
+
 // Workgroups are dispatched round-robin over the 8 XCDs; this maps the
 // dispatch id to a logical id so that each XCD receives one contiguous run of
 // logical work items (neighbouring blocks share keys, so they share its L2).
@@ -70,9 +82,9 @@ __device__ __forceinline__ int xcd_remap(int w, int total) {
 // v_permlane32_swap on two floats: lo gets a in lanes 0-31 and b of lane
 // l - 32 in lanes 32-63; hi gets a of lane l + 32 in lanes 0-31 and b in lanes
 // 32-63. Scalar arguments and results: the builtin mis-lowers when fed vector
-// elements directly, and a __builtin_bit_cast of an element of its result
-// reads element 0 whichever element is named, so each result goes through an
-// integer cast first.
+// elements directly. And a __builtin_bit_cast of any vector element (of this
+// builtin's result or of a loaded vector) reads element 0 whichever element is
+// named, so each element goes through an integer copy or cast first.
 __device__ __forceinline__ void lane_half_swap(float a, float b, float& lo, float& hi) {
   const auto sw = __builtin_amdgcn_permlane32_swap(__builtin_bit_cast(unsigned, a),
                                                    __builtin_bit_cast(unsigned, b), false, false);

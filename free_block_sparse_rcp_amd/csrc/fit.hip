@@ -156,10 +156,6 @@ __device__ inline FitScratch fit_scratch(double* base, int m, int D, int k) {
   return f;
 }
 
-__device__ __forceinline__ int probe_pos(int i, int N, int m) {
-  return (int)(((2LL * i + 1) * N) / (2LL * m));
-}
-
 __device__ __forceinline__ double row_inv_norm2(const float* row, int D) {
   double n2 = 0.0;
   for (int e = 0; e < D; ++e) {
@@ -172,10 +168,10 @@ __device__ __forceinline__ double row_inv_norm2(const float* row, int D) {
 // ---------------------------------------------------------------- prep
 // grid (H, ceil((d+1)/8)), block 512. Workgroup b accumulates rows [8b, 8b+8)
 // of Sigma (rows < d), of sum w [s;1] r^T and of the Gram (rows < d+1) over
-// chunks of 256 probe rows staged in LDS.
+// chunks of 256 probe rows staged in LDS. S_probe row i is s_i (fp32).
 template <int D>
-__global__ __launch_bounds__(kFitThreads) void k_fit_prep(const float* S_out, const float* O_probe,
-                                                          int N, int m, int kmax, double* scratch) {
+__global__ __launch_bounds__(kFitThreads) void k_fit_prep(const float* S_probe, const float* O_probe,
+                                                          int m, int kmax, double* scratch) {
   constexpr int NT = kFitThreads;
   constexpr int NX = D + 1;
   constexpr int RB = 8;
@@ -183,10 +179,9 @@ __global__ __launch_bounds__(kFitThreads) void k_fit_prep(const float* S_out, co
   __shared__ double ra[CH][RB];    // w_i * r_i[a] for the block's rows a
   __shared__ double xa[CH][RB];    // w_i * x_i[a]
   __shared__ double w_s[CH];
-  __shared__ int pos_s[CH];
   __shared__ double red2[2 * NT / 64];
   const int h = blockIdx.x, b = blockIdx.y, t = threadIdx.x;
-  const float* Sh = S_out + (size_t)h * N * D;
+  const float* Sh = S_probe + (size_t)h * m * D;
   const float* Op = O_probe + (size_t)h * m * D;
   FitScratch f = fit_scratch(scratch + (size_t)h * fit_doubles_per_head(m, D, kmax), m, D, kmax);
   int slot = 0;
@@ -200,15 +195,13 @@ __global__ __launch_bounds__(kFitThreads) void k_fit_prep(const float* S_out, co
     if (t < mi) {
       const double wi = row_inv_norm2(Op + (size_t)(i0 + t) * D, D);
       w_s[t] = wsum > 0.0 ? wi / wsum : 0.0;
-      pos_s[t] = probe_pos(i0 + t, N, m);
     }
     __syncthreads();
     for (int idx = t; idx < mi * RB; idx += NT) {
       const int i = idx / RB, u = idx % RB, a = a0 + u;
-      const int p = pos_s[i];
       double rv = 0.0, xv = 0.0;
       if (a < D) {
-        const double s = Sh[(size_t)p * D + a];
+        const double s = Sh[(size_t)(i0 + i) * D + a];
         rv = (double)Op[(size_t)(i0 + i) * D + a] - s;
         xv = s;
       } else if (a == D) {
@@ -226,10 +219,9 @@ __global__ __launch_bounds__(kFitThreads) void k_fit_prep(const float* S_out, co
 #pragma unroll
       for (int u = 0; u < RB; ++u) acc[u] = 0.0;
       for (int i = 0; i < mi; ++i) {
-        const int p = pos_s[i];
         double col;
-        if (kind == 2) col = c < D ? (double)Sh[(size_t)p * D + c] : 1.0;
-        else col = (double)Op[(size_t)(i0 + i) * D + c] - (double)Sh[(size_t)p * D + c];
+        if (kind == 2) col = c < D ? (double)Sh[(size_t)(i0 + i) * D + c] : 1.0;
+        else col = (double)Op[(size_t)(i0 + i) * D + c] - (double)Sh[(size_t)(i0 + i) * D + c];
         const double* rowv = kind == 0 ? ra[i] : xa[i];
 #pragma unroll
         for (int u = 0; u < RB; ++u) acc[u] += rowv[u] * col;
@@ -871,13 +863,13 @@ size_t fit_ws_per_head(const Dims& d) {
   return fit_doubles_per_head(d.m, d.D, d.k) * sizeof(double);
 }
 
-hipError_t launch_fit(const Dims& d, const float* S_out, const float* O_probe, float* U,
+hipError_t launch_fit(const Dims& d, const float* S_probe, const float* O_probe, float* U,
                       float* Theta, int32_t* rank_eff, char* fit_ws, hipStream_t st) {
   double* scratch = reinterpret_cast<double*>(fit_ws);
   const dim3 pgrid(d.H, (d.D + 1 + 7) / 8);
 #define SPR_FIT(DD)                                                                         \
   do {                                                                                      \
-    k_fit_prep<DD><<<pgrid, kFitThreads, 0, st>>>(S_out, O_probe, d.N, d.m, d.k, scratch); \
+    k_fit_prep<DD><<<pgrid, kFitThreads, 0, st>>>(S_probe, O_probe, d.m, d.k, scratch);     \
     k_fit<DD><<<d.H, kFitThreads, 0, st>>>(d.m, d.k, d.lam, U, Theta, rank_eff, scratch);   \
   } while (0)
   if (d.D == 128) SPR_FIT(128);

@@ -92,7 +92,8 @@ struct AttnArgs {
   const int32_t* block_ptr;    // sparse
   const int32_t* block_groups; // sparse
   const int32_t* group_off;    // sparse
-  void* out;                   // sparse: S_out fp32 (query order); dense: O dtype (token order)
+  void* out;                   // sparse: S_out dtype (query order); dense: O dtype (token order)
+  float* sprobe;               // sparse: fp32 rows of the probe positions [H][m][d] (or null)
   float* lse;                  // sparse / dense (may be null for dense)
   float* opart;                // probe: [H, nsplit, m, D] fp32
   float* lsepart;              // probe: [H, nsplit, m]
@@ -127,11 +128,11 @@ struct SupportArgs {
 hipError_t launch_support(const Dims& d, const SupportArgs& a, hipStream_t st);
 
 // ---- fit.hip
-hipError_t launch_fit(const Dims& d, const float* S_out, const float* O_probe, float* U,
+hipError_t launch_fit(const Dims& d, const float* S_probe, const float* O_probe, float* U,
                       float* Theta, int32_t* rank_eff, char* fit_ws, hipStream_t st);
 
 // ---- apply.hip
-hipError_t launch_apply(const Dims& d, const float* S_out, const int32_t* query_perm,
+hipError_t launch_apply(const Dims& d, const void* S_out, const int32_t* query_perm,
                         const float* O_probe, const float* U, const float* Theta,
                         const int32_t* rank_eff, void* O, char* ws, hipStream_t st);
 

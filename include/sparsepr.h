@@ -31,11 +31,11 @@
  *   library, see there.)
  * - Tensors are contiguous, head-major: [H, N, d] means element
  *   (h, i, e) at ((h * N) + i) * d + e. Per-head index arrays are [H, N] etc.
- * - `dtype` selects the element type of Q, K, V, Kp, Vp and O:
- *   SPARSEPR_F32 (IEEE binary32) or SPARSEPR_BF16 (bfloat16). All other
- *   floating arrays, including the sparse output S_out, are fp32: the fit
- *   and the apply consume S_out, and keeping it at fp32 keeps storage
- *   rounding out of the fitted map.
+ * - `dtype` selects the element type of Q, K, V, Kp, Vp, the sparse output
+ *   S_out and O: SPARSEPR_F32 (IEEE binary32) or SPARSEPR_BF16 (bfloat16).
+ *   All other floating arrays are fp32. The apply reads S_out once per row;
+ *   the fit reads the probe rows' sparse outputs from S_probe, an fp32 copy
+ *   of those rows, so the fitted map sees no storage rounding.
  * - Token index t in [0, N) is a row of Q/K/V. "Query order" position i
  *   refers to token query_perm[h, i].
  * - `stream` is a hipStream_t (NULL = legacy default stream). Work is only
@@ -64,7 +64,9 @@
 extern "C" {
 #endif
 
-#define SPARSEPR_ABI_VERSION 1
+/* 2: S_out has the element type `dtype` (fp32 on both paths in 1); the
+   probe rows' sparse outputs go to S_probe (fp32), which stage 4 reads */
+#define SPARSEPR_ABI_VERSION 2
 
 /* status codes */
 #define SPARSEPR_OK 0
@@ -221,17 +223,20 @@ int32_t sparsepr_route(const sparsepr_params* params, const void* Q, const float
  *
  * Inputs : Q [H,N,d]; Kp, Vp [H,N,d] (from stage 1); scale [H];
  *          group_off [H,G+1]; query_perm [H,N]; block_ptr, block_groups.
- * Outputs: S_out [H,N,d] fp32 in QUERY ORDER; lse [H,N] fp32 (query order).
+ * Outputs: S_out [H,N,d] dtype in QUERY ORDER; S_probe [H,m,d] fp32, row i =
+ *          S_out at probe position p_i (stage 4) before rounding to dtype
+ *          (may be NULL when m = 0); lse [H,N] fp32 (query order).
  */
 int32_t sparsepr_attend(const sparsepr_params* params, const void* Q, const void* Kp,
                         const void* Vp, const float* scale, const int32_t* group_off,
                         const int32_t* query_perm, const int32_t* block_ptr,
-                        const int32_t* block_groups, float* S_out, float* lse, void* stream);
+                        const int32_t* block_groups, void* S_out, float* S_probe, float* lse,
+                        void* stream);
 
 /*
  * Stage 3 on a subset of the query blocks, so that the probe fit can start
- * before the whole sparse output exists (stage 4 reads S_out only at the probe
- * positions p_i of its own description):
+ * before the whole sparse output exists (stage 4 reads only S_probe, the
+ * probe positions p_i of its own description):
  *   SPARSEPR_BLOCKS_ALL              every block (= sparsepr_attend);
  *   SPARSEPR_BLOCKS_WITH_PROBE       only blocks holding some probe position;
  *   SPARSEPR_BLOCKS_WITHOUT_PROBE    only the other blocks.
@@ -247,8 +252,8 @@ int32_t sparsepr_attend(const sparsepr_params* params, const void* Q, const void
 int32_t sparsepr_attend_subset(const sparsepr_params* params, const void* Q, const void* Kp,
                                const void* Vp, const float* scale, const int32_t* group_off,
                                const int32_t* query_perm, const int32_t* block_ptr,
-                               const int32_t* block_groups, float* S_out, float* lse,
-                               int32_t subset, void* stream);
+                               const int32_t* block_groups, void* S_out, float* S_probe,
+                               float* lse, int32_t subset, void* stream);
 
 /*
  * Stage 4 - exact probe rows and the probe-fitted map (arxivdaily 2608.18484,
@@ -258,7 +263,8 @@ int32_t sparsepr_attend_subset(const sparsepr_params* params, const void* Q, con
  *
  * Probe i < m is the query at position p_i = floor((i + 1/2) N / m) of the
  * query order. o_i = dense attention of that query over all N keys; the
- * keys may be given in any order (e.g. Kp, Vp). With s_i = S_out[p_i]:
+ * keys may be given in any order (e.g. Kp, Vp). With s_i = S_probe[i] (the
+ * sparse output at p_i, in fp32):
  *   r_i = o_i - s_i;  w_i = ||o_i||^-2 / sum ||o||^-2 (0 where o_i = 0);
  *   Sigma = sum_i w_i r_i r_i^T;  U = eigenvectors of Sigma's k_eff largest
  *   eigenvalues, k_eff = min(k, m, d), or 0 when trace(Sigma) = 0;
@@ -272,7 +278,7 @@ int32_t sparsepr_attend_subset(const sparsepr_params* params, const void* Q, con
  *   on [s; 1]: Theta^T [s; 1] = B^T [U^T s; 1].
  *
  * Inputs : Q [H,N,d]; K, V [H,N,d] (any key order); scale [H];
- *          query_perm [H,N]; S_out [H,N,d] fp32 (query order, from stage 3).
+ *          query_perm [H,N]; S_probe [H,m,d] fp32 (from stage 3).
  * Outputs: O_probe [H,m,d] fp32 exact probe outputs;
  *          U [H,d,k] fp32 (columns >= k_eff are zero); Theta [H,d+1,k] fp32
  *          (row d is the bias; columns >= k_eff zero); rank_eff [H] int32.
@@ -280,7 +286,7 @@ int32_t sparsepr_attend_subset(const sparsepr_params* params, const void* Q, con
  */
 int32_t sparsepr_probe_fit(const sparsepr_params* params, const void* Q, const void* K,
                            const void* V, const float* scale, const int32_t* query_perm,
-                           const float* S_out, float* O_probe, float* U, float* Theta,
+                           const float* S_probe, float* O_probe, float* U, float* Theta,
                            int32_t* rank_eff, void* workspace, size_t workspace_bytes,
                            void* stream);
 
@@ -292,13 +298,13 @@ int32_t sparsepr_probe_fit(const sparsepr_params* params, const void* Q, const v
  * For query position i with token q = query_perm[i]:
  *   O[q] = s_i + U Theta^T [s_i; 1]   if i is not a probe position,
  *   O[q] = O_probe[probe index]       if it is.
- * Inputs : S_out [H,N,d] fp32; query_perm [H,N]; O_probe [H,m,d]; U; Theta;
+ * Inputs : S_out [H,N,d] dtype; query_perm [H,N]; O_probe [H,m,d]; U; Theta;
  *          rank_eff [H]; workspace (the shared one; this stage keeps the
  *          per-head matrix Theta U^T there). Output: O [H,N,d] dtype in TOKEN
  *          ORDER. Errors: as the other stages (NULL arguments, a workspace
  *          smaller than sparsepr_workspace_bytes).
  */
-int32_t sparsepr_apply(const sparsepr_params* params, const float* S_out,
+int32_t sparsepr_apply(const sparsepr_params* params, const void* S_out,
                        const int32_t* query_perm, const float* O_probe, const float* U,
                        const float* Theta, const int32_t* rank_eff, void* O, void* workspace,
                        size_t workspace_bytes, void* stream);
@@ -320,7 +326,7 @@ int32_t sparsepr_apply(const sparsepr_params* params, const float* S_out,
  * other threads) race and must be serialised by the caller.
  */
 #define SPARSEPR_APPLY_SCRATCH_BYTES ((size_t)8 << 20)
-int32_t sparsepr_apply_noalloc(const sparsepr_params* params, const float* S_out,
+int32_t sparsepr_apply_noalloc(const sparsepr_params* params, const void* S_out,
                                const int32_t* query_perm, const float* O_probe, const float* U,
                                const float* Theta, const int32_t* rank_eff, void* O,
                                void* stream);

@@ -37,7 +37,7 @@ def test_header_declares_the_five_stages_and_helpers():
 def test_library_exports_every_declared_symbol(lib):
     for n in declared_functions():
         assert hasattr(lib, n), n
-    assert lib.sparsepr_abi_version() == 1
+    assert lib.sparsepr_abi_version() == 2
 
 
 def test_status_strings(lib):
@@ -135,14 +135,17 @@ def test_null_pointers_and_small_workspace_are_rejected(lib):
     st = lib.sparsepr_support_stats(ctypes.byref(p), 0, *args, 2, 0.9, *outs, fake,
                                     4 * 2 * 64 * 2049 - 1, None)
     assert st == 3
-    # attend with no lse
+    # attend with no lse, then with probes but no fp32 copy of their rows
     p.partition_mode = 0
     st = lib.sparsepr_attend(ctypes.byref(p), fake, fake, fake, fake, fake, fake, fake, fake, fake,
-                             None, None)
-    assert st == 1
+                             fake, None, None)
+    assert st == 1 and "lse" in lib.sparsepr_last_error().decode()
+    st = lib.sparsepr_attend(ctypes.byref(p), fake, fake, fake, fake, fake, fake, fake, fake, fake,
+                             None, fake, None)
+    assert st == 1 and "S_probe" in lib.sparsepr_last_error().decode()
     # attention on a block subset: the subset value is validated
     st = lib.sparsepr_attend_subset(ctypes.byref(p), fake, fake, fake, fake, fake, fake, fake, fake,
-                                    fake, fake, 3, None)
+                                    fake, fake, fake, 3, None)
     assert st == 1 and "subset" in lib.sparsepr_last_error().decode()
     # apply: output missing, then a workspace too small for the per-head matrix
     st = lib.sparsepr_apply(ctypes.byref(p), fake, fake, fake, fake, fake, fake, None, fake,

@@ -124,6 +124,7 @@ def test_debug_run_matches_bench_run(fr):
     # written extents only (buffers keep one slot when m or k is 0)
     m, k = fr.p.n_probes, fr.p.rank
     assert torch.equal(a.O_probe[:, :m], b.O_probe[:, :m])
+    assert torch.equal(a.S_probe[:, :m], b.S_probe[:, :m])
     assert torch.equal(a.U[:, :, :k], b.U[:, :, :k])
     assert torch.equal(a.Theta[:, :, :k], b.Theta[:, :, :k])
     ptr = a.block_ptr.cpu().numpy()
@@ -286,9 +287,12 @@ def test_probes_fit_apply_full(fr):
         Op = fr.get("O_probe", h)[:p.n_probes]
         ref, _ = orc.dense_attention(Q, K, V, tau, rows=ptok)
         assert rel_l2(Op, ref) < ATTN_TOL, "probe rows"
-        # fit on the GPU's probe inputs
+        # fit on the GPU's probe inputs: the fp32 copy of the probe rows' sparse
+        # outputs, which S_out holds rounded to the output type
         S = fr.get("S", h)
-        Sp = S[pos].astype(np.float64)
+        Sp32 = fr.get("S_probe", h)[:p.n_probes]
+        assert np.array_equal(bf16_round(Sp32) if p.dtype == "bf16" else Sp32, S[pos])
+        Sp = Sp32.astype(np.float64)
         Op64 = Op.astype(np.float64)
         w = orc.probe_weights(Op64)
         Rp = Op64 - Sp
@@ -332,6 +336,7 @@ def test_overlapped_call_matches(fr):
         assert torch.equal(getattr(op.buffers, n), getattr(b.b, n)), n
     m, k = fr.p.n_probes, fr.p.rank
     assert torch.equal(op.buffers.O_probe[:, :m], b.b.O_probe[:, :m])
+    assert torch.equal(op.buffers.S_probe[:, :m], b.b.S_probe[:, :m])
     assert torch.equal(op.buffers.U[:, :, :k], b.b.U[:, :, :k])
     assert torch.equal(op.buffers.Theta[:, :, :k], b.b.Theta[:, :, :k])
     del op
@@ -388,7 +393,7 @@ def test_per_query_error_full(fr):
         dd = np.abs(e_gpu - e_or)
         row = orc.relative_l2_rows(O_gpu, O_or)
         # Davis-Kahan bound from the GPU's own probe inputs
-        Sg = fr.get("S", h)[pos_p].astype(np.float64)
+        Sg = fr.get("S_probe", h)[:p.n_probes].astype(np.float64)
         Og = fr.get("O_probe", h)[:p.n_probes].astype(np.float64)
         wg = orc.probe_weights(Og)
         Sig_g = ((Og - Sg) * wg[:, None]).T @ (Og - Sg)

@@ -65,6 +65,7 @@ def head_arrays(r, h):
                                    "query_perm", "block_ptr", "lse", "O_probe", "U", "Theta",
                                    "rank_eff", "executed_pairs")}
     out["S"] = r.np("S")[h]
+    out["S_probe"] = r.np("S_probe")[h][:p.n_probes]
     out["O"] = r.np("O")[h]
     out["Kp"] = r.np("Kp")[h]
     out["block_groups"] = r.np("block_groups")[h]
@@ -202,19 +203,22 @@ def test_attend_probe_fit_apply_values(name):
         assert int(g["executed_pairs"]) == o["E"]
         if p.n_probes:
             assert rel_l2(g["O_probe"], o["Op"]) < tol, "probe rows"
+            # the fit's fp32 copy of the probe rows' sparse outputs is what
+            # S_out holds there before its rounding to the output type
+            pos = orc.probe_positions(p.n_tokens, p.n_probes)
+            Sp = g["S_probe"] if p.dtype == "f32" else bf16_round(g["S_probe"])
+            assert np.array_equal(Sp, g["S"][pos])
         assert rel_l2(g["O"], o["O"]) < tol, "final output"
 
 
 @pytest.mark.parametrize("name", list(WORKLOADS))
 def test_fit_matches_oracle_on_gpu_inputs(name):
-    """The fit alone: oracle fit on the GPU's probe inputs (S as stored, O_probe)."""
+    """The fit alone: oracle fit on the GPU's probe inputs (S_probe, O_probe)."""
     r = get_run(name)
     p = r.p
     for h in range(p.heads):
         g = head_arrays(r, h)
-        N = p.n_tokens
-        pos = orc.probe_positions(N, p.n_probes)
-        Sp = g["S"][pos].astype(np.float64)
+        Sp = g["S_probe"].astype(np.float64)       # the fit's inputs: fp32 sparse rows
         Op = g["O_probe"].astype(np.float64)
         w = orc.probe_weights(Op)
         Rp = Op - Sp
@@ -465,7 +469,7 @@ def test_semantic_partition_with_probe_correction():
         e_o = rel_l2(g["O"], o["O"])
         # the fit from the GPU's own S and probe rows, applied in fp64
         pos = orc.probe_positions(p.n_tokens, p.n_probes)
-        Sp = g["S"][pos].astype(np.float64)
+        Sp = g["S_probe"].astype(np.float64)
         Op = g["O_probe"].astype(np.float64)
         w, U, ev, Th = orc.fit_probe_map(Sp, Op, p.rank, p.ridge_lambda)
         S_q = g["S"].astype(np.float64)
@@ -747,7 +751,7 @@ def test_graph_capture_replays():
     idx = op.upload_indices(inp.sample_idx, inp.init_idx)
     op.run(Q, K, V, scale, idx)
     torch.cuda.synchronize()
-    ref = {n: getattr(op.buffers, n).clone() for n in ("O", "S", "lse", "query_perm", "key_perm")}
+    ref = {n: getattr(op.buffers, n).clone() for n in ("O", "S", "S_probe", "lse", "query_perm", "key_perm")}
     g = torch.cuda.CUDAGraph()
     with torch.cuda.graph(g):
         op.run(Q, K, V, scale, idx)
@@ -768,11 +772,14 @@ def test_attend_block_subsets_compose():
     """Blocks holding probe rows, then the others, write exactly the full attention."""
     r = run_pipeline(small_bf16(name="subsets", m=8, k=4, seed=17))   # 8 of 24 blocks hold probes
     p, b = r.p, r.b
-    full_S, full_lse = b.S.clone(), b.lse.clone()
+    full_S, full_lse, full_Sp = b.S.clone(), b.lse.clone(), b.S_probe.clone()
     b.S.fill_(float("nan"))
     b.lse.fill_(float("nan"))
+    b.S_probe.fill_(float("nan"))
     binding.attend(p, r.Q, r.scale, b, subset=binding.BLOCKS_WITH_PROBE)
     torch.cuda.synchronize()
+    # every probe row lies in such a block: the fit's inputs are complete
+    assert torch.equal(b.S_probe, full_Sp)
     # exactly the rows of blocks that hold a probe position are written
     pos = orc.probe_positions(p.n_tokens, p.n_probes)
     blocks = np.unique(pos // p.q_block)
@@ -784,6 +791,7 @@ def test_attend_block_subsets_compose():
     binding.attend(p, r.Q, r.scale, b, subset=binding.BLOCKS_WITHOUT_PROBE)
     torch.cuda.synchronize()
     assert torch.equal(b.S, full_S) and torch.equal(b.lse, full_lse)
+    assert torch.equal(b.S_probe, full_Sp)
 
 
 def test_overlapped_call_equals_serial():
