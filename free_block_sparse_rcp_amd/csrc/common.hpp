@@ -107,24 +107,34 @@ __device__ __forceinline__ uint64_t lanemask_lt() {
   return lane == 0 ? 0ull : (~0ull >> (64 - lane));
 }
 
-// Exclusive scan of one int per thread across a workgroup of NT threads.
-// `tmp` must hold NT ints of shared memory. Returns the exclusive prefix and
-// writes the total to *total. Contains __syncthreads().
+// Exclusive scan of one int per thread across a workgroup of NT threads
+// (whole waves): a scan inside each wave by lane shifts, then the wave totals
+// through `tmp` (at least NT / 64 ints of shared memory). Returns the
+// exclusive prefix and writes the total to *total. Contains two
+// __syncthreads(); `tmp` may be reused right after it returns.
 template <int NT>
 __device__ __forceinline__ int block_exclusive_scan(int v, int* tmp, int* total) {
-  const int t = threadIdx.x;
-  tmp[t] = v;
-  __syncthreads();
-  for (int off = 1; off < NT; off <<= 1) {
-    int add = t >= off ? tmp[t - off] : 0;
-    __syncthreads();
-    tmp[t] += add;
-    __syncthreads();
+  static_assert(NT % 64 == 0, "whole waves");
+  constexpr int NW = NT / 64;
+  const int t = threadIdx.x, lane = t & 63, w = t >> 6;
+  int x = v;
+#pragma unroll
+  for (int off = 1; off < 64; off <<= 1) {
+    const int y = __shfl_up(x, off);
+    if (lane >= off) x += y;
   }
-  int incl = tmp[t];
-  *total = tmp[NT - 1];
+  if (lane == 63) tmp[w] = x;
   __syncthreads();
-  return incl - v;
+  int before = 0, all = 0;
+#pragma unroll
+  for (int i = 0; i < NW; ++i) {
+    const int s = tmp[i];
+    before += i < w ? s : 0;
+    all += s;
+  }
+  *total = all;
+  __syncthreads();
+  return before + x - v;
 }
 
 template <int NT>
