@@ -640,11 +640,14 @@ __global__ __launch_bounds__(256) void k_digit_scatter(const KeyT* keys_in, KeyT
 // row is read once: a row is split into 16-byte chunks over CPR threads, and
 // the workgroup's 256 / CPR row slots take rows slot, slot + 256 / CPR, ... in
 // increasing order; the slots are then added in slot order, so the sum order is
-// fixed. grid (G, H), block 256.
-template <bool BF16, int D>
+// fixed. GATHER (the final grouping): each chunk read is also written to its
+// group-contiguous place in Kp, and the same chunk of V to Vp, so the paired
+// K/V groups cost no second read of K. grid (G, H), block 256.
+template <bool BF16, int D, bool GATHER>
 __global__ __launch_bounds__(256) void k_group_mean(const void* Kv, const int32_t* key_perm,
                                                     const int32_t* group_off, int N, int G,
-                                                    float* kbar) {
+                                                    float* kbar, const void* Vv, void* Kpv,
+                                                    void* Vpv) {
   using T = typename Elt<BF16>::T;
   constexpr int ROWB = D * (int)sizeof(T);
   constexpr int CPR = ROWB / 16;              // threads per row
@@ -660,6 +663,9 @@ __global__ __launch_bounds__(256) void k_group_mean(const void* Kv, const int32_
   if (e <= b) return;
   const int cc = t % CPR, slot = t / CPR;
   const char* K = static_cast<const char*>(Kv) + (size_t)h * N * ROWB + cc * 16;
+  const char* V = GATHER ? static_cast<const char*>(Vv) + (size_t)h * N * ROWB + cc * 16 : nullptr;
+  char* Kp = GATHER ? static_cast<char*>(Kpv) + (size_t)h * N * ROWB + cc * 16 : nullptr;
+  char* Vp = GATHER ? static_cast<char*>(Vpv) + (size_t)h * N * ROWB + cc * 16 : nullptr;
   const int32_t* perm = key_perm + (size_t)h * N;
   float acc[EPC];
 #pragma unroll
@@ -687,14 +693,36 @@ __global__ __launch_bounds__(256) void k_group_mean(const void* Kv, const int32_
     __syncthreads();
     int i = slot;
     for (; i + (U - 1) * RPP < n; i += U * RPP) {
-      u32x4 raw[U];
+      u32x4 raw[U], vraw[U];
 #pragma unroll
       for (int u = 0; u < U; ++u)
         raw[u] = *reinterpret_cast<const u32x4*>(K + (size_t)pidx[i + u * RPP] * ROWB);
+      if (GATHER) {
+#pragma unroll
+        for (int u = 0; u < U; ++u)
+          vraw[u] = *reinterpret_cast<const u32x4*>(V + (size_t)pidx[i + u * RPP] * ROWB);
+      }
 #pragma unroll
       for (int u = 0; u < U; ++u) add(raw[u]);
+      if (GATHER) {
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+          const size_t dst = (size_t)(c0 + i + u * RPP) * ROWB;
+          *reinterpret_cast<u32x4*>(Kp + dst) = raw[u];
+          *reinterpret_cast<u32x4*>(Vp + dst) = vraw[u];
+        }
+      }
     }
-    for (; i < n; i += RPP) add(*reinterpret_cast<const u32x4*>(K + (size_t)pidx[i] * ROWB));
+    for (; i < n; i += RPP) {
+      const u32x4 raw = *reinterpret_cast<const u32x4*>(K + (size_t)pidx[i] * ROWB);
+      add(raw);
+      if (GATHER) {
+        const size_t dst = (size_t)(c0 + i) * ROWB;
+        *reinterpret_cast<u32x4*>(Kp + dst) = raw;
+        *reinterpret_cast<u32x4*>(Vp + dst) =
+            *reinterpret_cast<const u32x4*>(V + (size_t)pidx[i] * ROWB);
+      }
+    }
   }
 #pragma unroll
   for (int j = 0; j < EPC; ++j) red[slot * D + cc * EPC + j] = acc[j];
@@ -730,24 +758,6 @@ __global__ void k_fill_i32(int32_t* p, size_t n, int32_t v) {
 __global__ void k_fill_f32(float* p, size_t n, float v) {
   const size_t i = (size_t)blockIdx.x * 256 + threadIdx.x;
   if (i < n) p[i] = v;
-}
-
-// Kp[i] = K[key_perm[i]], Vp[i] = V[key_perm[i]]: 16-byte copies.
-// grid (ceil(N * CPR / 256), H) where CPR = row bytes / 16.
-template <int ROWB>
-__global__ void k_gather_rows(const char* K, const char* V, const int32_t* perm, int N, char* Kp,
-                              char* Vp) {
-  constexpr int CPR = ROWB / 16;
-  const size_t f = (size_t)blockIdx.x * 256 + threadIdx.x;
-  const int h = blockIdx.y;
-  if (f >= (size_t)N * CPR) return;
-  const int i = (int)(f / CPR), ch = (int)(f % CPR);
-  const int src = clamp_idx(perm[(size_t)h * N + i], N);
-  const size_t hb = (size_t)h * N * ROWB;
-  const uint4 kv = *reinterpret_cast<const uint4*>(K + hb + (size_t)src * ROWB + ch * 16);
-  const uint4 vv = *reinterpret_cast<const uint4*>(V + hb + (size_t)src * ROWB + ch * 16);
-  *reinterpret_cast<uint4*>(Kp + hb + (size_t)i * ROWB + ch * 16) = kv;
-  *reinterpret_cast<uint4*>(Vp + hb + (size_t)i * ROWB + ch * 16) = vv;
 }
 
 // ------------------------------------------------------------- launchers
@@ -817,11 +827,18 @@ static hipError_t partition_impl(const Dims& d, const void* Q, const void* K, co
   const dim3 rows64((d.N + 63) / 64, d.H);
   const dim3 per_group(d.G, d.H);
 
-  auto regroup = [&]() -> hipError_t {
+  // groups from the labels, then their means; the final grouping also forms
+  // the paired K/V groups (when they are wanted) in the same pass over K
+  auto regroup = [&](bool last) -> hipError_t {
     hipError_t e = launch_sort_pass_u32(d, key_label, d.gbits, nullptr, key_perm, counts, totals,
                                         starts, group_off, st);
     if (e != hipSuccess) return e;
-    k_group_mean<BF16, D><<<per_group, 256, 0, st>>>(K, key_perm, group_off, d.N, d.G, kbar);
+    if (last && Kp != nullptr)
+      k_group_mean<BF16, D, true><<<per_group, 256, 0, st>>>(K, key_perm, group_off, d.N, d.G,
+                                                             kbar, V, Kp, Vp);
+    else
+      k_group_mean<BF16, D, false><<<per_group, 256, 0, st>>>(K, key_perm, group_off, d.N, d.G,
+                                                              kbar, nullptr, nullptr, nullptr);
     SPR_CHECK_LAUNCH();
     return hipSuccess;
   };
@@ -850,7 +867,7 @@ static hipError_t partition_impl(const Dims& d, const void* Q, const void* K, co
                                                              key_label, nullptr, dbg_it);
         SPR_CHECK_LAUNCH();
       }
-      hipError_t e = regroup();
+      hipError_t e = regroup(it == d.T - 1);
       if (e != hipSuccess) return e;
     }
   } else {
@@ -863,16 +880,9 @@ static hipError_t partition_impl(const Dims& d, const void* Q, const void* K, co
     k_random_labels<<<dim3((d.N + 255) / 256, d.H), 256, 0, st>>>(rand_key_perm, d.N, d.G,
                                                                    key_label);
     SPR_CHECK_LAUNCH();
-    hipError_t e = regroup();
+    hipError_t e = regroup(true);
     if (e != hipSuccess) return e;
   }
-  if (Kp == nullptr) return hipSuccess;
-  constexpr int ROWB = D * (BF16 ? 2 : 4);
-  const size_t nchunks = (size_t)d.N * (ROWB / 16);
-  k_gather_rows<ROWB><<<dim3((unsigned)((nchunks + 255) / 256), d.H), 256, 0, st>>>(
-      static_cast<const char*>(K), static_cast<const char*>(V), key_perm, d.N,
-      static_cast<char*>(Kp), static_cast<char*>(Vp));
-  SPR_CHECK_LAUNCH();
   return hipSuccess;
 }
 
