@@ -50,7 +50,7 @@ def load_traffic(workload):
 
 SPARSE_KERNEL = "k_attn_mfma<128, 128, 0>"   # sparsepr_attend's kernel (d=128, B_q=128)
 COPY_KERNEL = "neg_kernel"                    # the --calibration-copy-mib kernel
-PMC_KERNELS = ("k_attn_mfma|k_group_mean|k_gather_rows|k_apply_mfma|k_rowvec_mfma|k_route_scores|"
+PMC_KERNELS = ("k_attn_mfma|k_group_mean|k_apply_mfma|k_rowvec_mfma|k_route_scores|"
                "k_metric|neg_kernel")              # the kernels the per-kernel traffic table covers
 
 
