@@ -496,6 +496,9 @@ def main():
                     help="attend the blocks holding probe rows first and run the probe fit on a "
                          "second stream while the other blocks are attended (default: the five "
                          "stages back to back on one stream)")
+    ap.add_argument("--static-attention", action="store_true",
+                    help="deal the attention's query blocks out statically, one workgroup each "
+                         "(default: a persistent grid taking blocks from per-XCD work queues)")
     ap.add_argument("--calibration-copy-mib", type=int, default=0,
                     help="also run one plain device copy of this many MiB (a known-size "
                          "kernel for scaling the FETCH_SIZE / WRITE_SIZE counters)")
@@ -543,11 +546,17 @@ def main():
     dt = binding.torch_dtype(p)
     Q, K, V = (torch.from_numpy(x).to(dev, dt) for x in (inp.Q, inp.K, inp.V))
     scale = torch.from_numpy(inp.scale).to(dev)
-    op = binding.SparsePR(p, dev)
+    use_queue = not args.static_attention
+    op = binding.SparsePR(p, dev, use_queue=use_queue)
     idx = op.upload_indices(inp.sample_idx, inp.init_idx, inp.rand_key_perm, inp.rand_query_perm)
     b = op.buffers
     O_dense = torch.empty_like(Q)
     lse_dense = torch.empty(p.heads, p.n_tokens, dtype=torch.float32, device=dev)
+    dense_queue = torch.empty(binding.QUEUE_BYTES, dtype=torch.uint8, device=dev)
+
+    def dense_call():
+        binding.dense_attention(p, Q, K, V, scale, O_dense, lse_dense, queue=dense_queue,
+                                use_queue=use_queue)
 
     stages = ("partition", "route", "attend", "probe_fit", "apply")
 
@@ -568,7 +577,7 @@ def main():
     for _ in range(args.warmup):
         one_call()
         if not args.no_dense:
-            binding.dense_attention(p, Q, K, V, scale, O_dense, lse_dense)
+            dense_call()
     torch.cuda.synchronize()
 
     # timed region: K whole calls, events between stages (on the library's streams)
@@ -605,7 +614,7 @@ def main():
         torch.cuda.synchronize()
         e0.record()
         for _ in range(args.steps):
-            binding.dense_attention(p, Q, K, V, scale, O_dense, lse_dense)
+            dense_call()
         e1.record()
         torch.cuda.synchronize()
         dense_ms = e0.elapsed_time(e1) / args.steps
@@ -677,6 +686,8 @@ def main():
         "reconstruction_share": (stage_ms["probe_fit"] + stage_ms["apply"]) / call_ms,
         "pipeline": ("probe blocks attended first; probe fit on a second stream overlaps the "
                      "attention of the other blocks" if overlap else "stages back to back"),
+        "attention_blocks": ("per-XCD work queues, persistent grid" if use_queue
+                             else "static, one workgroup per block"),
         "executed_pairs": E, "realized_density": density,
         "dense_tflops": (4.0 * D * H * float(N) ** 2 / (dense_ms * 1e-3) / 1e12) if dense_ms else None,
         "quality": quality, "roofline": roofline, "cpu_baseline": cpu,

@@ -32,6 +32,7 @@ EXPORTS = ("sparsepr_abi_version", "sparsepr_status_string", "sparsepr_last_erro
            "sparsepr_attend_subset", "sparsepr_probe_fit", "sparsepr_apply",
            "sparsepr_apply_noalloc", "sparsepr_dense_attention", "sparsepr_support_stats")
 BLOCKS_ALL, BLOCKS_WITH_PROBE, BLOCKS_WITHOUT_PROBE = 0, 1, 2
+QUEUE_BYTES = 1024        # SPARSEPR_QUEUE_BYTES: the attention's optional work-queue buffer
 RESPONSE_COUPLED, RANDOM_BLOCK, SEMANTIC = 0, 1, 2   # partition modes
 
 
@@ -71,19 +72,19 @@ def load(path: Optional[str] = None) -> ctypes.CDLL:
     pp = ctypes.POINTER(CParams)
     lib.sparsepr_partition.argtypes = [pp] + [_c_p] * 14 + [_c_p, _c_sz, _c_p]
     lib.sparsepr_route.argtypes = [pp] + [_c_p] * 13 + [_c_p, _c_sz, _c_p]
-    lib.sparsepr_attend.argtypes = [pp] + [_c_p] * 11 + [_c_p]
-    lib.sparsepr_attend_subset.argtypes = [pp] + [_c_p] * 11 + [_c_i32, _c_p]
+    lib.sparsepr_attend.argtypes = [pp] + [_c_p] * 11 + [_c_p, _c_sz, _c_p]
+    lib.sparsepr_attend_subset.argtypes = [pp] + [_c_p] * 11 + [_c_i32, _c_p, _c_sz, _c_p]
     lib.sparsepr_probe_fit.argtypes = [pp] + [_c_p] * 10 + [_c_p, _c_sz, _c_p]
     lib.sparsepr_apply.argtypes = [pp] + [_c_p] * 7 + [_c_p, _c_sz, _c_p]
     lib.sparsepr_apply_noalloc.argtypes = [pp] + [_c_p] * 7 + [_c_p]
-    lib.sparsepr_dense_attention.argtypes = [pp] + [_c_p] * 6 + [_c_p]
+    lib.sparsepr_dense_attention.argtypes = [pp] + [_c_p] * 6 + [_c_p, _c_sz, _c_p]
     lib.sparsepr_support_stats.argtypes = ([pp, _c_i32] + [_c_p] * 8 + [_c_i32, ctypes.c_double] +
                                            [_c_p] * 7 + [_c_sz, _c_p])
     for name in ("sparsepr_partition", "sparsepr_route", "sparsepr_attend", "sparsepr_attend_subset",
                  "sparsepr_probe_fit", "sparsepr_apply", "sparsepr_apply_noalloc",
                  "sparsepr_dense_attention"):
         getattr(lib, name).restype = _c_i32
-    if lib.sparsepr_abi_version() != 2:
+    if lib.sparsepr_abi_version() != 3:
         raise RuntimeError("libsparsepr ABI version mismatch")
     _LIB = lib
     return lib
@@ -171,6 +172,7 @@ class Buffers:
     rank_eff: torch.Tensor
     O: torch.Tensor
     workspace: torch.Tensor
+    queue: torch.Tensor          # the attention's work-queue counters
     # semantic mode only: the query partition (its key_perm is the query order)
     query_label: Optional[torch.Tensor] = None
     query_order: Optional[torch.Tensor] = None
@@ -203,7 +205,8 @@ def alloc_buffers(p: Params, device) -> Buffers:
         U=torch.empty(H, D, max(p.rank, 1), **f32),
         Theta=torch.empty(H, D + 1, max(p.rank, 1), **f32),
         rank_eff=torch.empty(H, **i32), O=torch.empty(H, N, D, dtype=dt, device=device),
-        workspace=torch.empty(workspace_bytes(p), dtype=torch.uint8, device=device), **semantic)
+        workspace=torch.empty(workspace_bytes(p), dtype=torch.uint8, device=device),
+        queue=torch.empty(QUEUE_BYTES, dtype=torch.uint8, device=device), **semantic)
 
 
 # ------------------------------------------------------------ stage calls
@@ -243,16 +246,23 @@ def route(p: Params, Q, scale, b: Buffers, rand_query_perm=None, dbg_coords=None
         _ptr(dbg_block_score), _ptr(b.workspace), b.workspace.numel(), _stream(Q.device)))
 
 
-def attend(p: Params, Q, scale, b: Buffers, subset: int = BLOCKS_ALL) -> None:
+def _queue_args(queue):
+    return (None, 0) if queue is None else (_ptr(queue), queue.numel() * queue.element_size())
+
+
+def attend(p: Params, Q, scale, b: Buffers, subset: int = BLOCKS_ALL,
+           use_queue: bool = True) -> None:
+    """Stage 3; use_queue=False deals the blocks out statically (same results)."""
     lib = load()
     cp = c_params(p)
     args = (ctypes.byref(cp), _ptr(Q), _ptr(b.Kp), _ptr(b.Vp), _ptr(scale), _ptr(b.group_off),
             _ptr(b.query_perm), _ptr(b.block_ptr), _ptr(b.block_groups), _ptr(b.S),
             _ptr(b.S_probe), _ptr(b.lse))
+    q = _queue_args(b.queue if use_queue else None)
     if subset == BLOCKS_ALL:
-        _check(lib.sparsepr_attend(*args, _stream(Q.device)))
+        _check(lib.sparsepr_attend(*args, *q, _stream(Q.device)))
     else:
-        _check(lib.sparsepr_attend_subset(*args, subset, _stream(Q.device)))
+        _check(lib.sparsepr_attend_subset(*args, subset, *q, _stream(Q.device)))
 
 
 def probe_fit(p: Params, Q, scale, b: Buffers, K=None, V=None) -> None:
@@ -287,15 +297,24 @@ def apply_noalloc(p: Params, b: Buffers, O=None) -> torch.Tensor:
     return O
 
 
-def dense_attention(p: Params, Q, K, V, scale, O=None, lse=None):
+def dense_attention(p: Params, Q, K, V, scale, O=None, lse=None, queue=None,
+                    use_queue: bool = True):
+    """Exact attention. With use_queue, the work queue is ``queue`` or else a
+    buffer from torch's allocator on the current stream; use_queue=False deals
+    the blocks out statically (same results)."""
     lib = load()
     cp = c_params(p)
     if O is None:
         O = torch.empty_like(Q)
     if lse is None:
         lse = torch.empty(p.heads, p.n_tokens, dtype=torch.float32, device=Q.device)
+    if not use_queue:
+        queue = None
+    elif queue is None:
+        queue = torch.empty(QUEUE_BYTES, dtype=torch.uint8, device=Q.device)
     _check(lib.sparsepr_dense_attention(ctypes.byref(cp), _ptr(Q), _ptr(K), _ptr(V), _ptr(scale),
-                                        _ptr(O), _ptr(lse), _stream(Q.device)))
+                                        _ptr(O), _ptr(lse), *_queue_args(queue),
+                                        _stream(Q.device)))
     return O, lse
 
 
@@ -349,11 +368,12 @@ class SparsePR:
     ``buffers.O`` (token order) once the stream has been synchronised.
     """
 
-    def __init__(self, p: Params, device="cuda"):
+    def __init__(self, p: Params, device="cuda", use_queue: bool = True):
         load()
         self.p = p
         self.device = torch.device(device)
         self.buffers = alloc_buffers(p, self.device)
+        self.use_queue = use_queue      # the attention's work queue (False: static blocks)
         self._side = None
 
     def upload_indices(self, sample_idx=None, init_idx=None, rand_key_perm=None,
@@ -408,15 +428,16 @@ class SparsePR:
         mark("partition")
         route(p, Q, scale, b, rand_query_perm=qorder)
         mark("route")
+        uq = self.use_queue
         if not overlap:
-            attend(p, Q, scale, b)
+            attend(p, Q, scale, b, use_queue=uq)
             mark("attend")
             probe_fit(p, Q, scale, b)
             mark("probe_fit")
             apply(p, b)
             mark("apply")
             return b.O
-        attend(p, Q, scale, b, subset=BLOCKS_WITH_PROBE)
+        attend(p, Q, scale, b, subset=BLOCKS_WITH_PROBE, use_queue=uq)
         mark("attend_probe_blocks")
         fork = torch.cuda.Event()
         fork.record(main)
@@ -428,7 +449,7 @@ class SparsePR:
             mark("probe_fit", side)
         join = torch.cuda.Event()
         join.record(side)
-        attend(p, Q, scale, b, subset=BLOCKS_WITHOUT_PROBE)
+        attend(p, Q, scale, b, subset=BLOCKS_WITHOUT_PROBE, use_queue=uq)
         mark("attend")
         main.wait_event(join)
         mark("join")

@@ -206,6 +206,19 @@ static int32_t check_ws(const Dims& d, const void* ws, size_t ws_bytes) {
   return SPARSEPR_OK;
 }
 
+// The attention's work queues: optional; when given, SPARSEPR_QUEUE_BYTES of
+// 4-byte aligned device memory (8 counters, one per 128-byte line).
+static_assert(SPARSEPR_QUEUE_BYTES == 8 * kQueueStride * sizeof(int), "queue layout");
+static int32_t check_queue(const void* queue, size_t queue_bytes) {
+  if (queue == nullptr) return SPARSEPR_OK;
+  if (reinterpret_cast<uintptr_t>(queue) % 4 != 0)
+    return fail(SPARSEPR_ERR_INVALID_ARG, "queue must be 4-byte aligned");
+  if (queue_bytes < SPARSEPR_QUEUE_BYTES)
+    return fail(SPARSEPR_ERR_WORKSPACE, "queue of %d bytes needed (got %zu)", SPARSEPR_QUEUE_BYTES,
+                queue_bytes);
+  return SPARSEPR_OK;
+}
+
 static int32_t hip_status(hipError_t e, const char* stage) {
   if (e == hipSuccess) {
     g_last_error[0] = 0;
@@ -341,12 +354,14 @@ int32_t sparsepr_attend_subset(const sparsepr_params* params, const void* Q, con
                                const void* Vp, const float* scale, const int32_t* group_off,
                                const int32_t* query_perm, const int32_t* block_ptr,
                                const int32_t* block_groups, void* S_out, float* S_probe,
-                               float* lse, int32_t subset, void* stream) {
+                               float* lse, int32_t subset, void* queue, size_t queue_bytes,
+                               void* stream) {
   Dims d;
   int32_t s = make_dims(params, true, &d);
   if (s != SPARSEPR_OK) return s;
   if (subset < SPARSEPR_BLOCKS_ALL || subset > SPARSEPR_BLOCKS_WITHOUT_PROBE)
     return fail(SPARSEPR_ERR_INVALID_ARG, "subset must be 0, 1 or 2 (got %d)", subset);
+  if ((s = check_queue(queue, queue_bytes)) != SPARSEPR_OK) return s;
   SPR_REQUIRE(Q, "Q");
   SPR_REQUIRE(Kp, "Kp");
   SPR_REQUIRE(Vp, "Vp");
@@ -378,6 +393,7 @@ int32_t sparsepr_attend_subset(const sparsepr_params* params, const void* Q, con
   a.sprobe = d.m > 0 ? S_probe : nullptr;
   a.lse = lse;
   a.subset = subset;
+  a.qctr = static_cast<int*>(queue);
   return hip_status(launch_attention(d, ATTN_SPARSE, a, static_cast<hipStream_t>(stream)),
                     "sparsepr_attend");
 }
@@ -386,9 +402,10 @@ int32_t sparsepr_attend(const sparsepr_params* params, const void* Q, const void
                         const void* Vp, const float* scale, const int32_t* group_off,
                         const int32_t* query_perm, const int32_t* block_ptr,
                         const int32_t* block_groups, void* S_out, float* S_probe, float* lse,
-                        void* stream) {
+                        void* queue, size_t queue_bytes, void* stream) {
   return sparsepr_attend_subset(params, Q, Kp, Vp, scale, group_off, query_perm, block_ptr,
-                                block_groups, S_out, S_probe, lse, SPARSEPR_BLOCKS_ALL, stream);
+                                block_groups, S_out, S_probe, lse, SPARSEPR_BLOCKS_ALL, queue,
+                                queue_bytes, stream);
 }
 
 int32_t sparsepr_support_stats(const sparsepr_params* params, int32_t head, const void* Q,
@@ -570,7 +587,7 @@ int32_t sparsepr_apply_noalloc(const sparsepr_params* params, const void* S_out,
 
 int32_t sparsepr_dense_attention(const sparsepr_params* params, const void* Q, const void* K,
                                  const void* V, const float* scale, void* O, float* lse,
-                                 void* stream) {
+                                 void* queue, size_t queue_bytes, void* stream) {
   Dims d;
   int32_t s = make_dims(params, false, &d);
   if (s != SPARSEPR_OK) return s;
@@ -579,6 +596,7 @@ int32_t sparsepr_dense_attention(const sparsepr_params* params, const void* Q, c
   SPR_REQUIRE(V, "V");
   SPR_REQUIRE(scale, "scale");
   SPR_REQUIRE(O, "O");
+  if ((s = check_queue(queue, queue_bytes)) != SPARSEPR_OK) return s;
   AttnArgs a{};
   a.Q = Q;
   a.K = K;
@@ -592,6 +610,7 @@ int32_t sparsepr_dense_attention(const sparsepr_params* params, const void* Q, c
   a.nb = d.nb;
   a.out = O;
   a.lse = lse;
+  a.qctr = static_cast<int*>(queue);
   return hip_status(launch_attention(d, ATTN_DENSE, a, static_cast<hipStream_t>(stream)),
                     "sparsepr_dense_attention");
 }

@@ -15,6 +15,8 @@
 // and is read transposed with ds_read_b64_tr_b16. The key list of a block is the
 // concatenation of its routed groups' ranges in the group-contiguous Kp/Vp;
 // tiles run across group boundaries, so only the block's last tile is ragged.
+#include <atomic>
+
 #include "common.hpp"
 #include "internal.hpp"
 
@@ -83,6 +85,29 @@ __device__ __forceinline__ Item decode_item(const AttnArgs& a, int nqb) {
     it.sp = 0;
   }
   return it;
+}
+
+// Work queues of the persistent grid: one counter per XCD, kQueueStride ints
+// apart (one per 128-byte line), over the same per-XCD slices as the static
+// mapping above: queue x holds blocks [x c, x c + c) of every head, heads in
+// order. A workgroup takes from its own XCD's queue while it lasts, then from
+// the others, so XCDs that run faster take over the last blocks of the
+// slower ones. Counters only grow (an index at or past lim means empty; a
+// workgroup that finds every queue empty has added at most 8 in all).
+// Returns x * lim + index, or -1 once every queue is empty.
+__device__ __forceinline__ int take_item(int* ctr, int lim) {
+  const int x = blockIdx.x & 7;
+  int code = -1;
+  for (int y = 0; y < 8 && code < 0; ++y) {
+    const int z = (x + y) & 7;
+    const int i = atomicAdd(&ctr[z * kQueueStride], 1);
+    if (i < lim) code = z * lim + i;
+  }
+  return code;
+}
+
+__global__ void k_clear_queues(int* ctr) {
+  if (threadIdx.x < 8) ctr[threadIdx.x * kQueueStride] = 0;
 }
 
 // Whether query block b (positions [b B_q, b B_q + B_q)) holds a probe
@@ -291,7 +316,7 @@ template <int D, int BQ, int MODE>
 __global__ __launch_bounds__(BQ * 2)
 __attribute__((amdgpu_waves_per_eu(BQ == 128 ? (tile_keys<MODE>() == 32 ? 3 : 2) : 1,
                                    BQ == 128 ? (tile_keys<MODE>() == 32 ? 3 : 2) : 1)))
-void k_attn_mfma(AttnArgs a) {
+void k_attn_mfma(AttnArgs args) {
   constexpr int KT = tile_keys<MODE>();
   using TG = TileGeom<D, KT>;
   constexpr int NT = BQ * 2;
@@ -321,11 +346,38 @@ void k_attn_mfma(AttnArgs a) {
   char* const lds_k1 = lds_s1;
   char* const lds_v1 = lds_s1 + TG::KBYTES;
 
+  __shared__ int s_item;
+  // One item (query block, or probe split) per trip. With work queues the grid
+  // is persistent and loops until they are empty; without, each workgroup runs
+  // the item its id names.
+  const bool queued = MODE != ATTN_PROBE && args.qctr != nullptr;
+  for (int trip = 0;; ++trip) {
+  // The arguments are re-read on each trip, through an offset the compiler
+  // cannot prove zero, so that no value derived from them is held from one
+  // item to the next (it would not fit the register budget).
+  int kz = 0;
+  asm volatile("" : "+s"(kz));
+  const AttnArgs a = *(const AttnArgs*)((const char*)__builtin_amdgcn_kernarg_segment_ptr() + kz);
   const int nqb = MODE == ATTN_PROBE ? (a.m + BQ - 1) / BQ : a.nb;
-  const Item it = decode_item<MODE>(a, nqb);
-  if (it.h >= a.H) return;
+  Item it;
+  if (queued) {
+    __syncthreads();   // every wave is done with the previous item's LDS and s_item
+    if (threadIdx.x == 0) s_item = take_item(a.qctr, a.xcd_chunk * a.H);
+    __syncthreads();
+    const int code = s_item;
+    if (code < 0) break;
+    const int lim = a.xcd_chunk * a.H, x = code / lim, i = code - x * lim;
+    it.h = i / a.xcd_chunk;
+    it.b = x * a.xcd_chunk + i % a.xcd_chunk;
+    it.sp = 0;
+    if (it.b >= nqb) continue;   // padding slot of the last slice
+  } else {
+    if (trip > 0) break;
+    it = decode_item<MODE>(a, nqb);
+    if (it.h >= a.H) break;
+  }
   if (MODE == ATTN_SPARSE && a.subset != 0 && block_has_probe(it.b, a.N, a.m, BQ) != (a.subset == 1))
-    return;
+    continue;
   const int t = threadIdx.x;
   const int lane = t & 63;
   const int w = __builtin_amdgcn_readfirstlane(t >> 6);   // uniform across the wave
@@ -473,7 +525,7 @@ void k_attn_mfma(AttnArgs a) {
   const float l_tot = l_run + __shfl_xor(l_run, 32);
   const float inv = l_tot > 0.f ? 1.0f / l_tot : 0.f;
   const float lse = l_tot > 0.f ? (m_run + log2f(l_tot)) * kLn2 : -__builtin_inff();
-  if (!qvalid) return;
+  if (qvalid) {
   if (MODE == ATTN_PROBE) {
     float* op = a.opart + (((size_t)it.h * a.nsplit + it.sp) * a.m + qpos) * D;
 #pragma unroll
@@ -519,6 +571,8 @@ void k_attn_mfma(AttnArgs a) {
   if (MODE != ATTN_PROBE) {
     if (hl == 0 && a.lse != nullptr) a.lse[(size_t)it.h * a.N + qpos] = lse;
   }
+  }  // qvalid
+  }  // trips
 }
 
 // fp32 path: 64 query rows per workgroup, 4 lanes per query (dims 4u + lane%4),
@@ -662,6 +716,44 @@ __global__ void k_probe_merge(const float* opart, const float* lsepart, int m, i
   O_probe[((size_t)h * m + i) * D + e] = wsum > 0.f ? acc / wsum : 0.f;
 }
 
+// Workgroups of a kernel that the current device holds at once (0 if the
+// runtime cannot say), looked up once per device.
+template <typename Kernel>
+static int resident_workgroups(Kernel kernel, int threads) {
+  static std::atomic<int> cache[16];
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return 0;
+  if (dev < 16) {
+    const int c = cache[dev].load(std::memory_order_relaxed);
+    if (c > 0) return c;
+  }
+  int cus = 0, per = 0;
+  if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
+      hipOccupancyMaxActiveBlocksPerMultiprocessor(&per, kernel, threads, 0) != hipSuccess)
+    return 0;
+  const int n = cus * per;
+  if (dev < 16 && n > 0) cache[dev].store(n, std::memory_order_relaxed);
+  return n;
+}
+
+// Matrix-core launch. With work queues the grid is the resident workgroup
+// count (at most one per item) and the queues are cleared first on the same
+// stream; without, one workgroup per item.
+template <int D, int BQ, int MODE>
+static void launch_mfma(AttnArgs aa, int items, hipStream_t st) {
+  int grid = items;
+  if (aa.qctr != nullptr) {
+    const int res = resident_workgroups(k_attn_mfma<D, BQ, MODE>, BQ * 2);
+    if (res > 0) {
+      k_clear_queues<<<1, 64, 0, st>>>(aa.qctr);
+      grid = items < res ? items : res;
+    } else {
+      aa.qctr = nullptr;
+    }
+  }
+  k_attn_mfma<D, BQ, MODE><<<grid, BQ * 2, 0, st>>>(aa);
+}
+
 hipError_t launch_attention(const Dims& d, AttnMode mode, const AttnArgs& a, hipStream_t st) {
   const int nqb = mode == ATTN_PROBE ? (d.m + d.BQ - 1) / d.BQ : (d.N + d.BQ - 1) / d.BQ;
   int items = (mode == ATTN_PROBE ? nqb * d.nsplit : nqb) * d.H;
@@ -670,15 +762,17 @@ hipError_t launch_attention(const Dims& d, AttnMode mode, const AttnArgs& a, hip
   aa.xcd_chunk = 0;
   if (d.bf16) {
     if (mode != ATTN_PROBE) {
-      // head-synchronous XCD mapping (padding dispatches exit at once)
+      // head-synchronous XCD mapping (padding items exit at once)
       aa.xcd_chunk = (nqb + 7) / 8;
       items = 8 * aa.xcd_chunk * d.H;
+    } else {
+      aa.qctr = nullptr;
     }
-#define SPR_MFMA(DD, BB)                                                                    \
-  do {                                                                                      \
-    if (mode == ATTN_SPARSE) k_attn_mfma<DD, BB, ATTN_SPARSE><<<items, BB * 2, 0, st>>>(aa); \
-    else if (mode == ATTN_DENSE) k_attn_mfma<DD, BB, ATTN_DENSE><<<items, BB * 2, 0, st>>>(aa); \
-    else k_attn_mfma<DD, BB, ATTN_PROBE><<<items, BB * 2, 0, st>>>(aa);                     \
+#define SPR_MFMA(DD, BB)                                                   \
+  do {                                                                     \
+    if (mode == ATTN_SPARSE) launch_mfma<DD, BB, ATTN_SPARSE>(aa, items, st); \
+    else if (mode == ATTN_DENSE) launch_mfma<DD, BB, ATTN_DENSE>(aa, items, st); \
+    else launch_mfma<DD, BB, ATTN_PROBE>(aa, items, st);                  \
   } while (0)
     if (d.D == 128) {
       if (d.BQ == 128) SPR_MFMA(128, 128); else SPR_MFMA(128, 64);

@@ -99,7 +99,11 @@ struct AttnArgs {
   float* lsepart;              // probe: [H, nsplit, m]
   int xcd_chunk;               // > 0: head-synchronous XCD mapping with this many blocks per XCD
   int subset;                  // sparse: 0 all blocks, 1 blocks holding a probe row, 2 the others
+  int* qctr;                   // sparse / dense, bf16: 8 work-queue counters kQueueStride ints
+                               // apart (persistent grid), or null (one item per workgroup)
 };
+// Spacing of the attention's work-queue counters (ints): one per 128-byte line.
+constexpr int kQueueStride = 32;
 hipError_t launch_attention(const Dims& d, AttnMode mode, const AttnArgs& a, hipStream_t st);
 hipError_t launch_probe_merge(const Dims& d, const float* opart, const float* lsepart,
                               float* O_probe, hipStream_t st);

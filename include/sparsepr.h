@@ -65,8 +65,13 @@ extern "C" {
 #endif
 
 /* 2: S_out has the element type `dtype` (fp32 on both paths in 1); the
-   probe rows' sparse outputs go to S_probe (fp32), which stage 4 reads */
-#define SPARSEPR_ABI_VERSION 2
+   probe rows' sparse outputs go to S_probe (fp32), which stage 4 reads.
+   3: sparsepr_attend, sparsepr_attend_subset and sparsepr_dense_attention
+   take an optional work-queue buffer (queue, queue_bytes) before `stream`. */
+#define SPARSEPR_ABI_VERSION 3
+
+/* Bytes of the optional work-queue buffer of the attention entry points. */
+#define SPARSEPR_QUEUE_BYTES 1024
 
 /* status codes */
 #define SPARSEPR_OK 0
@@ -226,12 +231,24 @@ int32_t sparsepr_route(const sparsepr_params* params, const void* Q, const float
  * Outputs: S_out [H,N,d] dtype in QUERY ORDER; S_probe [H,m,d] fp32, row i =
  *          S_out at probe position p_i (stage 4) before rounding to dtype
  *          (may be NULL when m = 0); lse [H,N] fp32 (query order).
+ * Work queue (optional): queue = SPARSEPR_QUEUE_BYTES of 4-byte aligned
+ *          device memory, or NULL. On the bf16 path the call then keeps only
+ *          as many workgroups as the GPU holds at once and they take query
+ *          blocks from per-XCD counters in `queue`, so that faster XCDs take
+ *          over the last blocks of slower ones; with NULL each block gets its
+ *          own workgroup on a fixed XCD. The results are the same bit for bit
+ *          either way (each block is computed the same way wherever it runs).
+ *          The call clears the counters itself (with a kernel on `stream`)
+ *          and their contents afterwards mean nothing. Calls that may run at
+ *          the same time need distinct queue buffers; the fp32 path ignores it.
+ *          Errors: SPARSEPR_ERR_INVALID_ARG for a misaligned queue,
+ *          SPARSEPR_ERR_WORKSPACE for queue_bytes < SPARSEPR_QUEUE_BYTES.
  */
 int32_t sparsepr_attend(const sparsepr_params* params, const void* Q, const void* Kp,
                         const void* Vp, const float* scale, const int32_t* group_off,
                         const int32_t* query_perm, const int32_t* block_ptr,
                         const int32_t* block_groups, void* S_out, float* S_probe, float* lse,
-                        void* stream);
+                        void* queue, size_t queue_bytes, void* stream);
 
 /*
  * Stage 3 on a subset of the query blocks, so that the probe fit can start
@@ -253,7 +270,8 @@ int32_t sparsepr_attend_subset(const sparsepr_params* params, const void* Q, con
                                const void* Vp, const float* scale, const int32_t* group_off,
                                const int32_t* query_perm, const int32_t* block_ptr,
                                const int32_t* block_groups, void* S_out, float* S_probe,
-                               float* lse, int32_t subset, void* stream);
+                               float* lse, int32_t subset, void* queue, size_t queue_bytes,
+                               void* stream);
 
 /*
  * Stage 4 - exact probe rows and the probe-fitted map (arxivdaily 2608.18484,
@@ -378,11 +396,12 @@ int32_t sparsepr_support_stats(const sparsepr_params* params, int32_t head, cons
  * (arxivdaily 2608.18484, English abstract: speedups are over dense
  * attention). O[q] = softmax(tau q K^T) V, lse[q] = log sum exp(tau q K^T),
  * token order. Uses only heads, n_tokens, head_dim, dtype and q_block from
- * params. lse may be NULL. Needs no workspace.
+ * params. lse may be NULL. Needs no workspace; queue and queue_bytes as in
+ * sparsepr_attend (optional work queue, same results with or without).
  */
 int32_t sparsepr_dense_attention(const sparsepr_params* params, const void* Q, const void* K,
                                  const void* V, const float* scale, void* O, float* lse,
-                                 void* stream);
+                                 void* queue, size_t queue_bytes, void* stream);
 
 #ifdef __cplusplus
 }

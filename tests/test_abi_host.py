@@ -37,13 +37,19 @@ def test_header_declares_the_five_stages_and_helpers():
 def test_library_exports_every_declared_symbol(lib):
     for n in declared_functions():
         assert hasattr(lib, n), n
-    assert lib.sparsepr_abi_version() == 2
+    assert lib.sparsepr_abi_version() == 3
 
 
 def test_status_strings(lib):
     for code, name in binding.STATUS.items():
         assert lib.sparsepr_status_string(code).decode() == name
     assert lib.sparsepr_status_string(99).decode() == "SPARSEPR_UNKNOWN_STATUS"
+
+
+def test_queue_size_matches_header():
+    src = open(HEADER).read()
+    m = re.search(r"#define SPARSEPR_QUEUE_BYTES (\d+)", src)
+    assert m and int(m.group(1)) == binding.QUEUE_BYTES
 
 
 def test_params_struct_layout_matches_header():
@@ -138,14 +144,21 @@ def test_null_pointers_and_small_workspace_are_rejected(lib):
     # attend with no lse, then with probes but no fp32 copy of their rows
     p.partition_mode = 0
     st = lib.sparsepr_attend(ctypes.byref(p), fake, fake, fake, fake, fake, fake, fake, fake, fake,
-                             fake, None, None)
+                             fake, None, None, 0, None)
     assert st == 1 and "lse" in lib.sparsepr_last_error().decode()
     st = lib.sparsepr_attend(ctypes.byref(p), fake, fake, fake, fake, fake, fake, fake, fake, fake,
-                             None, fake, None)
+                             None, fake, None, 0, None)
     assert st == 1 and "S_probe" in lib.sparsepr_last_error().decode()
+    # the optional work queue: aligned, and at least SPARSEPR_QUEUE_BYTES
+    st = lib.sparsepr_attend(ctypes.byref(p), fake, fake, fake, fake, fake, fake, fake, fake, fake,
+                             fake, fake, fake, binding.QUEUE_BYTES - 1, None)
+    assert st == 3 and "queue" in lib.sparsepr_last_error().decode()
+    st = lib.sparsepr_attend(ctypes.byref(p), fake, fake, fake, fake, fake, fake, fake, fake, fake,
+                             fake, fake, ctypes.c_void_p(0x1002), binding.QUEUE_BYTES, None)
+    assert st == 1 and "aligned" in lib.sparsepr_last_error().decode()
     # attention on a block subset: the subset value is validated
     st = lib.sparsepr_attend_subset(ctypes.byref(p), fake, fake, fake, fake, fake, fake, fake, fake,
-                                    fake, fake, fake, 3, None)
+                                    fake, fake, fake, 3, None, 0, None)
     assert st == 1 and "subset" in lib.sparsepr_last_error().decode()
     # apply: output missing, then a workspace too small for the per-head matrix
     st = lib.sparsepr_apply(ctypes.byref(p), fake, fake, fake, fake, fake, fake, None, fake,
@@ -167,8 +180,13 @@ def test_null_pointers_and_small_workspace_are_rejected(lib):
     # dense attention validates only the shape fields
     q = binding.c_params(configs.TINY.params)
     q.head_dim = 80
-    st = lib.sparsepr_dense_attention(ctypes.byref(q), fake, fake, fake, fake, fake, None, None)
+    st = lib.sparsepr_dense_attention(ctypes.byref(q), fake, fake, fake, fake, fake, None, None, 0,
+                                      None)
     assert st == 2
+    q.head_dim = 128
+    st = lib.sparsepr_dense_attention(ctypes.byref(q), fake, fake, fake, fake, fake, None, fake, 16,
+                                      None)
+    assert st == 3 and "queue" in lib.sparsepr_last_error().decode()
 
 
 def test_index_validation_in_binding():

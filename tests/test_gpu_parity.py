@@ -794,6 +794,35 @@ def test_attend_block_subsets_compose():
     assert torch.equal(b.S_probe, full_Sp)
 
 
+@pytest.mark.parametrize("name", ["bf16_d128", "bf16_d64_bq64", "many_blocks"])
+def test_work_queue_equals_static_blocks(name):
+    """The attention with its work queues (a persistent grid taking query blocks
+    from per-XCD counters) writes exactly what one workgroup per block writes,
+    and so does dense attention; two calls in a row share one queue buffer.
+    "many_blocks" (6 heads, N = 29280: 1392 queue slots, 18 of them padding)
+    has more blocks than the GPU holds workgroups, so workgroups take several."""
+    if name == "many_blocks":
+        r = run_pipeline(small_bf16(name="queue_many", grid=(16, 30, 61), heads=6, seed=29),
+                         dbg=False)
+    else:
+        r = get_run(name)
+    p, b = r.p, r.b
+    print(f"[queue] {name}: H={p.heads} N={p.n_tokens} B_q={p.q_block}", flush=True)
+    ref = {n: getattr(b, n).clone() for n in ("S", "S_probe", "lse")}   # the queue is the default
+    for use_queue in (False, True, True):
+        for n in ref:
+            getattr(b, n).fill_(float("nan"))
+        binding.attend(p, r.Q, r.scale, b, use_queue=use_queue)
+        torch.cuda.synchronize()
+        for n, t in ref.items():
+            assert torch.equal(getattr(b, n), t), (use_queue, n)
+    O0, L0 = binding.dense_attention(p, r.Q, r.K, r.V, r.scale, use_queue=False)
+    for _ in range(2):
+        O1, L1 = binding.dense_attention(p, r.Q, r.K, r.V, r.scale, queue=b.queue)
+        torch.cuda.synchronize()
+        assert torch.equal(O0, O1) and torch.equal(L0, L1)
+
+
 def test_overlapped_call_equals_serial():
     wl = WORKLOADS["bf16_d128"]
     inp = get_run("bf16_d128").inp
