@@ -15,6 +15,8 @@
 // and is read transposed with ds_read_b64_tr_b16. The key list of a block is the
 // concatenation of its routed groups' ranges in the group-contiguous Kp/Vp;
 // tiles run across group boundaries, so only the block's last tile is ragged.
+// Given the caller's work-queue counters, the sparse and dense launches are
+// persistent grids that take query blocks from per-XCD queues (take_item).
 #include <atomic>
 
 #include "common.hpp"
