@@ -354,9 +354,10 @@ void k_attn_mfma(AttnArgs args) {
   // the item its id names.
   const bool queued = MODE != ATTN_PROBE && args.qctr != nullptr;
   for (int trip = 0;; ++trip) {
-  // The arguments are re-read on each trip, through an offset the compiler
-  // cannot prove zero, so that no value derived from them is held from one
-  // item to the next (it would not fit the register budget).
+  // The arguments are re-read on each trip from the kernel-argument segment
+  // (the struct is the kernel's only argument, at offset 0), through an offset
+  // the compiler cannot prove zero, so that no value derived from them is held
+  // from one item to the next (it would not fit the register budget).
   int kz = 0;
   asm volatile("" : "+s"(kz));
   const AttnArgs a = *(const AttnArgs*)((const char*)__builtin_amdgcn_kernarg_segment_ptr() + kz);
