@@ -719,10 +719,10 @@ __global__ void k_probe_merge(const float* opart, const float* lsepart, int m, i
   O_probe[((size_t)h * m + i) * D + e] = wsum > 0.f ? acc / wsum : 0.f;
 }
 
-// Workgroups of a kernel that the current device holds at once (0 if the
-// runtime cannot say), looked up once per device.
-template <typename Kernel>
-static int resident_workgroups(Kernel kernel, int threads) {
+// Workgroups of k_attn_mfma<D, BQ, MODE> that the current device holds at once
+// (0 if the runtime cannot say), looked up once per instantiation and device.
+template <int D, int BQ, int MODE>
+static int resident_workgroups() {
   static std::atomic<int> cache[16];
   int dev = 0;
   if (hipGetDevice(&dev) != hipSuccess) return 0;
@@ -732,7 +732,8 @@ static int resident_workgroups(Kernel kernel, int threads) {
   }
   int cus = 0, per = 0;
   if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
-      hipOccupancyMaxActiveBlocksPerMultiprocessor(&per, kernel, threads, 0) != hipSuccess)
+      hipOccupancyMaxActiveBlocksPerMultiprocessor(&per, k_attn_mfma<D, BQ, MODE>, BQ * 2, 0) !=
+          hipSuccess)
     return 0;
   const int n = cus * per;
   if (dev < 16 && n > 0) cache[dev].store(n, std::memory_order_relaxed);
@@ -746,7 +747,7 @@ template <int D, int BQ, int MODE>
 static void launch_mfma(AttnArgs aa, int items, hipStream_t st) {
   int grid = items;
   if (aa.qctr != nullptr) {
-    const int res = resident_workgroups(k_attn_mfma<D, BQ, MODE>, BQ * 2);
+    const int res = resident_workgroups<D, BQ, MODE>();
     if (res > 0) {
       k_clear_queues<<<1, 64, 0, st>>>(aa.qctr);
       grid = items < res ? items : res;
