@@ -41,7 +41,7 @@ class CParams(ctypes.Structure):
                 ("q_block", _c_i32), ("n_groups", _c_i32), ("n_samples", _c_i32),
                 ("kmeans_iters", _c_i32), ("density", ctypes.c_double), ("n_probes", _c_i32),
                 ("rank", _c_i32), ("ridge_lambda", ctypes.c_double), ("partition_mode", _c_i32),
-                ("reserved", _c_i32)]
+                ("reserved", _c_i32), ("probe_pos", ctypes.c_void_p)]
 
 
 class SparsePRError(RuntimeError):
@@ -84,7 +84,7 @@ def load(path: Optional[str] = None) -> ctypes.CDLL:
                  "sparsepr_probe_fit", "sparsepr_apply", "sparsepr_apply_noalloc",
                  "sparsepr_dense_attention"):
         getattr(lib, name).restype = _c_i32
-    if lib.sparsepr_abi_version() != 3:
+    if lib.sparsepr_abi_version() != 4:
         raise RuntimeError("libsparsepr ABI version mismatch")
     _LIB = lib
     return lib
@@ -100,10 +100,13 @@ def _check(status: int) -> None:
         raise SparsePRError(status, msg)
 
 
-def c_params(p: Params) -> CParams:
+def c_params(p: Params, probe_pos: Optional[torch.Tensor] = None) -> CParams:
+    """The C params struct; probe_pos is the call's device array of probe
+    positions (from probe_positions_tensor) or None for the default rule."""
     return CParams(p.heads, p.n_tokens, p.head_dim, SPARSEPR_BF16 if p.dtype == "bf16" else SPARSEPR_F32,
                    p.q_block, p.n_groups, p.n_samples, p.kmeans_iters, float(p.density), p.n_probes,
-                   p.rank, float(p.ridge_lambda), p.partition_mode, 0)
+                   p.rank, float(p.ridge_lambda), p.partition_mode, 0,
+                   None if probe_pos is None else probe_pos.data_ptr())
 
 
 def _ptr(t: Optional[torch.Tensor]):
@@ -149,6 +152,16 @@ def index_tensor(a, n: int, length: int, name: str, device, distinct: bool = Fal
     return torch.from_numpy(arr.astype(np.int32)).to(device)
 
 
+def probe_positions_tensor(positions, p: Params, device) -> torch.Tensor:
+    """Check caller-chosen probe positions on the host (m entries, strictly
+    increasing, in [0, N)) and upload them for Buffers.probe_pos."""
+    arr = np.asarray(positions.cpu().numpy() if isinstance(positions, torch.Tensor) else positions)
+    arr = arr.astype(np.int64).ravel()
+    if arr.size and np.any(np.diff(arr) <= 0):
+        raise ValueError("probe positions must be strictly increasing")
+    return index_tensor(arr, p.n_tokens, p.n_probes, "probe positions", device)
+
+
 @dataclass
 class Buffers:
     """Every device buffer of one call; reused across calls of the same shape."""
@@ -178,6 +191,8 @@ class Buffers:
     query_order: Optional[torch.Tensor] = None
     query_group_off: Optional[torch.Tensor] = None
     query_centroid: Optional[torch.Tensor] = None
+    # caller-chosen probe positions [m] (int32), or None for floor((i + 1/2) N / m)
+    probe_pos: Optional[torch.Tensor] = None
 
 
 def alloc_buffers(p: Params, device) -> Buffers:
@@ -254,7 +269,7 @@ def attend(p: Params, Q, scale, b: Buffers, subset: int = BLOCKS_ALL,
            use_queue: bool = True) -> None:
     """Stage 3; use_queue=False deals the blocks out statically (same results)."""
     lib = load()
-    cp = c_params(p)
+    cp = c_params(p, b.probe_pos)
     args = (ctypes.byref(cp), _ptr(Q), _ptr(b.Kp), _ptr(b.Vp), _ptr(scale), _ptr(b.group_off),
             _ptr(b.query_perm), _ptr(b.block_ptr), _ptr(b.block_groups), _ptr(b.S),
             _ptr(b.S_probe), _ptr(b.lse))
@@ -267,7 +282,7 @@ def attend(p: Params, Q, scale, b: Buffers, subset: int = BLOCKS_ALL,
 
 def probe_fit(p: Params, Q, scale, b: Buffers, K=None, V=None) -> None:
     lib = load()
-    cp = c_params(p)
+    cp = c_params(p, b.probe_pos)
     K = b.Kp if K is None else K
     V = b.Vp if V is None else V
     _check(lib.sparsepr_probe_fit(
@@ -278,7 +293,7 @@ def probe_fit(p: Params, Q, scale, b: Buffers, K=None, V=None) -> None:
 
 def apply(p: Params, b: Buffers) -> None:
     lib = load()
-    cp = c_params(p)
+    cp = c_params(p, b.probe_pos)
     _check(lib.sparsepr_apply(
         ctypes.byref(cp), _ptr(b.S), _ptr(b.query_perm), _ptr(b.O_probe), _ptr(b.U),
         _ptr(b.Theta), _ptr(b.rank_eff), _ptr(b.O), _ptr(b.workspace), b.workspace.numel(),
@@ -289,7 +304,7 @@ def apply_noalloc(p: Params, b: Buffers, O=None) -> torch.Tensor:
     """Stage 5 through the entry point that uses the library's fixed scratch
     instead of the workspace; writes O (default: b.O)."""
     lib = load()
-    cp = c_params(p)
+    cp = c_params(p, b.probe_pos)
     O = b.O if O is None else O
     _check(lib.sparsepr_apply_noalloc(
         ctypes.byref(cp), _ptr(b.S), _ptr(b.query_perm), _ptr(b.O_probe), _ptr(b.U),

@@ -139,6 +139,7 @@ static int32_t make_dims(const sparsepr_params* p, bool full, Dims* d) {
   d->gbits = 0;
   d->nsplit = 1;
   d->split_len = d->N;
+  d->ppos = nullptr;
   if (!full) return SPARSEPR_OK;
   if (p->reserved != 0) return fail(SPARSEPR_ERR_INVALID_ARG, "reserved must be 0");
   if (p->partition_mode != SPARSEPR_RESPONSE_COUPLED && p->partition_mode != SPARSEPR_RANDOM_BLOCK &&
@@ -169,6 +170,7 @@ static int32_t make_dims(const sparsepr_params* p, bool full, Dims* d) {
   d->S = p->n_samples;
   d->T = p->kmeans_iters;
   d->m = p->n_probes;
+  d->ppos = d->m > 0 ? p->probe_pos : nullptr;   // device array, not read here
   d->k = p->rank;
   d->mode = p->partition_mode;
   d->rho = p->density;
@@ -381,6 +383,7 @@ int32_t sparsepr_attend_subset(const sparsepr_params* params, const void* Q, con
   a.H = d.H;
   a.N = d.N;
   a.m = d.m;
+  a.ppos = d.ppos;
   a.nsplit = 1;
   a.split_len = d.N;
   a.G = d.G;
@@ -511,6 +514,7 @@ int32_t sparsepr_probe_fit(const sparsepr_params* params, const void* Q, const v
     a.H = d.H;
     a.N = d.N;
     a.m = d.m;
+  a.ppos = d.ppos;
     a.nsplit = d.nsplit;
     a.split_len = d.split_len;
     a.G = d.G;

@@ -21,7 +21,8 @@ template <bool BF16, int D>
 __global__ __launch_bounds__(256) void k_apply(const float* S, const int32_t* query_perm,
                                                const float* O_probe, const float* U,
                                                const float* Theta, const int32_t* rank_eff,
-                                               int N, int m, int kmax, void* Ov) {
+                                               const int32_t* ppos, int N, int m, int kmax,
+                                               void* Ov) {
   using E = Elt<BF16>;
   constexpr int EPT = D / 16;          // output elements per thread (contiguous)
   constexpr int CH = kApplyChunk;
@@ -107,7 +108,7 @@ __global__ __launch_bounds__(256) void k_apply(const float* S, const int32_t* qu
     if (r >= nrow) continue;
     const int pos = p0 + r;
     const int tok = clamp_idx(query_perm[(size_t)h * N + pos], N);
-    const int pi = probe_index(pos, N, m);
+    const int pi = probe_index(ppos, pos, N, m);
     float v[EPT];
     if (pi >= 0) {
       const float* op = O_probe + ((size_t)h * m + pi) * D + EPT * cg;
@@ -209,8 +210,8 @@ __global__ __launch_bounds__(256) void k_apply_weights(const float* U, const flo
 template <int D>
 __global__ __launch_bounds__(kApplyWaves * 64) void k_apply_mfma(const uint16_t* S, const int32_t* query_perm,
                                                     const float* O_probe, const uint16_t* wt,
-                                                    const float* bias, int N, int m,
-                                                    int wg_per_head, uint16_t* O) {
+                                                    const float* bias, const int32_t* ppos,
+                                                    int N, int m, int wg_per_head, uint16_t* O) {
   constexpr int WP = D + 8;            // bf16 elements per LDS row of W^T (conflict-free b128 reads)
   constexpr int NKK = D / 16, NDT = D / 32;
   constexpr int CPR = D / 8;           // 16-byte chunks per row
@@ -261,7 +262,7 @@ __global__ __launch_bounds__(kApplyWaves * 64) void k_apply_mfma(const uint16_t*
     // token of this lane's row, read early; the store loop takes each row's
     // token from the lane that owns the row
     const int tok = valid ? clamp_idx(query_perm[(size_t)h * N + pos], N) : 0;
-    const int pi = valid ? probe_index(pos, N, m) : -1;
+    const int pi = valid ? probe_index(ppos, pos, N, m) : -1;
     // W fragments are re-read from LDS every tile: kept opaque so that the
     // compiler does not hoist all of them into registers (occupancy)
     int woff = ql * WP + 8 * hl;
@@ -371,19 +372,19 @@ hipError_t launch_apply(const Dims& d, const void* S_out, const int32_t* query_p
     const uint16_t* Sb = static_cast<const uint16_t*>(S_out);
     if (d.D == 128) {
       k_apply_weights<128><<<d.H, 256, 0, st>>>(U, Theta, rank_eff, d.k, wt, bias);
-      k_apply_mfma<128><<<d.H * wgph, kApplyWaves * 64, 0, st>>>(Sb, query_perm, O_probe, wt, bias, d.N,
-                                                    d.m, wgph, Ob);
+      k_apply_mfma<128><<<d.H * wgph, kApplyWaves * 64, 0, st>>>(Sb, query_perm, O_probe, wt, bias,
+                                                                 d.ppos, d.N, d.m, wgph, Ob);
     } else {
       k_apply_weights<64><<<d.H, 256, 0, st>>>(U, Theta, rank_eff, d.k, wt, bias);
-      k_apply_mfma<64><<<d.H * wgph, kApplyWaves * 64, 0, st>>>(Sb, query_perm, O_probe, wt, bias, d.N,
-                                                   d.m, wgph, Ob);
+      k_apply_mfma<64><<<d.H * wgph, kApplyWaves * 64, 0, st>>>(Sb, query_perm, O_probe, wt, bias,
+                                                                d.ppos, d.N, d.m, wgph, Ob);
     }
     return hipGetLastError();
   }
   const dim3 grid((d.N + kApplyRows - 1) / kApplyRows, d.H);
 #define SPR_APPLY(B, DD)                                                                   \
   k_apply<B, DD><<<grid, 256, 0, st>>>(static_cast<const float*>(S_out), query_perm, O_probe, \
-                                        U, Theta, rank_eff, d.N, \
+                                        U, Theta, rank_eff, d.ppos, d.N, \
                                         d.m, d.k, O)
   if (d.D == 128) SPR_APPLY(false, 128); else SPR_APPLY(false, 64);
 #undef SPR_APPLY

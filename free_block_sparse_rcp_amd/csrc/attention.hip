@@ -113,12 +113,16 @@ __global__ void k_clear_queues(int* ctr) {
 }
 
 // Whether query block b (positions [b B_q, b B_q + B_q)) holds a probe
-// position p_i = floor((2i + 1) N / (2m)): the first probe at or after the
-// block start is i0 = ceil((2m lo - N) / (2N)).
-__device__ __forceinline__ bool block_has_probe(int b, int N, int m, int BQ) {
+// position: the caller's first position at or after the block start, or for
+// p_i = floor((2i + 1) N / (2m)) the first such probe i0 = ceil((2m lo - N) / (2N)).
+__device__ __forceinline__ bool block_has_probe(const int32_t* ppos, int b, int N, int m, int BQ) {
   if (m <= 0) return false;
   const int64_t lo = (int64_t)b * BQ;
   const int64_t hi = lo + BQ < N ? lo + BQ : N;
+  if (ppos != nullptr) {
+    const int i = probe_lower_bound(ppos, (int)lo, N, m);
+    return i < m && clamp_idx(ppos[i], N) < hi;
+  }
   const int64_t num = 2LL * m * lo - N;
   const int64_t i0 = num <= 0 ? 0 : (num + 2LL * N - 1) / (2LL * N);
   if (i0 >= m) return false;
@@ -134,7 +138,7 @@ __device__ __forceinline__ int query_token(const AttnArgs& a, const Item& it, in
     *valid = pi < a.m;
     *pos = pi;
     if (!*valid) return 0;
-    const int p = (int)(((2LL * pi + 1) * a.N) / (2LL * a.m));
+    const int p = probe_position(a.ppos, pi, a.N, a.m);
     return clamp_idx(a.query_perm[(size_t)it.h * a.N + p], a.N);
   }
   const int p = it.b * BQ + qi;
@@ -379,7 +383,7 @@ void k_attn_mfma(AttnArgs args) {
     it = decode_item<MODE>(a, nqb);
     if (it.h >= a.H) break;
   }
-  if (MODE == ATTN_SPARSE && a.subset != 0 && block_has_probe(it.b, a.N, a.m, BQ) != (a.subset == 1))
+  if (MODE == ATTN_SPARSE && a.subset != 0 && block_has_probe(a.ppos, it.b, a.N, a.m, BQ) != (a.subset == 1))
     continue;
   const int t = threadIdx.x;
   const int lane = t & 63;
@@ -557,7 +561,7 @@ void k_attn_mfma(AttnArgs args) {
         *reinterpret_cast<bf16x4*>(out + d0) = bv;
       }
     // a probe position's row also goes out unrounded, for the fit
-    const int pi = MODE == ATTN_SPARSE && a.sprobe != nullptr ? probe_index(qpos, a.N, a.m) : -1;
+    const int pi = MODE == ATTN_SPARSE && a.sprobe != nullptr ? probe_index(a.ppos, qpos, a.N, a.m) : -1;
     if (pi >= 0) {
       float* sp = a.sprobe + ((size_t)it.h * a.m + pi) * D;
 #pragma unroll
@@ -607,7 +611,7 @@ __global__ __launch_bounds__(256) void k_attn_valu(AttnArgs a, int BQ) {
     it.b = L % nqb;
     it.sp = 0;
   }
-  if (MODE == ATTN_SPARSE && a.subset != 0 && block_has_probe(it.b, a.N, a.m, BQ) != (a.subset == 1))
+  if (MODE == ATTN_SPARSE && a.subset != 0 && block_has_probe(a.ppos, it.b, a.N, a.m, BQ) != (a.subset == 1))
     return;
   const int t = threadIdx.x;
   const int qq = t & 3;
@@ -627,7 +631,7 @@ __global__ __launch_bounds__(256) void k_attn_valu(AttnArgs a, int BQ) {
     qvalid = pi < a.m;
     qpos = pi;
     qtok = qvalid ? clamp_idx(a.query_perm[(size_t)it.h * a.N +
-                                           (int)(((2LL * pi + 1) * a.N) / (2LL * a.m))], a.N) : 0;
+                                           probe_position(a.ppos, pi, a.N, a.m)], a.N) : 0;
   } else {
     qpos = it.b * BQ + qi;
     qvalid = qpos < a.N;
@@ -693,7 +697,7 @@ __global__ __launch_bounds__(256) void k_attn_valu(AttnArgs a, int BQ) {
     for (int u = 0; u < DU; ++u) out[4 * u + qq] = o[u] * inv;
     if (qq == 0 && a.lse != nullptr) a.lse[(size_t)it.h * a.N + qpos] = lse;
     // a probe position's row also goes to the fit's copy
-    const int pi = MODE == ATTN_SPARSE && a.sprobe != nullptr ? probe_index(qpos, a.N, a.m) : -1;
+    const int pi = MODE == ATTN_SPARSE && a.sprobe != nullptr ? probe_index(a.ppos, qpos, a.N, a.m) : -1;
     if (pi >= 0) {
       float* sp = a.sprobe + ((size_t)it.h * a.m + pi) * D;
 #pragma unroll

@@ -58,6 +58,25 @@ __device__ __forceinline__ uint32_t float_order_bits(float f) {
 // Key that sorts floats in DESCENDING order when sorted ascending.
 __device__ __forceinline__ uint32_t float_desc_bits(float f) { return ~float_order_bits(f); }
 
+// Query position of probe i < m: ppos[i] (clamped into [0, N)) when the
+// caller gave positions, else floor((2 i + 1) N / (2 m)).
+__device__ __forceinline__ int probe_position(const int32_t* ppos, int i, int N, int m) {
+  if (ppos != nullptr) return clamp_idx(ppos[i], N);
+  return (int)(((2LL * i + 1) * N) / (2LL * m));
+}
+
+// Lowest i < m whose given position is >= pos (m if none): binary search over
+// the caller's increasing positions; every read stays inside [0, m).
+__device__ __forceinline__ int probe_lower_bound(const int32_t* ppos, int pos, int N, int m) {
+  int lo = 0, hi = m;
+  while (lo < hi) {
+    const int mid = (lo + hi) >> 1;
+    if (clamp_idx(ppos[mid], N) < pos) lo = mid + 1;
+    else hi = mid;
+  }
+  return lo;
+}
+
 // Index i of the probe at query position pos (probe i sits at
 // floor((2 i + 1) N / (2 m))), or -1 when pos holds no probe.
 __device__ __forceinline__ int probe_index(int pos, int N, int m) {
@@ -68,6 +87,14 @@ __device__ __forceinline__ int probe_index(int pos, int N, int m) {
     if ((int)(((2 * i + 1) * N) / (2LL * m)) == pos) return (int)i;
   }
   return -1;
+}
+
+// The same with the caller's positions when ppos is not null.
+__device__ __forceinline__ int probe_index(const int32_t* ppos, int pos, int N, int m) {
+  if (ppos == nullptr) return probe_index(pos, N, m);
+  if (m <= 0) return -1;
+  const int i = probe_lower_bound(ppos, pos, N, m);
+  return i < m && clamp_idx(ppos[i], N) == pos ? i : -1;
 }
 
 // Workgroups are dispatched round-robin over the 8 XCDs; this maps the

@@ -22,6 +22,7 @@ struct Dims {
   int gbits;      // bits needed for a group index (0 when G == 1)
   int nsplit;     // probe attention: key splits
   int split_len;  // probe attention: keys per split (multiple of 64)
+  const int32_t* ppos;  // probe positions [m] (device), or null for the default rule
 };
 
 // ---- workspace layout (byte offsets; one workspace serves every stage)
@@ -101,6 +102,7 @@ struct AttnArgs {
   int subset;                  // sparse: 0 all blocks, 1 blocks holding a probe row, 2 the others
   int* qctr;                   // sparse / dense, bf16: 8 work-queue counters kQueueStride ints
                                // apart (persistent grid), or null (one item per workgroup)
+  const int32_t* ppos;         // sparse / probe: probe positions [m], or null (default rule)
 };
 // Spacing of the attention's work-queue counters (ints): one per 128-byte line.
 constexpr int kQueueStride = 32;

@@ -67,8 +67,9 @@ extern "C" {
 /* 2: S_out has the element type `dtype` (fp32 on both paths in 1); the
    probe rows' sparse outputs go to S_probe (fp32), which stage 4 reads.
    3: sparsepr_attend, sparsepr_attend_subset and sparsepr_dense_attention
-   take an optional work-queue buffer (queue, queue_bytes) before `stream`. */
-#define SPARSEPR_ABI_VERSION 3
+   take an optional work-queue buffer (queue, queue_bytes) before `stream`.
+   4: sparsepr_params ends with an optional `probe_pos` array. */
+#define SPARSEPR_ABI_VERSION 4
 
 /* Bytes of the optional work-queue buffer of the attention entry points. */
 #define SPARSEPR_QUEUE_BYTES 1024
@@ -111,6 +112,15 @@ typedef struct sparsepr_params {
   double ridge_lambda;    /* lambda > 0: ridge penalty (bias unpenalised) */
   int32_t partition_mode; /* SPARSEPR_RESPONSE_COUPLED, SPARSEPR_RANDOM_BLOCK or SPARSEPR_SEMANTIC */
   int32_t reserved;       /* must be 0 */
+  /* Probe positions p_i in the query order, shared by every head: NULL for
+     p_i = floor((i + 1/2) N / m) (the default), or a DEVICE array of m int32
+     that the caller owns and keeps unchanged from stage 3 to stage 5 (the
+     three stages must see the same positions). It must be strictly
+     increasing with every entry in [0, N). The library does not read it on
+     the host: entries outside [0, N) are clamped into it, and an array that
+     is not strictly increasing gives unspecified outputs (every access
+     stays inside the caller's buffers). Ignored when m = 0. */
+  const int32_t* probe_pos;
 } sparsepr_params;
 
 /* Version of this ABI (SPARSEPR_ABI_VERSION). */
@@ -279,8 +289,8 @@ int32_t sparsepr_attend_subset(const sparsepr_params* params, const void* Q, con
  * dense-minus-sparse differences; skillfed article and peercurrent abstract:
  * per head, call-specific, restricted to the probe residuals' subspace).
  *
- * Probe i < m is the query at position p_i = floor((i + 1/2) N / m) of the
- * query order. o_i = dense attention of that query over all N keys; the
+ * Probe i < m is the query at position p_i of the query order:
+ * params->probe_pos[i] when given, else floor((i + 1/2) N / m). o_i = dense attention of that query over all N keys; the
  * keys may be given in any order (e.g. Kp, Vp). With s_i = S_probe[i] (the
  * sparse output at p_i, in fp32):
  *   r_i = o_i - s_i;  w_i = ||o_i||^-2 / sum ||o||^-2 (0 where o_i = 0);

@@ -499,7 +499,7 @@ class HeadResult:
 
 def sparsepr_head(Q, K, V, scale, *, q_block, n_groups, kmeans_iters, density, n_probes,
                   rank, ridge_lambda, sample_idx=None, init_idx=None, partition_mode=0,
-                  rand_key_perm=None, rand_query_perm=None, keep_scores=False):
+                  rand_key_perm=None, rand_query_perm=None, keep_scores=False, probe_pos=None):
     """The whole operator for one head, in the pages' order ([AD]).
 
     1. keys: response profiles under the sampled queries, k-means, paired K/V
@@ -514,6 +514,9 @@ def sparsepr_head(Q, K, V, scale, *, q_block, n_groups, kmeans_iters, density, n
        sparse outputs' subspace coordinates (and a bias);
     6. add the predicted residual to unprobed rows; probes keep their exact
        output.
+
+    probe_pos: the probe positions in the query order (strictly increasing,
+    in [0, N)); None takes floor((i + 1/2) N / m).
     """
     Q = np.asarray(Q, F64)
     K = np.asarray(K, F64)
@@ -547,7 +550,13 @@ def sparsepr_head(Q, K, V, scale, *, q_block, n_groups, kmeans_iters, density, n
     bptr, bgrp = route(sigma, sizes, kappa)
     ksets = block_key_sets(bptr, bgrp, key_perm, group_off)
     S, lse = sparse_attention(Q, K, V, scale, blocks, ksets)
-    ppos = probe_positions(n, n_probes)
+    if probe_pos is None:
+        ppos = probe_positions(n, n_probes)
+    else:
+        ppos = np.asarray(probe_pos, np.int64).ravel()
+        if ppos.size != n_probes or (ppos.size and (ppos[0] < 0 or ppos[-1] >= n
+                                                    or np.any(np.diff(ppos) <= 0))):
+            raise ValueError("probe_pos must hold m strictly increasing positions in [0, N)")
     ptok = qperm[ppos]
     if n_probes > 0:
         O_p, _ = dense_attention(Q, K, V, scale, rows=ptok)

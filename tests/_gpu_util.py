@@ -55,7 +55,7 @@ def to_device(inp, p: Params, device="cuda"):
 
 
 def run_pipeline(wl: Workload, heads=None, dbg: bool = True, dbg_heads_ok: bool = True,
-                 inp=None, p: Optional[Params] = None) -> GpuRun:
+                 inp=None, p: Optional[Params] = None, probe_pos=None) -> GpuRun:
     p = p or wl.params
     inp = inp if inp is not None else wl.make_inputs(heads)
     if heads is not None:
@@ -65,6 +65,8 @@ def run_pipeline(wl: Workload, heads=None, dbg: bool = True, dbg_heads_ok: bool 
     Q, K, V, scale = to_device(inp, p)
     idx = op.upload_indices(inp.sample_idx, inp.init_idx, inp.rand_key_perm, inp.rand_query_perm)
     b = op.buffers
+    if probe_pos is not None:
+        b.probe_pos = binding.probe_positions_tensor(probe_pos, p, dev)
     H, N, G, nb = p.heads, p.n_tokens, p.n_groups, p.n_blocks
     d: Dict[str, torch.Tensor] = {}
     if dbg:

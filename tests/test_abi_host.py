@@ -5,6 +5,9 @@ import ctypes
 import os
 import re
 
+import numpy as np
+import torch
+
 import pytest
 
 from free_block_sparse_rcp_amd import binding, build, configs
@@ -37,7 +40,7 @@ def test_header_declares_the_five_stages_and_helpers():
 def test_library_exports_every_declared_symbol(lib):
     for n in declared_functions():
         assert hasattr(lib, n), n
-    assert lib.sparsepr_abi_version() == 3
+    assert lib.sparsepr_abi_version() == 4
 
 
 def test_status_strings(lib):
@@ -53,9 +56,10 @@ def test_queue_size_matches_header():
 
 
 def test_params_struct_layout_matches_header():
-    assert ctypes.sizeof(binding.CParams) == 64
+    assert ctypes.sizeof(binding.CParams) == 72
     assert binding.CParams.density.offset == 32
     assert binding.CParams.ridge_lambda.offset == 48
+    assert binding.CParams.probe_pos.offset == 64
 
 
 def _ws(lib, p):
@@ -197,3 +201,14 @@ def test_index_validation_in_binding():
         binding.index_tensor(np.array([1, 1]), 5, 2, "x", "cpu", distinct=True)
     t = binding.index_tensor(np.array([4, 0]), 5, 2, "x", "cpu", distinct=True)
     assert t.dtype.is_floating_point is False and t.tolist() == [4, 0]
+
+
+def test_probe_positions_checked_on_the_host():
+    p = configs.TINY.params
+    t = binding.probe_positions_tensor(np.arange(p.n_probes) * 3, p, "cpu")
+    assert t.dtype == torch.int32 and t.tolist() == list(range(0, 3 * p.n_probes, 3))
+    good = np.arange(p.n_probes) * 3
+    for bad in (good[:-1], np.r_[good[:-1], good[-2]], np.r_[-1, good[1:]],
+                np.r_[good[:-1], p.n_tokens], good[::-1]):
+        with pytest.raises(ValueError):
+            binding.probe_positions_tensor(bad, p, "cpu")

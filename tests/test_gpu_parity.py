@@ -75,8 +75,9 @@ def head_arrays(r, h):
     return out
 
 
-def oracle_on_gpu_indices(Q, K, V, tau, p, g):
-    """Steps after routing, in fp64, on the GPU's groups, order and routes."""
+def oracle_on_gpu_indices(Q, K, V, tau, p, g, probe_pos=None):
+    """Steps after routing, in fp64, on the GPU's groups, order and routes
+    (probe_pos: caller-chosen probe positions, None for the default rule)."""
     N = p.n_tokens
     qperm = g["query_perm"].astype(np.int64)
     blocks = orc.query_blocks(qperm, p.q_block)
@@ -84,7 +85,8 @@ def oracle_on_gpu_indices(Q, K, V, tau, p, g):
     bg = g["block_groups"][:bp[-1]].astype(np.int64)
     ksets = orc.block_key_sets(bp, bg, g["key_perm"].astype(np.int64), g["group_off"].astype(np.int64))
     S, lse = orc.sparse_attention(Q, K, V, tau, blocks, ksets)
-    ptok = qperm[orc.probe_positions(N, p.n_probes)]
+    ppos = orc.probe_positions(N, p.n_probes) if probe_pos is None else np.asarray(probe_pos)
+    ptok = qperm[ppos]
     if p.n_probes:
         Op, _ = orc.dense_attention(Q, K, V, tau, rows=ptok)
     else:

@@ -632,6 +632,54 @@ def test_step14_duplicate_of_a_probe_gets_its_exact_row():
     assert found >= 2
 
 
+def test_given_probe_positions():
+    """Caller-chosen probe positions (strictly increasing in the query order):
+    the default positions given explicitly change nothing; chosen ones put
+    the exact rows at exactly those queries, leave the pair count (m N for
+    the probes) unchanged, and place a probe by choice: with m <= k_eff + 1
+    and a vanishing penalty, an unprobed copy of a probe query in the same
+    block comes out as that probe's exact dense row; bad arrays are refused."""
+    Q, K, V = tiny_case(n=48, d=6, seed=211)
+    kw = dict(density=0.35, n_probes=5, rank=6, ridge_lambda=1e-12)
+    base, _, _ = run_head(Q, K, V, 0.8, **kw)
+    same, _, _ = run_head(Q, K, V, 0.8, probe_pos=orc.probe_positions(48, 5), **kw)
+    np.testing.assert_array_equal(same.O, base.O)
+    np.testing.assert_array_equal(same.probe_tokens, base.probe_tokens)
+    chosen = np.array([0, 3, 17, 30, 47])
+    res, _, _ = run_head(Q, K, V, 0.8, probe_pos=chosen, **kw)
+    np.testing.assert_array_equal(res.probe_tokens, res.query_perm[chosen])
+    dense, _ = orc.dense_attention(Q, K, V, 0.8, rows=res.probe_tokens)
+    np.testing.assert_array_equal(res.O[res.probe_tokens], dense)
+    assert res.executed_pairs == base.executed_pairs
+    # a duplicated query, the copy at the next position of the same block
+    found = 0
+    for a in range(48):
+        Q2 = Q.copy()
+        b = (a + 1) % 48
+        Q2[b] = Q2[a]
+        r1, _, _ = run_head(Q2, K, V, 0.8, **kw)
+        pos = np.argsort(r1.query_perm)
+        if pos[a] // 8 != pos[b] // 8:
+            continue
+        dense_a, _ = orc.dense_attention(Q2, K, V, 0.8, rows=[a])
+        if np.linalg.norm(dense_a[0] - r1.S[b]) < 1e-2:
+            continue
+        others = [q for q in range(48) if pos[q] // 8 != pos[a] // 8][:4]
+        ppos = np.sort(np.array([pos[a]] + [pos[q] for q in others]))
+        r2, _, _ = run_head(Q2, K, V, 0.8, probe_pos=ppos, **kw)
+        assert r2.U.shape[1] == 5
+        np.testing.assert_allclose(r2.O[b], dense_a[0], rtol=0, atol=1e-7)
+        np.testing.assert_allclose(r2.O[a], dense_a[0], rtol=0, atol=1e-13)
+        found += 1
+        if found == 3:
+            break
+    assert found >= 2
+    for bad in ([0, 3, 3, 30, 47], [0, 3, 17, 30, 48], [-1, 3, 17, 30, 47], [0, 3, 17, 30],
+                [3, 0, 17, 30, 47]):
+        with pytest.raises(ValueError):
+            run_head(Q, K, V, 0.8, probe_pos=np.array(bad), **kw)
+
+
 # ----------------------------------------------- P10 Lloyd, P11 CSR
 
 def test_p10_lloyd_monotone_and_valid():
