@@ -290,8 +290,9 @@ int32_t sparsepr_attend_subset(const sparsepr_params* params, const void* Q, con
  * per head, call-specific, restricted to the probe residuals' subspace).
  *
  * Probe i < m is the query at position p_i of the query order:
- * params->probe_pos[i] when given, else floor((i + 1/2) N / m). o_i = dense attention of that query over all N keys; the
- * keys may be given in any order (e.g. Kp, Vp). With s_i = S_probe[i] (the
+ * params->probe_pos[i] when given, else floor((i + 1/2) N / m).
+ * o_i = dense attention of that query over all N keys; the keys may be
+ * given in any order (e.g. Kp, Vp). With s_i = S_probe[i] (the
  * sparse output at p_i, in fp32):
  *   r_i = o_i - s_i;  w_i = ||o_i||^-2 / sum ||o||^-2 (0 where o_i = 0);
  *   Sigma = sum_i w_i r_i r_i^T;  U = eigenvectors of Sigma's k_eff largest
